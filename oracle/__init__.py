@@ -1,0 +1,259 @@
+"""Plain CPU oracle for the NVFP4 / FP8 block-scaled grouped GEMM and the MoE expert path.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  It shares no code with
+the GPU library; the arithmetic lives in ``oracle.c`` (fp64 sums, exact decode tables
+built from bit fields, nearest-search encoders, a scalar router).  This module only
+marshals numpy arrays into it and adds the few fp64 elementwise steps (combine) that
+are clearer in numpy.
+
+Every function is pinned by ``tests/test_oracle_*.py`` against brute force, closed
+forms, invariants or library routines.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_SO = os.path.join(_HERE, "liboracle.so")
+_LIB = None
+
+CFLAGS = ["-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-std=c11", "-fPIC", "-shared"]
+
+
+def build() -> str:
+    """Compile oracle.c with gcc (no fast-math, no FMA contraction) into liboracle.so."""
+    tmp = _SO + ".tmp"
+    subprocess.check_call(["gcc", *CFLAGS, _SRC, "-o", tmp, "-lm"])
+    os.replace(tmp, _SO)
+    return _SO
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_L = ctypes.c_long
+_D = ctypes.c_double
+_F = ctypes.c_float
+
+
+def _lib():
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(_SO):
+        build()
+    lib = ctypes.CDLL(_SO)
+    sig = {
+        "orc_init": (None, []),
+        "orc_e2m1_value": (_D, [_I]),
+        "orc_e4m3_value": (_D, [_I]),
+        "orc_encode_e2m1": (_I, [_D]),
+        "orc_encode_e4m3_sat": (_I, [_D]),
+        "orc_bf16_bits": (ctypes.c_uint16, [_D]),
+        "orc_bf16_value": (_D, [ctypes.c_uint16]),
+        "orc_bf16_bits_array": (None, [_P, _L, _P]),
+        "orc_encode_e2m1_array": (None, [_P, _L, _P]),
+        "orc_encode_e4m3_array": (None, [_P, _L, _P]),
+        "orc_nvfp4_row_dot": (None, [_P, _P, _L, _P, _P, _I, _I, _D, _P, _P]),
+        "orc_gemm_nvfp4_masked": (None, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _P]),
+        "orc_gemm_fp8_block": (None, [_P, _P, _P, _I, _P, _P, _I, _I, _P, _P]),
+        "orc_gemm_dense_fp8w": (None, [_P, _I, _P, _P, _I, _I, _P, _P]),
+        "orc_quantize_nvfp4": (None, [_P, _L, _I, _F, _P, _P]),
+        "orc_route_noaux": (None, [_P, _P, _I, _I, _I, _I, _I, _F, _P, _P]),
+        "orc_dispatch": (None, [_P, _I, _I, _I, _I, _P, _P]),
+        "orc_swiglu": (None, [_P, _I, _I, _P]),
+        "orc_num_threads": (_I, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    lib.orc_init()
+    _LIB = lib
+    return lib
+
+
+def _c(a, dtype):
+    """C-contiguous array of the given dtype (no copy when already so)."""
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def _p(a):
+    return a.ctypes.data_as(ctypes.c_void_p) if a is not None else None
+
+
+# ----------------------------------------------------------------------------- formats
+def e2m1_value(code: int) -> float:
+    return _lib().orc_e2m1_value(int(code))
+
+
+def e4m3_value(code: int) -> float:
+    return _lib().orc_e4m3_value(int(code))
+
+
+def e2m1_table() -> np.ndarray:
+    return np.array([e2m1_value(c) for c in range(16)])
+
+
+def e4m3_table() -> np.ndarray:
+    return np.array([e4m3_value(c) for c in range(256)])
+
+
+def encode_e2m1(v) -> np.ndarray:
+    v = _c(v, np.float64)
+    out = np.empty(v.shape, np.uint8)
+    _lib().orc_encode_e2m1_array(_p(v), v.size, _p(out))
+    return out
+
+
+def encode_e4m3_sat(v) -> np.ndarray:
+    v = _c(v, np.float64)
+    out = np.empty(v.shape, np.uint8)
+    _lib().orc_encode_e4m3_array(_p(v), v.size, _p(out))
+    return out
+
+
+def bf16_bits(v) -> np.ndarray:
+    """bf16 bit patterns (uint16) of fp64 values, rounded once to nearest even."""
+    v = _c(v, np.float64)
+    out = np.empty(v.shape, np.uint16)
+    _lib().orc_bf16_bits_array(_p(v), v.size, _p(out))
+    return out
+
+
+def bf16_value(bits) -> np.ndarray:
+    bits = _c(bits, np.uint16)
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def nvfp4_decode(codes, sf) -> np.ndarray:
+    """Decoded values dec[r, k] = e2m1(code) * e4m3(scale of k's 16-block), fp64."""
+    codes = _c(codes, np.uint8)
+    sf = _c(sf, np.uint8)
+    lo = codes & 15
+    hi = codes >> 4
+    nib = np.stack([lo, hi], axis=-1).reshape(*codes.shape[:-1], codes.shape[-1] * 2)
+    vals = e2m1_table()[nib]
+    scales = np.repeat(e4m3_table()[sf], 16, axis=-1)
+    return vals * scales
+
+
+# ----------------------------------------------------------------------------- GEMMs
+def gemm_nvfp4_masked(a, a_sf, b, b_sf, alpha, masked_m, max_m, N, K, out=None):
+    """Masked grouped NVFP4 NT GEMM.  Returns (y, s, out): y/s fp64 [G,max_m,N] (NaN in
+    rows not computed), out uint16 bf16 bits; ``out`` (if given) keeps its content in
+    rows at or beyond masked_m."""
+    lib = _lib()
+    G = len(masked_m)
+    a = _c(a, np.uint8); a_sf = _c(a_sf, np.uint8); b = _c(b, np.uint8); b_sf = _c(b_sf, np.uint8)
+    alpha = None if alpha is None else _c(alpha, np.float32)
+    mm = _c(masked_m, np.int32)
+    y = np.full((G, max_m, N), np.nan)
+    s = np.full((G, max_m, N), np.nan)
+    if out is None:
+        out = np.zeros((G, max_m, N), np.uint16)
+    else:
+        out = _c(out, np.uint16).copy()
+    lib.orc_gemm_nvfp4_masked(_p(a), _p(a_sf), _p(b), _p(b_sf), _p(alpha), _p(mm), G, max_m, N, K,
+                              _p(y), _p(s), _p(out))
+    return y, s, out
+
+
+def nvfp4_row_dot(a, a_sf, a_row, b, b_sf, K, alpha=1.0):
+    """One NVFP4 A row (row index a_row of [rows, K] codes/scales) against every row of B.
+    Returns (y, s) fp64 [nb]."""
+    lib = _lib()
+    a = _c(a, np.uint8); a_sf = _c(a_sf, np.uint8); b = _c(b, np.uint8); b_sf = _c(b_sf, np.uint8)
+    nb = b.size // (K // 2)
+    y = np.empty(nb)
+    s = np.empty(nb)
+    lib.orc_nvfp4_row_dot(_p(a), _p(a_sf), int(a_row), _p(b), _p(b_sf), nb, K, float(alpha), _p(y), _p(s))
+    return y, s
+
+
+def gemm_fp8_block(qa, sa, qb, sb, rows=None):
+    """FP8 1x128-activation / 128x128-weight block-scaled GEMM in fp64.
+    qa [Ma, K] uint8 e4m3, sa [Ma, K/128] f32, qb [N, K], sb [N/128, K/128];
+    rows selects which A rows to evaluate (default all).  Returns (y, s) [len(rows), N]."""
+    lib = _lib()
+    qa = _c(qa, np.uint8); sa = _c(sa, np.float32); qb = _c(qb, np.uint8); sb = _c(sb, np.float32)
+    N, K = qb.shape
+    r = None if rows is None else _c(rows, np.int32)
+    M = qa.shape[0] if r is None else len(r)
+    y = np.empty((M, N))
+    s = np.empty((M, N))
+    lib.orc_gemm_fp8_block(_p(qa), _p(sa), _p(r), M, _p(qb), _p(sb), N, K, _p(y), _p(s))
+    return y, s
+
+
+def gemm_dense_fp8w(a, qb, sb):
+    """Dense fp64 activations a [M, K] times FP8 128x128-block-scaled weights qb [N, K]."""
+    lib = _lib()
+    a = _c(a, np.float64); qb = _c(qb, np.uint8); sb = _c(sb, np.float32)
+    M, K = a.shape
+    N = qb.shape[0]
+    y = np.empty((M, N))
+    s = np.empty((M, N))
+    lib.orc_gemm_dense_fp8w(_p(a), M, _p(qb), _p(sb), N, K, _p(y), _p(s))
+    return y, s
+
+
+# ----------------------------------------------------------------------------- quantizer
+def quantize_nvfp4(x, g):
+    """NVFP4-quantize fp32 rows x [rows, K] with global dequant scale g (fp32).
+    Returns codes uint8 [rows, K/2], scales uint8 [rows, K/16]."""
+    lib = _lib()
+    x = _c(x, np.float32)
+    rows = x.size // x.shape[-1]
+    K = x.shape[-1]
+    codes = np.empty(x.shape[:-1] + (K // 2,), np.uint8)
+    sf = np.empty(x.shape[:-1] + (K // 16,), np.uint8)
+    lib.orc_quantize_nvfp4(_p(x), rows, K, float(np.float32(g)), _p(codes), _p(sf))
+    return codes, sf
+
+
+# ----------------------------------------------------------------------------- routing
+def route_noaux(logits, bias, n_group, topk_group, top_k, rsf):
+    lib = _lib()
+    assert top_k <= 64
+    logits = _c(logits, np.float32); bias = _c(bias, np.float32)
+    T, E = logits.shape
+    ids = np.empty((T, top_k), np.int32)
+    w = np.empty((T, top_k), np.float32)
+    lib.orc_route_noaux(_p(logits), _p(bias), T, E, n_group, topk_group, top_k, float(rsf), _p(ids), _p(w))
+    return ids, w
+
+
+def dispatch(ids, E, max_m):
+    lib = _lib()
+    ids = _c(ids, np.int32)
+    T, k = ids.shape
+    masked_m = np.empty(E, np.int32)
+    row = np.empty((T, k), np.int32)
+    lib.orc_dispatch(_p(ids), T, E, k, max_m, _p(masked_m), _p(row))
+    return masked_m, row
+
+
+def swiglu(gate_up, I):
+    lib = _lib()
+    gu = _c(gate_up, np.float64)
+    rows = gu.size // (2 * I)
+    h = np.empty(gu.shape[:-1] + (I,))
+    lib.orc_swiglu(_p(gu), rows, I, _p(h))
+    return h
+
+
+def combine(o, s_o, w):
+    """Weighted combine of one token: y* = sum_j w_j * o_j (fp64), S = sum_j |w_j| * S_j.
+    o, s_o: [top_k, H]; w: [top_k]."""
+    w = np.asarray(w, np.float64)[:, None]
+    return (w * o).sum(axis=0), (np.abs(w) * s_o).sum(axis=0)
+
+
+def num_threads() -> int:
+    return int(_lib().orc_num_threads())

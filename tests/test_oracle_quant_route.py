@@ -1,0 +1,200 @@
+"""Pins for the oracle's NVFP4 quantizer, no-aux router and dispatch (CPU only)."""
+import itertools
+
+import numpy as np
+import pytest
+from scipy.special import expit
+
+import oracle
+
+E2M1_MAGS = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def _nearest_e2m1(a):
+    """Independent rule for a non-negative magnitude: walk the midpoints."""
+    c = 0
+    for i in range(7):
+        mid = (E2M1_MAGS[i] + E2M1_MAGS[i + 1]) / 2
+        if a > mid or (a == mid and (i + 1) % 2 == 0):
+            c = i + 1
+    return c
+
+
+# ----------------------------------------------------------------------------- quantizer
+@pytest.mark.parametrize("g", [0.5, 1.0, 0.037])
+def test_quantize_round_trip(g):
+    rng = np.random.default_rng(20)
+    rows, K = 6, 128
+    codes = rng.integers(0, 16, (rows, K)).astype(np.uint8)
+    codes[:, ::16] = 7  # every block holds a +6
+    scode = rng.integers(0x18, 0x60, (rows, K // 16)).astype(np.uint8)  # general e4m3 scales
+    sval = oracle.e4m3_table()[scode]
+    # x = e2m1 * S * g formed in fp32 (each step exact: <= 6 significant bits)
+    x = (oracle.e2m1_table()[codes].astype(np.float32) *
+         np.repeat(sval.astype(np.float32), 16, axis=1) * np.float32(g)).astype(np.float32)
+    q, sf = oracle.quantize_nvfp4(x, g)
+    want_codes = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    # amax/(6g) recovers S exactly when 6g is exact; otherwise allow the neighbouring code
+    if g in (0.5, 1.0):
+        assert np.array_equal(sf, scode)
+        assert np.array_equal(q & 0x77, want_codes & 0x77)  # -0 inputs stay -0 (sign kept)
+        assert np.array_equal(q, want_codes)
+    else:
+        assert np.all(np.abs(sf.astype(int) - scode.astype(int)) <= 1)
+
+
+def test_quantize_zero_and_saturation():
+    K = 32
+    x = np.zeros((3, K), np.float32)
+    x[0, 5] = -0.0
+    x[0, 7] = -0.0
+    x[1, :16] = 1e6          # amax/(6g) = 1e6/6 > 448: scale saturates to 448
+    x[1, 3] = -1e6
+    x[2, 16:] = np.linspace(-5, 5, 16)
+    q, sf = oracle.quantize_nvfp4(x, 1.0)
+    assert sf[0, 0] == 0 and sf[0, 1] == 0
+    nib = np.stack([q & 15, q >> 4], -1).reshape(3, K)
+    assert nib[0, 5] == 8 and nib[0, 7] == 8 and nib[0, 0] == 0
+    assert sf[1, 0] == 0x7E
+    assert (nib[1, :16] == 7).sum() == 15 and nib[1, 3] == 15   # saturated at +-6
+    assert sf[2, 0] == 0 and sf[2, 1] == oracle.encode_e4m3_sat(5.0 / 6.0)
+
+
+def test_quantize_error_bound_random():
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((64, 256)).astype(np.float32)
+    g = np.float32(np.abs(x).max() / 2688.0)
+    q, sf = oracle.quantize_nvfp4(x, g)
+    dec = oracle.nvfp4_decode(q, sf) * float(g)
+    d = np.repeat(oracle.e4m3_table()[sf] * float(g), 16, axis=1)
+    xr = np.abs(x) / d
+    half_step = np.where(xr < 2, 0.25, np.where(xr < 4, 0.5, 1.0)) * d
+    ok = (xr <= 6.0)
+    assert np.all(np.abs(x - dec)[ok] <= half_step[ok] * (1 + 1e-6))
+    assert np.all(np.abs(x - dec)[~ok] <= np.abs(x)[~ok] - 6 * d[~ok] + 1e-6 * d[~ok])
+
+
+def test_quantize_rounding_rule_all_bf16():
+    """Every finite bf16 magnitude v (g = 1) placed beside a block maximum of 6 * 448 * ...:
+    the scale is fixed, so the code must be the nearest e2m1 of fl32(v * (1/d))."""
+    bits = np.arange(0, 0x7F80, dtype=np.uint32)          # all finite non-negative bf16
+    v = (bits << 16).view(np.float32)
+    amax = np.float32(6.0 * 16.0)                            # scale code 16.0 -> d = 16
+    v = v[v <= amax]
+    n = len(v)
+    blocks = np.zeros((n, 16), np.float32)
+    blocks[:, 0] = amax
+    blocks[:, 1] = v
+    q, sf = oracle.quantize_nvfp4(blocks, 1.0)
+    assert np.all(sf[:, 0] == oracle.encode_e4m3_sat(16.0))
+    got = (q[:, 0] >> 4).astype(int)
+    r = np.float32(1.0) / np.float32(16.0)
+    want = np.array([_nearest_e2m1(float(np.float32(x * r))) for x in v])
+    assert np.array_equal(got, want)
+
+
+# ----------------------------------------------------------------------------- router
+def _s_fp32(logits):
+    return (1.0 / (1.0 + np.exp(-logits.astype(np.float64)))).astype(np.float32)
+
+
+def _route_bruteforce(logits, bias, n_group, topk_group, top_k, rsf):
+    """Enumerate every admissible choice instead of greedy selection."""
+    E = logits.shape[0]
+    gsz = E // n_group
+    s = _s_fp32(logits)
+    sb = (s + bias).astype(np.float32)
+    gscore = []
+    for q in range(n_group):
+        vals = sorted(sb[q * gsz:(q + 1) * gsz].tolist(), reverse=True)
+        gscore.append(np.float32(np.float32(vals[0]) + np.float32(vals[1])))
+    # best group subset: lexicographically largest sorted score vector, then smallest indices
+    best = None
+    for sub in itertools.combinations(range(n_group), topk_group):
+        key = (sorted([float(gscore[q]) for q in sub], reverse=True), [-q for q in sub])
+        if best is None or key > best[0]:
+            best = (key, sub)
+    groups = best[1]
+    cand = [e for e in range(E) if e // gsz in groups]
+    bestk = None
+    for sub in itertools.combinations(cand, top_k):
+        order = sorted(sub, key=lambda e: (-float(sb[e]), e))
+        key = ([float(sb[e]) for e in order], [-e for e in order])
+        if bestk is None or key > bestk[0]:
+            bestk = (key, order)
+    ids = bestk[1]
+    den = np.float32(0)
+    for e in ids:
+        den = np.float32(den + s[e])
+    w = [np.float32(np.float32(s[e] / den) * np.float32(rsf)) for e in ids]
+    return np.array(ids, np.int32), np.array(w, np.float32)
+
+
+@pytest.mark.parametrize("E,ng,tg,k", [(8, 4, 2, 2), (16, 4, 2, 3), (12, 3, 1, 2), (16, 8, 4, 4)])
+def test_router_bruteforce(E, ng, tg, k):
+    rng = np.random.default_rng(E * 10 + k)
+    T = 40
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    logits[:5] = np.round(logits[:5])       # plant ties
+    bias = (rng.standard_normal(E) * 0.01).astype(np.float32)
+    ids, w = oracle.route_noaux(logits, bias, ng, tg, k, 2.5)
+    for t in range(T):
+        bi, bw = _route_bruteforce(logits[t], bias, ng, tg, k, 2.5)
+        assert np.array_equal(ids[t], bi), t
+        assert np.array_equal(w[t], bw), t
+
+
+def test_router_single_group_is_plain_topk():
+    rng = np.random.default_rng(30)
+    T, E, k = 50, 64, 8
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    logits[::7, ::3] = 0.25  # ties
+    bias = (rng.standard_normal(E) * 0.01).astype(np.float32)
+    ids, w = oracle.route_noaux(logits, bias, 1, 1, k, 1.0)
+    sb = (_s_fp32(logits) + bias).astype(np.float32)
+    for t in range(T):
+        order = np.lexsort((np.arange(E), -sb[t].astype(np.float64)))
+        assert np.array_equal(ids[t], order[:k])
+
+
+def test_router_ties_lower_index_and_invariants():
+    T, E = 3, 256
+    logits = np.zeros((T, E), np.float32)
+    bias = np.zeros(E, np.float32)
+    ids, w = oracle.route_noaux(logits, bias, 8, 4, 8, 2.5)
+    assert np.array_equal(ids[0], np.arange(8))         # all equal -> lowest indices, group 0
+    assert np.allclose(w, 2.5 / 8)
+    rng = np.random.default_rng(31)
+    T = 128
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    bias = (rng.standard_normal(E) * 0.01).astype(np.float32)
+    ids, w = oracle.route_noaux(logits, bias, 8, 4, 8, 2.5)
+    for t in range(T):
+        assert len(set(ids[t].tolist())) == 8
+        assert len(set((ids[t] // 32).tolist())) <= 4
+        # weights follow the library logistic function of the selected logits
+        ref = expit(logits[t, ids[t]].astype(np.float64))
+        assert np.allclose(w[t], 2.5 * ref / ref.sum(), rtol=4 * 2 ** -23, atol=0)
+        assert abs(float(w[t].astype(np.float64).sum()) - 2.5) < 16 * 2 ** -23 * 2.5
+        # slot order: s + bias non-increasing
+        sbt = (_s_fp32(logits[t]) + bias).astype(np.float32)[ids[t]]
+        assert np.all(sbt[:-1] >= sbt[1:])
+
+
+# ----------------------------------------------------------------------------- dispatch
+def test_dispatch_bruteforce_and_invariants():
+    rng = np.random.default_rng(40)
+    T, E, k = 30, 10, 3
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    for max_m in (100, 5):
+        mm, row = oracle.dispatch(ids, E, max_m)
+        for e in range(E):
+            toks = [t for t in range(T) if e in ids[t]]
+            assert mm[e] == min(len(toks), max_m)
+            for rank, t in enumerate(toks):
+                j = list(ids[t]).index(e)
+                assert row[t, j] == rank
+    mm, row = oracle.dispatch(ids, E, 1000)
+    assert mm.sum() == T * k
+    pairs = {(int(ids[t, j]), int(row[t, j])) for t in range(T) for j in range(k)}
+    assert len(pairs) == T * k
