@@ -72,6 +72,7 @@ double orc_e4m3_value(int code) { return E4M3[code & 255]; }
  * nearest even); magnitudes beyond 6 saturate to 6; the sign bit is signbit(v). */
 int orc_encode_e2m1(double v) {
   double a = fabs(v);
+  if (a > 6.0) return 7 | (signbit(v) ? 8 : 0); /* saturation (also for +-inf) */
   int best = 0;
   double bestd = INFINITY;
   for (int c = 0; c < 8; c++) {
@@ -84,6 +85,7 @@ int orc_encode_e2m1(double v) {
 /* Nearest finite e4m3fn code to v (ties to even code); |v| > 448 saturates. */
 int orc_encode_e4m3_sat(double v) {
   double a = fabs(v);
+  if (a > 448.0) return 0x7E | (signbit(v) ? 0x80 : 0); /* saturation (also for +-inf) */
   int best = 0;
   double bestd = INFINITY;
   for (int c = 0; c < 127; c++) { /* 0x00..0x7E: every finite non-negative code */

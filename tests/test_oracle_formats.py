@@ -65,6 +65,8 @@ def test_encode_e2m1_ties_and_saturation():
     for v, c in cases.items():
         assert oracle.encode_e2m1(v) == c, v
         assert oracle.encode_e2m1(-v) == c | 8, v
+    assert oracle.encode_e2m1(np.inf) == 7 and oracle.encode_e2m1(-np.inf) == 15
+    assert oracle.encode_e4m3_sat(np.array([np.inf, -np.inf])).tolist() == [0x7E, 0xFE]
     assert oracle.encode_e2m1(-0.0) == 8
     assert oracle.encode_e2m1(0.0) == 0
 
