@@ -1,0 +1,311 @@
+"""Benchmark of the block-scaled grouped-GEMM / MoE hot path on one MI355X.
+
+Default workload (one "step" = the whole decode GEMM1 path): 8 tokens routed top-8
+to 256 experts (ids from the seed) -> dispatch (masked_m, rows) -> NVFP4 quantization
+of the bf16 activations into the masked layout -> masked grouped NVFP4 GEMM1 against
+W13 [256, 4096, 7168] with bf16 output.  Inputs are resident in HBM before timing.
+
+Prints ONE JSON line with the metric, a roofline object for the dominant kernel
+(algorithmic bytes / its HIP-event-timed average duration) and the oracle's CPU
+baseline on a bounded sample.  Other workloads: --workload {decode_gemm1, masked_c0,
+hetero, moe_fp8, moe_nvfp4_decode, moe_nvfp4_prefill}; --all adds a per-workload
+table under "workloads".
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import datagen  # noqa: E402
+import fp8_grouped_gemm_nvfp4_amd as mxg  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+PEAK_TFLOPS = {"fp16": 2500.0, "bf16": 2500.0, "fp8": 5000.0, "fp4": 10100.0}
+NVFP4_ROW_BYTES = lambda K: K // 2 + K // 16  # codes + e4m3 scales per row  # noqa: E731
+
+
+def _ensure_built():
+    if not os.path.exists(mxg.LIB_PATH):
+        from fp8_grouped_gemm_nvfp4_amd import _build
+        _build.build()
+    mxg.lib()
+
+
+class Timer:
+    """HIP events on torch's current stream (the stream the library launches on)."""
+
+    def __init__(self):
+        self.pairs = []
+
+    def start(self):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.pairs.append([e, None])
+
+    def stop(self):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.pairs[-1][1] = e
+
+    def mean_ms(self):
+        return float(np.mean([a.elapsed_time(b) for a, b in self.pairs])) if self.pairs else float("nan")
+
+
+def timed_loop(step, steps, warmup):
+    for _ in range(warmup):
+        step(None)
+    torch.cuda.synchronize()
+    kt = Timer()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record()
+    for _ in range(steps):
+        step(kt)
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    return t0.elapsed_time(t1) / steps, kt.mean_ms(), wall
+
+
+# ----------------------------------------------------------------------------- workloads
+def bench_decode_gemm1(dev, steps, warmup, seed=1001, cpu=True):
+    wl = datagen.decode_gemm1_workload(seed, dev)
+    t, s = wl.tensors, wl.scalars
+    E, T, H, N, top_k, max_m = 256, s["T"], s["H"], s["N"], s["top_k"], 8
+    alpha = torch.full((E,), np.float32(s["g_x"]) * np.float32(s["g_w"]), dtype=torch.float32, device=dev)
+    masked_m = torch.empty((E,), dtype=torch.int32, device=dev)
+    row = torch.empty((T, top_k), dtype=torch.int32, device=dev)
+    a = torch.empty((E, max_m, H // 2), dtype=torch.uint8, device=dev)
+    a_sf = torch.empty((E, max_m, H // 16), dtype=torch.uint8, device=dev)
+    out = torch.empty((E, max_m, N), dtype=torch.bfloat16, device=dev)
+
+    def step(kt):
+        mxg.moe_dispatch(t["ids"], E, max_m, masked_m=masked_m, row=row)
+        mxg.moe_quantize_gather_nvfp4(t["x"], s["g_x"], t["ids"], row, E, max_m, a=a, a_sf=a_sf)
+        if kt:
+            kt.start()
+        mxg.mx_grouped_gemm_masked(a, a_sf, t["w13"], t["w13_sf"], alpha, masked_m, out)
+        if kt:
+            kt.stop()
+
+    ms, kms, wall = timed_loop(step, steps, warmup)
+    mm = masked_m.cpu().numpy()
+    n_act, rows = int((mm > 0).sum()), int(mm.sum())
+    w_bytes = n_act * N * NVFP4_ROW_BYTES(H)
+    gemm_bytes = w_bytes + rows * NVFP4_ROW_BYTES(H) + rows * N * 2
+    step_bytes = gemm_bytes + T * H * 2 + T * top_k * 4 * 2 + E * 4
+    flops = 2.0 * rows * N * H
+    res = dict(name=wl.name, ms=ms, kernel_ms=kms, wall_s=wall, bytes=step_bytes, kernel_bytes=gemm_bytes,
+               flops=flops, gbs=step_bytes / ms / 1e6, kernel_gbs=gemm_bytes / kms / 1e6,
+               tflops=flops / ms / 1e9, tokens_per_s=T / ms * 1e3, bound="hbm",
+               config=dict(workload=wl.name, experts=E, tokens=T, top_k=top_k, K=H, N=N, max_m=max_m,
+                           active_experts=n_act, sum_masked_m=rows))
+    if cpu:
+        res["cpu_baseline"] = cpu_baseline_decode_gemm1(t, s, step_bytes)
+    return res
+
+
+def cpu_baseline_decode_gemm1(t, s, step_bytes, min_seconds=10.0):
+    """The oracle's whole decode GEMM1 path (dispatch, quantize, every valid output row)
+    on the host cores, repeated until about min_seconds have elapsed."""
+    import oracle
+    E, H, N, max_m = 256, s["H"], s["N"], 8
+    ids = t["ids"].cpu().numpy()
+    x = t["x"].float().cpu().numpy()
+    mm, row = oracle.dispatch(ids, E, max_m)
+    active = np.nonzero(mm)[0]
+    w13 = {int(e): t["w13"][int(e)].cpu().numpy() for e in active}
+    w13sf = {int(e): t["w13_sf"][int(e)].cpu().numpy() for e in active}
+    alpha = float(np.float32(s["g_x"]) * np.float32(s["g_w"]))
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        mm, row = oracle.dispatch(ids, E, max_m)
+        xq, xsf = oracle.quantize_nvfp4(x, s["g_x"])
+        for tt in range(ids.shape[0]):
+            for j in range(ids.shape[1]):
+                e = int(ids[tt, j])
+                oracle.nvfp4_row_dot(xq, xsf, tt, w13[e], w13sf[e], H, alpha)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    return dict(value=step_bytes * reps / el / 1e9, unit="GB/s", cores=oracle.num_threads(), kind="oracle",
+                sample=f"the full decode GEMM1 step (dispatch, quantize, all {int(mm.sum())} valid rows x {N} "
+                       f"outputs, K={H}) repeated {reps}x in {el:.1f} s",
+                seconds_per_step=el / reps)
+
+
+def bench_masked_c0(dev, steps, warmup, seed=1000):
+    wl = datagen.masked_gemm_workload(seed, dev)
+    t = wl.tensors
+    out = torch.empty((4, 64, 512), dtype=torch.bfloat16, device=dev)
+
+    def step(kt):
+        if kt:
+            kt.start()
+        mxg.mx_grouped_gemm_masked(t["a"], t["a_sf"], t["b"], t["b_sf"], t["alpha"], t["masked_m"], out)
+        if kt:
+            kt.stop()
+
+    ms, kms, wall = timed_loop(step, steps, warmup)
+    mm = t["masked_m"].cpu().numpy()
+    rows, ng = int(mm.sum()), int((mm > 0).sum())
+    byts = ng * 512 * NVFP4_ROW_BYTES(1024) + rows * NVFP4_ROW_BYTES(1024) + rows * 512 * 2
+    flops = 2.0 * rows * 512 * 1024
+    return dict(name=wl.name, ms=ms, kernel_ms=kms, wall_s=wall, bytes=byts, kernel_bytes=byts, flops=flops,
+                gbs=byts / ms / 1e6, kernel_gbs=byts / kms / 1e6, tflops=flops / ms / 1e9, bound="launch",
+                config=dict(workload=wl.name, masked_m=mm.tolist()))
+
+
+def bench_hetero(dev, steps, warmup, seed=1002):
+    wl = datagen.hetero_gemm_workload(seed, dev)
+    groups = []
+    byts, flops = 0, 0.0
+    for q in wl.tensors["groups"]:
+        q = dict(q)
+        q["out"] = torch.empty((q["M"], q["N"]), dtype=torch.bfloat16, device=dev)
+        groups.append(q)
+        byts += (q["M"] + q["N"]) * NVFP4_ROW_BYTES(q["K"]) + q["M"] * q["N"] * 2
+        flops += 2.0 * q["M"] * q["N"] * q["K"]
+
+    def step(kt):
+        if kt:
+            kt.start()
+        mxg.mx_grouped_gemm(groups)
+        if kt:
+            kt.stop()
+
+    ms, kms, wall = timed_loop(step, steps, warmup)
+    return dict(name=wl.name, ms=ms, kernel_ms=kms, wall_s=wall, bytes=byts, kernel_bytes=byts, flops=flops,
+                gbs=byts / ms / 1e6, tflops=flops / ms / 1e9, kernel_tflops=flops / kms / 1e9, bound="mfma",
+                mfma_dtype="fp16", config=dict(workload=wl.name))
+
+
+def _moe_setup(dev, t, T, E=256, top_k=8):
+    ids, w = mxg.moe_route_noaux(t["logits"], t["bias"], 8, 4, top_k, 2.5)
+    mm_full, _ = mxg.moe_dispatch(ids, E, 1 << 20)
+    cap = max(64, -(-int(mm_full.max().item()) // 64) * 64)
+    masked_m, row = mxg.moe_dispatch(ids, E, cap)
+    torch.cuda.synchronize()
+    return ids, w, masked_m, row, cap
+
+
+def bench_moe(dev, steps, warmup, precision, T, seed):
+    E, H, I, top_k = 256, 7168, 2048, 8
+    if precision == "fp8":
+        wl = datagen.moe_fp8_workload(seed, dev, T=T)
+    else:
+        wl = datagen.moe_nvfp4_workload(seed, dev, T=T)
+    t, s = wl.tensors, wl.scalars
+    ids, w, masked_m, row, cap = _moe_setup(dev, t, T)
+    y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    if precision == "fp8":
+        d = mxg.make_moe_desc(mxg.MXG_MOE_FP8_BLOCK128, T, H, I, E, top_k, cap, t["xq"], t["w13"], t["w13_s"],
+                              t["w2"], t["w2_s"], ids, w, masked_m, row, y, x_scale=t["xs"])
+    else:
+        d = mxg.make_moe_desc(mxg.MXG_MOE_NVFP4, T, H, I, E, top_k, cap, t["x"], t["w13"], t["w13_sf"],
+                              t["w2"], t["w2_sf"], ids, w, masked_m, row, y, g_x=s["g_x"], g_w13=t["g_w13"],
+                              g_w2=t["g_w2"], g_h=s["g_h"])
+    ws = torch.empty((mxg.moe_expert_forward_workspace_size(d),), dtype=torch.uint8, device=dev)
+
+    def step(kt):
+        mxg.moe_route_noaux(t["logits"], t["bias"], 8, 4, top_k, 2.5, ids=ids, w=w)
+        mxg.moe_dispatch(ids, E, cap, masked_m=masked_m, row=row)
+        if kt:
+            kt.start()
+        mxg.moe_expert_forward(d, ws)
+        if kt:
+            kt.stop()
+
+    ms, kms, wall = timed_loop(step, steps, warmup)
+    mm = masked_m.cpu().numpy()
+    n_act, rows = int((mm > 0).sum()), int(mm.sum())
+    if precision == "fp8":
+        wbytes = n_act * (2 * I * H + H * I) + n_act * ((2 * I // 128) * (H // 128) + (H // 128) * (I // 128)) * 4
+        xbytes = T * H + T * (H // 128) * 4
+    else:
+        wbytes = n_act * (2 * I * NVFP4_ROW_BYTES(H) + H * NVFP4_ROW_BYTES(I))
+        xbytes = T * H * 2
+    byts = wbytes + xbytes + T * E * 4 + T * H * 2
+    flops = 2.0 * rows * (2 * I * H + H * I)
+    return dict(name=wl.name, ms=ms, kernel_ms=kms, wall_s=wall, bytes=byts, flops=flops,
+                gbs=byts / ms / 1e6, tflops=flops / ms / 1e9, tokens_per_s=T / ms * 1e3, bound="hbm",
+                config=dict(workload=wl.name, tokens=T, active_experts=n_act, max_m=cap))
+
+
+WORKLOADS = {
+    "decode_gemm1": lambda dev, k, w, cpu: bench_decode_gemm1(dev, k, w, cpu=cpu),
+    "masked_c0": lambda dev, k, w, cpu: bench_masked_c0(dev, k, w),
+    "hetero": lambda dev, k, w, cpu: bench_hetero(dev, k, w),
+    "moe_fp8": lambda dev, k, w, cpu: bench_moe(dev, k, w, "fp8", 4096, 1003),
+    "moe_nvfp4_decode": lambda dev, k, w, cpu: bench_moe(dev, k, w, "nvfp4", 64, 1004),
+    "moe_nvfp4_prefill": lambda dev, k, w, cpu: bench_moe(dev, k, w, "nvfp4", 8192, 1004),
+}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode_gemm1", choices=sorted(WORKLOADS))
+    ap.add_argument("--all", action="store_true", help="also time every other workload")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the path runs on a single MI355X with no sharding "
+              "or collectives; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    _ensure_built()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    r = WORKLOADS[args.workload](dev, args.steps, args.warmup, not args.no_cpu_baseline)
+
+    line = {
+        "metric": "masked grouped GEMM GB/s & TFLOP/s (% roofline); MoE layer tokens/s, 1 GPU",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": r["ms"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "data": "synthetic", "config": r["config"],
+    }
+    if r["bound"] == "mfma":
+        line.update(value=r["tflops"], unit="TFLOP/s", dtype="fp16-mfma/fp32-acc")
+        achieved = r["flops"] / r["kernel_ms"] / 1e9
+        line["roofline"] = dict(bound="mfma", achieved=achieved, peak=PEAK_TFLOPS["fp16"], unit="TFLOP/s",
+                                frac=achieved / PEAK_TFLOPS["fp16"], traffic=None)
+    else:
+        line.update(value=r["gbs"], unit="GB/s", dtype="fp16-mfma/fp32-acc")
+        kb = r.get("kernel_bytes", r["bytes"])
+        achieved = kb / r["kernel_ms"] / 1e6
+        line["roofline"] = dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
+                                frac=achieved / HBM_PEAK_GBS, traffic=None)
+    if "tokens_per_s" in r:
+        line["tokens_per_s"] = r["tokens_per_s"]
+    line["tflops"] = r["tflops"]
+    line["kernel_ms"] = r["kernel_ms"]
+    line["cpu_baseline"] = r.get("cpu_baseline")
+    if args.all:
+        rows = []
+        for name, fn in WORKLOADS.items():
+            if name == args.workload:
+                continue
+            q = fn(dev, max(5, args.steps // 5), 2, False)
+            rows.append({k: q[k] for k in ("name", "ms", "kernel_ms", "gbs", "tflops") if k in q} |
+                        ({"tokens_per_s": q["tokens_per_s"]} if "tokens_per_s" in q else {}))
+            torch.cuda.empty_cache()
+        line["workloads"] = rows
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,298 @@
+// api.cpp -- the C ABI (include/mxg.h): host-side argument validation, status
+// reporting and kernel dispatch.  Every check runs before the first HIP call,
+// so a rejected call leaves the GPU untouched.
+#include <hip/hip_runtime.h>
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return MXG_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(MXG_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_nvfp4_types(int ab_dtype, int sf_dtype, int c_dtype, int sf_vec_size) {
+  if (ab_dtype != MXG_E2M1 || sf_dtype != MXG_E4M3 || sf_vec_size != 16)
+    return fail(MXG_ERR_UNSUPPORTED,
+                "only ab_dtype=E2M1, sf_dtype=E4M3, sf_vec_size=16 is supported (got %d, %d, %d)",
+                ab_dtype, sf_dtype, sf_vec_size);
+  if (c_dtype != MXG_BF16 && c_dtype != MXG_F32)
+    return fail(MXG_ERR_UNSUPPORTED, "c_dtype must be BF16 or F32 (got %d)", c_dtype);
+  return MXG_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+extern "C" {
+
+const char* mxg_status_string(int status) {
+  switch (status) {
+    case MXG_OK: return "MXG_OK";
+    case MXG_ERR_INVALID_ARG: return "MXG_ERR_INVALID_ARG";
+    case MXG_ERR_UNSUPPORTED: return "MXG_ERR_UNSUPPORTED";
+    case MXG_ERR_WORKSPACE: return "MXG_ERR_WORKSPACE";
+    case MXG_ERR_HIP: return "MXG_ERR_HIP";
+    default: return "unknown status";
+  }
+}
+
+const char* mxg_last_error(void) { return g_err; }
+
+int mxg_version(void) { return 100; }
+
+int mx_grouped_gemm_masked(const uint8_t* a, const uint8_t* a_sf, const uint8_t* b,
+                           const uint8_t* b_sf, const float* alpha, const int32_t* masked_m,
+                           void* out, int G, int max_m, int N, int K, int ab_dtype, int sf_dtype,
+                           int c_dtype, int sf_vec_size, int cu_limit, void* stream) {
+  if (!a || !a_sf || !b || !b_sf || !masked_m || !out)
+    return fail(MXG_ERR_INVALID_ARG, "mx_grouped_gemm_masked: null pointer");
+  if (G < 1 || G > 65535 || max_m < 1 || N < 1 || K < 1 || cu_limit < 0)
+    return fail(MXG_ERR_INVALID_ARG, "mx_grouped_gemm_masked: bad sizes G=%d max_m=%d N=%d K=%d", G,
+                max_m, N, K);
+  int st = check_nvfp4_types(ab_dtype, sf_dtype, c_dtype, sf_vec_size);
+  if (st) return st;
+  if (K % 64 != 0) return fail(MXG_ERR_UNSUPPORTED, "mx_grouped_gemm_masked: K %% 64 != 0 (K=%d)", K);
+  if (!aligned16(a) || !aligned16(b) || !aligned16(out) || ((uintptr_t)a_sf & 1u) || ((uintptr_t)b_sf & 1u))
+    return fail(MXG_ERR_INVALID_ARG, "mx_grouped_gemm_masked: misaligned pointer");
+  if ((long long)G * max_m * N >= (1LL << 40))
+    return fail(MXG_ERR_UNSUPPORTED, "mx_grouped_gemm_masked: problem too large");
+  mxg::MaskedGemmArgs p{};
+  p.a = a; p.a_sf = a_sf; p.b = b; p.b_sf = b_sf; p.out = out;
+  p.masked_m = masked_m; p.alpha = alpha; p.alpha_scale = 1.0f;
+  p.G = G; p.max_m = max_m; p.N = N; p.K = K;
+  int epi = c_dtype == MXG_BF16 ? mxg::EPI_BF16 : mxg::EPI_F32;
+  return hip_status(mxg::gemm_nvfp4_masked(p, epi, cu_limit, (hipStream_t)stream),
+                    "mx_grouped_gemm_masked launch");
+}
+
+int mx_grouped_gemm(const mxg_group_desc* groups, int G, int ab_dtype, int sf_dtype, int c_dtype,
+                    int sf_vec_size, int cu_limit, void* stream) {
+  if (!groups) return fail(MXG_ERR_INVALID_ARG, "mx_grouped_gemm: null descriptor array");
+  if (G < 1 || G > MXG_MAX_GROUPS)
+    return fail(MXG_ERR_INVALID_ARG, "mx_grouped_gemm: G=%d outside [1, %d]", G, MXG_MAX_GROUPS);
+  if (cu_limit < 0) return fail(MXG_ERR_INVALID_ARG, "mx_grouped_gemm: cu_limit < 0");
+  int st = check_nvfp4_types(ab_dtype, sf_dtype, c_dtype, sf_vec_size);
+  if (st) return st;
+  mxg::HeteroGemmArgs p{};
+  p.G = G;
+  for (int g = 0; g < G; g++) {
+    const mxg_group_desc& d = groups[g];
+    if (d.M < 0 || d.N < 1 || d.K < 1 || d.ldc < 0)
+      return fail(MXG_ERR_INVALID_ARG, "mx_grouped_gemm: group %d has bad sizes", g);
+    if (d.K % 64 != 0) return fail(MXG_ERR_UNSUPPORTED, "mx_grouped_gemm: group %d K %% 64 != 0", g);
+    int ldc = d.ldc ? d.ldc : d.N;
+    if (ldc < d.N) return fail(MXG_ERR_INVALID_ARG, "mx_grouped_gemm: group %d ldc < N", g);
+    if (d.M > 0 && (!d.a || !d.a_sf || !d.b || !d.b_sf || !d.out))
+      return fail(MXG_ERR_INVALID_ARG, "mx_grouped_gemm: group %d null pointer", g);
+    if (d.M > 0 && (!aligned16(d.a) || !aligned16(d.b) || ((uintptr_t)d.a_sf & 1u) || ((uintptr_t)d.b_sf & 1u)))
+      return fail(MXG_ERR_INVALID_ARG, "mx_grouped_gemm: group %d misaligned pointer", g);
+    mxg::HeteroGroup& q = p.grp[g];
+    q.a = d.a; q.a_sf = d.a_sf; q.b = d.b; q.b_sf = d.b_sf; q.out = d.out;
+    q.M = d.M; q.N = d.N; q.K = d.K; q.ldc = ldc; q.alpha = d.alpha;
+  }
+  int epi = c_dtype == MXG_BF16 ? mxg::EPI_BF16 : mxg::EPI_F32;
+  return hip_status(mxg::gemm_nvfp4_hetero(p, epi, cu_limit, (hipStream_t)stream),
+                    "mx_grouped_gemm launch");
+}
+
+int mx_quantize_nvfp4(const void* x, int x_dtype, long rows, int K, float g, uint8_t* codes,
+                      uint8_t* sf, void* stream) {
+  if (!x || !codes || !sf) return fail(MXG_ERR_INVALID_ARG, "mx_quantize_nvfp4: null pointer");
+  if (rows < 0 || K < 16) return fail(MXG_ERR_INVALID_ARG, "mx_quantize_nvfp4: bad sizes");
+  if (K % 16 != 0) return fail(MXG_ERR_UNSUPPORTED, "mx_quantize_nvfp4: K %% 16 != 0");
+  if (x_dtype != MXG_BF16 && x_dtype != MXG_F32)
+    return fail(MXG_ERR_UNSUPPORTED, "mx_quantize_nvfp4: x_dtype must be BF16 or F32");
+  if (!(g > 0.0f) || g == __builtin_inff())
+    return fail(MXG_ERR_INVALID_ARG, "mx_quantize_nvfp4: global scale must be finite and > 0");
+  if (!aligned16(x) || ((uintptr_t)codes & 7u))
+    return fail(MXG_ERR_INVALID_ARG, "mx_quantize_nvfp4: misaligned pointer");
+  return hip_status(mxg::quantize_nvfp4(x, x_dtype, rows, K, g, codes, sf, (hipStream_t)stream),
+                    "mx_quantize_nvfp4 launch");
+}
+
+int moe_route_noaux(const float* logits, const float* bias, int T, int E, int n_group,
+                    int topk_group, int top_k, float rsf, int32_t* topk_ids, float* topk_w,
+                    void* stream) {
+  if (!logits || !bias || !topk_ids || !topk_w)
+    return fail(MXG_ERR_INVALID_ARG, "moe_route_noaux: null pointer");
+  if (T < 0 || E < 1 || n_group < 1 || topk_group < 1 || top_k < 1)
+    return fail(MXG_ERR_INVALID_ARG, "moe_route_noaux: bad sizes");
+  if (E != 256) return fail(MXG_ERR_UNSUPPORTED, "moe_route_noaux: E must be 256 (got %d)", E);
+  if (n_group != 1 && n_group != 2 && n_group != 4 && n_group != 8)
+    return fail(MXG_ERR_UNSUPPORTED, "moe_route_noaux: n_group must be 1, 2, 4 or 8");
+  if (topk_group > n_group) return fail(MXG_ERR_INVALID_ARG, "moe_route_noaux: topk_group > n_group");
+  if (top_k > 8) return fail(MXG_ERR_UNSUPPORTED, "moe_route_noaux: top_k > 8");
+  if (top_k > topk_group * (E / n_group))
+    return fail(MXG_ERR_INVALID_ARG, "moe_route_noaux: top_k exceeds the experts of the kept groups");
+  if (!aligned16(logits) || !aligned16(bias))
+    return fail(MXG_ERR_INVALID_ARG, "moe_route_noaux: misaligned pointer");
+  return hip_status(mxg::route_noaux(logits, bias, T, E, n_group, topk_group, top_k, rsf, topk_ids,
+                                     topk_w, (hipStream_t)stream),
+                    "moe_route_noaux launch");
+}
+
+int moe_dispatch(const int32_t* topk_ids, int T, int E, int top_k, int max_m, int32_t* masked_m,
+                 int32_t* row, void* stream) {
+  if (!topk_ids || !masked_m || !row) return fail(MXG_ERR_INVALID_ARG, "moe_dispatch: null pointer");
+  if (T < 0 || E < 1 || top_k < 1 || max_m < 1 || E > 65535)
+    return fail(MXG_ERR_INVALID_ARG, "moe_dispatch: bad sizes");
+  if ((long long)T * top_k >= (1LL << 31)) return fail(MXG_ERR_UNSUPPORTED, "moe_dispatch: too many slots");
+  return hip_status(mxg::dispatch(topk_ids, T, E, top_k, max_m, masked_m, row, (hipStream_t)stream),
+                    "moe_dispatch launch");
+}
+
+int moe_quantize_gather_nvfp4(const uint16_t* x, int T, int H, float g_x, const int32_t* topk_ids,
+                              const int32_t* row, int top_k, int E, int max_m, uint8_t* a,
+                              uint8_t* a_sf, void* stream) {
+  if (!x || !topk_ids || !row || !a || !a_sf)
+    return fail(MXG_ERR_INVALID_ARG, "moe_quantize_gather_nvfp4: null pointer");
+  if (T < 0 || H < 64 || top_k < 1 || E < 1 || max_m < 1)
+    return fail(MXG_ERR_INVALID_ARG, "moe_quantize_gather_nvfp4: bad sizes");
+  if (H % 64 != 0) return fail(MXG_ERR_UNSUPPORTED, "moe_quantize_gather_nvfp4: H %% 64 != 0");
+  if (!(g_x > 0.0f) || g_x == __builtin_inff())
+    return fail(MXG_ERR_INVALID_ARG, "moe_quantize_gather_nvfp4: g_x must be finite and > 0");
+  if (!aligned16(x) || !aligned16(a))
+    return fail(MXG_ERR_INVALID_ARG, "moe_quantize_gather_nvfp4: misaligned pointer");
+  return hip_status(mxg::quantize_gather_nvfp4(x, T, H, g_x, topk_ids, row, top_k, max_m, a, a_sf,
+                                               (hipStream_t)stream),
+                    "moe_quantize_gather_nvfp4 launch");
+}
+
+// ----------------------------------------------------------------------------- MoE layer
+static int check_moe(const mxg_moe_desc* d) {
+  if (!d) return fail(MXG_ERR_INVALID_ARG, "moe_expert_forward: null descriptor");
+  if (d->precision != MXG_MOE_FP8_BLOCK128 && d->precision != MXG_MOE_NVFP4)
+    return fail(MXG_ERR_UNSUPPORTED, "moe_expert_forward: unknown precision %d", d->precision);
+  if (d->T < 0 || d->H < 128 || d->I < 128 || d->E < 1 || d->top_k < 1 || d->max_m < 1)
+    return fail(MXG_ERR_INVALID_ARG, "moe_expert_forward: bad sizes");
+  if (d->H % 128 || d->I % 128)
+    return fail(MXG_ERR_UNSUPPORTED, "moe_expert_forward: H and I must be multiples of 128");
+  if (d->top_k > 8) return fail(MXG_ERR_UNSUPPORTED, "moe_expert_forward: top_k > 8");
+  if (!d->x || !d->w13 || !d->w13_scale || !d->w2 || !d->w2_scale || !d->topk_ids || !d->topk_w ||
+      !d->masked_m || !d->row || !d->y)
+    return fail(MXG_ERR_INVALID_ARG, "moe_expert_forward: null pointer");
+  if (d->precision == MXG_MOE_FP8_BLOCK128 && !d->x_scale)
+    return fail(MXG_ERR_INVALID_ARG, "moe_expert_forward: FP8 needs x_scale");
+  if (d->precision == MXG_MOE_NVFP4) {
+    if (!d->g_w13 || !d->g_w2) return fail(MXG_ERR_INVALID_ARG, "moe_expert_forward: NVFP4 needs g_w13/g_w2");
+    if (!(d->g_x > 0.0f) || !(d->g_h > 0.0f) || d->g_x == __builtin_inff() || d->g_h == __builtin_inff())
+      return fail(MXG_ERR_INVALID_ARG, "moe_expert_forward: g_x and g_h must be finite and > 0");
+  }
+  if (!aligned16(d->x) || !aligned16(d->w13) || !aligned16(d->w2) || !aligned16(d->y))
+    return fail(MXG_ERR_INVALID_ARG, "moe_expert_forward: misaligned pointer");
+  return MXG_OK;
+}
+
+int moe_expert_forward_workspace_layout(const mxg_moe_desc* d, size_t* off) {
+  int st = check_moe(d);
+  if (st) return st;
+  if (!off) return fail(MXG_ERR_INVALID_ARG, "moe_expert_forward_workspace_layout: null output");
+  size_t rows = (size_t)d->E * d->max_m;
+  size_t sz[5];
+  if (d->precision == MXG_MOE_FP8_BLOCK128) {
+    sz[0] = rows * d->H;                     // e4m3 activations
+    sz[1] = rows * (d->H / 128) * 4;         // fp32 1x128 scales
+    sz[2] = rows * d->I * 2;                 // bf16 h
+    sz[3] = 0;
+  } else {
+    sz[0] = rows * (d->H / 2);
+    sz[1] = rows * (d->H / 16);
+    sz[2] = rows * (d->I / 2);
+    sz[3] = rows * (d->I / 16);
+  }
+  sz[4] = rows * d->H * 4;                   // fp32 GEMM2 output
+  size_t o = 0;
+  for (int i = 0; i < 5; i++) {
+    off[i] = o;
+    o += align256(sz[i]);
+  }
+  off[5] = o;
+  return ok();
+}
+
+size_t moe_expert_forward_workspace_size(const mxg_moe_desc* d) {
+  size_t off[6];
+  if (moe_expert_forward_workspace_layout(d, off) != MXG_OK) return 0;
+  return off[5];
+}
+
+int moe_expert_forward(const mxg_moe_desc* d, void* ws, size_t ws_bytes, void* stream) {
+  size_t off[6];
+  int st = moe_expert_forward_workspace_layout(d, off);
+  if (st) return st;
+  if (!ws || ws_bytes < off[5])
+    return fail(MXG_ERR_WORKSPACE, "moe_expert_forward: workspace of %zu bytes needed, %zu given", off[5],
+                ws ? ws_bytes : (size_t)0);
+  if (((uintptr_t)ws & 255u) != 0) return fail(MXG_ERR_INVALID_ARG, "moe_expert_forward: workspace not 256-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t* w = (uint8_t*)ws;
+  const int E = d->E, H = d->H, I = d->I, T = d->T, k = d->top_k, mm = d->max_m;
+  float* o = (float*)(w + off[4]);
+  hipError_t e;
+  if (d->precision == MXG_MOE_FP8_BLOCK128) {
+    uint8_t* a = w + off[0];
+    float* a_s = (float*)(w + off[1]);
+    uint16_t* h = (uint16_t*)(w + off[2]);
+    e = mxg::gather_fp8((const uint8_t*)d->x, d->x_scale, T, H, d->topk_ids, d->row, k, mm, a, a_s, s);
+    if (e != hipSuccess) return hip_status(e, "gather_fp8");
+    mxg::Fp8GemmArgs p1{};
+    p1.a = a; p1.a_s = a_s; p1.b = d->w13; p1.b_s = (const float*)d->w13_scale; p1.out = h;
+    p1.masked_m = d->masked_m; p1.G = E; p1.max_m = mm; p1.N = 2 * I; p1.K = H;
+    e = mxg::gemm_fp8_swiglu(p1, 0, s);
+    if (e != hipSuccess) return hip_status(e, "gemm_fp8_swiglu");
+    mxg::Fp8GemmArgs p2{};
+    p2.a = (const uint8_t*)h; p2.b = d->w2; p2.b_s = (const float*)d->w2_scale; p2.out = o;
+    p2.masked_m = d->masked_m; p2.G = E; p2.max_m = mm; p2.N = H; p2.K = I;
+    e = mxg::gemm_bf16_fp8w(p2, 0, s);
+    if (e != hipSuccess) return hip_status(e, "gemm_bf16_fp8w");
+  } else {
+    uint8_t* a = w + off[0];
+    uint8_t* a_sf = w + off[1];
+    uint8_t* hc = w + off[2];
+    uint8_t* hsf = w + off[3];
+    e = mxg::quantize_gather_nvfp4((const uint16_t*)d->x, T, H, d->g_x, d->topk_ids, d->row, k, mm, a,
+                                   a_sf, s);
+    if (e != hipSuccess) return hip_status(e, "quantize_gather_nvfp4");
+    mxg::MaskedGemmArgs p1{};
+    p1.a = a; p1.a_sf = a_sf; p1.b = d->w13; p1.b_sf = (const uint8_t*)d->w13_scale;
+    p1.out = nullptr; p1.masked_m = d->masked_m; p1.alpha = d->g_w13; p1.alpha_scale = d->g_x;
+    p1.G = E; p1.max_m = mm; p1.N = 2 * I; p1.K = H;
+    p1.h_codes = hc; p1.h_sf = hsf; p1.dbg_h = d->dbg_h; p1.g_h = d->g_h;
+    e = mxg::gemm_nvfp4_masked(p1, mxg::EPI_SWIGLU_NVFP4, 0, s);
+    if (e != hipSuccess) return hip_status(e, "gemm1 nvfp4 swiglu");
+    mxg::MaskedGemmArgs p2{};
+    p2.a = hc; p2.a_sf = hsf; p2.b = d->w2; p2.b_sf = (const uint8_t*)d->w2_scale; p2.out = o;
+    p2.masked_m = d->masked_m; p2.alpha = d->g_w2; p2.alpha_scale = d->g_h;
+    p2.G = E; p2.max_m = mm; p2.N = H; p2.K = I;
+    e = mxg::gemm_nvfp4_masked(p2, mxg::EPI_F32, 0, s);
+    if (e != hipSuccess) return hip_status(e, "gemm2 nvfp4");
+  }
+  e = mxg::combine(o, d->topk_ids, d->row, d->topk_w, T, H, k, mm, d->y, s);
+  return hip_status(e, "combine");
+}
+
+}  // extern "C"

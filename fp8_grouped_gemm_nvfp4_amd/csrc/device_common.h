@@ -1,0 +1,135 @@
+// device_common.h -- gfx950 device helpers shared by the library's kernels:
+// vector types, NVFP4 / e4m3 / bf16 conversions and the NVFP4 block quantizer.
+//
+// Formats (the pages name them -- NVFP4 as 4-bit floats with block scale
+// factors in "The CuteDSL Gamble", "Input Knowledge Required"; e4m3fn scales
+// in the "llm-assisted-kernel-dev" README's mixture-of-experts table -- the bit
+// layouts are the OCP ones): e2m1 = [s e1 e0 m], bias 1, no inf/NaN;
+// e4m3fn = [s eeee mmm], bias 7, S.1111.111 = NaN, no inf, max 448.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxg {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef int int8v_t __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// e4m3fn byte -> fp32 value.  Placing the 7 magnitude bits at fp32 bit 20
+// gives the value times 2^-120 (normals and subnormals alike, since both
+// formats continue their subnormal ranges linearly); one exact multiply
+// restores it.  The NaN codes map to NaN.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  uint32_t mag = c & 0x7Fu;
+  float v = __uint_as_float(((c & 0x80u) << 24) | (mag << 20)) * 0x1p120f;
+  return mag == 0x7Fu ? __uint_as_float(0x7FC00000u) : v;
+}
+
+// fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return ((u >> 16) | 0x40u) & 0xFFFFu;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Round a fp32 value to the nearest finite e4m3fn code (ties to even mantissa),
+// saturating magnitudes above 448 to 448 (code 0x7E).
+__device__ __forceinline__ uint32_t f32_to_e4m3_rne_sat(float v) {
+  uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+  float a = __builtin_fabsf(v);
+  if (a != a) return sign | 0x7Fu;
+  if (a >= 464.0f) return sign | 0x7Eu;
+  if (a < 0x1p-6f) {
+    // subnormal range: multiples of 2^-9; a * 512 is exact, rintf rounds ties to even.
+    // A result of 8 is 2^-6, whose code (exponent field 1, mantissa 0) is also 8.
+    return sign | (uint32_t)__builtin_rintf(a * 512.0f);
+  }
+  uint32_t u = __float_as_uint(a);
+  int e = (int)(u >> 23) - 127;           // -6 .. 8
+  uint32_t mant = u & 0x7FFFFFu;
+  uint32_t m3 = mant >> 20, rem = mant & 0xFFFFFu;
+  if (rem > 0x80000u || (rem == 0x80000u && (m3 & 1u))) m3 += 1;
+  if (m3 == 8) { m3 = 0; e += 1; }
+  uint32_t code = ((uint32_t)(e + 7) << 3) | m3;
+  if (code > 0x7Eu) code = 0x7Eu;          // (448, 464) rounds to 448
+  return sign | code;
+}
+
+// Round a fp32 value to the nearest e2m1 code: magnitudes {0,.5,1,1.5,2,3,4,6};
+// at a midpoint the code with last bit 0 wins; beyond 6 saturates; sign kept.
+__device__ __forceinline__ uint32_t f32_to_e2m1_rne_sat(float v) {
+  uint32_t sign = (__float_as_uint(v) >> 28) & 0x8u;
+  float a = __builtin_fabsf(v);
+  uint32_t c = a <= 0.25f ? 0u
+             : a < 0.75f ? 1u
+             : a <= 1.25f ? 2u
+             : a < 1.75f ? 3u
+             : a <= 2.5f ? 4u
+             : a < 3.5f ? 5u
+             : a <= 5.0f ? 6u : 7u;
+  return sign | c;
+}
+
+// NVFP4 quantization of one 16-element block (fp32 values, fp32 arithmetic with
+// round-to-nearest at every step): S = e4m3(amax / (6 g)), d = S * g,
+// code_i = e2m1(x_i * (1 / d)).  Returns the scale byte; codes packed two per
+// byte (element 2i in the low nibble) into out[0..1] (little-endian dwords).
+__device__ __forceinline__ uint32_t quantize_block16(const float* x, float g, float six_g,
+                                                     uint32_t out[2]) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; i++) amax = __builtin_fmaxf(amax, __builtin_fabsf(x[i]));
+  float q = amax / six_g;
+  uint32_t s = f32_to_e4m3_rne_sat(q);
+  float sval = e4m3_to_f32(s);
+  uint32_t w0 = 0, w1 = 0;
+  if (sval == 0.0f) {
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+      uint32_t c = (__float_as_uint(x[i]) >> 28) & 0x8u;
+      if (i < 8) w0 |= c << (4 * i); else w1 |= c << (4 * (i - 8));
+    }
+  } else {
+    float d = sval * g;
+    float r = 1.0f / d;
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+      uint32_t c = f32_to_e2m1_rne_sat(x[i] * r);
+      if (i < 8) w0 |= c << (4 * i); else w1 |= c << (4 * (i - 8));
+    }
+  }
+  out[0] = w0;
+  out[1] = w1;
+  return s;
+}
+
+// Decode one dword of 8 e2m1 codes (element 0 in the low nibble) times the
+// block scale s (fp16, exact: e4m3 values fit fp16's normal range) into 8 fp16
+// values.  e2m1 * e4m3 has at most 6 significant bits and lies in
+// [2^-10, 2688], so every product is exact in fp16.
+__device__ __forceinline__ half8_t decode8_e2m1_f16(uint32_t w, half2_t s2) {
+  half2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s2;
+  half2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s2;
+  half2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s2;
+  half2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s2;
+  half8_t r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+__device__ __forceinline__ half2_t scale_e4m3_to_h2(uint32_t c) {
+  _Float16 h = (_Float16)e4m3_to_f32(c);
+  half2_t r = {h, h};
+  return r;
+}
+
+}  // namespace mxg

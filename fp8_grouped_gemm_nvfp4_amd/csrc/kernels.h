@@ -1,0 +1,90 @@
+// kernels.h -- host-visible launch interfaces of the library's HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/mxg.h"
+
+namespace mxg {
+
+enum { EPI_BF16 = 0, EPI_F32 = 1, EPI_SWIGLU_NVFP4 = 2, EPI_SWIGLU_BF16 = 3 };
+enum { MODE_MASKED = 0, MODE_HETERO = 1 };
+
+// Masked layout: A [G, max_m, K], B [G, N, K], C [G, max_m, N].  For the fused
+// SwiGLU epilogue N = 2I (W13 rows: gate [0, I), up [I, 2I)) and the outputs
+// are the NVFP4 codes/scales of h [G, max_m, I] (plus optional fp32 dbg_h).
+struct MaskedGemmArgs {
+  const uint8_t* a;
+  const uint8_t* a_sf;
+  const uint8_t* b;
+  const uint8_t* b_sf;
+  void* out;
+  const int32_t* masked_m;
+  const float* alpha;   // [G] or NULL
+  float alpha_scale;    // multiplies alpha[g]
+  int G, max_m, N, K;
+  int tiles_m, tiles_n, total_tiles;
+  uint8_t* h_codes;
+  uint8_t* h_sf;
+  float* dbg_h;
+  float g_h;
+};
+
+struct HeteroGroup {
+  const uint8_t* a;
+  const uint8_t* a_sf;
+  const uint8_t* b;
+  const uint8_t* b_sf;
+  void* out;
+  int M, N, K, ldc;
+  float alpha;
+  int tiles_m, tiles_n, tile_base;
+};
+
+struct HeteroGemmArgs {
+  HeteroGroup grp[MXG_MAX_GROUPS];
+  int G;
+  int total_tiles;
+};
+
+template <int MODE> struct ArgsOf;
+template <> struct ArgsOf<MODE_MASKED> { typedef MaskedGemmArgs type; };
+template <> struct ArgsOf<MODE_HETERO> { typedef HeteroGemmArgs type; };
+
+hipError_t gemm_nvfp4_masked(MaskedGemmArgs p, int epi, int cu_limit, hipStream_t s);
+hipError_t gemm_nvfp4_hetero(HeteroGemmArgs p, int epi, int cu_limit, hipStream_t s);
+
+// FP8 block-scaled GEMMs of the DeepSeek-V3-style expert path (masked layout).
+struct Fp8GemmArgs {
+  const uint8_t* a;     // GEMM1: e4m3 [G, max_m, K]; GEMM2: bf16 h [G, max_m, K]
+  const float* a_s;     // GEMM1: fp32 [G, max_m, K/128]; GEMM2: unused
+  const uint8_t* b;     // e4m3 [G, N, K]
+  const float* b_s;     // fp32 [G, N/128, K/128]
+  void* out;            // GEMM1: bf16 h [G, max_m, N/2]; GEMM2: fp32 [G, max_m, N]
+  const int32_t* masked_m;
+  int G, max_m, N, K;
+  int tiles_m, tiles_n, total_tiles;
+};
+hipError_t gemm_fp8_swiglu(Fp8GemmArgs p, int cu_limit, hipStream_t s);
+hipError_t gemm_bf16_fp8w(Fp8GemmArgs p, int cu_limit, hipStream_t s);
+
+// Quantization, routing, dispatch, gather and combine.
+hipError_t quantize_nvfp4(const void* x, int x_dtype, long rows, int K, float g, uint8_t* codes,
+                          uint8_t* sf, hipStream_t s);
+hipError_t route_noaux(const float* logits, const float* bias, int T, int E, int n_group,
+                       int topk_group, int top_k, float rsf, int32_t* ids, float* w,
+                       hipStream_t s);
+hipError_t dispatch(const int32_t* ids, int T, int E, int top_k, int max_m, int32_t* masked_m,
+                    int32_t* row, hipStream_t s);
+hipError_t quantize_gather_nvfp4(const uint16_t* x, int T, int H, float g_x, const int32_t* ids,
+                                 const int32_t* row, int top_k, int max_m, uint8_t* a,
+                                 uint8_t* a_sf, hipStream_t s);
+hipError_t gather_fp8(const uint8_t* xq, const float* xs, int T, int H, const int32_t* ids,
+                      const int32_t* row, int top_k, int max_m, uint8_t* a, float* a_s,
+                      hipStream_t s);
+hipError_t combine(const float* o, const int32_t* ids, const int32_t* row, const float* w, int T,
+                   int H, int top_k, int max_m, uint16_t* y, hipStream_t s);
+
+}  // namespace mxg

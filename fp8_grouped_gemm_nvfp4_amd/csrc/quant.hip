@@ -1,0 +1,161 @@
+// quant.hip -- NVFP4 quantization of activations, the gather of quantized
+// token rows into the per-expert masked layout, and the FP8 row gather.
+//
+// NVFP4 recipe (e2m1 values with per-16 e4m3 block scales and an fp32 global
+// scale; "The CuteDSL Gamble", "Input Knowledge Required"), per block, fp32,
+// round to nearest at every step: S = e4m3(amax / (6 g)), d = S * g,
+// code = e2m1(x * (1 / d)).  One thread owns one 16-element block, so loads of
+// consecutive threads are contiguous.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace mxg {
+
+template <bool BF16>
+__device__ __forceinline__ void load_block16(const void* x, size_t elem0, float v[16]) {
+  if constexpr (BF16) {
+    const u32x4_t* p = (const u32x4_t*)((const uint16_t*)x + elem0);
+    u32x4_t w0 = p[0], w1 = p[1];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      v[2 * i] = __uint_as_float(w0[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w0[i] & 0xFFFF0000u);
+      v[8 + 2 * i] = __uint_as_float(w1[i] << 16);
+      v[8 + 2 * i + 1] = __uint_as_float(w1[i] & 0xFFFF0000u);
+    }
+  } else {
+    const float4_t* p = (const float4_t*)((const float*)x + elem0);
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      float4_t w = p[i];
+      v[4 * i] = w[0]; v[4 * i + 1] = w[1]; v[4 * i + 2] = w[2]; v[4 * i + 3] = w[3];
+    }
+  }
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_quantize_nvfp4(const void* x, long nblocks, int K, float g,
+                                                        uint8_t* codes, uint8_t* sf) {
+  long b = (long)blockIdx.x * 256 + threadIdx.x;
+  if (b >= nblocks) return;
+  float v[16];
+  load_block16<BF16>(x, (size_t)b * 16, v);
+  uint32_t w[2];
+  uint32_t s = quantize_block16(v, g, 6.0f * g, w);
+  *(u32x2_t*)(codes + (size_t)b * 8) = u32x2_t{w[0], w[1]};
+  sf[b] = (uint8_t)s;
+  (void)K;
+}
+
+hipError_t quantize_nvfp4(const void* x, int x_dtype, long rows, int K, float g, uint8_t* codes,
+                          uint8_t* sf, hipStream_t s) {
+  long nblocks = rows * (long)(K / 16);
+  if (nblocks == 0) return hipSuccess;
+  dim3 grid((unsigned)((nblocks + 255) / 256));
+  if (x_dtype == MXG_BF16)
+    hipLaunchKernelGGL(k_quantize_nvfp4<true>, grid, dim3(256), 0, s, x, nblocks, K, g, codes, sf);
+  else
+    hipLaunchKernelGGL(k_quantize_nvfp4<false>, grid, dim3(256), 0, s, x, nblocks, K, g, codes, sf);
+  return hipGetLastError();
+}
+
+// Quantize token t's block once and write it to each expert row it was
+// dispatched to (slots with row >= max_m are dropped).
+__global__ __launch_bounds__(256) void k_quantize_gather(const uint16_t* x, int T, int H, float g,
+                                                         const int32_t* ids, const int32_t* row,
+                                                         int top_k, int max_m, uint8_t* a,
+                                                         uint8_t* a_sf) {
+  const int nb = H / 16;
+  long b = (long)blockIdx.x * 256 + threadIdx.x;
+  if (b >= (long)T * nb) return;
+  int t = (int)(b / nb), blk = (int)(b % nb);
+  float v[16];
+  load_block16<true>(x, (size_t)t * H + (size_t)blk * 16, v);
+  uint32_t w[2];
+  uint32_t s = quantize_block16(v, g, 6.0f * g, w);
+  for (int j = 0; j < top_k; j++) {
+    int e = ids[(size_t)t * top_k + j];
+    int r = row[(size_t)t * top_k + j];
+    if (r >= max_m) continue;
+    size_t dst = (size_t)e * max_m + r;
+    *(u32x2_t*)(a + dst * (H / 2) + (size_t)blk * 8) = u32x2_t{w[0], w[1]};
+    a_sf[dst * nb + blk] = (uint8_t)s;
+  }
+}
+
+hipError_t quantize_gather_nvfp4(const uint16_t* x, int T, int H, float g_x, const int32_t* ids,
+                                 const int32_t* row, int top_k, int max_m, uint8_t* a,
+                                 uint8_t* a_sf, hipStream_t s) {
+  long n = (long)T * (H / 16);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_quantize_gather, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, x, T, H,
+                     g_x, ids, row, top_k, max_m, a, a_sf);
+  return hipGetLastError();
+}
+
+// FP8 rows: copy the e4m3 codes (16 bytes per thread) and the 1x128 scales of
+// token t to every dispatched expert row.
+__global__ __launch_bounds__(256) void k_gather_fp8(const uint8_t* xq, const float* xs, int T, int H,
+                                                    const int32_t* ids, const int32_t* row, int top_k,
+                                                    int max_m, uint8_t* a, float* a_s) {
+  const int nc = H / 16;
+  long c = (long)blockIdx.x * 256 + threadIdx.x;
+  if (c >= (long)T * nc) return;
+  int t = (int)(c / nc), k = (int)(c % nc);
+  u32x4_t v = *(const u32x4_t*)(xq + (size_t)t * H + (size_t)k * 16);
+  bool has_scale = (k % 8) == 0;
+  float sc = has_scale ? xs[(size_t)t * (H / 128) + k / 8] : 0.0f;
+  for (int j = 0; j < top_k; j++) {
+    int e = ids[(size_t)t * top_k + j];
+    int r = row[(size_t)t * top_k + j];
+    if (r >= max_m) continue;
+    size_t dst = (size_t)e * max_m + r;
+    *(u32x4_t*)(a + dst * H + (size_t)k * 16) = v;
+    if (has_scale) a_s[dst * (H / 128) + k / 8] = sc;
+  }
+}
+
+hipError_t gather_fp8(const uint8_t* xq, const float* xs, int T, int H, const int32_t* ids,
+                      const int32_t* row, int top_k, int max_m, uint8_t* a, float* a_s,
+                      hipStream_t s) {
+  long n = (long)T * (H / 16);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_gather_fp8, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, xq, xs, T, H,
+                     ids, row, top_k, max_m, a, a_s);
+  return hipGetLastError();
+}
+
+// Weighted combine: y[t, :] = bf16(sum_j w[t, j] * o[ids[t, j], row[t, j], :]),
+// fp32 sum in slot order; each thread owns 4 consecutive columns.
+__global__ __launch_bounds__(256) void k_combine(const float* o, const int32_t* ids, const int32_t* row,
+                                                 const float* w, int T, int H, int top_k, int max_m,
+                                                 uint16_t* y) {
+  const int nq = H / 4;
+  long c = (long)blockIdx.x * 256 + threadIdx.x;
+  if (c >= (long)T * nq) return;
+  int t = (int)(c / nq), q = (int)(c % nq);
+  float4_t acc = {0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < top_k; j++) {
+    int e = ids[(size_t)t * top_k + j];
+    int r = row[(size_t)t * top_k + j];
+    if (r >= max_m) continue;
+    float wj = w[(size_t)t * top_k + j];
+    float4_t v = *(const float4_t*)(o + ((size_t)e * max_m + r) * H + (size_t)q * 4);
+#pragma unroll
+    for (int i = 0; i < 4; i++) acc[i] = __builtin_fmaf(wj, v[i], acc[i]);
+  }
+  uint32_t lo = f32_to_bf16_rne(acc[0]) | (f32_to_bf16_rne(acc[1]) << 16);
+  uint32_t hi = f32_to_bf16_rne(acc[2]) | (f32_to_bf16_rne(acc[3]) << 16);
+  *(u32x2_t*)(y + (size_t)t * H + (size_t)q * 4) = u32x2_t{lo, hi};
+}
+
+hipError_t combine(const float* o, const int32_t* ids, const int32_t* row, const float* w, int T,
+                   int H, int top_k, int max_m, uint16_t* y, hipStream_t s) {
+  long n = (long)T * (H / 4);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, o, ids, row, w, T,
+                     H, top_k, max_m, y);
+  return hipGetLastError();
+}
+
+}  // namespace mxg

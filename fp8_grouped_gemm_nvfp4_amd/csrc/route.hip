@@ -1,0 +1,158 @@
+// route.hip -- DeepSeek-V3 no-aux routing and the token -> expert permutation.
+//
+// Routing ("llm-assisted-kernel-dev" README, mixture-of-experts table:
+// sigmoid(logits) + bias, grouped top-k, routed_scaling_factor).  One
+// wavefront per token; with E = 256 each lane owns 4 consecutive experts, so
+// a group of E / n_group experts is a run of 64 / n_group lanes.  Group top-2
+// sums and the top-k rounds are wave reductions (xor shuffles); ties resolve to
+// the lower index at every comparison.  All value arithmetic is fp32 with
+// round to nearest; the sigmoid is evaluated in fp64 and rounded once.
+//
+// Dispatch (per-expert valid row count masked_m of the masked grouped GEMM,
+// "The CuteDSL Gamble", "The Message"): one workgroup per expert scans the
+// flattened [T * top_k] id list in order; wavefront ballots and a prefix count
+// give each matching slot its stable rank.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace mxg {
+
+__device__ __forceinline__ bool better(float v, int i, float w, int j) {
+  return v > w || (v == w && i < j);
+}
+
+__global__ __launch_bounds__(256) void k_route_noaux(const float* logits, const float* bias, int T,
+                                                     int n_group, int topk_group, int top_k, float rsf,
+                                                     int32_t* ids, float* wout) {
+  constexpr int E = 256;
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;  // whole wave exits together
+
+  float s[4], sb[4];
+  const float4_t lg = *(const float4_t*)(logits + (size_t)t * E + lane * 4);
+  const float4_t bs = *(const float4_t*)(bias + lane * 4);
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    s[i] = (float)(1.0 / (1.0 + exp(-(double)lg[i])));
+    sb[i] = s[i] + bs[i];
+  }
+  // group score: sum of the two largest sb in the group (values only)
+  float m1 = sb[0], m2 = -INFINITY;
+#pragma unroll
+  for (int i = 1; i < 4; i++) {
+    float v = sb[i];
+    if (v > m1) { m2 = m1; m1 = v; } else if (v > m2) { m2 = v; }
+  }
+  const int glanes = 64 / n_group;
+  for (int off = 1; off < glanes; off <<= 1) {
+    float o1 = __shfl_xor(m1, off), o2 = __shfl_xor(m2, off);
+    float n1 = fmaxf(m1, o1);
+    float n2 = fmaxf(fminf(m1, o1), fmaxf(m2, o2));
+    m1 = n1; m2 = n2;
+  }
+  const float gscore = m1 + m2;
+  const int mygroup = lane / glanes;
+  // rank of my group among all groups (score desc, index asc)
+  int rank = 0;
+  for (int q = 0; q < n_group; q++) {
+    float gq = __shfl(gscore, q * glanes);
+    if (better(gq, q, gscore, mygroup)) rank++;
+  }
+  const bool keep = rank < topk_group;
+
+  bool taken[4] = {false, false, false, false};
+  int my_id = -1;
+  float my_s = 0.0f;
+  for (int j = 0; j < top_k; j++) {
+    float bv = -INFINITY;
+    int bi = 0x7FFFFFFF;
+    float bsv = 0.0f;
+    if (keep) {
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        int e = lane * 4 + i;
+        if (!taken[i] && (bi == 0x7FFFFFFF || better(sb[i], e, bv, bi))) { bv = sb[i]; bi = e; bsv = s[i]; }
+      }
+    }
+    for (int off = 32; off >= 1; off >>= 1) {
+      float ov = __shfl_xor(bv, off);
+      int oi = __shfl_xor(bi, off);
+      float os = __shfl_xor(bsv, off);
+      bool take_other = (oi != 0x7FFFFFFF) && (bi == 0x7FFFFFFF || better(ov, oi, bv, bi));
+      if (take_other) { bv = ov; bi = oi; bsv = os; }
+    }
+    if ((bi >> 2) == lane) taken[bi & 3] = true;
+    if (lane == j) { my_id = bi; my_s = bsv; }
+  }
+  // denominator: fp32 sum of the selected s in slot order
+  float den = 0.0f;
+  for (int j = 0; j < top_k; j++) den = den + __shfl(my_s, j);
+  if (lane < top_k) {
+    ids[(size_t)t * top_k + lane] = my_id;
+    float q = my_s / den;
+    wout[(size_t)t * top_k + lane] = q * rsf;
+  }
+}
+
+hipError_t route_noaux(const float* logits, const float* bias, int T, int E, int n_group,
+                       int topk_group, int top_k, float rsf, int32_t* ids, float* w,
+                       hipStream_t s) {
+  (void)E;
+  if (T == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_route_noaux, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, logits, bias, T,
+                     n_group, topk_group, top_k, rsf, ids, w);
+  return hipGetLastError();
+}
+
+// One workgroup per expert e.  Each pass covers 1024 flattened slots (4 per
+// thread, in order); the rank of a matching slot is the number of matches at
+// smaller flat index, which equals the number of earlier tokens routed to e
+// because a token's ids are distinct.
+__global__ __launch_bounds__(256) void k_dispatch(const int32_t* ids, int n, int max_m,
+                                                  int32_t* masked_m, int32_t* row) {
+  const int e = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ int wave_tot[4];
+  int base = 0;
+  for (int f0 = 0; f0 < n; f0 += 1024) {
+    int f = f0 + tid * 4;
+    int match[4];
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      match[i] = (f + i < n) && ids[f + i] == e;
+      cnt += match[i];
+    }
+    // inclusive wave scan of cnt
+    int inc = cnt;
+    for (int off = 1; off < 64; off <<= 1) {
+      int v = __shfl_up(inc, off);
+      if (lane >= off) inc += v;
+    }
+    if (lane == 63) wave_tot[wave] = inc;
+    __syncthreads();
+    int before = 0, total = 0;
+    for (int w = 0; w < 4; w++) {
+      int tw = wave_tot[w];
+      if (w < wave) before += tw;
+      total += tw;
+    }
+    int r = base + before + inc - cnt;
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+      if (match[i]) row[f + i] = r++;
+    base += total;
+    __syncthreads();
+  }
+  if (tid == 0) masked_m[e] = base < max_m ? base : max_m;
+}
+
+hipError_t dispatch(const int32_t* ids, int T, int E, int top_k, int max_m, int32_t* masked_m,
+                    int32_t* row, hipStream_t s) {
+  hipLaunchKernelGGL(k_dispatch, dim3((unsigned)E), dim3(256), 0, s, ids, T * top_k, max_m, masked_m,
+                     row);
+  return hipGetLastError();
+}
+
+}  // namespace mxg

@@ -1,0 +1,244 @@
+/*
+ * mxg.h -- C ABI of the MI355X (gfx950) block-scaled grouped-GEMM / MoE library.
+ *
+ * Conventions shared by every entry point
+ *  - Pointers named as device pointers must point into HBM of the current HIP
+ *    device; host pointers are marked "host".  The caller owns every buffer;
+ *    the library allocates nothing inside a call.
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *    stream) and returns before the GPU work ends.  Inputs must stay alive and
+ *    unmodified, and outputs unread, until the stream has reached that point.
+ *  - Errors are return codes (mxg_status); nothing aborts or throws.  Argument
+ *    checks run on the host before any HIP call, so a rejected call touches no
+ *    GPU state.  mxg_last_error() gives a thread-local message for the last
+ *    failure on the calling thread.
+ *  - NVFP4 tensors: e2m1 codes, two per byte, element 2i in the low nibble,
+ *    row-major [rows, K/2]; one e4m3fn scale byte per 16 consecutive K
+ *    elements, row-major [rows, K/16]; one fp32 global dequantization scale
+ *    per tensor.  A value decodes as e2m1 * e4m3(scale) * global.
+ *  - All device pointers must be 16-byte aligned.
+ *  - Calls on one stream are ordered; calls on different streams that share
+ *    an output race.
+ */
+#ifndef MXG_H
+#define MXG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MXG_OK = 0,
+  MXG_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, bad combination */
+  MXG_ERR_UNSUPPORTED = 2, /* well-formed but outside what the kernels handle  */
+  MXG_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required      */
+  MXG_ERR_HIP = 4          /* a HIP launch or runtime call failed             */
+} mxg_status;
+
+typedef enum { MXG_E2M1 = 1, MXG_E4M3 = 2, MXG_BF16 = 3, MXG_F32 = 4 } mxg_dtype;
+
+/* Static text for a status code ("unknown status" for anything else). */
+const char* mxg_status_string(int status);
+/* Thread-local detail of the last failing call on this thread ("" if none). */
+const char* mxg_last_error(void);
+/* Library version, major * 10000 + minor * 100 + patch. */
+int mxg_version(void);
+
+/*
+ * Masked grouped NT GEMM over NVFP4 operands.
+ * Source: "The CuteDSL Gamble: Chasing Kernel Efficiency on Blackwell GPUs",
+ * section "The Message" -- grouped_gemm_nt_masked(lhs=(data, sf), rhs=(data,
+ * sf), out, masked_m, ab_dtype, sf_dtype, c_dtype, sf_vec_size, sm_count), a
+ * masked batched GEMM with scale factors and optional alpha at output.
+ *
+ *   out[g, m, n] = alpha[g] * sum_k dec(A)[g, m, k] * dec(B)[g, n, k]
+ *   for g < G, m < min(max(masked_m[g], 0), max_m), n < N, accumulated in fp32.
+ *
+ *   a, a_sf    device, A codes [G, max_m, K/2], scales [G, max_m, K/16]
+ *   b, b_sf    device, B codes [G, N, K/2],     scales [G, N, K/16]
+ *   alpha      device fp32 [G] (product of the A and B global scales), or NULL = 1
+ *   masked_m   device int32 [G], valid rows per group; clamped to [0, max_m]
+ *   out        device [G, max_m, N] of c_dtype (bf16, round to nearest even, or
+ *              fp32); rows at or beyond masked_m[g] are never written
+ *   ab_dtype = MXG_E2M1, sf_dtype = MXG_E4M3, sf_vec_size = 16 (the only
+ *   supported combination); c_dtype = MXG_BF16 or MXG_F32.
+ *   cu_limit   0 = use the whole GPU; > 0 caps the number of resident
+ *              workgroups to about that many CUs (sm_count analog)
+ * Requirements: G in [1, 65535], max_m >= 1, N >= 1, K % 64 == 0 (else
+ * MXG_ERR_UNSUPPORTED).  Rows of A at or beyond masked_m are never read.
+ */
+int mx_grouped_gemm_masked(const uint8_t* a, const uint8_t* a_sf, const uint8_t* b,
+                           const uint8_t* b_sf, const float* alpha, const int32_t* masked_m,
+                           void* out, int G, int max_m, int N, int K, int ab_dtype,
+                           int sf_dtype, int c_dtype, int sf_vec_size, int cu_limit,
+                           void* stream);
+
+/*
+ * One group of a heterogeneous grouped GEMM: its own (M, N, K), operand and
+ * output pointers (device), alpha by value, and the output row stride ldc in
+ * elements (0 = N).
+ * Source: "Helion Pretuned Kernels" README, kernel table row grouped_gemm
+ * (heterogeneous grouped NT cases with M/N tails) and the benchmark notes
+ * (device pointer tables set up before graph capture); "llm-assisted-kernel-
+ * dev" README, NVFP4 grouped GEMM table (group metadata moved from runtime GPU
+ * reads into launch-time specialization).
+ */
+typedef struct {
+  int M, N, K, ldc;
+  float alpha;
+  const uint8_t* a;    /* [M, K/2]  */
+  const uint8_t* a_sf; /* [M, K/16] */
+  const uint8_t* b;    /* [N, K/2]  */
+  const uint8_t* b_sf; /* [N, K/16] */
+  void* out;           /* [M, ldc] of c_dtype */
+} mxg_group_desc;
+
+#define MXG_MAX_GROUPS 32
+
+/*
+ * Heterogeneous grouped NVFP4 NT GEMM: out_g = alpha_g * A_g * B_g^T for every
+ * group.  `groups` is a HOST array of G descriptors (copied into the kernel's
+ * launch arguments, so nothing is read from device metadata); the pointers
+ * inside are device pointers.  G in [1, MXG_MAX_GROUPS]; each group needs
+ * M >= 0, N >= 1, K % 64 == 0.  Same dtype rules as mx_grouped_gemm_masked.
+ */
+int mx_grouped_gemm(const mxg_group_desc* groups, int G, int ab_dtype, int sf_dtype,
+                    int c_dtype, int sf_vec_size, int cu_limit, void* stream);
+
+/*
+ * NVFP4 quantization of rows of x [rows, K] (x_dtype MXG_BF16 or MXG_F32,
+ * device) with global dequantization scale g > 0 (host fp32).  Per 16-element
+ * block, in fp32 with round-to-nearest at every step:
+ *   S = e4m3_rne_sat(amax / (6 g));  d = value(S) * g;
+ *   code_i = e2m1_rne_sat(x_i * (1 / d))   (all codes keep the sign of x_i;
+ *   a block whose S rounds to 0 gets zero codes)
+ * Source: NVFP4 as e2m1 values with block scale factors and a global scale
+ * ("The CuteDSL Gamble", "Input Knowledge Required"); the per-step recipe is a
+ * reading of that description.  codes [rows, K/2], sf [rows, K/16] (device).
+ * K % 16 == 0 required.
+ */
+int mx_quantize_nvfp4(const void* x, int x_dtype, long rows, int K, float g, uint8_t* codes,
+                      uint8_t* sf, void* stream);
+
+/*
+ * DeepSeek-V3 no-aux routing.  Source: "llm-assisted-kernel-dev" README,
+ * mixture-of-experts table, moe_fibench_ref.py row (sigmoid(logits) + bias,
+ * grouped top-k, routed_scaling_factor).  Per token t:
+ *   s_e  = fp32 of the fp64 value 1 / (1 + exp(-logit_e))
+ *   sb_e = s_e + bias_e (fp32)
+ *   group score = fp32 sum of the two largest sb in each of n_group contiguous
+ *   groups of E / n_group experts; keep the topk_group best groups; take the
+ *   top_k best sb among their experts; ties go to the lower index; slot j
+ *   holds the j-th best.  w_j = fp32(fp32(s_j / sum_slots s) * rsf), the sum
+ *   taken in slot order.
+ *   logits device fp32 [T, E]; bias device fp32 [E];
+ *   topk_ids device int32 [T, top_k]; topk_w device fp32 [T, top_k].
+ * Supported: E == 256, n_group in {1, 2, 4, 8}, 1 <= topk_group <= n_group,
+ * 1 <= top_k <= 8, top_k <= topk_group * E / n_group.
+ */
+int moe_route_noaux(const float* logits, const float* bias, int T, int E, int n_group,
+                    int topk_group, int top_k, float rsf, int32_t* topk_ids, float* topk_w,
+                    void* stream);
+
+/*
+ * Token-to-expert permutation for the masked layout (stable counting sort in
+ * token order).  Source: the per-expert valid row count masked_m of
+ * grouped_gemm_nt_masked ("The CuteDSL Gamble", "The Message").
+ *   row[t, j]   = number of tokens t' < t routed to expert topk_ids[t, j]
+ *   masked_m[e] = min(number of tokens routed to e, max_m)
+ * A slot whose row is >= max_m does not fit the capacity and is dropped by the
+ * later stages.  topk_ids device int32 [T, top_k] (distinct per token, in
+ * [0, E)); masked_m device int32 [E]; row device int32 [T, top_k].
+ */
+int moe_dispatch(const int32_t* topk_ids, int T, int E, int top_k, int max_m, int32_t* masked_m,
+                 int32_t* row, void* stream);
+
+/*
+ * NVFP4-quantize the bf16 activations x [T, H] (global scale g_x, same recipe
+ * as mx_quantize_nvfp4) and scatter each token's codes/scales to every expert
+ * row it was dispatched to: a[e, row, :], a_sf[e, row, :] for each slot with
+ * row < max_m.  a [E, max_m, H/2], a_sf [E, max_m, H/16] (device).
+ * H % 64 == 0 required.
+ */
+int moe_quantize_gather_nvfp4(const uint16_t* x, int T, int H, float g_x,
+                              const int32_t* topk_ids, const int32_t* row, int top_k, int E,
+                              int max_m, uint8_t* a, uint8_t* a_sf, void* stream);
+
+/* Precision of moe_expert_forward. */
+typedef enum { MXG_MOE_FP8_BLOCK128 = 1, MXG_MOE_NVFP4 = 2 } mxg_moe_precision;
+
+/*
+ * The routed expert computation of one MoE layer: gather -> GEMM1 (W13, gate
+ * rows [0, I) and up rows [I, 2I)) -> SwiGLU h = silu(gate) * up -> GEMM2 (W2)
+ * -> weighted combine y[t] = sum_j w[t, j] * o[topk_ids[t, j], row[t, j]].
+ * Source: "llm-assisted-kernel-dev" README, mixture-of-experts table
+ * (moe_fibench_ref.py: FP8 e4m3fn hidden states and both weight sets with
+ * block scales; moe_fp8fpX_fused.py: GEMM1 -> SwiGLU -> GEMM2, BF16 default).
+ *
+ * MXG_MOE_FP8_BLOCK128:
+ *   x        e4m3 codes [T, H], x_scale fp32 [T, H/128] (1x128 blocks)
+ *   w13      e4m3 [E, 2I, H], w13_scale fp32 [E, 2I/128, H/128]
+ *   w2       e4m3 [E, H, I],  w2_scale fp32 [E, H/128, I/128]
+ *   h        = bf16 (round to nearest even) of silu(gate) * up
+ * MXG_MOE_NVFP4:
+ *   x        bf16 [T, H], quantized in the layer with global scale g_x
+ *   w13      codes [E, 2I, H/2], w13_scale e4m3 [E, 2I, H/16], g_w13 fp32 [E]
+ *   w2       codes [E, H, I/2],  w2_scale e4m3 [E, H, I/16],  g_w2 fp32 [E]
+ *   h        fp32 silu(gate) * up, requantized to NVFP4 with global scale g_h
+ * Both: GEMM outputs accumulate in fp32; GEMM2 results stay fp32 until the
+ * combine, which sums in slot order in fp32 and rounds y once to bf16.
+ *   topk_ids/topk_w/masked_m/row as produced by moe_route_noaux + moe_dispatch
+ *   (device); y device bf16 [T, H].
+ *   dbg_h    optional device fp32 [E, max_m, I]: NVFP4 only, receives the
+ *            pre-quantization intermediate for the rows it computes (NULL in
+ *            production; y is bit-identical either way).
+ * Requirements: H % 128 == 0, I % 128 == 0, 1 <= top_k <= 8, max_m >= 1.
+ * Workspace: ws of at least moe_expert_forward_workspace_size(desc) bytes,
+ * 256-byte aligned, device; its regions hold the gathered activations, h and
+ * the GEMM2 output (offsets from moe_expert_forward_workspace_layout).
+ */
+typedef struct {
+  int precision;
+  int T, H, I, E, top_k, max_m;
+  const void* x;
+  const float* x_scale;
+  float g_x;
+  const uint8_t* w13;
+  const void* w13_scale;
+  const float* g_w13;
+  const uint8_t* w2;
+  const void* w2_scale;
+  const float* g_w2;
+  float g_h;
+  const int32_t* topk_ids;
+  const float* topk_w;
+  const int32_t* masked_m;
+  const int32_t* row;
+  uint16_t* y;
+  float* dbg_h;
+} mxg_moe_desc;
+
+/* Bytes of workspace moe_expert_forward needs for this descriptor (0 on a bad
+ * descriptor). */
+size_t moe_expert_forward_workspace_size(const mxg_moe_desc* desc);
+
+/* Byte offsets (host array of 6) of the workspace regions:
+ *   [0] gathered activations (FP8: e4m3 [E, max_m, H]; NVFP4: codes [E, max_m, H/2])
+ *   [1] their scales (FP8: fp32 [E, max_m, H/128]; NVFP4: e4m3 [E, max_m, H/16])
+ *   [2] h (FP8: bf16 [E, max_m, I]; NVFP4: codes [E, max_m, I/2])
+ *   [3] h scales (FP8: unused; NVFP4: e4m3 [E, max_m, I/16])
+ *   [4] GEMM2 output fp32 [E, max_m, H]
+ *   [5] total size
+ * Returns MXG_OK or MXG_ERR_INVALID_ARG. */
+int moe_expert_forward_workspace_layout(const mxg_moe_desc* desc, size_t* offsets);
+
+int moe_expert_forward(const mxg_moe_desc* desc, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXG_H */

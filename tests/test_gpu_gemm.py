@@ -1,0 +1,201 @@
+"""GPU parity of the NVFP4 grouped GEMMs against the oracle (element by element on
+small cases, sampled rows at the workloads' full sizes)."""
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import oracle
+from _helpers import (SENT_BF16, SENT_F32, assert_within, bf16_from_bits_np, bf16_tensor_bits, log,
+                      np_, sentinel_bf16, sentinel_f32, ulp_f32)
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0") if torch.cuda.is_available() else None
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    import fp8_grouped_gemm_nvfp4_amd as mxg
+    mxg.lib()
+
+
+def _mxg():
+    import fp8_grouped_gemm_nvfp4_amd as mxg
+    return mxg
+
+
+def _run_masked(t, max_m, N, out_dtype=torch.bfloat16, cu_limit=0):
+    G = t["a"].shape[0]
+    if out_dtype == torch.bfloat16:
+        out = sentinel_bf16((G, max_m, N), DEV)
+    else:
+        out = sentinel_f32((G, max_m, N), DEV)
+    _mxg().mx_grouped_gemm_masked(t["a"], t["a_sf"], t["b"], t["b_sf"], t.get("alpha"), t["masked_m"], out,
+                                  cu_limit=cu_limit)
+    torch.cuda.synchronize()
+    return out
+
+
+def _check_masked(t, out, max_m, N, K, what):
+    h = {k: np_(v) for k, v in t.items() if v is not None}
+    mm = np.clip(h["masked_m"], 0, max_m)
+    y, s, _ = oracle.gemm_nvfp4_masked(h["a"], h["a_sf"], h["b"], h["b_sf"], h.get("alpha"), h["masked_m"],
+                                       max_m, N, K)
+    if out.dtype == torch.bfloat16:
+        bits = bf16_tensor_bits(out)
+        vals = bf16_from_bits_np(bits)
+        sent, ulp = SENT_BF16, None
+    else:
+        bits = np_(out.view(torch.int32)).view(np.uint32)
+        vals = np_(out).astype(np.float64)
+        sent, ulp = SENT_F32, ulp_f32
+    for g in range(len(mm)):
+        m = int(mm[g])
+        assert (bits[g, m:] == sent).all(), f"{what}: group {g} rows >= masked_m={m} were written"
+        if m:
+            kw = {} if ulp is None else {"ulp": ulp}
+            assert_within(vals[g, :m], y[g, :m], s[g, :m], f"{what} group {g}", **kw)
+
+
+@pytest.mark.parametrize("seed", [1000, 1001, 1002])
+def test_masked_gemm_g4_m64_n512_k1024(seed):
+    log(f"masked NVFP4 GEMM G=4 max_m=64 N=512 K=1024 seed={seed}")
+    wl = datagen.masked_gemm_workload(seed, DEV)
+    out = _run_masked(wl.tensors, 64, 512)
+    _check_masked(wl.tensors, out, 64, 512, 1024, f"seed {seed}")
+
+
+@pytest.mark.parametrize("G,max_m,N,K,mm", [
+    (4, 64, 512, 1024, [0, 64, 1, 63]),
+    (3, 64, 512, 1024, [99, -3, 17]),        # clamped to [0, max_m]
+    (1, 1, 16, 64, [1]),                     # smallest case, one K step
+    (2, 37, 520, 256, [37, 20]),             # M and N tails
+    (2, 200, 136, 128, [200, 129]),          # several 128-row tiles, ragged
+    (5, 8, 4096, 512, [1, 0, 8, 3, 1]),      # decode-shaped (16-row tiles)
+    (2, 16, 264, 192, [16, 5]),
+])
+def test_masked_gemm_edges(G, max_m, N, K, mm):
+    log(f"masked NVFP4 GEMM edge G={G} max_m={max_m} N={N} K={K} masked_m={mm}")
+    wl = datagen.masked_gemm_workload(7, DEV, G=G, max_m=max_m, N=N, K=K, masked_m=mm)
+    out = _run_masked(wl.tensors, max_m, N)
+    _check_masked(wl.tensors, out, max_m, N, K, "edge")
+
+
+def test_masked_gemm_general_scales_fp32_out_and_poison():
+    """General e4m3 scales (including subnormal codes and negative scales), fp32 output,
+    and A rows beyond masked_m poisoned with NaN scales (never read)."""
+    log("masked NVFP4 GEMM general scales / fp32 out / poisoned padding")
+    g = datagen.generator(11, DEV)
+    G, max_m, N, K = 3, 48, 200, 320
+    t = dict(a=datagen.uniform_bytes(g, (G, max_m, K // 2), DEV),
+             a_sf=torch.randint(0, 0x7F, (G, max_m, K // 16), generator=g, device=DEV, dtype=torch.int32).to(torch.uint8),
+             b=datagen.uniform_bytes(g, (G, N, K // 2), DEV),
+             b_sf=(torch.randint(0, 0x7F, (G, N, K // 16), generator=g, device=DEV, dtype=torch.int32)
+                   | (torch.randint(0, 2, (G, N, K // 16), generator=g, device=DEV, dtype=torch.int32) << 7)).to(torch.uint8),
+             masked_m=torch.tensor([48, 30, 5], dtype=torch.int32, device=DEV),
+             alpha=torch.tensor([0.37, 1.0, 3.5e-3], dtype=torch.float32, device=DEV))
+    t["a_sf"][1, 30:] = 0x7F
+    t["a_sf"][2, 5:] = 0xFF
+    for dt in (torch.float32, torch.bfloat16):
+        out = _run_masked(t, max_m, N, out_dtype=dt)
+        vals = np_(out.float())
+        for gg, m in enumerate([48, 30, 5]):
+            assert np.isfinite(vals[gg, :m]).all()
+        _check_masked(t, out, max_m, N, K, f"general scales {dt}")
+
+
+def test_masked_gemm_cu_limit_and_determinism():
+    log("masked NVFP4 GEMM cu_limit grid-stride path and run-to-run determinism")
+    wl = datagen.masked_gemm_workload(21, DEV, G=8, max_m=130, N=384, K=512)
+    o1 = _run_masked(wl.tensors, 130, 384)
+    o2 = _run_masked(wl.tensors, 130, 384)
+    o3 = _run_masked(wl.tensors, 130, 384, cu_limit=3)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(o1.view(torch.int16), o3.view(torch.int16))
+    _check_masked(wl.tensors, o3, 130, 384, 512, "cu_limit")
+
+
+def test_decode_gemm1_full_size():
+    """Decode-shaped MoE GEMM1 at its full size: 256 experts, 8 tokens top-8, K=7168,
+    N=4096 (gate and up stacked): dispatch, on-the-fly NVFP4 quantization of the bf16
+    activations into the masked layout, then the masked GEMM with bf16 output."""
+    log("decode GEMM1 E=256 T=8 top8 H=7168 N=4096")
+    mxg = _mxg()
+    wl = datagen.decode_gemm1_workload(1001, DEV)
+    t, s = wl.tensors, wl.scalars
+    E, T, H, N, max_m = 256, 8, 7168, 4096, 8
+    masked_m, row = mxg.moe_dispatch(t["ids"], E, max_m)
+    a, a_sf = mxg.moe_quantize_gather_nvfp4(t["x"], s["g_x"], t["ids"], row, E, max_m)
+    alpha = torch.full((E,), np.float32(s["g_x"]) * np.float32(s["g_w"]), dtype=torch.float32, device=DEV)
+    out = sentinel_bf16((E, max_m, N), DEV)
+    mxg.mx_grouped_gemm_masked(a, a_sf, t["w13"], t["w13_sf"], alpha, masked_m, out)
+    torch.cuda.synchronize()
+    ids = np_(t["ids"])
+    mm_o, row_o = oracle.dispatch(ids, E, max_m)
+    assert np.array_equal(np_(masked_m), mm_o) and np.array_equal(np_(row), row_o)
+    xq, xsf = oracle.quantize_nvfp4(np_(t["x"].float()), s["g_x"])
+    a_h, asf_h = np_(a), np_(a_sf)
+    for tt in range(T):
+        for j in range(8):
+            e, r = ids[tt, j], row_o[tt, j]
+            assert np.array_equal(a_h[e, r], xq[tt]) and np.array_equal(asf_h[e, r], xsf[tt])
+    bits = bf16_tensor_bits(out)
+    w_h, wsf_h = np_(t["w13"]), np_(t["w13_sf"])
+    active = np.nonzero(mm_o)[0]
+    for e in active:
+        assert (bits[e, mm_o[e]:] == SENT_BF16).all()
+        for m in range(mm_o[e]):
+            y, S = oracle.nvfp4_row_dot(a_h[e], asf_h[e], m, w_h[e], wsf_h[e], H, float(alpha[0].item()))
+            assert_within(bf16_from_bits_np(bits[e, m]), y, S, f"expert {e} row {m}")
+    idle = np.nonzero(mm_o == 0)[0]
+    assert (bits[idle] == SENT_BF16).all()
+    log(f"decode GEMM1 ok: {len(active)} active experts, sum masked_m={mm_o.sum()}")
+
+
+HETERO = ((128, 4096, 7168), (1000, 2048, 7168), (4096, 7168, 2048), (37, 4096, 4096))
+
+
+def _run_hetero(shapes, seed):
+    wl = datagen.hetero_gemm_workload(seed, DEV, shapes)
+    groups = []
+    for q in wl.tensors["groups"]:
+        q = dict(q)
+        q["out"] = sentinel_bf16((q["M"], q["N"]), DEV)
+        groups.append(q)
+    _mxg().mx_grouped_gemm(groups)
+    torch.cuda.synchronize()
+    return groups
+
+
+def test_hetero_gemm_full_size_sampled():
+    log("heterogeneous NVFP4 grouped GEMM (128,4096,7168) (1000,2048,7168) (4096,7168,2048) (37,4096,4096)")
+    groups = _run_hetero(HETERO, 1002)
+    rng = np.random.default_rng(5)
+    for gi, q in enumerate(groups):
+        M, N, K = q["M"], q["N"], q["K"]
+        bits = bf16_tensor_bits(q["out"])
+        assert not (bits == SENT_BF16).any(), f"group {gi}: unwritten outputs"
+        a, asf, b, bsf = np_(q["a"]), np_(q["a_sf"]), np_(q["b"]), np_(q["b_sf"])
+        rows = sorted(set(rng.choice(M, size=min(M, 6), replace=False).tolist() + [0, M - 1]))
+        for m in rows:
+            y, S = oracle.nvfp4_row_dot(a, asf, m, b, bsf, K, q["alpha"])
+            assert_within(bf16_from_bits_np(bits[m]), y, S, f"group {gi} row {m}")
+        log(f"group {gi} ({M},{N},{K}) rows {rows} ok")
+
+
+@pytest.mark.parametrize("shapes", [
+    ((37, 520, 1024), (0, 64, 128), (130, 600, 128), (1, 16, 64)),
+    ((256, 256, 256),),
+])
+def test_hetero_gemm_tails_full(shapes):
+    log(f"heterogeneous NVFP4 grouped GEMM tails {shapes}")
+    groups = _run_hetero(shapes, 3)
+    for gi, q in enumerate(groups):
+        if q["M"] == 0:
+            continue
+        bits = bf16_tensor_bits(q["out"])
+        y, S, _ = oracle.gemm_nvfp4_masked(np_(q["a"])[None], np_(q["a_sf"])[None], np_(q["b"])[None],
+                                           np_(q["b_sf"])[None], np.array([q["alpha"]], np.float32),
+                                           [q["M"]], q["M"], q["N"], q["K"])
+        assert_within(bf16_from_bits_np(bits), y[0], S[0], f"group {gi}")

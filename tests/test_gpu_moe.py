@@ -1,0 +1,208 @@
+"""GPU parity of the MoE expert path (routing -> dispatch -> GEMM1 -> SwiGLU -> GEMM2 ->
+combine) for the NVFP4 and the FP8 block-scaled precisions.
+
+Each stage is checked against the oracle applied to the GPU's own inputs to that stage
+(teacher forcing): a GPU that accumulates in fp32 may legitimately land on the other
+side of a bf16 / e2m1 rounding boundary than the fp64 oracle, and one flipped code
+changes everything downstream.  Integer stages (ids, rows, masked_m, codes, scale
+bytes) are bit-exact; the timed run (no debug output) must reproduce y bit for bit.
+
+SwiGLU tolerance (derived): with the GEMM1 outputs inside t_g = 1e-5 S_g + ulp32(g),
+t_u = 1e-5 S_u + ulp32(u), and |silu'| <= 1.1,
+    |h_gpu - h*| <= 1.1 (|u| + t_u) t_g + |silu(g)| t_u + 8 ulp32(h*)
+(+ 1 bf16 ulp when h is stored as bf16).
+"""
+import numpy as np
+import pytest
+import torch
+from scipy.special import expit
+
+import datagen
+import oracle
+from _helpers import assert_within, bf16_from_bits_np, bf16_tensor_bits, log, np_, ulp_bf16, ulp_f32
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0") if torch.cuda.is_available() else None
+E, TOPK = 256, 8
+
+
+def _mxg():
+    import fp8_grouped_gemm_nvfp4_amd as mxg
+    return mxg
+
+
+def _route_dispatch(t, cap=None):
+    mxg = _mxg()
+    ids, w = mxg.moe_route_noaux(t["logits"], t["bias"], 8, 4, TOPK, 2.5)
+    if cap is None:
+        mm_full, _ = mxg.moe_dispatch(ids, E, 1 << 20)
+        cap = max(64, -(-int(mm_full.max().item()) // 64) * 64)
+    masked_m, row = mxg.moe_dispatch(ids, E, cap)
+    torch.cuda.synchronize()
+    ids_o, w_o = oracle.route_noaux(np_(t["logits"]), np_(t["bias"]), 8, 4, TOPK, 2.5)
+    assert np.array_equal(np_(ids), ids_o), "routing ids"
+    assert np.array_equal(np_(w).view(np.uint32), w_o.view(np.uint32)), "routing weights"
+    mm_o, row_o = oracle.dispatch(ids_o, E, cap)
+    assert np.array_equal(np_(masked_m), mm_o) and np.array_equal(np_(row), row_o), "dispatch"
+    return ids, w, masked_m, row, cap
+
+
+def _swiglu_tol(g, u, Sg, Su, h):
+    tg = 1e-5 * Sg + ulp_f32(g)
+    tu = 1e-5 * Su + ulp_f32(u)
+    return 1.1 * (np.abs(u) + tu) * tg + np.abs(g * expit(g)) * tu + 8 * ulp_f32(h)
+
+
+def _tokens(T, n, seed):
+    if n is None or n >= T:
+        return list(range(T))
+    rng = np.random.default_rng(seed)
+    return sorted(rng.choice(T, size=n, replace=False).tolist())
+
+
+# ----------------------------------------------------------------------------- NVFP4
+def _run_nvfp4(T, H, I, seed, n_check, cap=None):
+    mxg = _mxg()
+    wl = datagen.moe_nvfp4_workload(seed, DEV, T=T, H=H, I=I)
+    t, s = wl.tensors, wl.scalars
+    ids, w, masked_m, row, max_m = _route_dispatch(t, cap)
+    y_dbg = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
+    y = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
+    dbg_h = torch.full((E, max_m, I), float("nan"), dtype=torch.float32, device=DEV)
+    common = dict(precision=mxg.MXG_MOE_NVFP4, T=T, H=H, I=I, E=E, top_k=TOPK, max_m=max_m,
+                  x=t["x"], w13=t["w13"], w13_scale=t["w13_sf"], w2=t["w2"], w2_scale=t["w2_sf"],
+                  topk_ids=ids, topk_w=w, masked_m=masked_m, row=row, g_x=s["g_x"], g_w13=t["g_w13"],
+                  g_w2=t["g_w2"], g_h=s["g_h"])
+    d_dbg = mxg.make_moe_desc(y=y_dbg, dbg_h=dbg_h, **common)
+    d = mxg.make_moe_desc(y=y, **common)
+    off = mxg.moe_expert_forward_workspace_layout(d)
+    ws = torch.empty((off[5],), dtype=torch.uint8, device=DEV)
+    mxg.moe_expert_forward(d_dbg, ws)
+    torch.cuda.synchronize()
+    wsh = {"a": np_(ws[off[0]:off[0] + E * max_m * H // 2]).reshape(E, max_m, H // 2),
+           "a_sf": np_(ws[off[1]:off[1] + E * max_m * H // 16]).reshape(E, max_m, H // 16),
+           "hc": np_(ws[off[2]:off[2] + E * max_m * I // 2]).reshape(E, max_m, I // 2),
+           "hsf": np_(ws[off[3]:off[3] + E * max_m * I // 16]).reshape(E, max_m, I // 16)}
+    mxg.moe_expert_forward(d, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y_dbg.view(torch.int16)), "timed run differs from debug run"
+
+    ids_h, w_h, row_h = np_(ids), np_(w), np_(row)
+    dbg = np_(dbg_h)
+    yb = bf16_from_bits_np(bf16_tensor_bits(y))
+    xq, xsf = oracle.quantize_nvfp4(np_(t["x"].float()), s["g_x"])
+    g_w13, g_w2 = np_(t["g_w13"]), np_(t["g_w2"])
+    wcache = {}
+
+    def weights(e):
+        if e not in wcache:
+            wcache[e] = (np_(t["w13"][e]), np_(t["w13_sf"][e]), np_(t["w2"][e]), np_(t["w2_sf"][e]))
+        return wcache[e]
+
+    toks = _tokens(T, n_check, seed)
+    for tt in toks:
+        o_list, so_list, wj = [], [], []
+        for j in range(TOPK):
+            e, r = int(ids_h[tt, j]), int(row_h[tt, j])
+            if r >= max_m:
+                continue  # dropped by the capacity
+            w13, w13sf, w2, w2sf = weights(e)
+            assert np.array_equal(wsh["a"][e, r], xq[tt]) and np.array_equal(wsh["a_sf"][e, r], xsf[tt]), \
+                f"quantized x token {tt} slot {j}"
+            gu, S1 = oracle.nvfp4_row_dot(wsh["a"][e], wsh["a_sf"][e], r, w13, w13sf, H,
+                                          float(g_w13[e]) * s["g_x"])
+            g, u, Sg, Su = gu[:I], gu[I:], S1[:I], S1[I:]
+            hstar = oracle.swiglu(gu[None], I)[0]
+            tol = _swiglu_tol(g, u, Sg, Su, hstar)
+            err = np.abs(dbg[e, r].astype(np.float64) - hstar)
+            assert np.all(err <= tol), f"h token {tt} slot {j}: max excess {np.max(err - tol)}"
+            hq, hs = oracle.quantize_nvfp4(dbg[e, r][None], s["g_h"])
+            assert np.array_equal(wsh["hc"][e, r], hq[0]) and np.array_equal(wsh["hsf"][e, r], hs[0]), \
+                f"requantized h token {tt} slot {j}"
+            o, So = oracle.nvfp4_row_dot(wsh["hc"][e], wsh["hsf"][e], r, w2, w2sf, I, float(g_w2[e]) * s["g_h"])
+            o_list.append(o); so_list.append(So); wj.append(w_h[tt, j])
+        if not o_list:
+            assert np.all(yb[tt] == 0), f"token {tt} fully dropped must give y = 0"
+            continue
+        ystar, S = oracle.combine(np.array(o_list), np.array(so_list), np.array(wj))
+        assert_within(yb[tt], ystar, S, f"y token {tt}")
+    log(f"NVFP4 MoE T={T} H={H} I={I} max_m={max_m}: {len(toks)} tokens checked, "
+        f"{len(wcache)} experts touched")
+
+
+def test_moe_nvfp4_small_full():
+    log("NVFP4 MoE small: T=64 H=512 I=256 E=256, every token")
+    _run_nvfp4(64, 512, 256, 4000, None)
+
+
+def test_moe_nvfp4_capacity_drop():
+    log("NVFP4 MoE with a capacity below the busiest expert (slots dropped)")
+    _run_nvfp4(96, 256, 128, 4001, None, cap=2)
+
+
+def test_moe_nvfp4_decode_full_size():
+    log("NVFP4 MoE decode: T=64 H=7168 I=2048, 6 tokens checked")
+    _run_nvfp4(64, 7168, 2048, 1004, 6)
+
+
+def test_moe_nvfp4_prefill_full_size():
+    log("NVFP4 MoE prefill: T=8192 H=7168 I=2048, 3 tokens checked")
+    _run_nvfp4(8192, 7168, 2048, 1004, 3)
+
+
+# ----------------------------------------------------------------------------- FP8
+def _run_fp8(T, H, I, seed, n_check):
+    mxg = _mxg()
+    wl = datagen.moe_fp8_workload(seed, DEV, T=T, H=H, I=I)
+    t = wl.tensors
+    ids, w, masked_m, row, max_m = _route_dispatch(t)
+    y = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
+    d = mxg.make_moe_desc(mxg.MXG_MOE_FP8_BLOCK128, T, H, I, E, TOPK, max_m, t["xq"], t["w13"], t["w13_s"],
+                          t["w2"], t["w2_s"], ids, w, masked_m, row, y, x_scale=t["xs"])
+    off = mxg.moe_expert_forward_workspace_layout(d)
+    ws = torch.empty((off[5],), dtype=torch.uint8, device=DEV)
+    mxg.moe_expert_forward(d, ws)
+    torch.cuda.synchronize()
+    y1 = y.clone()
+    mxg.moe_expert_forward(d, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y1.view(torch.int16)), "two runs differ"
+    a = np_(ws[off[0]:off[0] + E * max_m * H]).reshape(E, max_m, H)
+    a_s = np_(ws[off[1]:off[1] + E * max_m * (H // 128) * 4].view(torch.float32)).reshape(E, max_m, H // 128)
+    hb = np_(ws[off[2]:off[2] + E * max_m * I * 2].view(torch.int16)).view(np.uint16).reshape(E, max_m, I)
+    ids_h, w_h, row_h = np_(ids), np_(w), np_(row)
+    xq, xs = np_(t["xq"]), np_(t["xs"])
+    yb = bf16_from_bits_np(bf16_tensor_bits(y))
+    toks = _tokens(T, n_check, seed)
+    touched = set()
+    for tt in toks:
+        o_list, so_list, wj = [], [], []
+        for j in range(TOPK):
+            e, r = int(ids_h[tt, j]), int(row_h[tt, j])
+            touched.add(e)
+            assert np.array_equal(a[e, r], xq[tt]) and np.array_equal(a_s[e, r], xs[tt]), f"gathered x {tt}/{j}"
+            w13, w13s = np_(t["w13"][e]), np_(t["w13_s"][e])
+            gu, S1 = oracle.gemm_fp8_block(xq, xs, w13, w13s, rows=[tt])
+            gu, S1 = gu[0], S1[0]
+            g, u = gu[:I], gu[I:]
+            hstar = oracle.swiglu(gu[None], I)[0]
+            tol = _swiglu_tol(g, u, S1[:I], S1[I:], hstar) + ulp_bf16(hstar)
+            hv = bf16_from_bits_np(hb[e, r])
+            err = np.abs(hv - hstar)
+            assert np.all(err <= tol), f"h token {tt} slot {j}: max excess {np.max(err - tol)}"
+            o, So = oracle.gemm_dense_fp8w(hv[None], np_(t["w2"][e]), np_(t["w2_s"][e]))
+            o_list.append(o[0]); so_list.append(So[0]); wj.append(w_h[tt, j])
+        ystar, S = oracle.combine(np.array(o_list), np.array(so_list), np.array(wj))
+        assert_within(yb[tt], ystar, S, f"y token {tt}")
+    log(f"FP8 MoE T={T} H={H} I={I} max_m={max_m}: {len(toks)} tokens, {len(touched)} experts")
+
+
+def test_moe_fp8_small_full():
+    log("FP8 MoE small: T=128 H=512 I=256 E=256, every token")
+    _run_fp8(128, 512, 256, 3000, None)
+
+
+def test_moe_fp8_full_size():
+    log("FP8 MoE prefill: T=4096 H=7168 I=2048, 3 tokens checked")
+    _run_fp8(4096, 7168, 2048, 1003, 3)

@@ -1,0 +1,116 @@
+"""GPU parity of routing, dispatch and NVFP4 quantization: bit-exact against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import oracle
+from _helpers import log, np_
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0") if torch.cuda.is_available() else None
+
+
+def _mxg():
+    import fp8_grouped_gemm_nvfp4_amd as mxg
+    return mxg
+
+
+@pytest.mark.parametrize("T,ng,tg,k,seed", [
+    (4096, 8, 4, 8, 3), (8192, 8, 4, 8, 4), (64, 8, 4, 8, 5), (1, 8, 4, 8, 6),
+    (333, 1, 1, 8, 7), (200, 4, 2, 6, 8), (100, 2, 1, 1, 9),
+])
+def test_route_bit_exact(T, ng, tg, k, seed):
+    log(f"route T={T} n_group={ng} topk_group={tg} top_k={k}")
+    gen = datagen.generator(seed, DEV)
+    logits, bias = datagen.router_inputs(gen, T, 256, DEV)
+    if T >= 64:
+        logits[: T // 8] = torch.round(logits[: T // 8] * 4) / 4  # planted ties
+    ids, w = _mxg().moe_route_noaux(logits, bias, ng, tg, k, 2.5)
+    torch.cuda.synchronize()
+    ids_o, w_o = oracle.route_noaux(np_(logits), np_(bias), ng, tg, k, 2.5)
+    ids_g, w_g = np_(ids), np_(w)
+    bad = np.nonzero((ids_g != ids_o).any(axis=1))[0]
+    assert len(bad) == 0, f"{len(bad)} tokens differ, first {bad[:3]}: {ids_g[bad[0]]} vs {ids_o[bad[0]]}"
+    assert np.array_equal(w_g.view(np.uint32), w_o.view(np.uint32)), "weights differ"
+
+
+@pytest.mark.parametrize("T,k,max_m", [(8, 8, 8), (64, 8, 64), (4096, 8, 256), (8192, 8, 512), (1000, 3, 5)])
+def test_dispatch_bit_exact(T, k, max_m):
+    log(f"dispatch T={T} top_k={k} max_m={max_m}")
+    gen = datagen.generator(T + k, DEV)
+    ids = datagen.distinct_topk_ids(gen, T, 256, k, DEV)
+    mm, row = _mxg().moe_dispatch(ids, 256, max_m)
+    torch.cuda.synchronize()
+    mm_o, row_o = oracle.dispatch(np_(ids), 256, max_m)
+    assert np.array_equal(np_(mm), mm_o)
+    assert np.array_equal(np_(row), row_o)
+
+
+def _quant_inputs(gen, rows, K):
+    x = torch.randn((rows, K), generator=gen, device=DEV) * 3
+    x[0] = 0.0
+    x[1, ::2] = -0.0
+    x[2] = 1e30
+    x[3] = torch.randn((K,), generator=gen, device=DEV) * 1e-30
+    x[4, ::16] = 6.0
+    x[5] = torch.arange(K, device=DEV, dtype=torch.float32) / 8 - K / 16
+    return x
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("g", [1.0, 0.0123, 37.5])
+def test_quantize_bit_exact(dtype, g):
+    log(f"NVFP4 quantize dtype={dtype} g={g}")
+    gen = datagen.generator(17, DEV)
+    x = _quant_inputs(gen, 512, 1024).to(dtype)
+    codes, sf = _mxg().mx_quantize_nvfp4(x, g)
+    torch.cuda.synchronize()
+    c_o, s_o = oracle.quantize_nvfp4(np_(x.float()), g)
+    assert np.array_equal(np_(sf), s_o)
+    assert np.array_equal(np_(codes), c_o)
+
+
+def test_quantize_all_bf16_values():
+    """Every finite bf16 value, in blocks whose maxima sweep the scale range."""
+    log("NVFP4 quantize over all finite bf16 values")
+    bits = torch.arange(0, 0x10000, dtype=torch.int32, device=DEV)
+    keep = (bits & 0x7F80) != 0x7F80
+    v = bits[keep].to(torch.int16).view(torch.bfloat16)
+    n = (v.numel() // 16) * 16
+    x = v[:n].reshape(-1, 16)
+    x = x[torch.randperm(x.shape[0], generator=datagen.generator(3, DEV), device=DEV)].contiguous()
+    for g in (1.0, 2.0 ** -100, 1e-3):
+        codes, sf = _mxg().mx_quantize_nvfp4(x, g)
+        torch.cuda.synchronize()
+        c_o, s_o = oracle.quantize_nvfp4(np_(x.float()), g)
+        assert np.array_equal(np_(sf), s_o), g
+        assert np.array_equal(np_(codes), c_o), g
+
+
+def test_quantize_gather_bit_exact():
+    log("quantize + gather into the masked layout, T=300 top8 H=7168 max_m=12 (some slots dropped)")
+    gen = datagen.generator(19, DEV)
+    T, H, E, k, max_m = 300, 7168, 256, 8, 12
+    ids = datagen.distinct_topk_ids(gen, T, E, k, DEV)
+    x = datagen.bf16_normal(gen, (T, H), DEV)
+    g_x = datagen.global_scale_from_amax(x)
+    mxg = _mxg()
+    mm, row = mxg.moe_dispatch(ids, E, max_m)
+    a = torch.full((E, max_m, H // 2), 0xEE, dtype=torch.uint8, device=DEV)
+    a_sf = torch.full((E, max_m, H // 16), 0xEE, dtype=torch.uint8, device=DEV)
+    mxg.moe_quantize_gather_nvfp4(x, g_x, ids, row, E, max_m, a=a, a_sf=a_sf)
+    torch.cuda.synchronize()
+    c_o, s_o = oracle.quantize_nvfp4(np_(x.float()), g_x)
+    mm_o, row_o = oracle.dispatch(np_(ids), E, max_m)
+    a_h, asf_h, ids_h = np_(a), np_(a_sf), np_(ids)
+    filled = np.zeros((E, max_m), bool)
+    for t in range(T):
+        for j in range(k):
+            e, r = ids_h[t, j], row_o[t, j]
+            if r < max_m:
+                assert np.array_equal(a_h[e, r], c_o[t]) and np.array_equal(asf_h[e, r], s_o[t])
+                filled[e, r] = True
+    assert (a_h[~filled] == 0xEE).all() and (asf_h[~filled] == 0xEE).all()
+    assert filled.sum() == mm_o.sum()
