@@ -195,7 +195,7 @@ def bench_hetero(dev, steps, warmup, seed=1002):
 def _moe_setup(dev, t, T, E=256, top_k=8):
     ids, w = mxg.moe_route_noaux(t["logits"], t["bias"], 8, 4, top_k, 2.5)
     mm_full, _ = mxg.moe_dispatch(ids, E, 1 << 20)
-    cap = max(64, -(-int(mm_full.max().item()) // 64) * 64)
+    cap = max(16, -(-int(mm_full.max().item()) // 16) * 16)
     masked_m, row = mxg.moe_dispatch(ids, E, cap)
     torch.cuda.synchronize()
     return ids, w, masked_m, row, cap

@@ -306,8 +306,9 @@ static int grid_for(int total, int cu_limit) {
 }
 
 hipError_t gemm_nvfp4_masked(MaskedGemmArgs p, int epi, int cu_limit, hipStream_t s) {
-  // Tile shape by row capacity: decode-shaped groups (few rows) stream B
-  // through a 16-row tile; larger groups use square tiles.
+  // Decode-shaped groups (small row capacity) stream B through registers in the
+  // skinny kernel; larger groups use LDS-staged square tiles.
+  if (p.max_m <= SKINNY_MAX_M && p.K % 512 == 0) return gemm_nvfp4_skinny(p, epi, cu_limit, s);
   if (epi == EPI_SWIGLU_NVFP4) {
     if (p.max_m <= 16) {
       p.tiles_m = (p.max_m + 15) / 16; p.tiles_n = (p.N / 2) / 128;

@@ -1,0 +1,405 @@
+// gemm_nvfp4_skinny.hip -- masked grouped NVFP4 NT GEMM for decode-shaped groups
+// (at most 16 valid rows per M tile), where the time is the read of the active
+// groups' B (expert weights) from HBM.
+//
+// Same operation as the tiled kernel (masked batched GEMM with scale factors and
+// alpha at output, "The CuteDSL Gamble", "The Message"); the decode regime is the
+// one the page's single-stream measurements sit in (M = 1 grouped GEMMs,
+// "Assumptions Embedded in the Message").
+//
+// MI355X design:
+//  * Weights go from HBM straight into LDS by DMA (global_load_lds_dwordx4, no
+//    registers): each wave owns a ring of STAGES LDS stages and keeps
+//    STAGES - 1 chunks of 512 K-elements in flight ahead of its compute.
+//  * Every DMA instruction covers 4 rows x 256 contiguous bytes of codes (the
+//    16 rows' 32 scale bytes per chunk take one more): runs long enough for HBM
+//    to stream near its peak.  The lane -> 16-byte-unit mapping is XOR-swizzled
+//    by row so that the operand reads (16 rows, one unit each) are bank-conflict
+//    free.
+//  * Weights are decoded e2m1 x e4m3 into exact fp16 (hardware fp4 and fp8
+//    converts, one packed multiply) and fed to v_mfma_f32_16x16x32_f16.  Inside a
+//    chunk, lane group q owns elements j*128 + q*32 .. +32 of each 128-slice j;
+//    the activation operand uses the same order.
+//  * Activations (<= 16 rows) are decoded once per chunk by the workgroup into
+//    LDS as fp16 (double buffered, one barrier per chunk).
+//  * Output tile D[n][m] (weights x activations): lane l holds 4 consecutive n for
+//    one m, so stores are 8-byte (bf16) or 16-byte (fp32) vectors.
+//  * Fused SwiGLU + NVFP4 requantization (MoE GEMM1): a wave's two tiles are the
+//    gate rows and the matching up rows, so h = silu(gate) * up is formed in
+//    registers; the 16-column block amax is two cross-lane shuffles away.
+//  * Persistent grid over a compacted list of (group, M tile) entries with valid
+//    rows, built in LDS with wavefront ballots: idle groups cost nothing.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace mxg {
+
+namespace sk {
+constexpr int KC = 512;                         // K elements per chunk
+constexpr int APITCH = KC + 8;                  // fp16 per LDS activation row
+constexpr int CODE_BYTES = 16 * 256;            // codes of one 16-row tile chunk
+constexpr int TILE_STAGE = CODE_BYTES + 512;    // + the 16 rows' scale bytes
+constexpr int MAX_LIST = 512;                   // (group, M tile) entries kept in LDS
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Per-lane DMA source offsets of one tile: codes of rows 4i + lane/16 with the
+// swizzled unit, scales of row lane/2 (lanes < 32 only).
+struct TileSrc {
+  size_t code[4];
+  size_t scale;
+};
+
+__device__ __forceinline__ TileSrc tile_src(int first_row, int nlimit, int row_off, int K, int lane) {
+  TileSrc s;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    int r = 4 * i + (lane >> 4);
+    int g = first_row + r;
+    g = (g < nlimit ? g : nlimit - 1) + row_off;  // rows past the end re-read a valid row (never stored)
+    s.code[i] = (size_t)g * (K / 2) + (size_t)(((lane & 15) ^ r) * 16);
+  }
+  int r = (lane & 31) >> 1;
+  int g = first_row + r;
+  g = (g < nlimit ? g : nlimit - 1) + row_off;
+  s.scale = (size_t)g * (K / 16) + (size_t)((lane & 1) * 16);
+  return s;
+}
+
+// Every asynchronous operation of the main loop is an LDS DMA issued with
+// inline assembly, and the waits are explicit partial vmcnt waits: the compiler
+// would otherwise drain all outstanding DMAs (vmcnt(0)) before each LDS read,
+// serializing the prefetch ring.  No register-destination load is issued this
+// way, so no register can be overwritten behind the compiler's back.
+__device__ __forceinline__ void dma16(const uint8_t* g, uint8_t* lds) {
+  // the LDS base is wave-uniform; readfirstlane puts it in an SGPR for M0
+  uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0) : "memory");
+}
+
+template <int NT>
+__device__ __forceinline__ void dma_chunk(uint8_t* stage, const uint8_t* B, const uint8_t* Bsf,
+                                          const TileSrc* src, int chunk) {
+#pragma unroll
+  for (int t = 0; t < NT; t++) {
+    uint8_t* st = stage + t * sk::TILE_STAGE;
+#pragma unroll
+    for (int i = 0; i < 4; i++) dma16(B + src[t].code[i] + (size_t)chunk * (sk::KC / 2), st + i * 1024);
+    if ((threadIdx.x & 63) < 32) dma16(Bsf + src[t].scale + (size_t)chunk * (sk::KC / 16), st + sk::CODE_BYTES);
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Raw activation chunk in LDS: codes [16 rows][256 B], then scales [16][32 B].
+constexpr int A_RAW = 16 * 256 + 16 * 32;
+
+// DMA (by one wave) of activation chunk `chunk` into a raw stage: instruction i
+// covers rows 4i .. 4i+3; rows past the valid count re-read row 0.
+__device__ __forceinline__ void dma_a_chunk(uint8_t* raw, const uint8_t* A, const uint8_t* Asf, int K,
+                                            int rows, int chunk, int lane) {
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    int r = 4 * i + (lane >> 4);
+    r = r < rows ? r : 0;
+    dma16(A + (size_t)r * (K / 2) + (size_t)chunk * (sk::KC / 2) + (lane & 15) * 16, raw + i * 1024);
+  }
+  int r = lane >> 1;
+  r = r < rows ? r : 0;
+  if (lane < 32) dma16(Asf + (size_t)r * (K / 16) + (size_t)chunk * (sk::KC / 16) + (lane & 1) * 16, raw + 4096);
+}
+
+// Decode a raw activation chunk into the fp16 buffer: thread t owns row t / TPR
+// and EPT consecutive elements (threads of padding rows skip).
+template <int THREADS>
+__device__ __forceinline__ void decode_a_chunk(_Float16* As, const uint8_t* raw, int rows, int tid) {
+  constexpr int TPR = THREADS / 16, EPT = sk::KC / TPR;  // 16 or 32 elements
+  const int r = tid / TPR, seg = tid % TPR;
+  if (r >= rows) return;
+  half8_t* dst = (half8_t*)(As + r * sk::APITCH + seg * EPT);
+  if constexpr (EPT == 32) {
+    u32x4_t c = *(const u32x4_t*)(raw + r * 256 + seg * 16);
+    uint32_t sc = *(const uint16_t*)(raw + 4096 + r * 32 + seg * 2);
+    half2_t s0 = scale_e4m3_to_h2(sc & 0xFFu), s1 = scale_e4m3_to_h2(sc >> 8);
+    dst[0] = decode8_e2m1_f16(c[0], s0);
+    dst[1] = decode8_e2m1_f16(c[1], s0);
+    dst[2] = decode8_e2m1_f16(c[2], s1);
+    dst[3] = decode8_e2m1_f16(c[3], s1);
+  } else {
+    u32x2_t c = *(const u32x2_t*)(raw + r * 256 + seg * 8);
+    half2_t s0 = scale_e4m3_to_h2(raw[4096 + r * 32 + seg]);
+    dst[0] = decode8_e2m1_f16(c[0], s0);
+    dst[1] = decode8_e2m1_f16(c[1], s0);
+  }
+}
+
+// MFMA over one staged chunk.  Lane (n = l%16, q = l/16) reads unit 4j + q of
+// row n (at swizzled position (4j+q) ^ n) and the two scale bytes of its
+// elements' 16-blocks.  Activation lanes of padding rows read row rows-1
+// (their output columns are never stored).
+template <int NT>
+__device__ __forceinline__ void compute_chunk(float4_t (&acc)[NT], const uint8_t* stage, const _Float16* As,
+                                              int lane, int rows) {
+  const int n = lane & 15, q = lane >> 4;
+  const int ma = n < rows ? n : rows - 1;
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    u32x4_t w[NT];
+    half2_t sc[NT][2];
+#pragma unroll
+    for (int t = 0; t < NT; t++) {
+      const uint8_t* st = stage + t * sk::TILE_STAGE;
+      w[t] = *(const u32x4_t*)(st + n * 256 + (((4 * j + q) ^ n) * 16));
+      uint32_t sb = *(const uint16_t*)(st + sk::CODE_BYTES + n * 32 + j * 8 + q * 2);
+      half2_t s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sb, 1.0f, false);
+      sc[t][0] = half2_t{s01[0], s01[0]};
+      sc[t][1] = half2_t{s01[1], s01[1]};
+    }
+#pragma unroll
+    for (int s = 0; s < 4; s++) {
+      half8_t act = *(const half8_t*)(As + ma * sk::APITCH + j * 128 + q * 32 + s * 8);
+#pragma unroll
+      for (int t = 0; t < NT; t++) {
+        half8_t wv = decode8_e2m1_f16(w[t][s], sc[t][s >> 1]);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wv, act, acc[t], 0, 0, 0);
+      }
+    }
+  }
+}
+
+// NVFP4 quantization of one 16-column block spread over the 4 lanes
+// {m, m+16, m+32, m+48} (4 values each, element (lane/16)*4 + r).  Same operation
+// sequence as quantize_block16.  Returns this lane's 16 code bits (element order)
+// and the scale byte.
+__device__ __forceinline__ uint32_t quantize_block_x4(const float h[4], float g, float six_g,
+                                                      uint32_t& scale) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int r = 0; r < 4; r++) amax = __builtin_fmaxf(amax, __builtin_fabsf(h[r]));
+  amax = __builtin_fmaxf(amax, __shfl_xor(amax, 16));
+  amax = __builtin_fmaxf(amax, __shfl_xor(amax, 32));
+  float qv = amax / six_g;
+  uint32_t s = f32_to_e4m3_rne_sat(qv);
+  float sval = e4m3_to_f32(s);
+  uint32_t bits = 0;
+  if (sval == 0.0f) {
+#pragma unroll
+    for (int r = 0; r < 4; r++) bits |= ((__float_as_uint(h[r]) >> 28) & 0x8u) << (4 * r);
+  } else {
+    float d = sval * g;
+    float rc = 1.0f / d;
+#pragma unroll
+    for (int r = 0; r < 4; r++) bits |= f32_to_e2m1_rne_sat(h[r] * rc) << (4 * r);
+  }
+  scale = s;
+  return bits;
+}
+
+// Work unit = (group g, 16-row M tile mt, N tile nt).  Every workgroup builds the
+// same compacted list of (g, mt) entries with valid rows in LDS (wavefront
+// ballots) and the persistent grid strides over entries x N tiles; beyond
+// MAX_LIST entries the dense index space is walked instead.
+template <int NT, int EPI, int WAVES, int STAGES>
+__global__ __launch_bounds__(WAVES * 64) void k_gemm_nvfp4_skinny(const MaskedGemmArgs p) {
+  constexpr bool SWIGLU = (EPI == EPI_SWIGLU_NVFP4);
+  constexpr int THREADS = WAVES * 64;
+  static_assert(!SWIGLU || NT == 2, "SwiGLU pairs one gate and one up tile per wave");
+  __shared__ __attribute__((aligned(16))) _Float16 As[2][16 * sk::APITCH];
+  __shared__ __attribute__((aligned(16))) uint8_t Araw[STAGES][A_RAW];
+  __shared__ __attribute__((aligned(16))) uint8_t Bst[WAVES][STAGES][NT * sk::TILE_STAGE];
+  __shared__ int list[sk::MAX_LIST];
+  __shared__ int list_n;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: branches on it are scalar
+  const int q = lane >> 4;
+  const int K = p.K, nchunks = K / sk::KC;
+  const bool compact = p.G * p.tiles_m <= sk::MAX_LIST;
+
+  int total;
+  if (compact) {
+    if (wave == 0) {
+      int count = 0;
+      for (int base = 0; base < p.G * p.tiles_m; base += 64) {
+        int idx = base + lane;  // idx = g * tiles_m + mt
+        bool act = false;
+        if (idx < p.G * p.tiles_m) {
+          int g = idx / p.tiles_m, mt = idx % p.tiles_m;
+          int mm = p.masked_m[g];
+          mm = mm < 0 ? 0 : (mm > p.max_m ? p.max_m : mm);
+          act = mt * 16 < mm;
+        }
+        unsigned long long bal = __ballot(act);
+        int before = __popcll(bal & ((1ull << lane) - 1ull));
+        if (act) list[count + before] = idx;
+        count += __popcll(bal);
+      }
+      if (lane == 0) list_n = count;
+    }
+    __syncthreads();
+    total = list_n * p.tiles_n;
+  } else {
+    total = p.G * p.tiles_m * p.tiles_n;
+  }
+
+  for (int t = blockIdx.x; t < total; t += gridDim.x) {
+    const int nt = t % p.tiles_n;
+    const int idx = compact ? list[t / p.tiles_n] : t / p.tiles_n;
+    const int mt = idx % p.tiles_m, g = idx / p.tiles_m;
+    int mm = p.masked_m[g];
+    mm = mm < 0 ? 0 : (mm > p.max_m ? p.max_m : mm);
+    const int m0 = mt * 16;
+    if (m0 >= mm) continue;
+    const int rows = mm - m0 < 16 ? mm - m0 : 16;
+    const uint8_t* A = p.a + ((size_t)g * p.max_m + m0) * (K / 2);
+    const uint8_t* Asf = p.a_sf + ((size_t)g * p.max_m + m0) * (K / 16);
+    const uint8_t* B = p.b + (size_t)g * p.N * (K / 2);
+    const uint8_t* Bsf = p.b_sf + (size_t)g * p.N * (K / 16);
+
+    // this wave's weight tiles
+    int ncol0;  // first output column (n) of tile 0
+    TileSrc src[NT];
+    if constexpr (SWIGLU) {
+      const int I = p.N / 2;
+      ncol0 = nt * (16 * WAVES) + wave * 16;
+      src[0] = tile_src(ncol0, I, 0, K, lane);
+      src[1] = tile_src(ncol0, I, I, K, lane);
+    } else {
+      ncol0 = nt * (16 * NT * WAVES) + wave * (16 * NT);
+#pragma unroll
+      for (int i = 0; i < NT; i++) src[i] = tile_src(ncol0 + 16 * i, p.N, 0, K, lane);
+    }
+    uint8_t* ring = &Bst[wave][0][0];
+
+    float4_t acc[NT];
+#pragma unroll
+    for (int i = 0; i < NT; i++) acc[i] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+    // Issue order per iteration c: wave 0 DMAs activation chunk c+2 (5 ops), then
+    // every wave DMAs its weight chunk c+2 (5 NT ops).  Before computing chunk c
+    // a wave needs its weight chunk c (and wave 0 also activation chunk c+1,
+    // which the next step decodes): at most the ops issued after those may stay
+    // outstanding.  Chunk indices are clamped at the end (re-reads from L2), so
+    // the counts hold for every iteration.
+    static_assert(STAGES == 3, "wait counts below assume three stages");
+    constexpr int W_OPS = 5 * NT, A_OPS = 5;
+    constexpr int WAIT_OTHER = 2 * W_OPS;            // weight chunks c+1, c+2
+    constexpr int WAIT_WAVE0 = W_OPS + A_OPS + W_OPS; // weight c+1, activation c+2, weight c+2
+    auto clampc = [&](int c) { return c < nchunks ? c : nchunks - 1; };
+    if (wave == 0) {
+      dma_a_chunk(Araw[0], A, Asf, K, rows, 0, lane);
+      dma_a_chunk(Araw[1], A, Asf, K, rows, clampc(1), lane);
+    }
+    dma_chunk<NT>(ring, B, Bsf, src, 0);
+    dma_chunk<NT>(ring + NT * sk::TILE_STAGE, B, Bsf, src, clampc(1));
+    if (wave == 0) wait_vmcnt<A_OPS + 2 * W_OPS>();  // activation chunk 0 landed
+    __syncthreads();
+    decode_a_chunk<THREADS>(As[0], Araw[0], rows, tid);
+
+    for (int c = 0; c < nchunks; c++) {
+      if (wave == 0) dma_a_chunk(Araw[(c + 2) % 3], A, Asf, K, rows, clampc(c + 2), lane);
+      dma_chunk<NT>(ring + ((c + 2) % 3) * (NT * sk::TILE_STAGE), B, Bsf, src, clampc(c + 2));
+      if (wave == 0) wait_vmcnt<WAIT_WAVE0>();
+      else wait_vmcnt<WAIT_OTHER>();
+      // After this barrier: every wave finished chunk c-1 (so the activation
+      // buffer (c+1)&1 may be rewritten), activation buffer c&1 is complete, and
+      // activation chunk c+1 is in LDS.
+      __syncthreads();
+      compute_chunk<NT>(acc, ring + (c % 3) * (NT * sk::TILE_STAGE), As[c & 1], lane, rows);
+      if (c + 1 < nchunks) decode_a_chunk<THREADS>(As[(c + 1) & 1], Araw[(c + 1) % 3], rows, tid);
+    }
+    wait_vmcnt<0>();  // the tail re-reads must land before the stages are reused
+    __syncthreads();
+
+    const int m = lane & 15;
+    const size_t orow = (size_t)g * p.max_m + m0 + m;
+    const float alpha = (p.alpha ? p.alpha[g] : 1.0f) * p.alpha_scale;
+    if constexpr (EPI == EPI_BF16 || EPI == EPI_F32) {
+#pragma unroll
+      for (int i = 0; i < NT; i++) {
+        const int n = ncol0 + i * 16 + q * 4;
+        if (m < rows && n < p.N) {
+          float v[4];
+#pragma unroll
+          for (int r = 0; r < 4; r++) v[r] = alpha * acc[i][r];
+          if (n + 4 <= p.N && (p.N & 3) == 0) {
+            if constexpr (EPI == EPI_BF16) {
+              uint32_t lo = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
+              uint32_t hi = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
+              *(u32x2_t*)((uint16_t*)p.out + orow * p.N + n) = u32x2_t{lo, hi};
+            } else {
+              *(float4_t*)((float*)p.out + orow * p.N + n) = float4_t{v[0], v[1], v[2], v[3]};
+            }
+          } else {
+            for (int r = 0; r < 4 && n + r < p.N; r++) {
+              if constexpr (EPI == EPI_BF16) ((uint16_t*)p.out)[orow * p.N + n + r] = (uint16_t)f32_to_bf16_rne(v[r]);
+              else ((float*)p.out)[orow * p.N + n + r] = v[r];
+            }
+          }
+        }
+      }
+    } else {
+      const int I = p.N / 2;
+      float h[4];
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        float gt = alpha * acc[0][r], up = alpha * acc[1][r];
+        h[r] = gt / (1.0f + expf(-gt)) * up;
+      }
+      const int hc = ncol0 + q * 4;  // this lane's first h column
+      if (p.dbg_h && m < rows && hc < I)
+        *(float4_t*)(p.dbg_h + orow * I + hc) = float4_t{h[0], h[1], h[2], h[3]};
+      uint32_t sbyte;
+      uint32_t bits = quantize_block_x4(h, p.g_h, 6.0f * p.g_h, sbyte);
+      uint32_t b1 = __shfl_xor(bits, 16);  // q ^ 1
+      uint32_t b2 = __shfl_xor(bits, 32);  // q ^ 2
+      uint32_t b3 = __shfl_xor(bits, 48);  // q ^ 3
+      if (q == 0 && m < rows && ncol0 < I) {
+        uint32_t w0 = bits | (b1 << 16), w1 = b2 | (b3 << 16);
+        *(u32x2_t*)(p.h_codes + orow * (I / 2) + ncol0 / 2) = u32x2_t{w0, w1};
+        p.h_sf[orow * (I / 16) + ncol0 / 16] = (uint8_t)sbyte;
+      }
+    }
+  }
+}
+
+static int resident_grid(const void* kernel, int threads, int cu_limit) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess) return 0;
+  if (per_cu < 1) per_cu = 1;
+  if (cu_limit > 0 && cu_limit < cus) cus = cu_limit;
+  return cus * per_cu;
+}
+
+template <int NT, int EPI, int WAVES, int STAGES>
+static hipError_t launch_skinny(MaskedGemmArgs p, int cu_limit, hipStream_t s) {
+  p.tiles_m = (p.max_m + 15) / 16;
+  p.tiles_n = (EPI == EPI_SWIGLU_NVFP4) ? (p.N / 2 + 16 * WAVES - 1) / (16 * WAVES)
+                                        : (p.N + 16 * NT * WAVES - 1) / (16 * NT * WAVES);
+  p.total_tiles = p.G * p.tiles_m * p.tiles_n;
+  if (p.total_tiles == 0) return hipSuccess;
+  const void* k = (const void*)k_gemm_nvfp4_skinny<NT, EPI, WAVES, STAGES>;
+  int grid = resident_grid(k, WAVES * 64, cu_limit);
+  if (grid <= 0) return hipErrorInvalidValue;
+  if (grid > p.total_tiles) grid = p.total_tiles;
+  hipLaunchKernelGGL((k_gemm_nvfp4_skinny<NT, EPI, WAVES, STAGES>), dim3(grid), dim3(WAVES * 64), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t gemm_nvfp4_skinny(MaskedGemmArgs p, int epi, int cu_limit, hipStream_t s) {
+  switch (epi) {
+    case EPI_BF16: return launch_skinny<1, EPI_BF16, 8, 3>(p, cu_limit, s);
+    case EPI_F32: return launch_skinny<1, EPI_F32, 8, 3>(p, cu_limit, s);
+    case EPI_SWIGLU_NVFP4: return launch_skinny<2, EPI_SWIGLU_NVFP4, 4, 3>(p, cu_limit, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace mxg

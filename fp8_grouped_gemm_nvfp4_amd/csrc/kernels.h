@@ -55,6 +55,10 @@ template <> struct ArgsOf<MODE_HETERO> { typedef HeteroGemmArgs type; };
 
 hipError_t gemm_nvfp4_masked(MaskedGemmArgs p, int epi, int cu_limit, hipStream_t s);
 hipError_t gemm_nvfp4_hetero(HeteroGemmArgs p, int epi, int cu_limit, hipStream_t s);
+// Decode-shaped masked GEMM (16-row M tiles, weights streamed into registers);
+// requires K % 512 == 0.
+hipError_t gemm_nvfp4_skinny(MaskedGemmArgs p, int epi, int cu_limit, hipStream_t s);
+constexpr int SKINNY_MAX_M = 32;  // row capacity up to which the skinny kernel is used
 
 // FP8 block-scaled GEMMs of the DeepSeek-V3-style expert path (masked layout).
 struct Fp8GemmArgs {

@@ -74,6 +74,11 @@ def test_masked_gemm_g4_m64_n512_k1024(seed):
     (2, 200, 136, 128, [200, 129]),          # several 128-row tiles, ragged
     (5, 8, 4096, 512, [1, 0, 8, 3, 1]),      # decode-shaped (16-row tiles)
     (2, 16, 264, 192, [16, 5]),
+    # decode-shaped kernel (row capacity <= 32, K % 512 == 0)
+    (6, 16, 520, 1024, [1, 16, 0, 7, 15, 2]),
+    (4, 32, 384, 512, [17, 32, 16, 31]),
+    (3, 8, 4096, 7168, [1, 8, 3]),
+    (2, 1, 64, 2048, [1, 1]),
 ])
 def test_masked_gemm_edges(G, max_m, N, K, mm):
     log(f"masked NVFP4 GEMM edge G={G} max_m={max_m} N={N} K={K} masked_m={mm}")
@@ -105,6 +110,14 @@ def test_masked_gemm_general_scales_fp32_out_and_poison():
         _check_masked(t, out, max_m, N, K, f"general scales {dt}")
 
 
+@pytest.mark.parametrize("max_m,K", [(16, 1024), (48, 512)])
+def test_masked_gemm_fp32_out(max_m, K):
+    log(f"masked NVFP4 GEMM fp32 output max_m={max_m} K={K}")
+    wl = datagen.masked_gemm_workload(23, DEV, G=3, max_m=max_m, N=256, K=K, masked_m=[max_m, 1, max_m - 3])
+    out = _run_masked(wl.tensors, max_m, 256, out_dtype=torch.float32)
+    _check_masked(wl.tensors, out, max_m, 256, K, "fp32 out")
+
+
 def test_masked_gemm_cu_limit_and_determinism():
     log("masked NVFP4 GEMM cu_limit grid-stride path and run-to-run determinism")
     wl = datagen.masked_gemm_workload(21, DEV, G=8, max_m=130, N=384, K=512)
@@ -114,6 +127,11 @@ def test_masked_gemm_cu_limit_and_determinism():
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
     assert torch.equal(o1.view(torch.int16), o3.view(torch.int16))
     _check_masked(wl.tensors, o3, 130, 384, 512, "cu_limit")
+    wl = datagen.masked_gemm_workload(22, DEV, G=8, max_m=16, N=384, K=1024)
+    o1 = _run_masked(wl.tensors, 16, 384)
+    o2 = _run_masked(wl.tensors, 16, 384, cu_limit=2)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    _check_masked(wl.tensors, o2, 16, 384, 1024, "cu_limit skinny")
 
 
 def test_decode_gemm1_full_size():

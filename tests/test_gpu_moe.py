@@ -37,7 +37,7 @@ def _route_dispatch(t, cap=None):
     ids, w = mxg.moe_route_noaux(t["logits"], t["bias"], 8, 4, TOPK, 2.5)
     if cap is None:
         mm_full, _ = mxg.moe_dispatch(ids, E, 1 << 20)
-        cap = max(64, -(-int(mm_full.max().item()) // 64) * 64)
+        cap = max(16, -(-int(mm_full.max().item()) // 16) * 16)
     masked_m, row = mxg.moe_dispatch(ids, E, cap)
     torch.cuda.synchronize()
     ids_o, w_o = oracle.route_noaux(np_(t["logits"]), np_(t["bias"]), 8, 4, TOPK, 2.5)
@@ -134,6 +134,11 @@ def _run_nvfp4(T, H, I, seed, n_check, cap=None):
 def test_moe_nvfp4_small_full():
     log("NVFP4 MoE small: T=64 H=512 I=256 E=256, every token")
     _run_nvfp4(64, 512, 256, 4000, None)
+
+
+def test_moe_nvfp4_decode_small_full():
+    log("NVFP4 MoE decode-shaped: T=32 H=1024 I=512 (capacity <= 32), every token")
+    _run_nvfp4(32, 1024, 512, 4002, None)
 
 
 def test_moe_nvfp4_capacity_drop():
