@@ -76,7 +76,7 @@ int mx_grouped_gemm_masked(const uint8_t* a, const uint8_t* a_sf, const uint8_t*
   int st = check_nvfp4_types(ab_dtype, sf_dtype, c_dtype, sf_vec_size);
   if (st) return st;
   if (K % 64 != 0) return fail(MXG_ERR_UNSUPPORTED, "mx_grouped_gemm_masked: K %% 64 != 0 (K=%d)", K);
-  if (!aligned16(a) || !aligned16(b) || !aligned16(out) || ((uintptr_t)a_sf & 1u) || ((uintptr_t)b_sf & 1u))
+  if (!aligned16(a) || !aligned16(b) || !aligned16(out) || !aligned16(a_sf) || !aligned16(b_sf))
     return fail(MXG_ERR_INVALID_ARG, "mx_grouped_gemm_masked: misaligned pointer");
   if ((long long)G * max_m * N >= (1LL << 40))
     return fail(MXG_ERR_UNSUPPORTED, "mx_grouped_gemm_masked: problem too large");
@@ -108,7 +108,7 @@ int mx_grouped_gemm(const mxg_group_desc* groups, int G, int ab_dtype, int sf_dt
     if (ldc < d.N) return fail(MXG_ERR_INVALID_ARG, "mx_grouped_gemm: group %d ldc < N", g);
     if (d.M > 0 && (!d.a || !d.a_sf || !d.b || !d.b_sf || !d.out))
       return fail(MXG_ERR_INVALID_ARG, "mx_grouped_gemm: group %d null pointer", g);
-    if (d.M > 0 && (!aligned16(d.a) || !aligned16(d.b) || ((uintptr_t)d.a_sf & 1u) || ((uintptr_t)d.b_sf & 1u)))
+    if (d.M > 0 && (!aligned16(d.a) || !aligned16(d.b) || !aligned16(d.a_sf) || !aligned16(d.b_sf)))
       return fail(MXG_ERR_INVALID_ARG, "mx_grouped_gemm: group %d misaligned pointer", g);
     mxg::HeteroGroup& q = p.grp[g];
     q.a = d.a; q.a_sf = d.a_sf; q.b = d.b; q.b_sf = d.b_sf; q.out = d.out;

@@ -306,9 +306,12 @@ static int grid_for(int total, int cu_limit) {
 }
 
 hipError_t gemm_nvfp4_masked(MaskedGemmArgs p, int epi, int cu_limit, hipStream_t s) {
-  // Decode-shaped groups (small row capacity) stream B through registers in the
-  // skinny kernel; larger groups use LDS-staged square tiles.
-  if (p.max_m <= SKINNY_MAX_M && p.K % 512 == 0) return gemm_nvfp4_skinny(p, epi, cu_limit, s);
+  // Decode-shaped groups (small row capacity) stream B into LDS by DMA in the skinny
+  // kernel; larger groups use LDS-staged square tiles.
+  if (p.max_m <= SKINNY_MAX_M && p.K % 512 == 0) {
+    const hipError_t e = gemm_nvfp4_skinny(p, epi, cu_limit, s);
+    if (e != hipErrorNotSupported) return e;
+  }
   if (epi == EPI_SWIGLU_NVFP4) {
     if (p.max_m <= 16) {
       p.tiles_m = (p.max_m + 15) / 16; p.tiles_n = (p.N / 2) / 128;
