@@ -132,4 +132,32 @@ __device__ __forceinline__ half2_t scale_e4m3_to_h2(uint32_t c) {
   return r;
 }
 
+// NVFP4 quantization of one 16-column block spread over the 4 lanes
+// {m, m+16, m+32, m+48} (4 values each, element (lane/16)*4 + r).  Same operation
+// sequence as quantize_block16.  Returns this lane's 16 code bits (element order)
+// and the scale byte.
+__device__ __forceinline__ uint32_t quantize_block_x4(const float h[4], float g, float six_g,
+                                                      uint32_t& scale) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int r = 0; r < 4; r++) amax = __builtin_fmaxf(amax, __builtin_fabsf(h[r]));
+  amax = __builtin_fmaxf(amax, __shfl_xor(amax, 16));
+  amax = __builtin_fmaxf(amax, __shfl_xor(amax, 32));
+  float qv = amax / six_g;
+  uint32_t s = f32_to_e4m3_rne_sat(qv);
+  float sval = e4m3_to_f32(s);
+  uint32_t bits = 0;
+  if (sval == 0.0f) {
+#pragma unroll
+    for (int r = 0; r < 4; r++) bits |= ((__float_as_uint(h[r]) >> 28) & 0x8u) << (4 * r);
+  } else {
+    float d = sval * g;
+    float rc = 1.0f / d;
+#pragma unroll
+    for (int r = 0; r < 4; r++) bits |= f32_to_e2m1_rne_sat(h[r] * rc) << (4 * r);
+  }
+  scale = s;
+  return bits;
+}
+
 }  // namespace mxg

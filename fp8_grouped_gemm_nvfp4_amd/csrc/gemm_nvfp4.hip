@@ -14,7 +14,8 @@
 //    are exact in fp32, so the only rounding is the fp32 accumulation.
 //  * Decode happens once per element per workgroup, on the way from HBM into
 //    LDS (global -> registers -> v_cvt_scalef32_pk_f16_fp4 + v_pk_mul_f16 ->
-//    LDS), double-buffered, one barrier per 64-wide K step.
+//    LDS), double-buffered, one barrier per 64-wide K step.  The raw bytes are
+//    prefetched 3 steps ahead in a register ring.
 //  * Tiles: BM x BN output per 256-thread workgroup, waves laid out WAVES_M x
 //    WAVES_N, each wave a grid of 16x16 MFMA tiles.  A grid-stride loop over
 //    tiles bounds the number of resident workgroups when a CU cap is given.
@@ -27,6 +28,7 @@
 namespace mxg {
 
 constexpr int BK = 64;          // K elements per step (4 NVFP4 blocks)
+constexpr int XCD_CHUNK = 8;    // consecutive tiles that run on one XCD
 constexpr int LDS_PITCH = 72;   // fp16 elements per LDS row (64 + 8 pad)
 
 struct TileJob {
@@ -92,24 +94,21 @@ struct Stage {
   uint32_t sc[CH];
 };
 
-// Load chunk c (16 bytes = 32 elements) of a ROWS-row operand tile.  Row r of
-// the tile is global row rowmap(r); rows >= nvalid load zeros.
+// Load chunk c (16 bytes = 32 elements) of a ROWS-row operand tile.  Row r of the tile
+// is global row grow[i], already clamped into the operand's valid rows (rows beyond the
+// valid range re-read a valid row; their results are never stored), so every load is
+// unconditional and the compiler can keep several steps of loads in flight.
 template <int ROWS, int CH>
 __device__ __forceinline__ void load_tile(Stage<CH>& s, const uint8_t* codes, const uint8_t* sf,
                                           int K, int k0, const int* grow, int tid) {
 #pragma unroll
   for (int i = 0; i < CH; i++) {
-    int c = tid + i * 256;
-    int h = c & 1;
-    int gr = (c < ROWS * 2) ? grow[i] : -1;
-    if (gr >= 0) {
-      const uint8_t* src = codes + (size_t)gr * (K / 2) + (k0 / 2) + h * 16;
+    const int c = tid + i * 256;
+    if (ROWS * 2 >= 256 * (i + 1) || c < ROWS * 2) {
+      const int h = c & 1;
+      const uint8_t* src = codes + (size_t)grow[i] * (K / 2) + (k0 / 2) + h * 16;
       s.codes[i] = *(const u32x4_t*)src;
-      const uint16_t* ssrc = (const uint16_t*)(sf + (size_t)gr * (K / 16) + (k0 / 16) + h * 2);
-      s.sc[i] = *ssrc;
-    } else {
-      s.codes[i] = u32x4_t{0, 0, 0, 0};
-      s.sc[i] = 0;
+      s.sc[i] = *(const uint16_t*)(sf + (size_t)grow[i] * (K / 16) + (k0 / 16) + h * 2);
     }
   }
 }
@@ -119,7 +118,7 @@ __device__ __forceinline__ void store_tile(const Stage<CH>& s, _Float16* lds, in
 #pragma unroll
   for (int i = 0; i < CH; i++) {
     int c = tid + i * 256;
-    if (c < ROWS * 2) {
+    if (ROWS * 2 >= 256 * (i + 1) || c < ROWS * 2) {
       int r = c >> 1, h = c & 1;
       half2_t s0 = scale_e4m3_to_h2(s.sc[i] & 0xFFu);
       half2_t s1 = scale_e4m3_to_h2(s.sc[i] >> 8);
@@ -150,30 +149,42 @@ __global__ __launch_bounds__(256) void k_gemm_nvfp4(const typename ArgsOf<MODE>:
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int total = p.total_tiles;
 
-  for (int t = blockIdx.x; t < total; t += gridDim.x) {
+  // A grid that covers every tile walks them XCD-aware: workgroup b runs on XCD b % 8,
+  // chunks of XCD_CHUNK consecutive tiles (the M tiles of one B panel are adjacent) go
+  // to the XCDs in turn, so a chunk shares one L2 and heavy tile ranges spread over all
+  // XCDs.  A capped grid strides over the tiles.
+  const bool cover = (int)gridDim.x >= total;
+  for (int t0 = blockIdx.x; t0 < (cover ? (int)gridDim.x : total); t0 += gridDim.x) {
+    int t = t0;
+    if (cover) {
+      const int xcd = t0 & 7, slot = t0 >> 3;
+      t = ((slot / XCD_CHUNK) * 8 + xcd) * XCD_CHUNK + slot % XCD_CHUNK;
+    }
+    if (t >= total) continue;
     TileJob j;
     bool ok;
     if constexpr (MODE == MODE_MASKED) ok = masked_tile<BM, BN, SWIGLU>(p, t, j);
     else ok = hetero_tile<BM, BN>(p, t, j);
     if (!ok) continue;
 
-    // global rows this thread stages (A: valid rows only; B: N tail -> -1)
+    // global rows this thread stages, clamped into the valid rows
     int arow[CH_A], brow[CH_B];
 #pragma unroll
     for (int i = 0; i < CH_A; i++) {
-      int r = (tid + i * 256) >> 1;
-      arow[i] = (j.m0 + r < j.M) ? j.m0 + r : -1;
+      const int r = (tid + i * 256) >> 1;
+      arow[i] = (j.m0 + r < j.M) ? j.m0 + r : j.M - 1;
     }
 #pragma unroll
     for (int i = 0; i < CH_B; i++) {
-      int r = (tid + i * 256) >> 1;
+      const int r = (tid + i * 256) >> 1;
       int gr;
       if constexpr (SWIGLU) {
-        int half_n = j.N / 2;  // I
+        const int half_n = j.N / 2;  // I
         int hc = j.n0 + (r < BN / 2 ? r : r - BN / 2);
-        gr = (hc < half_n) ? (r < BN / 2 ? hc : half_n + hc) : -1;
+        hc = hc < half_n ? hc : half_n - 1;
+        gr = r < BN / 2 ? hc : half_n + hc;
       } else {
-        gr = (j.n0 + r < j.N) ? j.n0 + r : -1;
+        gr = (j.n0 + r < j.N) ? j.n0 + r : j.N - 1;
       }
       brow[i] = gr;
     }
@@ -184,44 +195,66 @@ __global__ __launch_bounds__(256) void k_gemm_nvfp4(const typename ArgsOf<MODE>:
 #pragma unroll
       for (int n = 0; n < TN; n++) acc[i][n] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-    Stage<CH_A> sa;
-    Stage<CH_B> sb;
+    // Register ring: slot d holds the raw bytes of step kt+1 for kt = d (mod P), loaded P
+    // steps before they are stored to LDS; loads are issued in consumption order, so the
+    // compiler's in-order vmcnt waits keep the next P-1 steps in flight.
+    constexpr int P = 3;
     const int KT = j.K / BK;
-    load_tile<BM, CH_A>(sa, j.a, j.a_sf, j.K, 0, arow, tid);
-    load_tile<BN, CH_B>(sb, j.b, j.b_sf, j.K, 0, brow, tid);
-    store_tile<BM, CH_A>(sa, smem, tid);
-    store_tile<BN, CH_B>(sb, smem + BM * LDS_PITCH, tid);
+    auto load_step = [&](int kt, Stage<CH_A>& a, Stage<CH_B>& b) {
+      kt = kt < KT ? kt : KT - 1;  // prefetches past the end re-read the last step
+      load_tile<BM, CH_A>(a, j.a, j.a_sf, j.K, kt * BK, arow, tid);
+      load_tile<BN, CH_B>(b, j.b, j.b_sf, j.K, kt * BK, brow, tid);
+    };
+    Stage<CH_A> sa[P];
+    Stage<CH_B> sb[P];
+    {
+      Stage<CH_A> a0;
+      Stage<CH_B> b0;
+      load_step(0, a0, b0);
+      store_tile<BM, CH_A>(a0, smem, tid);
+      store_tile<BN, CH_B>(b0, smem + BM * LDS_PITCH, tid);
+    }
+#pragma unroll
+    for (int d = 0; d < P; d++) {
+      load_step(d + 1, sa[d], sb[d]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     __syncthreads();
 
-    for (int kt = 0; kt < KT; kt++) {
-      _Float16* As = smem + (kt & 1) * (BM + BN) * LDS_PITCH;
-      _Float16* Bs = As + BM * LDS_PITCH;
-      if (kt + 1 < KT) {
-        load_tile<BM, CH_A>(sa, j.a, j.a_sf, j.K, (kt + 1) * BK, arow, tid);
-        load_tile<BN, CH_B>(sb, j.b, j.b_sf, j.K, (kt + 1) * BK, brow, tid);
-      }
+    for (int kt0 = 0; kt0 < KT; kt0 += P) {
 #pragma unroll
-      for (int ks = 0; ks < BK / 32; ks++) {
-        half8_t af[TM], bfr[TN];
-        const int koff = ks * 32 + (lane >> 4) * 8;
+      for (int d = 0; d < P; d++) {
+        const int kt = kt0 + d;
+        if (kt < KT) {
+          const _Float16* As = smem + (kt & 1) * (BM + BN) * LDS_PITCH;
+          const _Float16* Bs = As + BM * LDS_PITCH;
 #pragma unroll
-        for (int i = 0; i < TM; i++)
-          af[i] = *(const half8_t*)(As + (wm * WM + i * 16 + (lane & 15)) * LDS_PITCH + koff);
+          for (int ks = 0; ks < BK / 32; ks++) {
+            half8_t af[TM], bfr[TN];
+            const int koff = ks * 32 + (lane >> 4) * 8;
 #pragma unroll
-        for (int n = 0; n < TN; n++)
-          bfr[n] = *(const half8_t*)(Bs + (wn * WN + n * 16 + (lane & 15)) * LDS_PITCH + koff);
+            for (int i = 0; i < TM; i++)
+              af[i] = *(const half8_t*)(As + (wm * WM + i * 16 + (lane & 15)) * LDS_PITCH + koff);
 #pragma unroll
-        for (int i = 0; i < TM; i++)
+            for (int n = 0; n < TN; n++)
+              bfr[n] = *(const half8_t*)(Bs + (wn * WN + n * 16 + (lane & 15)) * LDS_PITCH + koff);
 #pragma unroll
-          for (int n = 0; n < TN; n++)
-            acc[i][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bfr[n], acc[i][n], 0, 0, 0);
-      }
-      if (kt + 1 < KT) {
+            for (int i = 0; i < TM; i++)
+#pragma unroll
+              for (int n = 0; n < TN; n++)
+                acc[i][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bfr[n], acc[i][n], 0, 0, 0);
+          }
+        }
+        // step kt+1 into the other buffer (its last readers finished before the previous
+        // barrier); past the end this writes a buffer that is not read again
         _Float16* An = smem + ((kt + 1) & 1) * (BM + BN) * LDS_PITCH;
-        store_tile<BM, CH_A>(sa, An, tid);
-        store_tile<BN, CH_B>(sb, An + BM * LDS_PITCH, tid);
+        store_tile<BM, CH_A>(sa[d], An, tid);
+        store_tile<BN, CH_B>(sb[d], An + BM * LDS_PITCH, tid);
+        __builtin_amdgcn_sched_barrier(0);
+        load_step(kt + 1 + P, sa[d], sb[d]);
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
       }
-      __syncthreads();
     }
 
     if constexpr (EPI == EPI_BF16 || EPI == EPI_F32) {
@@ -297,12 +330,15 @@ static hipError_t launch(const typename ArgsOf<MODE>::type& p, int grid, hipStre
   return hipGetLastError();
 }
 
+// Without a CU cap every tile gets a workgroup; the grid is a multiple of 8 chunks so that
+// the kernel's XCD-aware remapping reaches every tile index.  With a cap the workgroups
+// stride over the tiles.
 static int grid_for(int total, int cu_limit) {
   if (cu_limit > 0) {
     int cap = cu_limit * 2;
     return total < cap ? total : cap;
   }
-  return total;
+  return (total + 8 * XCD_CHUNK - 1) / (8 * XCD_CHUNK) * (8 * XCD_CHUNK);
 }
 
 hipError_t gemm_nvfp4_masked(MaskedGemmArgs p, int epi, int cu_limit, hipStream_t s) {
@@ -312,6 +348,7 @@ hipError_t gemm_nvfp4_masked(MaskedGemmArgs p, int epi, int cu_limit, hipStream_
     const hipError_t e = gemm_nvfp4_skinny(p, epi, cu_limit, s);
     if (e != hipErrorNotSupported) return e;
   }
+
   if (epi == EPI_SWIGLU_NVFP4) {
     if (p.max_m <= 16) {
       p.tiles_m = (p.max_m + 15) / 16; p.tiles_n = (p.N / 2) / 128;

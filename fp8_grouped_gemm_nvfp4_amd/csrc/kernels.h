@@ -55,8 +55,8 @@ template <> struct ArgsOf<MODE_HETERO> { typedef HeteroGemmArgs type; };
 
 hipError_t gemm_nvfp4_masked(MaskedGemmArgs p, int epi, int cu_limit, hipStream_t s);
 hipError_t gemm_nvfp4_hetero(HeteroGemmArgs p, int epi, int cu_limit, hipStream_t s);
-// Decode-shaped masked GEMM (16-row M tiles, weights streamed into registers);
-// requires K % 512 == 0.
+// Decode-shaped masked GEMM (8- or 16-row M tiles, weights streamed into LDS by DMA);
+// returns hipErrorNotSupported without launching for shapes it does not take.
 hipError_t gemm_nvfp4_skinny(MaskedGemmArgs p, int epi, int cu_limit, hipStream_t s);
 constexpr int SKINNY_MAX_M = 32;  // row capacity up to which the skinny kernel is used
 
