@@ -192,6 +192,8 @@ static int check_moe(const mxg_moe_desc* d) {
   if (d->H % 128 || d->I % 128)
     return fail(MXG_ERR_UNSUPPORTED, "moe_expert_forward: H and I must be multiples of 128");
   if (d->top_k > 8) return fail(MXG_ERR_UNSUPPORTED, "moe_expert_forward: top_k > 8");
+  if (d->precision == MXG_MOE_FP8_BLOCK128 && d->E > 1024)
+    return fail(MXG_ERR_UNSUPPORTED, "moe_expert_forward: FP8 takes at most 1024 experts");
   if (!d->x || !d->w13 || !d->w13_scale || !d->w2 || !d->w2_scale || !d->topk_ids || !d->topk_w ||
       !d->masked_m || !d->row || !d->y)
     return fail(MXG_ERR_INVALID_ARG, "moe_expert_forward: null pointer");
@@ -215,8 +217,8 @@ int moe_expert_forward_workspace_layout(const mxg_moe_desc* d, size_t* off) {
   size_t sz[5];
   if (d->precision == MXG_MOE_FP8_BLOCK128) {
     sz[0] = rows * d->H;                     // e4m3 activations
-    sz[1] = rows * (d->H / 128) * 4;         // fp32 1x128 scales
-    sz[2] = rows * d->I * 2;                 // bf16 h
+    sz[1] = (size_t)d->E * (d->H / 128) * mxg::fp8_scale_stride(d->max_m) * 4;  // fp32 1x128 scales
+    sz[2] = (rows + 1) * d->I * 2;           // bf16 h, plus one row that masked rows' stores land in
     sz[3] = 0;
   } else {
     sz[0] = rows * (d->H / 2);
@@ -262,6 +264,7 @@ int moe_expert_forward(const mxg_moe_desc* d, void* ws, size_t ws_bytes, void* s
     mxg::Fp8GemmArgs p1{};
     p1.a = a; p1.a_s = a_s; p1.b = d->w13; p1.b_s = (const float*)d->w13_scale; p1.out = h;
     p1.masked_m = d->masked_m; p1.G = E; p1.max_m = mm; p1.N = 2 * I; p1.K = H;
+    p1.a_s_stride = mxg::fp8_scale_stride(mm);
     e = mxg::gemm_fp8_swiglu(p1, 0, s);
     if (e != hipSuccess) return hip_status(e, "gemm_fp8_swiglu");
     mxg::Fp8GemmArgs p2{};

@@ -160,4 +160,29 @@ __device__ __forceinline__ uint32_t quantize_block_x4(const float h[4], float g,
   return bits;
 }
 
+// LDS DMA (global_load_lds_*): 64 lanes each copy 16 (or 4) bytes from their own global
+// address into LDS at base + lane * 16 (or 4), without passing through registers.  The
+// streaming kernels issue every asynchronous operation of their main loops this way and
+// wait with explicit partial vmcnt waits: the compiler, which cannot see these loads,
+// would otherwise drain all outstanding loads (vmcnt(0)) before each LDS read.  No
+// register-destination load is issued with inline assembly, so no register can be
+// overwritten behind the compiler's back.
+__device__ __forceinline__ void dma16(const void* g, void* lds) {
+  // the LDS base is wave-uniform; readfirstlane puts it in an SGPR for M0
+  uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0) : "memory");
+}
+__device__ __forceinline__ void dma4(const void* g, void* lds) {
+  uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(m0) : "memory");
+}
+
+// Wait until at most N of this wave's vector memory operations are outstanding (they
+// complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 }  // namespace mxg

@@ -32,184 +32,345 @@ static int fp8_grid(int total, int cu_limit) {
   if (cu_limit > 0) return total < cu_limit * 2 ? total : cu_limit * 2;
   return (total + 8 * FP8_XCD_CHUNK - 1) / (8 * FP8_XCD_CHUNK) * (8 * FP8_XCD_CHUNK);
 }
-constexpr int FP8_P = 3;   // K steps of raw bytes prefetched in a register ring (GEMM1)
-constexpr int FP8_P2 = 2;  // the same for GEMM2, whose two accumulator sets leave fewer registers
+constexpr int FP8_P2 = 2;  // K steps of raw bytes prefetched in a register ring (GEMM2)
 
 // ----------------------------------------------------------------------------- GEMM1
-namespace g1 {
-constexpr int BM = 128, BN = 128, BK = 128, PITCH = 144;  // bytes per LDS row
-constexpr int HN = BN / 2;                                 // h columns per tile
+// Persistent and weight-streaming.  A work item is (expert g, 256-row M tile, 64 h
+// columns): the item's 64 gate rows and 64 up rows of W13 against up to 256 activation
+// rows, so every weight panel is read from HBM once per expert whenever masked_m <= 256.
+// The items of a workgroup are bx + i * grid, where bx numbers the workgroups XCD by XCD
+// (workgroup b runs on XCD b % 8): the workgroups of one XCD run neighbouring N tiles of
+// one expert together and share its activation rows in their L2.
+//
+// Operands travel from HBM into LDS by DMA through two rings that run on across item
+// boundaries: activations (and their row scales) one step ahead, weights (and the two
+// block scales) DB steps ahead, since they come from HBM while the activations are
+// mostly L2 hits.  One step is one 128-wide K block.  Activation rows past masked_m
+// are not fetched at all in 8-row groups (the rest re-read the last valid row).  In LDS, 128-byte row r holds
+// its eight 16-byte chunks XOR-permuted by (r ^ r >> 3) & 7, which keeps the MFMA
+// operand reads free of bank conflicts.
+//
+// Waves: 4 (M, 64 rows each) x 2 (N).  Wave (wm, wn) owns rows 64 wm.. and h columns
+// 32 wn.. of the item, i.e. gate columns 32 wn.. and the matching up columns, so the
+// SwiGLU epilogue runs in registers.  A wave whose 64 rows are all masked skips the
+// MFMAs and the epilogue but keeps issuing its share of the DMAs.
+#ifndef MXG_F1_DB
+#define MXG_F1_DB 4
+#endif
+namespace f1 {
+constexpr int BM = 256, BN = 128, HN = BN / 2, BK = 128;
+constexpr int WAVES = 8, THREADS = WAVES * 64;
+constexpr int A_STAGE = BM * BK + BM * 4;  // codes, then the fp32 row scales
+constexpr int B_STAGE = BN * BK + 16;      // codes, then the {gate, up} block scales
+constexpr int MAX_G = 1024;
+// DMA instructions per wave per step: 4 of activations (32 rows), 2 of weights (16 rows);
+// wave 0 adds the activation row scales, wave 1 the two weight block scales
+constexpr int A_OPS = 4, B_OPS = 2;
+// vmcnt allowance at the top of step j: A(j) is followed by B(j + DB - DA) and DA - 1
+// full steps, B(j) by DB - 1 full steps
+constexpr int wait_count(int da, int db, int ao, int bo) {
+  return (bo + (da - 1) * (ao + bo)) < (db - 1) * (ao + bo) ? bo + (da - 1) * (ao + bo) : (db - 1) * (ao + bo);
+}
+}  // namespace f1
+
+__device__ __forceinline__ int f1_swz(int r) { return (r ^ (r >> 3)) & 7; }
+
+// tprefix[g] = sum over g' < g of the M tiles of expert g' (ceil(clamped masked_m / BM));
+// tprefix[G] = the number of (expert, M tile) units.  The clamped masked_m values go to
+// LDS too: a global load inside the main loop would make the compiler drain the DMAs.
+__device__ __forceinline__ void f1_tile_prefix(const Fp8GemmArgs& p, int* tprefix, int* mm_s, int tid) {
+  if (tid < 64) {
+    const int lane = tid;
+    int run = 0;
+    for (int base = 0; base < p.G; base += 64) {
+      const int g = base + lane;
+      int c = 0;
+      if (g < p.G) {
+        int mm = p.masked_m[g];
+        mm = mm < 0 ? 0 : (mm > p.max_m ? p.max_m : mm);
+        c = (mm + f1::BM - 1) / f1::BM;
+        mm_s[g] = mm;
+      }
+      int x = c;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(x, d);
+        if (lane >= d) x += y;
+      }
+      if (g < p.G) tprefix[g] = run + x - c;
+      run += __shfl(x, 63);
+    }
+    if (lane == 0) tprefix[p.G] = run;
+  }
+  __syncthreads();
 }
 
-__global__ __launch_bounds__(256) void k_gemm_fp8_swiglu(const Fp8GemmArgs p) {
-  using namespace g1;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (BM + BN) * PITCH + 2 * BM * 4 + 2 * 4 * 4];
-  float* sa_lds = (float*)(smem + 2 * (BM + BN) * PITCH);  // [2][BM] activation scales
-  float* sw_lds = sa_lds + 2 * BM;                          // [2][4] weight scale per wave
+struct F1Item {
+  int g, m0, mm, n0;
+};
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+template <int DA, int DB>
+__global__ __launch_bounds__(f1::THREADS) void k_gemm_fp8_swiglu(const Fp8GemmArgs p) {
+  using namespace f1;
+  constexpr int SA = DA + 1, SB = DB + 1;
+  // DA = 1: the wait for A(j) counts only B(j + DB - 1) behind it, so the number of
+  // activation DMAs a wave issues per step may vary (masked 8-row groups are skipped)
+  static_assert(DA == 1 && DB >= 2, "ring depths");
+  __shared__ __attribute__((aligned(16))) uint8_t ringA[SA * A_STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t ringB[SB * B_STAGE];
+  __shared__ int tprefix[MAX_G + 1];
+  __shared__ int mm_s[MAX_G];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: branches on it are scalar
   const int wm = wave >> 1, wn = wave & 1;
-  const int I = p.N / 2, K = p.K, KB = K / 128;
+  const int G = p.G, K = p.K, KB = K / BK, N = p.N, I = N / 2, cap = p.max_m, capS = p.a_s_stride;
+  const int tiles_n = I / HN;
 
-  const bool cover = (int)gridDim.x >= p.total_tiles;
-  for (int t0 = blockIdx.x; t0 < (cover ? (int)gridDim.x : p.total_tiles); t0 += gridDim.x) {
-    const int t = fp8_tile_of(t0, cover);
-    if (t >= p.total_tiles) continue;
-    int mt = t % p.tiles_m, rest = t / p.tiles_m;
-    int nt = rest % p.tiles_n, g = rest / p.tiles_n;
-    int mm = p.masked_m[g];
-    mm = mm < 0 ? 0 : (mm > p.max_m ? p.max_m : mm);
-    int m0 = mt * BM;
-    if (m0 >= mm) continue;
-    int n0 = nt * HN;  // h column origin
-    const uint8_t* A = p.a + (size_t)g * p.max_m * K;
-    const float* As_g = p.a_s + (size_t)g * p.max_m * KB;
-    const uint8_t* B = p.b + (size_t)g * p.N * K;
-    const float* Bs_g = p.b_s + (size_t)g * (p.N / 128) * KB;
+  f1_tile_prefix(p, tprefix, mm_s, tid);
+  const int total = __builtin_amdgcn_readfirstlane(tprefix[G]) * tiles_n;
+  const int grid = gridDim.x;
+  const int bx = (grid & 7) == 0 ? (int)(blockIdx.x & 7) * (grid >> 3) + (int)(blockIdx.x >> 3) : (int)blockIdx.x;
+  if (bx >= total) return;
+  const int n_items = (total - 1 - bx) / grid + 1;
+  const int nsteps = n_items * KB;
 
-    // each thread stages 4 chunks of A and 4 of B (16 B each): chunk c -> row c/8, col
-    // (c%8)*16; rows are clamped into the valid ones (clamped rows are never stored), so
-    // every load is unconditional
-    int arow[4], brow[4];
+  auto item_at = [&](int k) {
+    F1Item it;
+    const int w = bx + k * grid;
+    const int u = w / tiles_n, nt = w - u * tiles_n;
+    int lo = 0, hi = G;  // tprefix[lo] <= u < tprefix[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (__builtin_amdgcn_readfirstlane(tprefix[mid]) <= u) lo = mid;
+      else hi = mid;
+    }
+    it.g = lo;
+    it.m0 = (u - __builtin_amdgcn_readfirstlane(tprefix[lo])) * BM;
+    it.mm = __builtin_amdgcn_readfirstlane(mm_s[lo]);
+    it.n0 = nt * HN;
+    return it;
+  };
+
+  // ---- DMA cursors: per-lane sources of the current item (rows past masked_m re-read
+  // the last valid row, never stored); past the last step they stay on it
+  const uint8_t* asrc[A_OPS];
+  const float* asrc_s;
+  int a_n = 0;  // this wave's activation DMAs per step: 8-row groups entirely past masked_m are skipped
+  auto a_setup = [&](const F1Item& it) {
+    const uint8_t* A = p.a + (size_t)it.g * cap * K;
+    const int left = it.mm - it.m0 - 32 * wave;
+    a_n = left <= 0 ? 0 : (left >= 8 * A_OPS ? A_OPS : (left + 7) / 8);
+#pragma unroll
+    for (int j = 0; j < A_OPS; j++) {
+      const int r = 32 * wave + 8 * j + (lane >> 3);
+      const int row = it.m0 + r < it.mm ? it.m0 + r : it.mm - 1;
+      asrc[j] = A + (size_t)row * K + (((lane & 7) ^ f1_swz(r)) << 4);
+    }
+    const int rs = it.m0 + 4 * lane < capS - 4 ? it.m0 + 4 * lane : capS - 4;
+    asrc_s = p.a_s + (size_t)it.g * KB * capS + rs;
+  };
+  const uint8_t* bsrc[B_OPS];
+  const float* bsrc_s;
+  auto b_setup = [&](const F1Item& it) {
+    const uint8_t* B = p.b + (size_t)it.g * N * K;
+#pragma unroll
+    for (int j = 0; j < B_OPS; j++) {
+      const int r = 16 * wave + 8 * j + (lane >> 3);
+      const int brow = r < HN ? it.n0 + r : I + it.n0 + (r - HN);
+      bsrc[j] = B + (size_t)brow * K + (((lane & 7) ^ f1_swz(r)) << 4);
+    }
+    const int blk = (lane == 0 ? it.n0 : I + it.n0) / 128;
+    bsrc_s = p.b_s + ((size_t)it.g * (N / 128) + blk) * KB;
+  };
+  int a_k = 0, a_kb = 0, a_step = 0, a_st = 0;
+  int b_k = 0, b_kb = 0, b_step = 0, b_st = 0;
+  auto issue_a = [&]() {
+    uint8_t* st = ringA + a_st * A_STAGE;
+#pragma unroll
+    for (int j = 0; j < A_OPS; j++)
+      if (j < a_n) dma16(asrc[j] + a_kb * BK, st + (32 * wave + 8 * j) * BK);
+    if (wave == 0) dma16(asrc_s + (size_t)a_kb * capS, st + BM * BK);
+    a_st = a_st + 1 == SA ? 0 : a_st + 1;
+    if (a_step + 1 < nsteps) {
+      a_step++;
+      if (++a_kb == KB) {
+        a_kb = 0;
+        a_setup(item_at(++a_k));
+      }
+    }
+  };
+  auto issue_b = [&]() {
+    uint8_t* st = ringB + b_st * B_STAGE;
+#pragma unroll
+    for (int j = 0; j < B_OPS; j++) dma16(bsrc[j] + b_kb * BK, st + (16 * wave + 8 * j) * BK);
+    if (wave == 1 && lane < 2) dma4(bsrc_s + b_kb, st + BN * BK);
+    b_st = b_st + 1 == SB ? 0 : b_st + 1;
+    if (b_step + 1 < nsteps) {
+      b_step++;
+      if (++b_kb == KB) {
+        b_kb = 0;
+        b_setup(item_at(++b_k));
+      }
+    }
+  };
+
+  {
+    const F1Item it0 = item_at(0);
+    a_setup(it0);
+    b_setup(it0);
+  }
+  // prologue in the steady-state order: "step" i < 0 issues A(i + DA) (if >= 0), then B(i + DB)
+#pragma unroll
+  for (int i = -DB; i < 0; i++) {
+    if (i + DA >= 0) issue_a();
+    issue_b();
+  }
+
+  float4_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+#pragma unroll
+    for (int n = 0; n < 4; n++) acc[i][n] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+  F1Item cit = item_at(0);
+  int c_k = 0, c_kb = 0, c_sa = 0, c_sb = 0;
+  const int q = lane >> 4, rr = lane & 15, odd = lane & 1;
+
+  // A finished item's h values (bf16 pairs) wait in registers for the next step: stored
+  // right after its barrier, they sit in the counter just ahead of that step's
+  // activation DMA and hold up no wait for a weight DMA issued before them.  Masked rows
+  // store into the scratch row after the last expert.
+  uint32_t hw[4][2][2];
+  bool pend = false;
+  F1Item pit = cit;
+  auto store_h = [&]() {
+    uint16_t* H = (uint16_t*)p.out;
+    uint16_t* scratch_row = H + (size_t)G * cap * I;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      int c = tid + i * 256, r = c >> 3;
-      arow[i] = (m0 + r < mm) ? m0 + r : mm - 1;
-      int hc = n0 + (r < HN ? r : r - HN);
-      hc = hc < I ? hc : I - 1;
-      brow[i] = r < HN ? hc : I + hc;
-    }
-    const int srow = (m0 + (tid & (BM - 1)) < mm) ? m0 + (tid & (BM - 1)) : mm - 1;
-    // weight scale row-blocks of this wave's columns (gate for wn = 0, up for wn = 1)
-    const int bblk = (wn == 0 ? n0 : I + n0) / 128;
-
-    struct Slot {
-      u32x4_t a[4], b[4];
-      float sa, sw;  // activation scale of row srow, weight scale of this wave's block
-    };
-    auto gload = [&](int kb, Slot& sl) {
-      kb = kb < KB ? kb : KB - 1;  // prefetches past the end re-read the last block
+      const int row0 = pit.m0 + 64 * wm + 16 * i + 4 * q;
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
-        int c = tid + i * 256, col = (c & 7) * 16;
-        sl.a[i] = *(const u32x4_t*)(A + (size_t)arow[i] * K + kb * 128 + col);
-        sl.b[i] = *(const u32x4_t*)(B + (size_t)brow[i] * K + kb * 128 + col);
+      for (int n = 0; n < 2; n++) {
+        const int c = (pit.n0 + 32 * wn + 16 * n + rr) & ~1;
+        const int ra = row0 + odd, rb = row0 + 2 + odd;
+        uint16_t* pa = ra < pit.mm ? H + ((size_t)pit.g * cap + ra) * I + c : scratch_row + c;
+        uint16_t* pb = rb < pit.mm ? H + ((size_t)pit.g * cap + rb) * I + c : scratch_row + c;
+        *(uint32_t*)pa = hw[i][n][0];
+        *(uint32_t*)pb = hw[i][n][1];
       }
-      sl.sa = As_g[(size_t)srow * KB + kb];
-      sl.sw = Bs_g[(size_t)bblk * KB + kb];
-    };
-    auto lstore = [&](int buf, const Slot& sl) {
-      uint8_t* As = smem + buf * (BM + BN) * PITCH;
-      uint8_t* Bs = As + BM * PITCH;
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        int c = tid + i * 256, r = c >> 3, col = (c & 7) * 16;
-        *(u32x4_t*)(As + r * PITCH + col) = sl.a[i];
-        *(u32x4_t*)(Bs + r * PITCH + col) = sl.b[i];
-      }
-      if (tid < BM) sa_lds[buf * BM + tid] = sl.sa;
-      if ((tid & 63) == 0) sw_lds[buf * 4 + (tid >> 6)] = sl.sw;
-    };
-
-    float4_t acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; i++)
-#pragma unroll
-      for (int n = 0; n < 4; n++) acc[i][n] = float4_t{0.f, 0.f, 0.f, 0.f};
-
-    // register ring: slot d holds block kb+1 for kb = d (mod P), issued in consumption order
-    Slot ring[FP8_P];
-    {
-      Slot s0;
-      gload(0, s0);
-      lstore(0, s0);
     }
-#pragma unroll
-    for (int d = 0; d < FP8_P; d++) {
-      gload(d + 1, ring[d]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+  };
+
+  for (int s = 0; s < nsteps; s++) {
+    if (wave == 0) wait_vmcnt<wait_count(DA, DB, A_OPS + 1, B_OPS)>();
+    else if (wave == 1) wait_vmcnt<wait_count(DA, DB, A_OPS, B_OPS + 1)>();
+    else wait_vmcnt<wait_count(DA, DB, A_OPS, B_OPS)>();
+    // every wave's DMAs of step s have landed, and every wave is done with step s - 1,
+    // whose stages the next issues overwrite
     __syncthreads();
-    for (int kb0 = 0; kb0 < KB; kb0 += FP8_P) {
+    if (pend) {
+      store_h();
+      pend = false;
+    }
+    issue_a();
+    issue_b();
+
+    const bool active = cit.m0 + 64 * wm < cit.mm;
+    if (active) {
+      const uint8_t* As = ringA + c_sa * A_STAGE;
+      const uint8_t* Bs = ringB + c_sb * B_STAGE;
+      int8v_t af[4], bfr[4];
 #pragma unroll
-      for (int d = 0; d < FP8_P; d++) {
-        const int kb = kb0 + d;
-        const int buf = kb & 1;
-        if (kb < KB) {
-          const uint8_t* As = smem + buf * (BM + BN) * PITCH;
-          const uint8_t* Bs = As + BM * PITCH;
-          int8v_t af[4], bfr[4];
-          const int koff = (lane >> 4) * 32;
+      for (int i = 0; i < 4; i++) {
+        const int r = 64 * wm + 16 * i + rr;
+        const uint8_t* row = As + r * BK;
+        const int f = f1_swz(r);
+        const u32x4_t x0 = *(const u32x4_t*)(row + (((2 * q) ^ f) << 4));
+        const u32x4_t x1 = *(const u32x4_t*)(row + (((2 * q + 1) ^ f) << 4));
+        af[i] = int8v_t{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3], (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+      }
 #pragma unroll
-          for (int i = 0; i < 4; i++) {
-            const u32x4_t* pa = (const u32x4_t*)(As + (wm * 64 + i * 16 + (lane & 15)) * PITCH + koff);
-            u32x4_t x0 = pa[0], x1 = pa[1];
-            af[i] = int8v_t{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3], (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
-            const u32x4_t* pb = (const u32x4_t*)(Bs + (wn * 64 + i * 16 + (lane & 15)) * PITCH + koff);
-            u32x4_t y0 = pb[0], y1 = pb[1];
-            bfr[i] = int8v_t{(int)y0[0], (int)y0[1], (int)y0[2], (int)y0[3], (int)y1[0], (int)y1[1], (int)y1[2], (int)y1[3]};
-          }
-          const float sbw = sw_lds[buf * 4 + wave];
-          float4_t sav[4];
+      for (int n = 0; n < 4; n++) {
+        const int r = (n < 2 ? 32 * wn + 16 * n : HN + 32 * wn + 16 * (n - 2)) + rr;
+        const uint8_t* row = Bs + r * BK;
+        const int f = f1_swz(r);
+        const u32x4_t y0 = *(const u32x4_t*)(row + (((2 * q) ^ f) << 4));
+        const u32x4_t y1 = *(const u32x4_t*)(row + (((2 * q + 1) ^ f) << 4));
+        bfr[n] = int8v_t{(int)y0[0], (int)y0[1], (int)y0[2], (int)y0[3], (int)y1[0], (int)y1[1], (int)y1[2], (int)y1[3]};
+      }
+      const float* AS = (const float*)(As + BM * BK);
+      const float* WS = (const float*)(Bs + BN * BK);
+      const float wg = WS[0], wu = WS[1];
 #pragma unroll
-          for (int i = 0; i < 4; i++)
-            sav[i] = *(const float4_t*)(sa_lds + buf * BM + wm * 64 + i * 16 + (lane >> 4) * 4);
+      for (int i = 0; i < 4; i++) {
+        const float4_t sa = *(const float4_t*)(AS + 64 * wm + 16 * i + 4 * q);
 #pragma unroll
-          for (int i = 0; i < 4; i++)
+        for (int n = 0; n < 4; n++) {
+          // 128 exact e4m3 products summed in fp32 (unit e8m0 scales), then promoted with
+          // the row's activation scale times the block's weight scale
+          const float4_t t = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              af[i], bfr[n], float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+          const float w = n < 2 ? wg : wu;
 #pragma unroll
-            for (int n = 0; n < 4; n++) {
-              float4_t tmp = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                  af[i], bfr[n], float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
-#pragma unroll
-              for (int r = 0; r < 4; r++) acc[i][n][r] = __builtin_fmaf(tmp[r], sav[i][r] * sbw, acc[i][n][r]);
-            }
+          for (int r = 0; r < 4; r++) acc[i][n][r] = __builtin_fmaf(t[r], sa[r] * w, acc[i][n][r]);
         }
-        // block kb+1 into the other buffer (its readers finished before the last barrier);
-        // past the end this writes a buffer that is not read again
-        lstore(buf ^ 1, ring[d]);
-        __builtin_amdgcn_sched_barrier(0);
-        gload(kb + 1 + FP8_P, ring[d]);
-        __builtin_amdgcn_sched_barrier(0);
-        __syncthreads();
       }
     }
+    c_sa = c_sa + 1 == SA ? 0 : c_sa + 1;
+    c_sb = c_sb + 1 == SB ? 0 : c_sb + 1;
 
-    // SwiGLU epilogue through LDS (fp32 tile, gate columns [0, HN), up [HN, BN))
-    constexpr int CP = BN + 4;
-    float* cs = (float*)smem;
+    if (++c_kb == KB) {
+      // SwiGLU in registers: lanes 2c and 2c+1 hold neighbouring columns of the same four
+      // rows; one swap gives each lane both columns of two rows (rows +odd and +2+odd)
+      if (active) {
 #pragma unroll
-    for (int i = 0; i < 4; i++)
+        for (int i = 0; i < 4; i++)
 #pragma unroll
-      for (int n = 0; n < 4; n++)
+          for (int n = 0; n < 2; n++) {
+            uint32_t b[4];
 #pragma unroll
-        for (int r = 0; r < 4; r++)
-          cs[(wm * 64 + i * 16 + (lane >> 4) * 4 + r) * CP + wn * 64 + n * 16 + (lane & 15)] = acc[i][n][r];
-    __syncthreads();
-    uint16_t* H = (uint16_t*)p.out;
-    for (int q = tid; q < BM * (HN / 2); q += 256) {
-      int rr = q / (HN / 2), cp = (q % (HN / 2)) * 2;
-      int row = m0 + rr, hc = n0 + cp;
-      if (row >= mm || hc >= I) continue;
-      uint32_t packed = 0;
-#pragma unroll
-      for (int e = 0; e < 2; e++) {
-        float gt = cs[rr * CP + cp + e], up = cs[rr * CP + HN + cp + e];
-        float h = gt / (1.0f + expf(-gt)) * up;
-        packed |= f32_to_bf16_rne(h) << (16 * e);
+            for (int r = 0; r < 4; r++) {
+              const float gt = acc[i][n][r], up = acc[i][n + 2][r];
+              b[r] = f32_to_bf16_rne(gt / (1.0f + expf(-gt)) * up);
+            }
+            const uint32_t y0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)(odd ? b[0] : b[1]), 0xB1, 0xF, 0xF, false);
+            const uint32_t y1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)(odd ? b[2] : b[3]), 0xB1, 0xF, 0xF, false);
+            hw[i][n][0] = odd ? (y0 | (b[1] << 16)) : (b[0] | (y0 << 16));
+            hw[i][n][1] = odd ? (y1 | (b[3] << 16)) : (b[2] | (y1 << 16));
+          }
+        pend = true;
+        pit = cit;
       }
-      *(uint32_t*)(H + ((size_t)g * p.max_m + row) * I + hc) = packed;
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int n = 0; n < 4; n++) acc[i][n] = float4_t{0.f, 0.f, 0.f, 0.f};
+      c_kb = 0;
+      if (++c_k < n_items) cit = item_at(c_k);
     }
-    __syncthreads();
   }
+  if (pend) store_h();
+  wait_vmcnt<0>();  // the trailing re-reads land before the workgroup ends
+}
+
+template <int DA, int DB>
+static hipError_t launch_fp8_swiglu(Fp8GemmArgs p, int cu_limit, hipStream_t s) {
+  using namespace f1;
+  if (p.G > MAX_G || (p.N / 2) % HN != 0 || p.K % BK != 0 || p.a_s_stride % 4 != 0 ||
+      p.a_s_stride < p.max_m || p.a_s_stride < 4)
+    return hipErrorNotSupported;
+  if ((long long)p.G * ((p.max_m + BM - 1) / BM) * ((p.N / 2) / HN) > 0x7FFFFFFFLL) return hipErrorNotSupported;
+  const void* k = (const void*)k_gemm_fp8_swiglu<DA, DB>;
+  const int grid = resident_grid(k, THREADS, cu_limit);
+  if (grid <= 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((k_gemm_fp8_swiglu<DA, DB>), dim3(grid), dim3(THREADS), 0, s, p);
+  return hipGetLastError();
 }
 
 hipError_t gemm_fp8_swiglu(Fp8GemmArgs p, int cu_limit, hipStream_t s) {
-  p.tiles_m = (p.max_m + g1::BM - 1) / g1::BM;
-  p.tiles_n = (p.N / 2) / g1::HN;
-  p.total_tiles = p.G * p.tiles_m * p.tiles_n;
-  if (p.total_tiles == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_gemm_fp8_swiglu, dim3(fp8_grid(p.total_tiles, cu_limit)), dim3(256), 0, s, p);
-  return hipGetLastError();
+  if (p.G <= 0 || p.max_m <= 0 || p.N <= 0 || p.K <= 0) return hipSuccess;
+  return launch_fp8_swiglu<1, MXG_F1_DB>(p, cu_limit, s);
 }
 
 // ----------------------------------------------------------------------------- GEMM2

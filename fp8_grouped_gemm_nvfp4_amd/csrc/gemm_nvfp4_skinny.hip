@@ -68,23 +68,6 @@ __device__ __forceinline__ TileSrc tile_src(int first_row, int nlimit, int row_o
   return s;
 }
 
-// Every asynchronous operation of the main loop is an LDS DMA issued with inline
-// assembly, and the waits are explicit partial vmcnt waits: the compiler would otherwise
-// drain all outstanding DMAs (vmcnt(0)) before each LDS read, serializing the prefetch
-// ring.  No register-destination load is issued this way, so no register can be
-// overwritten behind the compiler's back.
-__device__ __forceinline__ void dma16(const uint8_t* g, uint8_t* lds) {
-  // the LDS base is wave-uniform; readfirstlane puts it in an SGPR for M0
-  uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0) : "memory");
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
 template <int NT>
 __device__ __forceinline__ void dma_w_chunk(uint8_t* stage, const uint8_t* B, const uint8_t* Bsf,
                                             const TileSrc* src, int chunk, int lane) {
@@ -454,7 +437,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_nvfp4_skinny(const MaskedGe
   wait_vmcnt<0>();  // the trailing re-reads land before the waves end
 }
 
-static int resident_grid(const void* kernel, int threads, int cu_limit) {
+int resident_grid(const void* kernel, int threads, int cu_limit) {
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;

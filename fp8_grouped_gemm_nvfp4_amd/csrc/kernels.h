@@ -60,17 +60,24 @@ hipError_t gemm_nvfp4_hetero(HeteroGemmArgs p, int epi, int cu_limit, hipStream_
 hipError_t gemm_nvfp4_skinny(MaskedGemmArgs p, int epi, int cu_limit, hipStream_t s);
 constexpr int SKINNY_MAX_M = 32;  // row capacity up to which the skinny kernel is used
 
+// Workgroups of `kernel` (with `threads` threads) resident on the device at once, over
+// at most cu_limit CUs when cu_limit > 0; 0 on a runtime error.
+int resident_grid(const void* kernel, int threads, int cu_limit);
+
 // FP8 block-scaled GEMMs of the DeepSeek-V3-style expert path (masked layout).
 struct Fp8GemmArgs {
   const uint8_t* a;     // GEMM1: e4m3 [G, max_m, K]; GEMM2: bf16 h [G, max_m, K]
-  const float* a_s;     // GEMM1: fp32 [G, max_m, K/128]; GEMM2: unused
+  const float* a_s;     // GEMM1: fp32 [G, K/128, a_s_stride] (row scales, transposed); GEMM2: unused
   const uint8_t* b;     // e4m3 [G, N, K]
   const float* b_s;     // fp32 [G, N/128, K/128]
-  void* out;            // GEMM1: bf16 h [G, max_m, N/2]; GEMM2: fp32 [G, max_m, N]
+  void* out;            // GEMM1: bf16 h [G * max_m + 1, N/2] (the last row takes the stores of
+                        // masked rows); GEMM2: fp32 [G, max_m, N]
   const int32_t* masked_m;
   int G, max_m, N, K;
+  int a_s_stride;       // GEMM1: max_m rounded up to a multiple of 4
   int tiles_m, tiles_n, total_tiles;
 };
+constexpr int fp8_scale_stride(int max_m) { return (max_m + 3) / 4 * 4; }
 hipError_t gemm_fp8_swiglu(Fp8GemmArgs p, int cu_limit, hipStream_t s);
 hipError_t gemm_bf16_fp8w(Fp8GemmArgs p, int cu_limit, hipStream_t s);
 
@@ -85,6 +92,7 @@ hipError_t dispatch(const int32_t* ids, int T, int E, int top_k, int max_m, int3
 hipError_t quantize_gather_nvfp4(const uint16_t* x, int T, int H, float g_x, const int32_t* ids,
                                  const int32_t* row, int top_k, int max_m, uint8_t* a,
                                  uint8_t* a_sf, hipStream_t s);
+// a_s receives the row scales transposed: [E, H/128, fp8_scale_stride(max_m)].
 hipError_t gather_fp8(const uint8_t* xq, const float* xs, int T, int H, const int32_t* ids,
                       const int32_t* row, int top_k, int max_m, uint8_t* a, float* a_s,
                       hipStream_t s);

@@ -94,7 +94,8 @@ hipError_t quantize_gather_nvfp4(const uint16_t* x, int T, int H, float g_x, con
 }
 
 // FP8 rows: copy the e4m3 codes (16 bytes per thread) and the 1x128 scales of
-// token t to every dispatched expert row.
+// token t to every dispatched expert row.  The scales are stored transposed, one
+// contiguous column of rows per (expert, 128-block), as the GEMM streams them.
 __global__ __launch_bounds__(256) void k_gather_fp8(const uint8_t* xq, const float* xs, int T, int H,
                                                     const int32_t* ids, const int32_t* row, int top_k,
                                                     int max_m, uint8_t* a, float* a_s) {
@@ -111,7 +112,7 @@ __global__ __launch_bounds__(256) void k_gather_fp8(const uint8_t* xq, const flo
     if (r >= max_m) continue;
     size_t dst = (size_t)e * max_m + r;
     *(u32x4_t*)(a + dst * H + (size_t)k * 16) = v;
-    if (has_scale) a_s[dst * (H / 128) + k / 8] = sc;
+    if (has_scale) a_s[((size_t)e * (H / 128) + k / 8) * fp8_scale_stride(max_m) + r] = sc;
   }
 }
 

@@ -195,7 +195,8 @@ typedef enum { MXG_MOE_FP8_BLOCK128 = 1, MXG_MOE_NVFP4 = 2 } mxg_moe_precision;
  *   dbg_h    optional device fp32 [E, max_m, I]: NVFP4 only, receives the
  *            pre-quantization intermediate for the rows it computes (NULL in
  *            production; y is bit-identical either way).
- * Requirements: H % 128 == 0, I % 128 == 0, 1 <= top_k <= 8, max_m >= 1.
+ * Requirements: H % 128 == 0, I % 128 == 0, 1 <= top_k <= 8, max_m >= 1; FP8 also
+ * E <= 1024 (else MXG_ERR_UNSUPPORTED).
  * Workspace: ws of at least moe_expert_forward_workspace_size(desc) bytes,
  * 256-byte aligned, device; its regions hold the gathered activations, h and
  * the GEMM2 output (offsets from moe_expert_forward_workspace_layout).
@@ -227,8 +228,9 @@ size_t moe_expert_forward_workspace_size(const mxg_moe_desc* desc);
 
 /* Byte offsets (host array of 6) of the workspace regions:
  *   [0] gathered activations (FP8: e4m3 [E, max_m, H]; NVFP4: codes [E, max_m, H/2])
- *   [1] their scales (FP8: fp32 [E, max_m, H/128]; NVFP4: e4m3 [E, max_m, H/16])
- *   [2] h (FP8: bf16 [E, max_m, I]; NVFP4: codes [E, max_m, I/2])
+ *   [1] their scales (FP8: fp32 [E, H/128, max_m rounded up to a multiple of 4], i.e.
+ *       transposed; NVFP4: e4m3 [E, max_m, H/16])
+ *   [2] h (FP8: bf16 [E, max_m, I] followed by one scratch row; NVFP4: codes [E, max_m, I/2])
  *   [3] h scales (FP8: unused; NVFP4: e4m3 [E, max_m, I/16])
  *   [4] GEMM2 output fp32 [E, max_m, H]
  *   [5] total size

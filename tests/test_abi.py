@@ -122,6 +122,21 @@ def _desc(**kw):
     return d
 
 
+def test_moe_fp8_workspace_layout_and_expert_limit():
+    L = mxg.lib()
+    off = (ctypes.c_size_t * 6)()
+    d = _desc(precision=mxg.MXG_MOE_FP8_BLOCK128, max_m=241)
+    assert L.moe_expert_forward_workspace_layout(ctypes.byref(d), off) == mxg.MXG_OK
+    rows = 256 * 241
+    assert off[1] - off[0] >= rows * 7168                       # e4m3 activations
+    assert off[2] - off[1] >= 256 * (7168 // 128) * 244 * 4      # transposed scales, stride 244
+    assert off[3] - off[2] >= (rows + 1) * 2048 * 2              # h plus the scratch row
+    assert off[5] - off[4] >= rows * 7168 * 4
+    for E, want in ((1024, mxg.MXG_OK), (1025, mxg.MXG_ERR_UNSUPPORTED)):
+        d = _desc(precision=mxg.MXG_MOE_FP8_BLOCK128, E=E)
+        assert L.moe_expert_forward_workspace_layout(ctypes.byref(d), off) == want, E
+
+
 def test_moe_workspace_layout_and_rejects():
     L = mxg.lib()
     d = _desc()

@@ -157,7 +157,7 @@ def test_moe_nvfp4_prefill_full_size():
 
 
 # ----------------------------------------------------------------------------- FP8
-def _run_fp8(T, H, I, seed, n_check):
+def _run_fp8(T, H, I, seed, n_check, n_deep=0):
     mxg = _mxg()
     wl = datagen.moe_fp8_workload(seed, DEV, T=T, H=H, I=I)
     t = wl.tensors
@@ -174,12 +174,19 @@ def _run_fp8(T, H, I, seed, n_check):
     torch.cuda.synchronize()
     assert torch.equal(y.view(torch.int16), y1.view(torch.int16)), "two runs differ"
     a = np_(ws[off[0]:off[0] + E * max_m * H]).reshape(E, max_m, H)
-    a_s = np_(ws[off[1]:off[1] + E * max_m * (H // 128) * 4].view(torch.float32)).reshape(E, max_m, H // 128)
+    cap_s = (max_m + 3) // 4 * 4  # the row scales are stored transposed: [E, H/128, cap_s]
+    a_s = np_(ws[off[1]:off[1] + E * (H // 128) * cap_s * 4].view(torch.float32)).reshape(E, H // 128, cap_s)
+    a_s = np.ascontiguousarray(a_s[:, :, :max_m].transpose(0, 2, 1))
     hb = np_(ws[off[2]:off[2] + E * max_m * I * 2].view(torch.int16)).view(np.uint16).reshape(E, max_m, I)
     ids_h, w_h, row_h = np_(ids), np_(w), np_(row)
     xq, xs = np_(t["xq"]), np_(t["xs"])
     yb = bf16_from_bits_np(bf16_tensor_bits(y))
     toks = _tokens(T, n_check, seed)
+    if n_deep:
+        # tokens with a slot past the first 256 rows of its expert (a later M tile)
+        deep = np.flatnonzero((row_h >= 256).any(axis=1))
+        assert len(deep) >= n_deep, "workload has too few rows past 256"
+        toks = sorted(set(toks) | set(deep[np.linspace(0, len(deep) - 1, n_deep).astype(int)].tolist()))
     touched = set()
     for tt in toks:
         o_list, so_list, wj = [], [], []
@@ -206,6 +213,11 @@ def _run_fp8(T, H, I, seed, n_check):
 def test_moe_fp8_small_full():
     log("FP8 MoE small: T=128 H=512 I=256 E=256, every token")
     _run_fp8(128, 512, 256, 3000, None)
+
+
+def test_moe_fp8_two_m_tiles():
+    log("FP8 MoE with masked_m past 256: T=8192 H=512 I=256 E=256, 24 tokens")
+    _run_fp8(8192, 512, 256, 3001, 8, n_deep=16)
 
 
 def test_moe_fp8_full_size():
