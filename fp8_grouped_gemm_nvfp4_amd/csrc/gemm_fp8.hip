@@ -11,28 +11,17 @@
 //   row's activation scale times the block's weight scale.  Epilogue:
 //   h = silu(gate) * up in fp32, stored as bf16 (round to nearest even).
 // GEMM2:  A = h bf16 [G, max_m, I], B = W2 e4m3 [G, H, I] with 128x128 fp32
-//   scales; fp8 is widened exactly to bf16 on the way into LDS and the bf16
-//   MFMA (16x16x32) accumulates each 128-K scale block before promotion.
-//   Output fp32 [G, max_m, H].
+//   scales; fp8 is widened exactly to bf16 and the bf16 MFMA (16x16x32)
+//   accumulates each 128-K scale block before promotion.  Output fp32 [G, max_m, H].
+//
+// Both kernels are persistent and stream the weights through LDS by DMA; at the
+// prefill shapes they are bound by the L1 -> L2 request rate of the CUs, so every
+// expert's weights are read once (256-row M tiles) and the activations, which the N
+// tiles of an expert re-read, come from the L2 of one XCD.
 #include "device_common.h"
 #include "kernels.h"
 
 namespace mxg {
-
-// XCD-aware tile order for a grid that covers every tile (workgroup b runs on XCD b % 8):
-// chunks of 8 consecutive tiles (the M tiles of one weight panel are adjacent) go to the
-// XCDs in turn.  A capped grid strides over the tiles in order.
-constexpr int FP8_XCD_CHUNK = 8;
-__device__ __forceinline__ int fp8_tile_of(int t0, bool cover) {
-  if (!cover) return t0;
-  const int xcd = t0 & 7, slot = t0 >> 3;
-  return ((slot / FP8_XCD_CHUNK) * 8 + xcd) * FP8_XCD_CHUNK + slot % FP8_XCD_CHUNK;
-}
-static int fp8_grid(int total, int cu_limit) {
-  if (cu_limit > 0) return total < cu_limit * 2 ? total : cu_limit * 2;
-  return (total + 8 * FP8_XCD_CHUNK - 1) / (8 * FP8_XCD_CHUNK) * (8 * FP8_XCD_CHUNK);
-}
-constexpr int FP8_P2 = 2;  // K steps of raw bytes prefetched in a register ring (GEMM2)
 
 // ----------------------------------------------------------------------------- GEMM1
 // Persistent and weight-streaming.  A work item is (expert g, 256-row M tile, 64 h
@@ -50,10 +39,11 @@ constexpr int FP8_P2 = 2;  // K steps of raw bytes prefetched in a register ring
 // its eight 16-byte chunks XOR-permuted by (r ^ r >> 3) & 7, which keeps the MFMA
 // operand reads free of bank conflicts.
 //
-// Waves: 4 (M, 64 rows each) x 2 (N).  Wave (wm, wn) owns rows 64 wm.. and h columns
-// 32 wn.. of the item, i.e. gate columns 32 wn.. and the matching up columns, so the
-// SwiGLU epilogue runs in registers.  A wave whose 64 rows are all masked skips the
-// MFMAs and the epilogue but keeps issuing its share of the DMAs.
+// Waves: 4 (M) x 2 (N).  Wave (wm, wn) owns the 16-row groups 16 wm + 64 i (i = 0..3)
+// and h columns 32 wn.. of the item, i.e. gate columns 32 wn.. and the matching up
+// columns, so the SwiGLU epilogue runs in registers.  Interleaving the row groups keeps
+// both waves of every SIMD busy when masked_m <= 128; row groups that are entirely
+// masked skip their MFMAs, and every wave keeps issuing its share of the DMAs.
 #ifndef MXG_F1_DB
 #define MXG_F1_DB 4
 #endif
@@ -249,7 +239,7 @@ __global__ __launch_bounds__(f1::THREADS) void k_gemm_fp8_swiglu(const Fp8GemmAr
     uint16_t* scratch_row = H + (size_t)G * cap * I;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      const int row0 = pit.m0 + 64 * wm + 16 * i + 4 * q;
+      const int row0 = pit.m0 + 16 * wm + 64 * i + 4 * q;
 #pragma unroll
       for (int n = 0; n < 2; n++) {
         const int c = (pit.n0 + 32 * wn + 16 * n + rr) & ~1;
@@ -276,14 +266,15 @@ __global__ __launch_bounds__(f1::THREADS) void k_gemm_fp8_swiglu(const Fp8GemmAr
     issue_a();
     issue_b();
 
-    const bool active = cit.m0 + 64 * wm < cit.mm;
+    const bool active = cit.m0 + 16 * wm < cit.mm;
     if (active) {
       const uint8_t* As = ringA + c_sa * A_STAGE;
       const uint8_t* Bs = ringB + c_sb * B_STAGE;
       int8v_t af[4], bfr[4];
 #pragma unroll
       for (int i = 0; i < 4; i++) {
-        const int r = 64 * wm + 16 * i + rr;
+        if (cit.m0 + 16 * wm + 64 * i >= cit.mm) break;
+        const int r = 16 * wm + 64 * i + rr;
         const uint8_t* row = As + r * BK;
         const int f = f1_swz(r);
         const u32x4_t x0 = *(const u32x4_t*)(row + (((2 * q) ^ f) << 4));
@@ -304,7 +295,8 @@ __global__ __launch_bounds__(f1::THREADS) void k_gemm_fp8_swiglu(const Fp8GemmAr
       const float wg = WS[0], wu = WS[1];
 #pragma unroll
       for (int i = 0; i < 4; i++) {
-        const float4_t sa = *(const float4_t*)(AS + 64 * wm + 16 * i + 4 * q);
+        if (cit.m0 + 16 * wm + 64 * i >= cit.mm) break;
+        const float4_t sa = *(const float4_t*)(AS + 16 * wm + 64 * i + 4 * q);
 #pragma unroll
         for (int n = 0; n < 4; n++) {
           // 128 exact e4m3 products summed in fp32 (unit e8m0 scales), then promoted with
@@ -374,178 +366,254 @@ hipError_t gemm_fp8_swiglu(Fp8GemmArgs p, int cu_limit, hipStream_t s) {
 }
 
 // ----------------------------------------------------------------------------- GEMM2
-namespace g2 {
-constexpr int BM = 128, BN = 128, BK = 64, PITCH = 72;  // bf16 elements per LDS row
+// Persistent and weight-streaming like GEMM1.  A work item is (expert g, 256-row M tile,
+// 128 output columns, one 128-row block of W2's scales); a step is 64 K: 256 bf16 h rows
+// x 128 bytes and 128 e4m3 weight rows x 64 bytes, both by DMA (h one step ahead, W2 DB
+// steps ahead).  The weights are widened exactly to bf16 in registers
+// (v_cvt_scalef32_pk_bf16_fp8, scale 1) for the bf16 MFMA; each 128-K scale block is
+// summed in fp32 before it is promoted with the block's weight scale.  The waves own
+// interleaved 16-row groups as in GEMM1.  LDS rows are
+// XOR-swizzled (h: 16-byte chunk ^ (r ^ r >> 3) & 7; W2: 16-byte chunk ^ (r >> 2) & 3).
+namespace f2 {
+constexpr int BM = 256, BN = 128, BK = 64;
+constexpr int WAVES = 8, THREADS = WAVES * 64;
+constexpr int A_STAGE = BM * BK * 2;  // bf16 h rows, 128 bytes each
+constexpr int B_STAGE = BN * BK + 16; // e4m3 W2 rows, 64 bytes each, then the block scale
+constexpr int A_OPS = 4, B_OPS = 1;   // DMAs per wave per step (wave 1 adds the scale)
+constexpr int DB = 6;
+}  // namespace f2
+
+__device__ __forceinline__ int f2_swz_b(int r) { return (r >> 2) & 3; }
+
+// 4 x 4 transpose inside each quad of lanes: lane q's v[r] (row r, column q) becomes lane
+// r's element q, so that each lane ends up with four consecutive columns of one row.
+__device__ __forceinline__ float4_t quad_transpose(float4_t v, int lane) {
+  const int q = lane & 3;
+  const bool o1 = (q & 1) != 0, o2 = (q & 2) != 0;
+  const float s0 = o1 ? v[0] : v[1], s1 = o1 ? v[2] : v[3];
+  const float r0 = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(s0), 0xB1, 0xF, 0xF, false));
+  const float r1 = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(s1), 0xB1, 0xF, 0xF, false));
+  if (o1) { v[0] = r0; v[2] = r1; } else { v[1] = r0; v[3] = r1; }
+  const float t0 = o2 ? v[0] : v[2], t1 = o2 ? v[1] : v[3];
+  const float u0 = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(t0), 0x4E, 0xF, 0xF, false));
+  const float u1 = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(t1), 0x4E, 0xF, 0xF, false));
+  if (o2) { v[0] = u0; v[1] = u1; } else { v[2] = u0; v[3] = u1; }
+  return v;
 }
 
-__global__ __launch_bounds__(256) void k_gemm_bf16_fp8w(const Fp8GemmArgs p) {
-  using namespace g2;
-  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * (BM + BN) * PITCH];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+__global__ __launch_bounds__(f2::THREADS) void k_gemm_bf16_fp8w(const Fp8GemmArgs p) {
+  using namespace f2;
+  constexpr int SA = 2, SB = DB + 1;
+  __shared__ __attribute__((aligned(16))) uint8_t ringA[SA * A_STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t ringB[SB * B_STAGE];
+  __shared__ int tprefix[f1::MAX_G + 1];
+  __shared__ int mm_s[f1::MAX_G];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int K = p.K, KB = K / 128, N = p.N;
+  const int G = p.G, K = p.K, KB = K / 128, N = p.N, cap = p.max_m;
+  const int tiles_n = N / BN, KT = K / BK;
 
-  const bool cover = (int)gridDim.x >= p.total_tiles;
-  for (int t0 = blockIdx.x; t0 < (cover ? (int)gridDim.x : p.total_tiles); t0 += gridDim.x) {
-    const int t = fp8_tile_of(t0, cover);
-    if (t >= p.total_tiles) continue;
-    int mt = t % p.tiles_m, rest = t / p.tiles_m;
-    int nt = rest % p.tiles_n, g = rest / p.tiles_n;
-    int mm = p.masked_m[g];
-    mm = mm < 0 ? 0 : (mm > p.max_m ? p.max_m : mm);
-    int m0 = mt * BM;
-    if (m0 >= mm) continue;
-    int n0 = nt * BN;
-    const uint16_t* A = (const uint16_t*)p.a + (size_t)g * p.max_m * K;
-    const uint8_t* B = p.b + (size_t)g * N * K;
-    const float* Bs_g = p.b_s + (size_t)g * (N / 128) * KB;
+  f1_tile_prefix(p, tprefix, mm_s, tid);
+  const int total = __builtin_amdgcn_readfirstlane(tprefix[G]) * tiles_n;
+  const int grid = gridDim.x;
+  const int bx = (grid & 7) == 0 ? (int)(blockIdx.x & 7) * (grid >> 3) + (int)(blockIdx.x >> 3) : (int)blockIdx.x;
+  if (bx >= total) return;
+  const int n_items = (total - 1 - bx) / grid + 1;
+  const int nsteps = n_items * KT;
 
-    // A: 128 rows x 64 bf16 = 1024 chunks of 8 bf16 -> 4 per thread (row c/8, col (c%8)*8)
-    // B: 128 rows x 64 fp8 = 512 chunks of 16 fp8 -> 2 per thread (row c/4, col (c%4)*16)
-    // Rows are clamped into the valid ones (never stored), so every load is unconditional.
-    int arow[4], brow[2];
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      int r = (tid + i * 256) >> 3;
-      arow[i] = (m0 + r < mm) ? m0 + r : mm - 1;
+  auto item_at = [&](int k) {
+    F1Item it;
+    const int w = bx + k * grid;
+    const int u = w / tiles_n, nt = w - u * tiles_n;
+    int lo = 0, hi = G;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (__builtin_amdgcn_readfirstlane(tprefix[mid]) <= u) lo = mid;
+      else hi = mid;
     }
-#pragma unroll
-    for (int i = 0; i < 2; i++) {
-      int r = (tid + i * 256) >> 2;
-      brow[i] = (n0 + r < N) ? n0 + r : N - 1;
-    }
-    struct Slot {
-      u32x4_t a[4], b[2];
-      float sw;  // weight scale of the step's 128 x 128 block
-    };
-    const int KT = K / BK;
-    auto gload = [&](int kt, Slot& sl) {
-      kt = kt < KT ? kt : KT - 1;  // prefetches past the end re-read the last step
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        int c = tid + i * 256, col = (c & 7) * 8;
-        sl.a[i] = *(const u32x4_t*)(A + (size_t)arow[i] * K + kt * BK + col);
-      }
-#pragma unroll
-      for (int i = 0; i < 2; i++) {
-        int c = tid + i * 256, col = (c & 3) * 16;
-        sl.b[i] = *(const u32x4_t*)(B + (size_t)brow[i] * K + kt * BK + col);
-      }
-      sl.sw = Bs_g[(size_t)(n0 / 128) * KB + (kt >> 1)];
-    };
-    auto lstore = [&](int buf, const Slot& sl) {
-      __bf16* As = smem + buf * (BM + BN) * PITCH;
-      __bf16* Bs = As + BM * PITCH;
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        int c = tid + i * 256, r = c >> 3, col = (c & 7) * 8;
-        *(u32x4_t*)(As + r * PITCH + col) = sl.a[i];
-      }
-#pragma unroll
-      for (int i = 0; i < 2; i++) {
-        int c = tid + i * 256, r = c >> 2, col = (c & 3) * 16;
-        u32x4_t o0, o1;
-#pragma unroll
-        for (int w = 0; w < 4; w++) {
-          bf16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(sl.b[i][w], 1.0f, false);
-          bf16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(sl.b[i][w] >> 16, 1.0f, false);
-          uint32_t ulo = *(uint32_t*)&lo, uhi = *(uint32_t*)&hi;
-          if (w < 2) { o0[2 * w] = ulo; o0[2 * w + 1] = uhi; }
-          else { o1[2 * (w - 2)] = ulo; o1[2 * (w - 2) + 1] = uhi; }
-        }
-        u32x4_t* dst = (u32x4_t*)(Bs + r * PITCH + col);
-        dst[0] = o0;
-        dst[1] = o1;
-      }
-    };
+    it.g = lo;
+    it.m0 = (u - __builtin_amdgcn_readfirstlane(tprefix[lo])) * f1::BM;
+    it.mm = __builtin_amdgcn_readfirstlane(mm_s[lo]);
+    it.n0 = nt * BN;
+    return it;
+  };
 
-    float4_t acc[4][4], tmp[4][4];
+  const uint8_t* asrc[A_OPS];
+  int a_n = 0;
+  auto a_setup = [&](const F1Item& it) {
+    const uint8_t* A = p.a + (size_t)it.g * cap * K * 2;
+    const int left = it.mm - it.m0 - 32 * wave;
+    a_n = left <= 0 ? 0 : (left >= 8 * A_OPS ? A_OPS : (left + 7) / 8);
 #pragma unroll
-    for (int i = 0; i < 4; i++)
-#pragma unroll
-      for (int n = 0; n < 4; n++) { acc[i][n] = float4_t{0.f, 0.f, 0.f, 0.f}; tmp[i][n] = acc[i][n]; }
-
-    // register ring: slot d holds step kt+1 for kt = d (mod P), issued in consumption order
-    Slot ring[FP8_P2];
-    float sw_cur;  // weight scale of the step being computed
-    {
-      Slot s0;
-      gload(0, s0);
-      lstore(0, s0);
-      sw_cur = s0.sw;
+    for (int j = 0; j < A_OPS; j++) {
+      const int r = 32 * wave + 8 * j + (lane >> 3);
+      const int row = it.m0 + r < it.mm ? it.m0 + r : it.mm - 1;
+      asrc[j] = A + (size_t)row * K * 2 + (((lane & 7) ^ f1_swz(r)) << 4);
     }
+  };
+  const uint8_t* bsrc;
+  const float* bsrc_s;
+  auto b_setup = [&](const F1Item& it) {
+    const int r = 16 * wave + (lane >> 2);
+    bsrc = p.b + ((size_t)it.g * N + it.n0 + r) * K + (((lane & 3) ^ f2_swz_b(r)) << 4);
+    bsrc_s = p.b_s + ((size_t)it.g * (N / 128) + it.n0 / 128) * KB;
+  };
+  int a_k = 0, a_kt = 0, a_step = 0, a_st = 0;
+  int b_k = 0, b_kt = 0, b_step = 0, b_st = 0;
+  auto issue_a = [&]() {
+    uint8_t* st = ringA + a_st * A_STAGE;
 #pragma unroll
-    for (int d = 0; d < FP8_P2; d++) {
-      gload(d + 1, ring[d]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    __syncthreads();
-    for (int kt0 = 0; kt0 < KT; kt0 += FP8_P2) {
-#pragma unroll
-      for (int d = 0; d < FP8_P2; d++) {
-        const int kt = kt0 + d;
-        const int buf = kt & 1;
-        if (kt < KT) {
-          const __bf16* As = smem + buf * (BM + BN) * PITCH;
-          const __bf16* Bs = As + BM * PITCH;
-#pragma unroll
-          for (int ks = 0; ks < BK / 32; ks++) {
-            bf16x8_t af[4], bfr[4];
-            const int koff = ks * 32 + (lane >> 4) * 8;
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-              af[i] = *(const bf16x8_t*)(As + (wm * 64 + i * 16 + (lane & 15)) * PITCH + koff);
-              bfr[i] = *(const bf16x8_t*)(Bs + (wn * 64 + i * 16 + (lane & 15)) * PITCH + koff);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; i++)
-#pragma unroll
-              for (int n = 0; n < 4; n++)
-                tmp[i][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[n], tmp[i][n], 0, 0, 0);
-          }
-          if ((kt & 1) == 1) {  // end of a 128-wide scale block: promote
-            const float sbw = sw_cur;
-#pragma unroll
-            for (int i = 0; i < 4; i++)
-#pragma unroll
-              for (int n = 0; n < 4; n++)
-#pragma unroll
-                for (int r = 0; r < 4; r++) {
-                  acc[i][n][r] = __builtin_fmaf(tmp[i][n][r], sbw, acc[i][n][r]);
-                  tmp[i][n][r] = 0.f;
-                }
-          }
-        }
-        // step kt+1 into the other buffer; past the end this writes a buffer not read again
-        sw_cur = ring[d].sw;
-        lstore(buf ^ 1, ring[d]);
-        __builtin_amdgcn_sched_barrier(0);
-        gload(kt + 1 + FP8_P2, ring[d]);
-        __builtin_amdgcn_sched_barrier(0);
-        __syncthreads();
+    for (int j = 0; j < A_OPS; j++)
+      if (j < a_n) dma16(asrc[j] + a_kt * (BK * 2), st + (32 * wave + 8 * j) * (BK * 2));
+    a_st ^= 1;
+    if (a_step + 1 < nsteps) {
+      a_step++;
+      if (++a_kt == KT) {
+        a_kt = 0;
+        a_setup(item_at(++a_k));
       }
     }
+  };
+  auto issue_b = [&]() {
+    uint8_t* st = ringB + b_st * B_STAGE;
+    dma16(bsrc + b_kt * BK, st + 16 * wave * BK);
+    if (wave == 1 && lane == 0) dma4(bsrc_s + (b_kt >> 1), st + BN * BK);
+    b_st = b_st + 1 == SB ? 0 : b_st + 1;
+    if (b_step + 1 < nsteps) {
+      b_step++;
+      if (++b_kt == KT) {
+        b_kt = 0;
+        b_setup(item_at(++b_k));
+      }
+    }
+  };
+
+  {
+    const F1Item it0 = item_at(0);
+    a_setup(it0);
+    b_setup(it0);
+  }
+#pragma unroll
+  for (int i = -DB; i < 0; i++) {
+    if (i + 1 >= 0) issue_a();
+    issue_b();
+  }
+
+  // acc: promoted sums; tmp: the current 128-K block, and between the end of an item and
+  // the next barrier the item's results (transposed, one row of 4 columns per lane)
+  float4_t acc[4][4], tmp[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+#pragma unroll
+    for (int n = 0; n < 4; n++) acc[i][n] = tmp[i][n] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+  F1Item cit = item_at(0);
+  int c_k = 0, c_kt = 0, c_sa = 0, c_sb = 0;
+  const int q = lane >> 4, rr = lane & 15;
+  bool pend = false;
+  F1Item pit = cit;
+  auto store_out = [&]() {
     float* O = (float*)p.out;
 #pragma unroll
-    for (int i = 0; i < 4; i++)
+    for (int i = 0; i < 4; i++) {
+      const int row = pit.m0 + 16 * wm + 64 * i + 4 * q + (lane & 3);
 #pragma unroll
       for (int n = 0; n < 4; n++) {
-        int col = n0 + wn * 64 + n * 16 + (lane & 15);
+        const int col = pit.n0 + 64 * wn + 16 * n + 4 * (rr >> 2);
+        if (row < pit.mm) *(float4_t*)(O + ((size_t)pit.g * cap + row) * N + col) = tmp[i][n];
+        tmp[i][n] = float4_t{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+  };
+
+  for (int s = 0; s < nsteps; s++) {
+    if (wave == 1) wait_vmcnt<B_OPS + 1>();
+    else wait_vmcnt<B_OPS>();
+    __syncthreads();
+    if (pend) {
+      store_out();
+      pend = false;
+    }
+    issue_a();
+    issue_b();
+
+    const bool active = cit.m0 + 16 * wm < cit.mm;
+    if (active) {
+      const uint8_t* As = ringA + c_sa * A_STAGE;
+      const uint8_t* Bs = ringB + c_sb * B_STAGE;
 #pragma unroll
-        for (int r = 0; r < 4; r++) {
-          int row = m0 + wm * 64 + i * 16 + (lane >> 4) * 4 + r;
-          if (row < mm && col < N) O[((size_t)g * p.max_m + row) * N + col] = acc[i][n][r];
+      for (int ks = 0; ks < BK / 32; ks++) {
+        bf16x8_t af[4], bfr[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          if (cit.m0 + 16 * wm + 64 * i >= cit.mm) break;
+          const int r = 16 * wm + 64 * i + rr;
+          af[i] = *(const bf16x8_t*)(As + r * (BK * 2) + (((ks * 4 + q) ^ f1_swz(r)) << 4));
+        }
+#pragma unroll
+        for (int n = 0; n < 4; n++) {
+          const int r = 64 * wn + 16 * n + rr;
+          const u32x2_t raw = *(const u32x2_t*)(Bs + r * BK + (((ks * 2 + (q >> 1)) ^ f2_swz_b(r)) << 4) + (q & 1) * 8);
+          const bf16x2_t w0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[0], 1.0f, false);
+          const bf16x2_t w1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[0], 1.0f, true);
+          const bf16x2_t w2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[1], 1.0f, false);
+          const bf16x2_t w3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[1], 1.0f, true);
+          bfr[n] = bf16x8_t{w0[0], w0[1], w1[0], w1[1], w2[0], w2[1], w3[0], w3[1]};
+        }
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          if (cit.m0 + 16 * wm + 64 * i >= cit.mm) break;
+#pragma unroll
+          for (int n = 0; n < 4; n++)
+            tmp[i][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[n], tmp[i][n], 0, 0, 0);
         }
       }
+      if (c_kt & 1) {  // end of a 128-wide scale block: promote
+        const float sw = *(const float*)(Bs + BN * BK);
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+          for (int n = 0; n < 4; n++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+              acc[i][n][r] = __builtin_fmaf(tmp[i][n][r], sw, acc[i][n][r]);
+              tmp[i][n][r] = 0.f;
+            }
+      }
+    }
+    c_sa ^= 1;
+    c_sb = c_sb + 1 == SB ? 0 : c_sb + 1;
+
+    if (++c_kt == KT) {
+      if (active) {
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+          for (int n = 0; n < 4; n++) {
+            tmp[i][n] = quad_transpose(acc[i][n], lane);
+            acc[i][n] = float4_t{0.f, 0.f, 0.f, 0.f};
+          }
+        pend = true;
+        pit = cit;
+      }
+      c_kt = 0;
+      if (++c_k < n_items) cit = item_at(c_k);
+    }
   }
+  if (pend) store_out();
+  wait_vmcnt<0>();  // the trailing re-reads land before the workgroup ends
 }
 
 hipError_t gemm_bf16_fp8w(Fp8GemmArgs p, int cu_limit, hipStream_t s) {
-  p.tiles_m = (p.max_m + g2::BM - 1) / g2::BM;
-  p.tiles_n = (p.N + g2::BN - 1) / g2::BN;
-  p.total_tiles = p.G * p.tiles_m * p.tiles_n;
-  if (p.total_tiles == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_gemm_bf16_fp8w, dim3(fp8_grid(p.total_tiles, cu_limit)), dim3(256), 0, s, p);
+  using namespace f2;
+  if (p.G <= 0 || p.max_m <= 0 || p.N <= 0 || p.K <= 0) return hipSuccess;
+  if (p.G > f1::MAX_G || p.N % BN != 0 || p.K % 128 != 0) return hipErrorNotSupported;
+  if ((long long)p.G * ((p.max_m + BM - 1) / BM) * (p.N / BN) > 0x7FFFFFFFLL) return hipErrorNotSupported;
+  const int grid = resident_grid((const void*)k_gemm_bf16_fp8w, THREADS, cu_limit);
+  if (grid <= 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_gemm_bf16_fp8w, dim3(grid), dim3(THREADS), 0, s, p);
   return hipGetLastError();
 }
 
