@@ -18,18 +18,16 @@
 // prefill shapes they are bound by the L1 -> L2 request rate of the CUs, so every
 // expert's weights are read once (256-row M tiles) and the activations, which the N
 // tiles of an expert re-read, come from the L2 of one XCD.
-#include "device_common.h"
 #include "kernels.h"
+#include "stream_common.h"
 
 namespace mxg {
 
 // ----------------------------------------------------------------------------- GEMM1
-// Persistent and weight-streaming.  A work item is (expert g, 256-row M tile, 64 h
-// columns): the item's 64 gate rows and 64 up rows of W13 against up to 256 activation
-// rows, so every weight panel is read from HBM once per expert whenever masked_m <= 256.
-// The items of a workgroup are bx + i * grid, where bx numbers the workgroups XCD by XCD
-// (workgroup b runs on XCD b % 8): the workgroups of one XCD run neighbouring N tiles of
-// one expert together and share its activation rows in their L2.
+// Persistent and weight-streaming.  A work item (stream_common.h) is (expert g, 256-row M
+// tile, 64 h columns): the item's 64 gate rows and 64 up rows of W13 against up to 256
+// activation rows, so every weight panel is read from HBM once per expert whenever
+// masked_m <= 256.
 //
 // Operands travel from HBM into LDS by DMA through two rings that run on across item
 // boundaries: activations (and their row scales) one step ahead, weights (and the two
@@ -52,7 +50,8 @@ constexpr int BM = 256, BN = 128, HN = BN / 2, BK = 128;
 constexpr int WAVES = 8, THREADS = WAVES * 64;
 constexpr int A_STAGE = BM * BK + BM * 4;  // codes, then the fp32 row scales
 constexpr int B_STAGE = BN * BK + 16;      // codes, then the {gate, up} block scales
-constexpr int MAX_G = 1024;
+constexpr int MAX_G = STREAM_MAX_G;
+static_assert(BM == STREAM_BM, "M tile of the shared work distribution");
 // DMA instructions per wave per step: 4 of activations (32 rows), 2 of weights (16 rows);
 // wave 0 adds the activation row scales, wave 1 the two weight block scales
 constexpr int A_OPS = 4, B_OPS = 2;
@@ -64,40 +63,6 @@ constexpr int wait_count(int da, int db, int ao, int bo) {
 }  // namespace f1
 
 __device__ __forceinline__ int f1_swz(int r) { return (r ^ (r >> 3)) & 7; }
-
-// tprefix[g] = sum over g' < g of the M tiles of expert g' (ceil(clamped masked_m / BM));
-// tprefix[G] = the number of (expert, M tile) units.  The clamped masked_m values go to
-// LDS too: a global load inside the main loop would make the compiler drain the DMAs.
-__device__ __forceinline__ void f1_tile_prefix(const Fp8GemmArgs& p, int* tprefix, int* mm_s, int tid) {
-  if (tid < 64) {
-    const int lane = tid;
-    int run = 0;
-    for (int base = 0; base < p.G; base += 64) {
-      const int g = base + lane;
-      int c = 0;
-      if (g < p.G) {
-        int mm = p.masked_m[g];
-        mm = mm < 0 ? 0 : (mm > p.max_m ? p.max_m : mm);
-        c = (mm + f1::BM - 1) / f1::BM;
-        mm_s[g] = mm;
-      }
-      int x = c;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int y = __shfl_up(x, d);
-        if (lane >= d) x += y;
-      }
-      if (g < p.G) tprefix[g] = run + x - c;
-      run += __shfl(x, 63);
-    }
-    if (lane == 0) tprefix[p.G] = run;
-  }
-  __syncthreads();
-}
-
-struct F1Item {
-  int g, m0, mm, n0;
-};
 
 template <int DA, int DB>
 __global__ __launch_bounds__(f1::THREADS) void k_gemm_fp8_swiglu(const Fp8GemmArgs p) {
@@ -117,37 +82,22 @@ __global__ __launch_bounds__(f1::THREADS) void k_gemm_fp8_swiglu(const Fp8GemmAr
   const int G = p.G, K = p.K, KB = K / BK, N = p.N, I = N / 2, cap = p.max_m, capS = p.a_s_stride;
   const int tiles_n = I / HN;
 
-  f1_tile_prefix(p, tprefix, mm_s, tid);
+  stream_tile_prefix(p.masked_m, p.G, p.max_m, tprefix, mm_s, tid);
   const int total = __builtin_amdgcn_readfirstlane(tprefix[G]) * tiles_n;
   const int grid = gridDim.x;
-  const int bx = (grid & 7) == 0 ? (int)(blockIdx.x & 7) * (grid >> 3) + (int)(blockIdx.x >> 3) : (int)blockIdx.x;
+  const int bx = stream_bx();
   if (bx >= total) return;
   const int n_items = (total - 1 - bx) / grid + 1;
   const int nsteps = n_items * KB;
 
-  auto item_at = [&](int k) {
-    F1Item it;
-    const int w = bx + k * grid;
-    const int u = w / tiles_n, nt = w - u * tiles_n;
-    int lo = 0, hi = G;  // tprefix[lo] <= u < tprefix[hi]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (__builtin_amdgcn_readfirstlane(tprefix[mid]) <= u) lo = mid;
-      else hi = mid;
-    }
-    it.g = lo;
-    it.m0 = (u - __builtin_amdgcn_readfirstlane(tprefix[lo])) * BM;
-    it.mm = __builtin_amdgcn_readfirstlane(mm_s[lo]);
-    it.n0 = nt * HN;
-    return it;
-  };
+  auto item_at = [&](int k) { return stream_item(bx + k * grid, tiles_n, G, tprefix, mm_s, HN); };
 
   // ---- DMA cursors: per-lane sources of the current item (rows past masked_m re-read
   // the last valid row, never stored); past the last step they stay on it
   const uint8_t* asrc[A_OPS];
   const float* asrc_s;
   int a_n = 0;  // this wave's activation DMAs per step: 8-row groups entirely past masked_m are skipped
-  auto a_setup = [&](const F1Item& it) {
+  auto a_setup = [&](const StreamItem& it) {
     const uint8_t* A = p.a + (size_t)it.g * cap * K;
     const int left = it.mm - it.m0 - 32 * wave;
     a_n = left <= 0 ? 0 : (left >= 8 * A_OPS ? A_OPS : (left + 7) / 8);
@@ -162,7 +112,7 @@ __global__ __launch_bounds__(f1::THREADS) void k_gemm_fp8_swiglu(const Fp8GemmAr
   };
   const uint8_t* bsrc[B_OPS];
   const float* bsrc_s;
-  auto b_setup = [&](const F1Item& it) {
+  auto b_setup = [&](const StreamItem& it) {
     const uint8_t* B = p.b + (size_t)it.g * N * K;
 #pragma unroll
     for (int j = 0; j < B_OPS; j++) {
@@ -206,7 +156,7 @@ __global__ __launch_bounds__(f1::THREADS) void k_gemm_fp8_swiglu(const Fp8GemmAr
   };
 
   {
-    const F1Item it0 = item_at(0);
+    const StreamItem it0 = item_at(0);
     a_setup(it0);
     b_setup(it0);
   }
@@ -223,7 +173,7 @@ __global__ __launch_bounds__(f1::THREADS) void k_gemm_fp8_swiglu(const Fp8GemmAr
 #pragma unroll
     for (int n = 0; n < 4; n++) acc[i][n] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-  F1Item cit = item_at(0);
+  StreamItem cit = item_at(0);
   int c_k = 0, c_kb = 0, c_sa = 0, c_sb = 0;
   const int q = lane >> 4, rr = lane & 15, odd = lane & 1;
 
@@ -233,7 +183,7 @@ __global__ __launch_bounds__(f1::THREADS) void k_gemm_fp8_swiglu(const Fp8GemmAr
   // store into the scratch row after the last expert.
   uint32_t hw[4][2][2];
   bool pend = false;
-  F1Item pit = cit;
+  StreamItem pit = cit;
   auto store_h = [&]() {
     uint16_t* H = (uint16_t*)p.out;
     uint16_t* scratch_row = H + (size_t)G * cap * I;
@@ -415,34 +365,19 @@ __global__ __launch_bounds__(f2::THREADS) void k_gemm_bf16_fp8w(const Fp8GemmArg
   const int G = p.G, K = p.K, KB = K / 128, N = p.N, cap = p.max_m;
   const int tiles_n = N / BN, KT = K / BK;
 
-  f1_tile_prefix(p, tprefix, mm_s, tid);
+  stream_tile_prefix(p.masked_m, p.G, p.max_m, tprefix, mm_s, tid);
   const int total = __builtin_amdgcn_readfirstlane(tprefix[G]) * tiles_n;
   const int grid = gridDim.x;
-  const int bx = (grid & 7) == 0 ? (int)(blockIdx.x & 7) * (grid >> 3) + (int)(blockIdx.x >> 3) : (int)blockIdx.x;
+  const int bx = stream_bx();
   if (bx >= total) return;
   const int n_items = (total - 1 - bx) / grid + 1;
   const int nsteps = n_items * KT;
 
-  auto item_at = [&](int k) {
-    F1Item it;
-    const int w = bx + k * grid;
-    const int u = w / tiles_n, nt = w - u * tiles_n;
-    int lo = 0, hi = G;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (__builtin_amdgcn_readfirstlane(tprefix[mid]) <= u) lo = mid;
-      else hi = mid;
-    }
-    it.g = lo;
-    it.m0 = (u - __builtin_amdgcn_readfirstlane(tprefix[lo])) * f1::BM;
-    it.mm = __builtin_amdgcn_readfirstlane(mm_s[lo]);
-    it.n0 = nt * BN;
-    return it;
-  };
+  auto item_at = [&](int k) { return stream_item(bx + k * grid, tiles_n, G, tprefix, mm_s, BN); };
 
   const uint8_t* asrc[A_OPS];
   int a_n = 0;
-  auto a_setup = [&](const F1Item& it) {
+  auto a_setup = [&](const StreamItem& it) {
     const uint8_t* A = p.a + (size_t)it.g * cap * K * 2;
     const int left = it.mm - it.m0 - 32 * wave;
     a_n = left <= 0 ? 0 : (left >= 8 * A_OPS ? A_OPS : (left + 7) / 8);
@@ -455,7 +390,7 @@ __global__ __launch_bounds__(f2::THREADS) void k_gemm_bf16_fp8w(const Fp8GemmArg
   };
   const uint8_t* bsrc;
   const float* bsrc_s;
-  auto b_setup = [&](const F1Item& it) {
+  auto b_setup = [&](const StreamItem& it) {
     const int r = 16 * wave + (lane >> 2);
     bsrc = p.b + ((size_t)it.g * N + it.n0 + r) * K + (((lane & 3) ^ f2_swz_b(r)) << 4);
     bsrc_s = p.b_s + ((size_t)it.g * (N / 128) + it.n0 / 128) * KB;
@@ -491,7 +426,7 @@ __global__ __launch_bounds__(f2::THREADS) void k_gemm_bf16_fp8w(const Fp8GemmArg
   };
 
   {
-    const F1Item it0 = item_at(0);
+    const StreamItem it0 = item_at(0);
     a_setup(it0);
     b_setup(it0);
   }
@@ -509,11 +444,11 @@ __global__ __launch_bounds__(f2::THREADS) void k_gemm_bf16_fp8w(const Fp8GemmArg
 #pragma unroll
     for (int n = 0; n < 4; n++) acc[i][n] = tmp[i][n] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-  F1Item cit = item_at(0);
+  StreamItem cit = item_at(0);
   int c_k = 0, c_kt = 0, c_sa = 0, c_sb = 0;
   const int q = lane >> 4, rr = lane & 15;
   bool pend = false;
-  F1Item pit = cit;
+  StreamItem pit = cit;
   auto store_out = [&]() {
     float* O = (float*)p.out;
 #pragma unroll

@@ -348,6 +348,11 @@ hipError_t gemm_nvfp4_masked(MaskedGemmArgs p, int epi, int cu_limit, hipStream_
     const hipError_t e = gemm_nvfp4_skinny(p, epi, cu_limit, s);
     if (e != hipErrorNotSupported) return e;
   }
+  // Larger groups stream the weights through LDS in 256-row M tiles.
+  if (p.max_m > SKINNY_MAX_M) {
+    const hipError_t e = gemm_nvfp4_stream(p, epi, cu_limit, s);
+    if (e != hipErrorNotSupported) return e;
+  }
 
   if (epi == EPI_SWIGLU_NVFP4) {
     if (p.max_m <= 16) {

@@ -1,0 +1,302 @@
+// gemm_nvfp4_stream.hip -- masked grouped NT GEMM over NVFP4 operands for groups with
+// more rows than the decode kernel takes (MoE prefill), persistent and weight-streaming.
+//
+// Operation ("The CuteDSL Gamble", "The Message"; the MoE GEMM1 / GEMM2 of the
+// "llm-assisted-kernel-dev" README's NVFP4 rows):
+//   C[g, m, n] = alpha_g * sum_k dec(A)[g, m, k] * dec(B)[g, n, k],  m < masked_m[g],
+// dec(X) = e2m1(code) * e4m3(scale of the 16-element block); with the SwiGLU epilogue
+// h = silu(gate) * up is requantized to NVFP4 with the fixed global scale g_h.
+//
+// Work distribution as in stream_common.h: an item is (group, 256-row M tile, 128
+// output columns or 64 gate + 64 up columns), so every weight panel is read from HBM
+// once per group whenever masked_m <= 256.  One step is 128 K: per row 64 code bytes
+// and 8 scale bytes.  Everything arrives by LDS DMA: the activation codes and scales
+// one step ahead, the weight codes and scales DB steps ahead.  Code rows are 64 bytes
+// with their 16-byte chunks XOR-permuted by ((r >> 1) ^ (r >> 3)) & 3, which keeps the
+// 16-lane MFMA operand reads free of bank conflicts.
+//
+// Compute: each lane reads one 16-byte chunk (32 codes, two 16-blocks) per operand row
+// and step and decodes it in registers, 8 elements per 16x16x32 fp16 MFMA, exactly
+// (e2m1 * e4m3 fits fp16; products are exact in fp32).  The K order inside a step is
+// permuted identically for both operands, which only reorders the fp32 sum.  The MFMA
+// computes the transposed tile D = B A^T, so each lane ends with four consecutive
+// output columns of one row: 16-byte fp32 stores, and the 16-column NVFP4 blocks of
+// the SwiGLU epilogue sit in 4 lanes (quantize_block_x4).  Waves: 4 (M) x 2 (N); wave
+// (wm, wn) owns the 16-row groups 16 wm + 64 i, so both waves of a SIMD compute when
+// masked_m <= 128.
+#include "kernels.h"
+#include "stream_common.h"
+
+namespace mxg {
+
+namespace ns {
+constexpr int BM = STREAM_BM, BN = 128, BK = 128;
+constexpr int WAVES = 8, THREADS = WAVES * 64;
+constexpr int A_CODE = BM * 64, A_STAGE = A_CODE + BM * 8;  // codes [256][64], scales [256][8]
+constexpr int B_CODE = BN * 64, B_STAGE = B_CODE + BN * 8;  // codes [128][64], scales [128][8]
+constexpr int DB = 6;                                       // weight steps in flight
+}  // namespace ns
+
+__device__ __forceinline__ int ns_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+
+template <int EPI>
+__global__ __launch_bounds__(ns::THREADS) void k_gemm_nvfp4_stream(const MaskedGemmArgs p) {
+  using namespace ns;
+  constexpr bool SWIGLU = (EPI == EPI_SWIGLU_NVFP4);
+  constexpr int SA = 2, SB = DB + 1;
+  __shared__ __attribute__((aligned(16))) uint8_t ringA[SA * A_STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t ringB[SB * B_STAGE];
+  __shared__ int tprefix[STREAM_MAX_G + 1];
+  __shared__ int mm_s[STREAM_MAX_G];
+  __shared__ float alpha_s[STREAM_MAX_G];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: branches on it are scalar
+  const int wm = wave >> 1, wn = wave & 1;
+  const int G = p.G, K = p.K, KT = K / BK, N = p.N, cap = p.max_m;
+  const int I = N / 2;
+  const int ncols = SWIGLU ? BN / 2 : BN;  // output (h) columns per item
+  const int tiles_n = SWIGLU ? I / ncols : N / ncols;
+
+  for (int g = tid; g < G; g += THREADS) alpha_s[g] = (p.alpha ? p.alpha[g] : 1.0f) * p.alpha_scale;
+  stream_tile_prefix(p.masked_m, G, cap, tprefix, mm_s, tid);
+  const int total = __builtin_amdgcn_readfirstlane(tprefix[G]) * tiles_n;
+  const int grid = gridDim.x;
+  const int bx = stream_bx();
+  if (bx >= total) return;
+  const int n_items = (total - 1 - bx) / grid + 1;
+  const int nsteps = n_items * KT;
+  auto item_at = [&](int k) { return stream_item(bx + k * grid, tiles_n, G, tprefix, mm_s, ncols); };
+
+  // B row r of an item (stage row): SwiGLU rows [0, 64) are gate rows n0 + r, [64, 128)
+  // the matching up rows I + n0 + r - 64
+  auto b_row = [&](const StreamItem& it, int r) {
+    if constexpr (SWIGLU) return r < BN / 2 ? it.n0 + r : I + it.n0 + (r - BN / 2);
+    else return it.n0 + r;
+  };
+
+  // ---- DMA cursors (rows past masked_m re-read the last valid row and are never stored;
+  // 16-row code groups and 32-row scale groups entirely past it are not fetched)
+  const uint8_t* asrc[2];
+  const uint8_t* asrc_s;
+  int a_n = 0, a_ns = 0;
+  auto a_setup = [&](const StreamItem& it) {
+    const int left = it.mm - it.m0 - 32 * wave;
+    a_n = left <= 0 ? 0 : (left > 16 ? 2 : 1);
+    a_ns = left > 0 ? 1 : 0;
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+      const int r = 32 * wave + 16 * j + (lane >> 2);
+      const int row = it.m0 + r < it.mm ? it.m0 + r : it.mm - 1;
+      asrc[j] = p.a + ((size_t)it.g * cap + row) * (K / 2) + (((lane & 3) ^ ns_swz(r)) << 4);
+    }
+    const int r = 32 * wave + (lane >> 1);
+    const int row = it.m0 + r < it.mm ? it.m0 + r : it.mm - 1;
+    asrc_s = p.a_sf + ((size_t)it.g * cap + row) * (K / 16) + (lane & 1) * 4;
+  };
+  const uint8_t* bsrc;
+  const uint8_t* bsrc_s;
+  auto b_setup = [&](const StreamItem& it) {
+    const int r = 16 * wave + (lane >> 2);
+    bsrc = p.b + ((size_t)it.g * N + b_row(it, r)) * (K / 2) + (((lane & 3) ^ ns_swz(r)) << 4);
+    const int rs = 32 * (wave & 3) + (lane >> 1);
+    bsrc_s = p.b_sf + ((size_t)it.g * N + b_row(it, rs)) * (K / 16) + (lane & 1) * 4;
+  };
+  int a_k = 0, a_kt = 0, a_step = 0, a_st = 0;
+  int b_k = 0, b_kt = 0, b_step = 0, b_st = 0;
+  auto issue_a = [&]() {
+    uint8_t* st = ringA + a_st * A_STAGE;
+#pragma unroll
+    for (int j = 0; j < 2; j++)
+      if (j < a_n) dma16(asrc[j] + a_kt * (BK / 2), st + (32 * wave + 16 * j) * 64);
+    if (a_ns) dma4(asrc_s + a_kt * (BK / 16), st + A_CODE + 32 * wave * 8);
+    a_st ^= 1;
+    if (a_step + 1 < nsteps) {
+      a_step++;
+      if (++a_kt == KT) {
+        a_kt = 0;
+        a_setup(item_at(++a_k));
+      }
+    }
+  };
+  auto issue_b = [&]() {
+    uint8_t* st = ringB + b_st * B_STAGE;
+    dma16(bsrc + b_kt * (BK / 2), st + 16 * wave * 64);
+    if (wave < 4) dma4(bsrc_s + b_kt * (BK / 16), st + B_CODE + 32 * wave * 8);
+    b_st = b_st + 1 == SB ? 0 : b_st + 1;
+    if (b_step + 1 < nsteps) {
+      b_step++;
+      if (++b_kt == KT) {
+        b_kt = 0;
+        b_setup(item_at(++b_k));
+      }
+    }
+  };
+
+  {
+    const StreamItem it0 = item_at(0);
+    a_setup(it0);
+    b_setup(it0);
+  }
+  // prologue in the steady-state order: "step" i < 0 issues A(i + 1) (if >= 0), then B(i + DB)
+#pragma unroll
+  for (int i = -DB; i < 0; i++) {
+    if (i + 1 >= 0) issue_a();
+    issue_b();
+  }
+
+  float4_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+#pragma unroll
+    for (int n = 0; n < 4; n++) acc[i][n] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+  StreamItem cit = item_at(0);
+  int c_k = 0, c_kt = 0, c_sa = 0, c_sb = 0;
+  const int q = lane >> 4, rr = lane & 15;
+
+  for (int s = 0; s < nsteps; s++) {
+    // A(s) is followed only by B(s + DB - 1) (1 or 2 DMAs of this wave), whatever number
+    // of activation DMAs the wave skipped
+    if (wave < 4) wait_vmcnt<2>();
+    else wait_vmcnt<1>();
+    // every wave's DMAs of step s have landed and every wave is done with step s - 1,
+    // whose stages the next issues overwrite
+    __syncthreads();
+    issue_a();
+    issue_b();
+
+    const bool active = cit.m0 + 16 * wm < cit.mm;
+    if (active) {
+      const uint8_t* As = ringA + c_sa * A_STAGE;
+      const uint8_t* Bs = ringB + c_sb * B_STAGE;
+      u32x4_t araw[4], braw[4];
+      uint32_t asc[4], bsc[4];
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        if (cit.m0 + 16 * wm + 64 * i >= cit.mm) break;
+        const int r = 16 * wm + 64 * i + rr;
+        araw[i] = *(const u32x4_t*)(As + r * 64 + ((q ^ ns_swz(r)) << 4));
+        asc[i] = *(const uint16_t*)(As + A_CODE + r * 8 + 2 * q);
+      }
+#pragma unroll
+      for (int n = 0; n < 4; n++) {
+        const int r = (SWIGLU ? (n < 2 ? 32 * wn + 16 * n : BN / 2 + 32 * wn + 16 * (n - 2)) : 64 * wn + 16 * n) + rr;
+        braw[n] = *(const u32x4_t*)(Bs + r * 64 + ((q ^ ns_swz(r)) << 4));
+        bsc[n] = *(const uint16_t*)(Bs + B_CODE + r * 8 + 2 * q);
+      }
+      half2_t as2[4][2], bs2[4][2];
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const half2_t s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(asc[i], 1.0f, false);
+        as2[i][0] = half2_t{s01[0], s01[0]};
+        as2[i][1] = half2_t{s01[1], s01[1]};
+      }
+#pragma unroll
+      for (int n = 0; n < 4; n++) {
+        const half2_t s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(bsc[n], 1.0f, false);
+        bs2[n][0] = half2_t{s01[0], s01[0]};
+        bs2[n][1] = half2_t{s01[1], s01[1]};
+      }
+#pragma unroll
+      for (int ks = 0; ks < 4; ks++) {
+        // dword ks of a lane's chunk q holds K elements 32 q + 8 ks .. +7 of the step,
+        // in 16-block 2 q + ks / 2
+        half8_t bf[4];
+#pragma unroll
+        for (int n = 0; n < 4; n++) bf[n] = decode8_e2m1_f16(braw[n][ks], bs2[n][ks >> 1]);
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          if (cit.m0 + 16 * wm + 64 * i >= cit.mm) break;
+          const half8_t af = decode8_e2m1_f16(araw[i][ks], as2[i][ks >> 1]);
+#pragma unroll
+          for (int n = 0; n < 4; n++) acc[i][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bf[n], af, acc[i][n], 0, 0, 0);
+        }
+      }
+    }
+    c_sa ^= 1;
+    c_sb = c_sb + 1 == SB ? 0 : c_sb + 1;
+
+    if (++c_kt == KT) {
+      // lane (rr, q) holds, for row group i, output row 16 wm + 64 i + rr and the four
+      // columns 4 q .. 4 q + 3 of each 16-column group n
+      if (active) {
+        const float alpha = alpha_s[cit.g];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const int m = cit.m0 + 16 * wm + 64 * i + rr;
+          const bool ok = m < cit.mm;
+          const size_t orow = (size_t)cit.g * cap + m;
+          if constexpr (SWIGLU) {
+#pragma unroll
+            for (int n = 0; n < 2; n++) {
+              float h[4];
+#pragma unroll
+              for (int r = 0; r < 4; r++) {
+                const float gt = alpha * acc[i][n][r], up = alpha * acc[i][n + 2][r];
+                h[r] = gt / (1.0f + expf(-gt)) * up;
+              }
+              const int hc0 = cit.n0 + 32 * wn + 16 * n;  // first column of this lane's 16-block
+              if (p.dbg_h && ok) *(float4_t*)(p.dbg_h + orow * I + hc0 + 4 * q) = float4_t{h[0], h[1], h[2], h[3]};
+              uint32_t sbyte;
+              const uint32_t bits = quantize_block_x4(h, p.g_h, 6.0f * p.g_h, sbyte);
+              const uint32_t b1 = __shfl_xor(bits, 16), b2 = __shfl_xor(bits, 32), b3 = __shfl_xor(bits, 48);
+              if (q == 0 && ok) {
+                *(u32x2_t*)(p.h_codes + orow * (I / 2) + hc0 / 2) = u32x2_t{bits | (b1 << 16), b2 | (b3 << 16)};
+                p.h_sf[orow * (I / 16) + hc0 / 16] = (uint8_t)sbyte;
+              }
+            }
+          } else {
+#pragma unroll
+            for (int n = 0; n < 4; n++) {
+              const int c = cit.n0 + 64 * wn + 16 * n + 4 * q;
+              const float4_t v = acc[i][n] * alpha;
+              if (!ok) continue;
+              if constexpr (EPI == EPI_BF16) {
+                const uint32_t lo = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
+                const uint32_t hi = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
+                *(u32x2_t*)((uint16_t*)p.out + orow * N + c) = u32x2_t{lo, hi};
+              } else {
+                *(float4_t*)((float*)p.out + orow * N + c) = v;
+              }
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int n = 0; n < 4; n++) acc[i][n] = float4_t{0.f, 0.f, 0.f, 0.f};
+      c_kt = 0;
+      if (++c_k < n_items) cit = item_at(c_k);
+    }
+  }
+  wait_vmcnt<0>();  // the trailing re-reads land before the workgroup ends
+}
+
+template <int EPI>
+static hipError_t launch_stream(const MaskedGemmArgs& p, int cu_limit, hipStream_t s) {
+  const void* k = (const void*)k_gemm_nvfp4_stream<EPI>;
+  const int grid = resident_grid(k, ns::THREADS, cu_limit);
+  if (grid <= 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((k_gemm_nvfp4_stream<EPI>), dim3(grid), dim3(ns::THREADS), 0, s, p);
+  return hipGetLastError();
+}
+
+// Returns hipErrorNotSupported (nothing launched) for shapes the kernel does not take.
+hipError_t gemm_nvfp4_stream(MaskedGemmArgs p, int epi, int cu_limit, hipStream_t s) {
+  using namespace ns;
+  if (p.G <= 0 || p.G > STREAM_MAX_G || p.K % BK != 0 || p.K <= 0 || p.max_m <= 0) return hipErrorNotSupported;
+  const int ncols = epi == EPI_SWIGLU_NVFP4 ? BN / 2 : BN;
+  const int n_out = epi == EPI_SWIGLU_NVFP4 ? p.N / 2 : p.N;
+  if (n_out % ncols != 0 || (epi == EPI_SWIGLU_NVFP4 && p.N % 2 != 0)) return hipErrorNotSupported;
+  if ((long long)p.G * ((p.max_m + BM - 1) / BM) * (n_out / ncols) > 0x7FFFFFFFLL) return hipErrorNotSupported;
+  switch (epi) {
+    case EPI_BF16: return launch_stream<EPI_BF16>(p, cu_limit, s);
+    case EPI_F32: return launch_stream<EPI_F32>(p, cu_limit, s);
+    case EPI_SWIGLU_NVFP4: return launch_stream<EPI_SWIGLU_NVFP4>(p, cu_limit, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace mxg

@@ -59,6 +59,9 @@ hipError_t gemm_nvfp4_hetero(HeteroGemmArgs p, int epi, int cu_limit, hipStream_
 // returns hipErrorNotSupported without launching for shapes it does not take.
 hipError_t gemm_nvfp4_skinny(MaskedGemmArgs p, int epi, int cu_limit, hipStream_t s);
 constexpr int SKINNY_MAX_M = 32;  // row capacity up to which the skinny kernel is used
+// Larger masked groups (prefill): persistent weight-streaming kernel, 256-row M tiles;
+// returns hipErrorNotSupported without launching for shapes it does not take.
+hipError_t gemm_nvfp4_stream(MaskedGemmArgs p, int epi, int cu_limit, hipStream_t s);
 
 // Workgroups of `kernel` (with `threads` threads) resident on the device at once, over
 // at most cu_limit CUs when cu_limit > 0; 0 on a runtime error.

@@ -79,6 +79,10 @@ def test_masked_gemm_g4_m64_n512_k1024(seed):
     (4, 32, 384, 512, [17, 32, 16, 31]),
     (3, 8, 4096, 7168, [1, 8, 3]),
     (2, 1, 64, 2048, [1, 1]),
+    # weight-streaming kernel (row capacity > 32, N % 128 == 0, K % 128 == 0)
+    (3, 300, 256, 384, [300, 257, 31]),      # two 256-row M tiles, ragged
+    (2, 96, 384, 128, [96, 65]),             # one K step, rows across a 64-row boundary
+    (4, 40, 128, 256, [33, 0, 40, 1]),       # empty group, 1-row group
 ])
 def test_masked_gemm_edges(G, max_m, N, K, mm):
     log(f"masked NVFP4 GEMM edge G={G} max_m={max_m} N={N} K={K} masked_m={mm}")
@@ -110,7 +114,7 @@ def test_masked_gemm_general_scales_fp32_out_and_poison():
         _check_masked(t, out, max_m, N, K, f"general scales {dt}")
 
 
-@pytest.mark.parametrize("max_m,K", [(16, 1024), (48, 512)])
+@pytest.mark.parametrize("max_m,K", [(16, 1024), (48, 512), (272, 640)])
 def test_masked_gemm_fp32_out(max_m, K):
     log(f"masked NVFP4 GEMM fp32 output max_m={max_m} K={K}")
     wl = datagen.masked_gemm_workload(23, DEV, G=3, max_m=max_m, N=256, K=K, masked_m=[max_m, 1, max_m - 3])

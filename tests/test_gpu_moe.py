@@ -62,7 +62,7 @@ def _tokens(T, n, seed):
 
 
 # ----------------------------------------------------------------------------- NVFP4
-def _run_nvfp4(T, H, I, seed, n_check, cap=None):
+def _run_nvfp4(T, H, I, seed, n_check, cap=None, n_deep=0):
     mxg = _mxg()
     wl = datagen.moe_nvfp4_workload(seed, DEV, T=T, H=H, I=I)
     t, s = wl.tensors, wl.scalars
@@ -101,6 +101,11 @@ def _run_nvfp4(T, H, I, seed, n_check, cap=None):
         return wcache[e]
 
     toks = _tokens(T, n_check, seed)
+    if n_deep:
+        # tokens with a slot past the first 256 rows of its expert (a later M tile)
+        deep = np.flatnonzero(((row_h >= 256) & (row_h < max_m)).any(axis=1))
+        assert len(deep) >= n_deep, "workload has too few rows past 256"
+        toks = sorted(set(toks) | set(deep[np.linspace(0, len(deep) - 1, n_deep).astype(int)].tolist()))
     for tt in toks:
         o_list, so_list, wj = [], [], []
         for j in range(TOPK):
@@ -144,6 +149,16 @@ def test_moe_nvfp4_decode_small_full():
 def test_moe_nvfp4_capacity_drop():
     log("NVFP4 MoE with a capacity below the busiest expert (slots dropped)")
     _run_nvfp4(96, 256, 128, 4001, None, cap=2)
+
+
+def test_moe_nvfp4_prefill_small():
+    log("NVFP4 MoE prefill, small dims: T=4096 H=512 I=256 (row capacity 240), 48 tokens")
+    _run_nvfp4(4096, 512, 256, 4003, 48)
+
+
+def test_moe_nvfp4_prefill_two_m_tiles():
+    log("NVFP4 MoE prefill with masked_m past 256: T=8192 H=512 I=256, 24 tokens")
+    _run_nvfp4(8192, 512, 256, 4004, 8, n_deep=16)
 
 
 def test_moe_nvfp4_decode_full_size():
