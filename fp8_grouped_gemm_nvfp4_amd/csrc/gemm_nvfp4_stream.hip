@@ -15,15 +15,16 @@
 // with their 16-byte chunks XOR-permuted by ((r >> 1) ^ (r >> 3)) & 3, which keeps the
 // 16-lane MFMA operand reads free of bank conflicts.
 //
-// Compute: each lane reads one 16-byte chunk (32 codes, two 16-blocks) per operand row
-// and step and decodes it in registers, 8 elements per 16x16x32 fp16 MFMA, exactly
-// (e2m1 * e4m3 fits fp16; products are exact in fp32).  The K order inside a step is
-// permuted identically for both operands, which only reorders the fp32 sum.  The MFMA
-// computes the transposed tile D = B A^T, so each lane ends with four consecutive
-// output columns of one row: 16-byte fp32 stores, and the 16-column NVFP4 blocks of
-// the SwiGLU epilogue sit in 4 lanes (quantize_block_x4).  Waves: 4 (M) x 2 (N); wave
-// (wm, wn) owns the 16-row groups 16 wm + 64 i, so both waves of a SIMD compute when
-// masked_m <= 128.
+// Compute: decoding is exact (e2m1 * e4m3 fits fp16; fp16 products are exact in fp32).
+// The weight step is decoded once per workgroup into an fp16 LDS tile, one step ahead;
+// for the activations each lane reads one 16-byte chunk (32 codes, two 16-blocks) per
+// row and step and decodes it in registers, 8 elements per 16x16x32 fp16 MFMA.  The K
+// order inside a step is permuted identically for both operands, which only reorders
+// the fp32 sum.  The MFMA computes the transposed tile D = B A^T, so each lane ends
+// with four consecutive output columns of one row: 16-byte fp32 stores, and the
+// 16-column NVFP4 blocks of the SwiGLU epilogue sit in 4 lanes (quantize_block_x4).
+// Waves: 4 (M) x 2 (N); wave (wm, wn) owns the 16-row groups 16 wm + 64 i, so both
+// waves of a SIMD compute when masked_m <= 128.
 #include "kernels.h"
 #include "stream_common.h"
 
@@ -34,7 +35,7 @@ constexpr int BM = STREAM_BM, BN = 128, BK = 128;
 constexpr int WAVES = 8, THREADS = WAVES * 64;
 constexpr int A_CODE = BM * 64, A_STAGE = A_CODE + BM * 8;  // codes [256][64], scales [256][8]
 constexpr int B_CODE = BN * 64, B_STAGE = B_CODE + BN * 8;  // codes [128][64], scales [128][8]
-constexpr int DB = 6;                                       // weight steps in flight
+constexpr int DB = 4;                                       // weight steps in flight (>= 3)
 }  // namespace ns
 
 __device__ __forceinline__ int ns_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
@@ -44,8 +45,10 @@ __global__ __launch_bounds__(ns::THREADS) void k_gemm_nvfp4_stream(const MaskedG
   using namespace ns;
   constexpr bool SWIGLU = (EPI == EPI_SWIGLU_NVFP4);
   constexpr int SA = 2, SB = DB + 1;
+  static_assert(DB >= 3, "B(s + 1) must be issued before A(s)");
   __shared__ __attribute__((aligned(16))) uint8_t ringA[SA * A_STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t ringB[SB * B_STAGE];
+  __shared__ __attribute__((aligned(16))) _Float16 bdec[2][BN * BK];
   __shared__ int tprefix[STREAM_MAX_G + 1];
   __shared__ int mm_s[STREAM_MAX_G];
   __shared__ float alpha_s[STREAM_MAX_G];
@@ -145,6 +148,30 @@ __global__ __launch_bounds__(ns::THREADS) void k_gemm_nvfp4_stream(const MaskedG
     issue_b();
   }
 
+  // The weight step is decoded once per workgroup into fp16 (thread t: row t / 4, 16-byte
+  // code chunk t % 4), one step ahead of its use; row r's 16-byte fp16 chunk c (K 8c ..
+  // 8c + 7 in the permuted order of the activation side) sits at chunk c ^ (r & 15).
+  int d_st = 0;  // raw stage of the next weight step to decode
+  auto decode_b = [&](int buf) {
+    const uint8_t* st = ringB + d_st * B_STAGE;
+    const int r = tid >> 2, cq = tid & 3;
+    const u32x4_t raw = *(const u32x4_t*)(st + r * 64 + ((cq ^ ns_swz(r)) << 4));
+    const uint32_t sb = *(const uint16_t*)(st + B_CODE + r * 8 + 2 * cq);
+    const half2_t s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sb, 1.0f, false);
+    const half2_t s0 = half2_t{s01[0], s01[0]}, s1 = half2_t{s01[1], s01[1]};
+    _Float16* row = bdec[buf] + r * BK;
+#pragma unroll
+    for (int ks = 0; ks < 4; ks++)
+      *(half8_t*)(row + ((((4 * cq + ks) ^ (r & 15))) << 3)) = decode8_e2m1_f16(raw[ks], ks < 2 ? s0 : s1);
+    d_st = d_st + 1 == SB ? 0 : d_st + 1;
+  };
+  // B(0) is followed by DB - 2 weight steps, A(0) and B(DB - 1): allowing only the weight
+  // DMAs behind it outstanding is enough
+  if (wave < 4) wait_vmcnt<2 * (DB - 1)>();
+  else wait_vmcnt<DB - 1>();
+  __syncthreads();
+  decode_b(0);
+
   float4_t acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; i++)
@@ -152,7 +179,7 @@ __global__ __launch_bounds__(ns::THREADS) void k_gemm_nvfp4_stream(const MaskedG
     for (int n = 0; n < 4; n++) acc[i][n] = float4_t{0.f, 0.f, 0.f, 0.f};
 
   StreamItem cit = item_at(0);
-  int c_k = 0, c_kt = 0, c_sa = 0, c_sb = 0;
+  int c_k = 0, c_kt = 0, c_sa = 0;
   const int q = lane >> 4, rr = lane & 15;
 
   for (int s = 0; s < nsteps; s++) {
@@ -165,13 +192,17 @@ __global__ __launch_bounds__(ns::THREADS) void k_gemm_nvfp4_stream(const MaskedG
     __syncthreads();
     issue_a();
     issue_b();
+    // weight step s + 1 (issued before A(s), so it has landed) into the other fp16 buffer,
+    // whose readers finished step s - 1 before the barrier; past the end it re-decodes
+    // a stage that is not read again
+    decode_b((s + 1) & 1);
 
     const bool active = cit.m0 + 16 * wm < cit.mm;
     if (active) {
       const uint8_t* As = ringA + c_sa * A_STAGE;
-      const uint8_t* Bs = ringB + c_sb * B_STAGE;
-      u32x4_t araw[4], braw[4];
-      uint32_t asc[4], bsc[4];
+      const _Float16* Bd = bdec[s & 1];
+      u32x4_t araw[4];
+      uint32_t asc[4];
 #pragma unroll
       for (int i = 0; i < 4; i++) {
         if (cit.m0 + 16 * wm + 64 * i >= cit.mm) break;
@@ -179,13 +210,7 @@ __global__ __launch_bounds__(ns::THREADS) void k_gemm_nvfp4_stream(const MaskedG
         araw[i] = *(const u32x4_t*)(As + r * 64 + ((q ^ ns_swz(r)) << 4));
         asc[i] = *(const uint16_t*)(As + A_CODE + r * 8 + 2 * q);
       }
-#pragma unroll
-      for (int n = 0; n < 4; n++) {
-        const int r = (SWIGLU ? (n < 2 ? 32 * wn + 16 * n : BN / 2 + 32 * wn + 16 * (n - 2)) : 64 * wn + 16 * n) + rr;
-        braw[n] = *(const u32x4_t*)(Bs + r * 64 + ((q ^ ns_swz(r)) << 4));
-        bsc[n] = *(const uint16_t*)(Bs + B_CODE + r * 8 + 2 * q);
-      }
-      half2_t as2[4][2], bs2[4][2];
+      half2_t as2[4][2];
 #pragma unroll
       for (int i = 0; i < 4; i++) {
         const half2_t s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(asc[i], 1.0f, false);
@@ -193,18 +218,15 @@ __global__ __launch_bounds__(ns::THREADS) void k_gemm_nvfp4_stream(const MaskedG
         as2[i][1] = half2_t{s01[1], s01[1]};
       }
 #pragma unroll
-      for (int n = 0; n < 4; n++) {
-        const half2_t s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(bsc[n], 1.0f, false);
-        bs2[n][0] = half2_t{s01[0], s01[0]};
-        bs2[n][1] = half2_t{s01[1], s01[1]};
-      }
-#pragma unroll
       for (int ks = 0; ks < 4; ks++) {
         // dword ks of a lane's chunk q holds K elements 32 q + 8 ks .. +7 of the step,
         // in 16-block 2 q + ks / 2
         half8_t bf[4];
 #pragma unroll
-        for (int n = 0; n < 4; n++) bf[n] = decode8_e2m1_f16(braw[n][ks], bs2[n][ks >> 1]);
+        for (int n = 0; n < 4; n++) {
+          const int r = (SWIGLU ? (n < 2 ? 32 * wn + 16 * n : BN / 2 + 32 * wn + 16 * (n - 2)) : 64 * wn + 16 * n) + rr;
+          bf[n] = *(const half8_t*)(Bd + r * BK + (((4 * q + ks) ^ rr) << 3));
+        }
 #pragma unroll
         for (int i = 0; i < 4; i++) {
           if (cit.m0 + 16 * wm + 64 * i >= cit.mm) break;
@@ -215,7 +237,6 @@ __global__ __launch_bounds__(ns::THREADS) void k_gemm_nvfp4_stream(const MaskedG
       }
     }
     c_sa ^= 1;
-    c_sb = c_sb + 1 == SB ? 0 : c_sb + 1;
 
     if (++c_kt == KT) {
       // lane (rr, q) holds, for row group i, output row 16 wm + 64 i + rr and the four
