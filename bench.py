@@ -191,6 +191,23 @@ def timed_loop(step, steps, warmup):
     return t0.elapsed_time(t1) / steps, kt.mean_ms(), wall
 
 
+def binding_roof(byts, flops, mfma_dtype):
+    """'hbm' or 'mfma': whichever floor (bytes at the HBM peak, flops at the MFMA peak of
+    the dtype the path computes in) is longer."""
+    return "mfma" if flops / PEAK_TFLOPS[mfma_dtype] / 1e9 > byts / HBM_PEAK_GBS / 1e6 else "hbm"
+
+
+def roofline_row(r):
+    """Floor of a workload at its binding roof, and the fraction of it achieved (floor
+    over the measured step time)."""
+    hbm_ms = r["bytes"] / HBM_PEAK_GBS / 1e6
+    dt = r.get("mfma_dtype", "fp16")
+    mfma_ms = r["flops"] / PEAK_TFLOPS[dt] / 1e9
+    floor = max(hbm_ms, mfma_ms)
+    return dict(bound="mfma" if mfma_ms > hbm_ms else "hbm", mfma_dtype=dt, floor_ms=floor,
+                frac=floor / r["ms"])
+
+
 # ----------------------------------------------------------------------------- workloads
 def bench_decode_gemm1(dev, steps, warmup, seed=1001, cpu=True):
     wl = datagen.decode_gemm1_workload(seed, dev)
@@ -352,8 +369,11 @@ def bench_moe(dev, steps, warmup, precision, T, seed):
         xbytes = T * H * 2
     byts = wbytes + xbytes + T * E * 4 + T * H * 2
     flops = 2.0 * rows * (2 * I * H + H * I)
+    # the FP8 GEMMs run on the fp8 MFMA, the exact NVFP4 decode on the fp16 MFMA
+    mfma_dtype = "fp8" if precision == "fp8" else "fp16"
     return dict(name=wl.name, ms=ms, kernel_ms=kms, wall_s=wall, bytes=byts, flops=flops,
-                gbs=byts / ms / 1e6, tflops=flops / ms / 1e9, tokens_per_s=T / ms * 1e3, bound="hbm",
+                gbs=byts / ms / 1e6, tflops=flops / ms / 1e9, tokens_per_s=T / ms * 1e3,
+                bound=binding_roof(byts, flops, mfma_dtype), mfma_dtype=mfma_dtype,
                 config=dict(workload=wl.name, tokens=T, active_experts=n_act, max_m=cap))
 
 
@@ -398,13 +418,14 @@ def main():
         "ms_per_step": r["ms"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "data": "synthetic", "config": r["config"],
     }
+    dt = r.get("mfma_dtype", "fp16")
     if r["bound"] == "mfma":
-        line.update(value=r["tflops"], unit="TFLOP/s", dtype="fp16-mfma/fp32-acc")
+        line.update(value=r["tflops"], unit="TFLOP/s", dtype=f"{dt}-mfma/fp32-acc")
         achieved = r["flops"] / r["kernel_ms"] / 1e9
-        line["roofline"] = dict(bound="mfma", achieved=achieved, peak=PEAK_TFLOPS["fp16"], unit="TFLOP/s",
-                                frac=achieved / PEAK_TFLOPS["fp16"], traffic=None)
+        line["roofline"] = dict(bound="mfma", achieved=achieved, peak=PEAK_TFLOPS[dt], unit="TFLOP/s",
+                                frac=achieved / PEAK_TFLOPS[dt], traffic=None)
     else:
-        line.update(value=r["gbs"], unit="GB/s", dtype="fp16-mfma/fp32-acc")
+        line.update(value=r["gbs"], unit="GB/s", dtype=f"{dt}-mfma/fp32-acc")
         kb = r.get("kernel_bytes", r["bytes"])
         achieved = kb / r["kernel_ms"] / 1e6
         line["roofline"] = dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
@@ -421,7 +442,8 @@ def main():
                 continue
             q = fn(dev, max(5, args.steps // 5), 2, False)
             rows.append({k: q[k] for k in ("name", "ms", "kernel_ms", "gbs", "tflops") if k in q} |
-                        ({"tokens_per_s": q["tokens_per_s"]} if "tokens_per_s" in q else {}))
+                        ({"tokens_per_s": q["tokens_per_s"]} if "tokens_per_s" in q else {}) |
+                        {"roofline": roofline_row(q)})
             torch.cuda.empty_cache()
         line["workloads"] = rows
     if args.copy_calibration:
