@@ -27,9 +27,11 @@
 //    buffered, one barrier per chunk).
 //  * Output tile D[n][m] (weights x activations): lane l holds 4 consecutive n for one
 //    m, so stores are 8-byte (bf16) or 16-byte (fp32) vectors.
-//  * Fused SwiGLU + NVFP4 requantization (MoE GEMM1): a wave's two tiles are the gate
-//    rows and the matching up rows, so h = silu(gate) * up is formed in registers; the
-//    16-column block amax is two cross-lane shuffles away.
+//  * Fused SwiGLU + NVFP4 requantization (MoE GEMM1): waves 2k and 2k+1 stream the gate
+//    rows and the matching up rows (8 waves, one tile each, as for the plain outputs);
+//    at a unit's end the up wave hands its tile to the gate wave through LDS, which
+//    forms h = silu(gate) * up in registers; the 16-column block amax is two cross-lane
+//    shuffles away.  (A wave may also hold both tiles, NT = 2.)
 //  * Persistent grid over a compacted list of (group, M tile) entries with valid rows,
 //    built in LDS with wavefront ballots: idle groups cost nothing.
 #include "device_common.h"
@@ -240,8 +242,12 @@ struct UnitCursor {
 template <int MR, int NT, int EPI, int WAVES, int S, int DA>
 __global__ __launch_bounds__(WAVES * 64) void k_gemm_nvfp4_skinny(const MaskedGemmArgs p) {
   constexpr bool SWIGLU = (EPI == EPI_SWIGLU_NVFP4);
+  // SwiGLU pairs a gate tile with the matching up tile: in one wave (NT = 2), or in the
+  // waves 2k (gate) and 2k+1 (up) with one tile each (NT = 1, PAIRED)
+  constexpr bool PAIRED = SWIGLU && NT == 1;
   constexpr int THREADS = WAVES * 64;
-  static_assert(!SWIGLU || NT == 2, "SwiGLU pairs one gate and one up tile per wave");
+  static_assert(!SWIGLU || NT == 2 || (NT == 1 && WAVES % 2 == 0), "SwiGLU tile pairing");
+  static_assert(!PAIRED || WAVES / 2 * 64 * 16 <= MR * sk::APITCH * 2, "exchange fits an activation buffer");
   static_assert(S >= DA - 1 && DA >= 3, "prefetch distances");
   constexpr int W_OPS = 5 * NT, A_OPS = ARaw<MR>::OPS;
   // vmcnt allowances (ops that may stay outstanding): see the issue order below
@@ -272,11 +278,15 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_nvfp4_skinny(const MaskedGe
 
   const int gq = (int)gridDim.x / tiles_n, gr = (int)gridDim.x % tiles_n;
   auto ncol0_of = [&](int nt) {
+    if constexpr (PAIRED) return nt * (16 * (WAVES / 2)) + (wave >> 1) * 16;
     return SWIGLU ? nt * (16 * WAVES) + wave * 16 : nt * (16 * NT * WAVES) + wave * (16 * NT);
   };
   auto weight_src = [&](const Unit& un, TileSrc (&src)[NT]) {
     const int c0 = ncol0_of(un.nt);
-    if constexpr (SWIGLU) {
+    if constexpr (PAIRED) {
+      const int I = p.N / 2;
+      src[0] = tile_src(c0, I, (wave & 1) ? I : 0, K, lane);
+    } else if constexpr (SWIGLU) {
       const int I = p.N / 2;
       src[0] = tile_src(c0, I, 0, K, lane);
       src[1] = tile_src(c0, I, I, K, lane);
@@ -395,25 +405,38 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_nvfp4_skinny(const MaskedGe
         }
       } else {
         const int I = p.N / 2;
+        float4_t upv;
+        if constexpr (PAIRED) {
+          // The up wave hands its tile to the gate wave through activation buffer (f+1)&1:
+          // its readers (step f-1) are past this step's barrier, and it is rewritten only
+          // by the decode at the end of this step, after a second barrier.
+          float4_t* xchg = (float4_t*)As[(f + 1) & 1];
+          if (wave & 1) xchg[(wave >> 1) * 64 + lane] = acc[0];
+          __syncthreads();
+          upv = xchg[(wave >> 1) * 64 + lane];
+        } else {
+          upv = acc[1];
+        }
         float h[4];
 #pragma unroll
         for (int r = 0; r < 4; r++) {
-          float gt = alpha * acc[0][r], up = alpha * acc[1][r];
+          float gt = alpha * acc[0][r], up = alpha * upv[r];
           h[r] = gt / (1.0f + expf(-gt)) * up;
         }
         const int hc = ncol0 + q * 4;  // this lane's first h column
-        if (p.dbg_h && m < cu.rows && hc < I)
+        if (p.dbg_h && m < cu.rows && hc < I && !(PAIRED && (wave & 1)))
           *(float4_t*)(p.dbg_h + orow * I + hc) = float4_t{h[0], h[1], h[2], h[3]};
         uint32_t sbyte;
         uint32_t bits = quantize_block_x4(h, p.g_h, 6.0f * p.g_h, sbyte);
         uint32_t b1 = __shfl_xor(bits, 16);  // q ^ 1
         uint32_t b2 = __shfl_xor(bits, 32);  // q ^ 2
         uint32_t b3 = __shfl_xor(bits, 48);  // q ^ 3
-        if (q == 0 && m < cu.rows && ncol0 < I) {
+        if (q == 0 && m < cu.rows && ncol0 < I && !(PAIRED && (wave & 1))) {
           uint32_t w0 = bits | (b1 << 16), w1 = b2 | (b3 << 16);
           *(u32x2_t*)(p.h_codes + orow * (I / 2) + ncol0 / 2) = u32x2_t{w0, w1};
           p.h_sf[orow * (I / 16) + ncol0 / 16] = (uint8_t)sbyte;
         }
+        if constexpr (PAIRED) __syncthreads();  // the exchange is read before the decode below
       }
 #pragma unroll
       for (int t = 0; t < NT; t++) acc[t] = float4_t{0.f, 0.f, 0.f, 0.f};
@@ -451,7 +474,8 @@ template <int MR, int NT, int EPI, int WAVES, int S, int DA>
 static hipError_t launch_skinny(MaskedGemmArgs p, int cu_limit, hipStream_t s) {
   p.tiles_m = (p.max_m + MR - 1) / MR;
   if (p.G * p.tiles_m > sk::MAX_LIST || p.tiles_m > 4) return hipErrorNotSupported;
-  p.tiles_n = (EPI == EPI_SWIGLU_NVFP4) ? (p.N / 2 + 16 * WAVES - 1) / (16 * WAVES)
+  constexpr int HCOLS = NT == 2 ? 16 * WAVES : 16 * (WAVES / 2);  // h columns per SwiGLU unit
+  p.tiles_n = (EPI == EPI_SWIGLU_NVFP4) ? (p.N / 2 + HCOLS - 1) / HCOLS
                                         : (p.N + 16 * NT * WAVES - 1) / (16 * NT * WAVES);
   p.total_tiles = p.G * p.tiles_m * p.tiles_n;
   if (p.total_tiles == 0) return hipSuccess;
@@ -473,8 +497,8 @@ hipError_t gemm_nvfp4_skinny(MaskedGemmArgs p, int epi, int cu_limit, hipStream_
     case EPI_F32:
       return small ? launch_skinny<8, 1, EPI_F32, 8, 3, 4>(p, cu_limit, s) : launch_skinny<16, 1, EPI_F32, 8, 3, 3>(p, cu_limit, s);
     case EPI_SWIGLU_NVFP4:
-      return small ? launch_skinny<8, 2, EPI_SWIGLU_NVFP4, 4, 3, 4>(p, cu_limit, s)
-                   : launch_skinny<16, 2, EPI_SWIGLU_NVFP4, 4, 3, 3>(p, cu_limit, s);
+      return small ? launch_skinny<8, 1, EPI_SWIGLU_NVFP4, 8, 3, 4>(p, cu_limit, s)
+                   : launch_skinny<16, 1, EPI_SWIGLU_NVFP4, 8, 3, 3>(p, cu_limit, s);
     default: return hipErrorInvalidValue;
   }
 }
