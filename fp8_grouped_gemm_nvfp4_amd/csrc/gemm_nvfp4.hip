@@ -386,6 +386,10 @@ hipError_t gemm_nvfp4_masked(MaskedGemmArgs p, int epi, int cu_limit, hipStream_
 }
 
 hipError_t gemm_nvfp4_hetero(HeteroGemmArgs p, int epi, int cu_limit, hipStream_t s) {
+  {
+    const hipError_t e = gemm_nvfp4_stream_hetero(p, epi, cu_limit, s);
+    if (e != hipErrorNotSupported) return e;
+  }
   constexpr int BM = 128, BN = 128;
   int base = 0;
   for (int g = 0; g < p.G; g++) {

@@ -40,10 +40,19 @@ constexpr int DB = 4;                                       // weight steps in f
 
 __device__ __forceinline__ int ns_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
-template <int EPI>
-__global__ __launch_bounds__(ns::THREADS) void k_gemm_nvfp4_stream(const MaskedGemmArgs p) {
+// Operands of one work item: the group's code / scale bases (row 0), the tile origin,
+// the group's valid rows and its depth.
+struct NsJob {
+  const uint8_t *a, *a_sf, *b, *b_sf;
+  int g, m0, mm, n0, K;
+};
+
+template <int EPI, int MODE>
+__global__ __launch_bounds__(ns::THREADS) void k_gemm_nvfp4_stream(const typename ArgsOf<MODE>::type p) {
   using namespace ns;
   constexpr bool SWIGLU = (EPI == EPI_SWIGLU_NVFP4);
+  constexpr bool MASKED = (MODE == MODE_MASKED);
+  static_assert(MASKED || !SWIGLU, "the SwiGLU epilogue is the MoE GEMM1's (masked)");
   constexpr int SA = 2, SB = DB + 1;
   static_assert(DB >= 3, "B(s + 1) must be issued before A(s)");
   __shared__ __attribute__((aligned(16))) uint8_t ringA[SA * A_STAGE];
@@ -56,24 +65,68 @@ __global__ __launch_bounds__(ns::THREADS) void k_gemm_nvfp4_stream(const MaskedG
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: branches on it are scalar
   const int wm = wave >> 1, wn = wave & 1;
-  const int G = p.G, K = p.K, KT = K / BK, N = p.N, cap = p.max_m;
+  const int G = p.G;
+  int N = 0, cap = 0, tiles_n = 0, total = 0;  // masked: common N, row capacity, N tiles
+  const int ncols = SWIGLU ? BN / 2 : BN;      // output (h) columns per item
+  if constexpr (MASKED) {
+    N = p.N;
+    cap = p.max_m;
+    tiles_n = SWIGLU ? (N / 2) / ncols : N / ncols;
+    for (int g = tid; g < G; g += THREADS) alpha_s[g] = (p.alpha ? p.alpha[g] : 1.0f) * p.alpha_scale;
+    stream_tile_prefix(p.masked_m, G, cap, tprefix, mm_s, tid);
+    total = __builtin_amdgcn_readfirstlane(tprefix[G]) * tiles_n;
+  } else {
+    // heterogeneous groups: tprefix counts items (M tiles x N tiles) per group
+    if (tid == 0) {
+      int run = 0;
+      for (int g = 0; g < G; g++) {
+        tprefix[g] = run;
+        run += (p.grp[g].M + BM - 1) / BM * (p.grp[g].N / BN);
+      }
+      tprefix[G] = run;
+    }
+    __syncthreads();
+    total = __builtin_amdgcn_readfirstlane(tprefix[G]);
+  }
   const int I = N / 2;
-  const int ncols = SWIGLU ? BN / 2 : BN;  // output (h) columns per item
-  const int tiles_n = SWIGLU ? I / ncols : N / ncols;
-
-  for (int g = tid; g < G; g += THREADS) alpha_s[g] = (p.alpha ? p.alpha[g] : 1.0f) * p.alpha_scale;
-  stream_tile_prefix(p.masked_m, G, cap, tprefix, mm_s, tid);
-  const int total = __builtin_amdgcn_readfirstlane(tprefix[G]) * tiles_n;
   const int grid = gridDim.x;
   const int bx = stream_bx();
   if (bx >= total) return;
   const int n_items = (total - 1 - bx) / grid + 1;
-  const int nsteps = n_items * KT;
-  auto item_at = [&](int k) { return stream_item(bx + k * grid, tiles_n, G, tprefix, mm_s, ncols); };
+
+  auto job_at = [&](int k) {
+    NsJob j;
+    if constexpr (MASKED) {
+      const StreamItem it = stream_item(bx + k * grid, tiles_n, G, tprefix, mm_s, ncols);
+      j.g = it.g; j.m0 = it.m0; j.mm = it.mm; j.n0 = it.n0; j.K = p.K;
+      j.a = p.a + (size_t)it.g * cap * (p.K / 2);
+      j.a_sf = p.a_sf + (size_t)it.g * cap * (p.K / 16);
+      j.b = p.b + (size_t)it.g * N * (p.K / 2);
+      j.b_sf = p.b_sf + (size_t)it.g * N * (p.K / 16);
+    } else {
+      const int w = bx + k * grid;
+      int lo = 0, hi = G;  // tprefix[lo] <= w < tprefix[hi]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (__builtin_amdgcn_readfirstlane(tprefix[mid]) <= w) lo = mid;
+        else hi = mid;
+      }
+      const HeteroGroup& q = p.grp[lo];
+      const int tn = q.N / BN, local = w - __builtin_amdgcn_readfirstlane(tprefix[lo]);
+      const int mt = local / tn;
+      j.g = lo; j.m0 = mt * BM; j.mm = q.M; j.n0 = (local - mt * tn) * BN; j.K = q.K;
+      j.a = q.a; j.a_sf = q.a_sf; j.b = q.b; j.b_sf = q.b_sf;
+    }
+    return j;
+  };
+  int nsteps = 0;
+  if constexpr (MASKED) nsteps = n_items * (p.K / BK);
+  else
+    for (int k = 0; k < n_items; k++) nsteps += job_at(k).K / BK;
 
   // B row r of an item (stage row): SwiGLU rows [0, 64) are gate rows n0 + r, [64, 128)
   // the matching up rows I + n0 + r - 64
-  auto b_row = [&](const StreamItem& it, int r) {
+  auto b_row = [&](const NsJob& it, int r) {
     if constexpr (SWIGLU) return r < BN / 2 ? it.n0 + r : I + it.n0 + (r - BN / 2);
     else return it.n0 + r;
   };
@@ -82,8 +135,10 @@ __global__ __launch_bounds__(ns::THREADS) void k_gemm_nvfp4_stream(const MaskedG
   // 16-row code groups and 32-row scale groups entirely past it are not fetched)
   const uint8_t* asrc[2];
   const uint8_t* asrc_s;
-  int a_n = 0, a_ns = 0;
-  auto a_setup = [&](const StreamItem& it) {
+  int a_n = 0, a_ns = 0, a_KT = 0;
+  auto a_setup = [&](const NsJob& it) {
+    const int K = it.K;
+    a_KT = K / BK;
     const int left = it.mm - it.m0 - 32 * wave;
     a_n = left <= 0 ? 0 : (left > 16 ? 2 : 1);
     a_ns = left > 0 ? 1 : 0;
@@ -91,19 +146,22 @@ __global__ __launch_bounds__(ns::THREADS) void k_gemm_nvfp4_stream(const MaskedG
     for (int j = 0; j < 2; j++) {
       const int r = 32 * wave + 16 * j + (lane >> 2);
       const int row = it.m0 + r < it.mm ? it.m0 + r : it.mm - 1;
-      asrc[j] = p.a + ((size_t)it.g * cap + row) * (K / 2) + (((lane & 3) ^ ns_swz(r)) << 4);
+      asrc[j] = it.a + (size_t)row * (K / 2) + (((lane & 3) ^ ns_swz(r)) << 4);
     }
     const int r = 32 * wave + (lane >> 1);
     const int row = it.m0 + r < it.mm ? it.m0 + r : it.mm - 1;
-    asrc_s = p.a_sf + ((size_t)it.g * cap + row) * (K / 16) + (lane & 1) * 4;
+    asrc_s = it.a_sf + (size_t)row * (K / 16) + (lane & 1) * 4;
   };
   const uint8_t* bsrc;
   const uint8_t* bsrc_s;
-  auto b_setup = [&](const StreamItem& it) {
+  int b_KT = 0;
+  auto b_setup = [&](const NsJob& it) {
+    const int K = it.K;
+    b_KT = K / BK;
     const int r = 16 * wave + (lane >> 2);
-    bsrc = p.b + ((size_t)it.g * N + b_row(it, r)) * (K / 2) + (((lane & 3) ^ ns_swz(r)) << 4);
+    bsrc = it.b + (size_t)b_row(it, r) * (K / 2) + (((lane & 3) ^ ns_swz(r)) << 4);
     const int rs = 32 * (wave & 3) + (lane >> 1);
-    bsrc_s = p.b_sf + ((size_t)it.g * N + b_row(it, rs)) * (K / 16) + (lane & 1) * 4;
+    bsrc_s = it.b_sf + (size_t)b_row(it, rs) * (K / 16) + (lane & 1) * 4;
   };
   int a_k = 0, a_kt = 0, a_step = 0, a_st = 0;
   int b_k = 0, b_kt = 0, b_step = 0, b_st = 0;
@@ -116,9 +174,9 @@ __global__ __launch_bounds__(ns::THREADS) void k_gemm_nvfp4_stream(const MaskedG
     a_st ^= 1;
     if (a_step + 1 < nsteps) {
       a_step++;
-      if (++a_kt == KT) {
+      if (++a_kt == a_KT) {
         a_kt = 0;
-        a_setup(item_at(++a_k));
+        a_setup(job_at(++a_k));
       }
     }
   };
@@ -129,15 +187,15 @@ __global__ __launch_bounds__(ns::THREADS) void k_gemm_nvfp4_stream(const MaskedG
     b_st = b_st + 1 == SB ? 0 : b_st + 1;
     if (b_step + 1 < nsteps) {
       b_step++;
-      if (++b_kt == KT) {
+      if (++b_kt == b_KT) {
         b_kt = 0;
-        b_setup(item_at(++b_k));
+        b_setup(job_at(++b_k));
       }
     }
   };
 
   {
-    const StreamItem it0 = item_at(0);
+    const NsJob it0 = job_at(0);
     a_setup(it0);
     b_setup(it0);
   }
@@ -178,7 +236,7 @@ __global__ __launch_bounds__(ns::THREADS) void k_gemm_nvfp4_stream(const MaskedG
 #pragma unroll
     for (int n = 0; n < 4; n++) acc[i][n] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-  StreamItem cit = item_at(0);
+  NsJob cit = job_at(0);
   int c_k = 0, c_kt = 0, c_sa = 0;
   const int q = lane >> 4, rr = lane & 15;
 
@@ -238,16 +296,27 @@ __global__ __launch_bounds__(ns::THREADS) void k_gemm_nvfp4_stream(const MaskedG
     }
     c_sa ^= 1;
 
-    if (++c_kt == KT) {
+    if (++c_kt == cit.K / BK) {
       // lane (rr, q) holds, for row group i, output row 16 wm + 64 i + rr and the four
       // columns 4 q .. 4 q + 3 of each 16-column group n
       if (active) {
-        const float alpha = alpha_s[cit.g];
+        float alpha;
+        void* obase;
+        size_t ldo;
+        if constexpr (MASKED) {
+          alpha = alpha_s[cit.g];
+          obase = p.out;
+          ldo = N;
+        } else {
+          alpha = p.grp[cit.g].alpha;
+          obase = p.grp[cit.g].out;
+          ldo = p.grp[cit.g].ldc;
+        }
 #pragma unroll
         for (int i = 0; i < 4; i++) {
           const int m = cit.m0 + 16 * wm + 64 * i + rr;
           const bool ok = m < cit.mm;
-          const size_t orow = (size_t)cit.g * cap + m;
+          const size_t orow = MASKED ? (size_t)cit.g * cap + m : (size_t)m;
           if constexpr (SWIGLU) {
 #pragma unroll
             for (int n = 0; n < 2; n++) {
@@ -276,9 +345,9 @@ __global__ __launch_bounds__(ns::THREADS) void k_gemm_nvfp4_stream(const MaskedG
               if constexpr (EPI == EPI_BF16) {
                 const uint32_t lo = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
                 const uint32_t hi = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
-                *(u32x2_t*)((uint16_t*)p.out + orow * N + c) = u32x2_t{lo, hi};
+                *(u32x2_t*)((uint16_t*)obase + orow * ldo + c) = u32x2_t{lo, hi};
               } else {
-                *(float4_t*)((float*)p.out + orow * N + c) = v;
+                *(float4_t*)((float*)obase + orow * ldo + c) = v;
               }
             }
           }
@@ -289,18 +358,18 @@ __global__ __launch_bounds__(ns::THREADS) void k_gemm_nvfp4_stream(const MaskedG
 #pragma unroll
         for (int n = 0; n < 4; n++) acc[i][n] = float4_t{0.f, 0.f, 0.f, 0.f};
       c_kt = 0;
-      if (++c_k < n_items) cit = item_at(c_k);
+      if (++c_k < n_items) cit = job_at(c_k);
     }
   }
   wait_vmcnt<0>();  // the trailing re-reads land before the workgroup ends
 }
 
-template <int EPI>
-static hipError_t launch_stream(const MaskedGemmArgs& p, int cu_limit, hipStream_t s) {
-  const void* k = (const void*)k_gemm_nvfp4_stream<EPI>;
+template <int EPI, int MODE>
+static hipError_t launch_stream(const typename ArgsOf<MODE>::type& p, int cu_limit, hipStream_t s) {
+  const void* k = (const void*)k_gemm_nvfp4_stream<EPI, MODE>;
   const int grid = resident_grid(k, ns::THREADS, cu_limit);
   if (grid <= 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((k_gemm_nvfp4_stream<EPI>), dim3(grid), dim3(ns::THREADS), 0, s, p);
+  hipLaunchKernelGGL((k_gemm_nvfp4_stream<EPI, MODE>), dim3(grid), dim3(ns::THREADS), 0, s, p);
   return hipGetLastError();
 }
 
@@ -313,11 +382,46 @@ hipError_t gemm_nvfp4_stream(MaskedGemmArgs p, int epi, int cu_limit, hipStream_
   if (n_out % ncols != 0 || (epi == EPI_SWIGLU_NVFP4 && p.N % 2 != 0)) return hipErrorNotSupported;
   if ((long long)p.G * ((p.max_m + BM - 1) / BM) * (n_out / ncols) > 0x7FFFFFFFLL) return hipErrorNotSupported;
   switch (epi) {
-    case EPI_BF16: return launch_stream<EPI_BF16>(p, cu_limit, s);
-    case EPI_F32: return launch_stream<EPI_F32>(p, cu_limit, s);
-    case EPI_SWIGLU_NVFP4: return launch_stream<EPI_SWIGLU_NVFP4>(p, cu_limit, s);
+    case EPI_BF16: return launch_stream<EPI_BF16, MODE_MASKED>(p, cu_limit, s);
+    case EPI_F32: return launch_stream<EPI_F32, MODE_MASKED>(p, cu_limit, s);
+    case EPI_SWIGLU_NVFP4: return launch_stream<EPI_SWIGLU_NVFP4, MODE_MASKED>(p, cu_limit, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+// Heterogeneous groups: every group with rows needs N % 128 == 0, K % 128 == 0 and an
+// output row stride and base that keep the 4-column stores aligned; the groups are
+// reordered by decreasing K so that the round-robin deal of the items balances.
+hipError_t gemm_nvfp4_stream_hetero(HeteroGemmArgs p, int epi, int cu_limit, hipStream_t s) {
+  using namespace ns;
+  if (epi != EPI_BF16 && epi != EPI_F32) return hipErrorNotSupported;
+  const uintptr_t out_align = epi == EPI_BF16 ? 8 : 16;
+  long long items = 0;
+  for (int g = 0; g < p.G; g++) {
+    const HeteroGroup& q = p.grp[g];
+    if (q.M == 0) continue;
+    if (q.N % BN != 0 || q.K % BK != 0 || q.ldc % 4 != 0 || ((uintptr_t)q.out & (out_align - 1)) != 0)
+      return hipErrorNotSupported;
+    items += (long long)(q.M + BM - 1) / BM * (q.N / BN);
+  }
+  if (items == 0) return hipSuccess;
+  if (items > 0x7FFFFFFFLL) return hipErrorNotSupported;
+  HeteroGemmArgs r = p;
+  bool taken[MXG_MAX_GROUPS] = {};
+  int n = 0;
+  for (int pass = 0; pass < p.G; pass++) {  // stable selection by decreasing K, empty groups dropped
+    int best = -1;
+    for (int g = 0; g < p.G; g++) {
+      if (p.grp[g].M == 0 || taken[g]) continue;
+      if (best < 0 || p.grp[g].K > p.grp[best].K) best = g;
+    }
+    if (best < 0) break;
+    r.grp[n++] = p.grp[best];
+    taken[best] = true;
+  }
+  r.G = n;
+  return epi == EPI_BF16 ? launch_stream<EPI_BF16, MODE_HETERO>(r, cu_limit, s)
+                         : launch_stream<EPI_F32, MODE_HETERO>(r, cu_limit, s);
 }
 
 }  // namespace mxg

@@ -62,6 +62,9 @@ constexpr int SKINNY_MAX_M = 32;  // row capacity up to which the skinny kernel 
 // Larger masked groups (prefill): persistent weight-streaming kernel, 256-row M tiles;
 // returns hipErrorNotSupported without launching for shapes it does not take.
 hipError_t gemm_nvfp4_stream(MaskedGemmArgs p, int epi, int cu_limit, hipStream_t s);
+// The same kernel over heterogeneous groups (bf16 / fp32 outputs); hipErrorNotSupported for
+// groups it does not take (N or K not a multiple of 128, unaligned output rows).
+hipError_t gemm_nvfp4_stream_hetero(HeteroGemmArgs p, int epi, int cu_limit, hipStream_t s);
 
 // Workgroups of `kernel` (with `threads` threads) resident on the device at once, over
 // at most cu_limit CUs when cu_limit > 0; 0 on a runtime error.

@@ -206,6 +206,41 @@ def test_hetero_gemm_full_size_sampled():
         log(f"group {gi} ({M},{N},{K}) rows {rows} ok")
 
 
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_hetero_gemm_streaming_shapes_and_ldc(out_dtype):
+    # every group takes the weight-streaming kernel (N, K multiples of 128): several M
+    # tiles with a ragged tail, an empty group, different depths, a padded output stride
+    shapes = ((300, 256, 384), (0, 128, 128), (64, 384, 1024), (513, 128, 256))
+    log(f"heterogeneous NVFP4 grouped GEMM, streaming shapes {shapes}, {out_dtype}, ldc = N + 68")
+    wl = datagen.hetero_gemm_workload(11, DEV, shapes)
+    groups = []
+    for q in wl.tensors["groups"]:
+        q = dict(q)
+        q["ldc"] = q["N"] + 68
+        mk = sentinel_bf16 if out_dtype == torch.bfloat16 else sentinel_f32
+        q["out"] = mk((max(q["M"], 1), q["ldc"]), DEV)
+        groups.append(q)
+    _mxg().mx_grouped_gemm(groups, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    for gi, q in enumerate(groups):
+        M, N, K = q["M"], q["N"], q["K"]
+        if M == 0:
+            continue
+        if out_dtype == torch.bfloat16:
+            bits = bf16_tensor_bits(q["out"])
+            assert (bits[:, N:] == SENT_BF16).all(), f"group {gi}: padding columns written"
+            got = bf16_from_bits_np(bits[:, :N])
+        else:
+            o = np_(q["out"])
+            assert (o[:, N:].view(np.uint32) == np.uint32(SENT_F32 & 0xFFFFFFFF)).all(), \
+                f"group {gi}: padding columns written"
+            got = o[:, :N].astype(np.float64)
+        y, S, _ = oracle.gemm_nvfp4_masked(np_(q["a"])[None], np_(q["a_sf"])[None], np_(q["b"])[None],
+                                           np_(q["b_sf"])[None], np.array([q["alpha"]], np.float32),
+                                           [M], M, N, K)
+        assert_within(got, y[0], S[0], f"group {gi}")
+
+
 @pytest.mark.parametrize("shapes", [
     ((37, 520, 1024), (0, 64, 128), (130, 600, 128), (1, 16, 64)),
     ((256, 256, 256),),
