@@ -79,6 +79,9 @@ def test_masked_gemm_g4_m64_n512_k1024(seed):
     (4, 32, 384, 512, [17, 32, 16, 31]),
     (3, 8, 4096, 7168, [1, 8, 3]),
     (2, 1, 64, 2048, [1, 1]),
+    # decode-shaped kernel (row capacity <= 8)
+    (3, 8, 200, 1024, [8, 1, 5]),            # N tail inside a 128-column unit
+    (4, 8, 48, 4096, [2, 0, 8, 7]),          # N below one 128-column unit
     # weight-streaming kernel (row capacity > 32, N % 128 == 0, K % 128 == 0)
     (3, 300, 256, 384, [300, 257, 31]),      # two 256-row M tiles, ragged
     (2, 96, 384, 128, [96, 65]),             # one K step, rows across a 64-row boundary
@@ -114,7 +117,7 @@ def test_masked_gemm_general_scales_fp32_out_and_poison():
         _check_masked(t, out, max_m, N, K, f"general scales {dt}")
 
 
-@pytest.mark.parametrize("max_m,K", [(16, 1024), (48, 512), (272, 640)])
+@pytest.mark.parametrize("max_m,K", [(16, 1024), (8, 1024), (48, 512), (272, 640)])
 def test_masked_gemm_fp32_out(max_m, K):
     log(f"masked NVFP4 GEMM fp32 output max_m={max_m} K={K}")
     wl = datagen.masked_gemm_workload(23, DEV, G=3, max_m=max_m, N=256, K=K, masked_m=[max_m, 1, max_m - 3])
