@@ -317,20 +317,30 @@ hipError_t gemm_fp8_swiglu(Fp8GemmArgs p, int cu_limit, hipStream_t s) {
 
 // ----------------------------------------------------------------------------- GEMM2
 // Persistent and weight-streaming like GEMM1.  A work item is (expert g, 256-row M tile,
-// 128 output columns, one 128-row block of W2's scales); a step is 64 K: 256 bf16 h rows
-// x 128 bytes and 128 e4m3 weight rows x 64 bytes, both by DMA (h one step ahead, W2 DB
-// steps ahead).  The weights are widened exactly to bf16 in registers
-// (v_cvt_scalef32_pk_bf16_fp8, scale 1) for the bf16 MFMA; each 128-K scale block is
-// summed in fp32 before it is promoted with the block's weight scale.  The waves own
-// interleaved 16-row groups as in GEMM1.  LDS rows are
-// XOR-swizzled (h: 16-byte chunk ^ (r ^ r >> 3) & 7; W2: 16-byte chunk ^ (r >> 2) & 3).
+// BN output columns); a step is 64 K: 256 bf16 h rows x 128 bytes and BN e4m3 weight rows
+// x 64 bytes, both by DMA (h one step ahead, W2 DB steps ahead).  The weights are widened
+// exactly to bf16 in registers (v_cvt_scalef32_pk_bf16_fp8, scale 1) for the bf16 MFMA.
+// The waves own interleaved 16-row groups as in GEMM1 and BN / 2 columns each, which lie in
+// one 128-row block of W2's scales, so a wave's block scale c_k is one number per 128-K
+// block.  Instead of summing each block apart and promoting it (a second set of
+// accumulators), a wave keeps one sum in units of the current block's scale: before block
+// k it multiplies the sum by c_{k-1} / c_k, and the epilogue multiplies by the last c_k.
+// The sum equals sum_k c_k * P_k exactly up to those fp32 roundings (about three per
+// block), and the freed registers pay for twice the columns per item, which halves the
+// re-reads of h.  A block whose scale is zero contributes nothing and is skipped.
+// LDS rows are XOR-swizzled (h: 16-byte chunk ^ (r ^ r >> 3) & 7; W2: 16-byte chunk ^
+// (r >> 2) & 3).
 namespace f2 {
-constexpr int BM = 256, BN = 128, BK = 64;
+constexpr int BM = 256, BK = 64;
 constexpr int WAVES = 8, THREADS = WAVES * 64;
 constexpr int A_STAGE = BM * BK * 2;  // bf16 h rows, 128 bytes each
-constexpr int B_STAGE = BN * BK + 16; // e4m3 W2 rows, 64 bytes each, then the block scale
-constexpr int A_OPS = 4, B_OPS = 1;   // DMAs per wave per step (wave 1 adds the scale)
-constexpr int DB = 6;
+constexpr int A_OPS = 4;              // h DMAs per wave per step (32 rows)
+template <int NBW>
+struct Cfg {
+  static constexpr int BN = 32 * NBW;              // two waves across, 16 * NBW columns each
+  static constexpr int B_STAGE = BN * BK + 16;     // e4m3 W2 rows, 64 bytes each, then two block scales
+  static constexpr int B_OPS = BN * BK / (WAVES * 1024);  // weight DMAs per wave per step
+};
 }  // namespace f2
 
 __device__ __forceinline__ int f2_swz_b(int r) { return (r >> 2) & 3; }
@@ -351,8 +361,12 @@ __device__ __forceinline__ float4_t quad_transpose(float4_t v, int lane) {
   return v;
 }
 
+template <int NBW, int DB>
 __global__ __launch_bounds__(f2::THREADS) void k_gemm_bf16_fp8w(const Fp8GemmArgs p) {
   using namespace f2;
+  constexpr int BN = Cfg<NBW>::BN, B_STAGE = Cfg<NBW>::B_STAGE, B_OPS = Cfg<NBW>::B_OPS;
+  constexpr int WCOLS = 16 * NBW;
+  static_assert(B_OPS >= 1 && WCOLS <= 128 && 128 % WCOLS == 0, "a wave's columns share one scale block");
   constexpr int SA = 2, SB = DB + 1;
   __shared__ __attribute__((aligned(16))) uint8_t ringA[SA * A_STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t ringB[SB * B_STAGE];
@@ -388,12 +402,17 @@ __global__ __launch_bounds__(f2::THREADS) void k_gemm_bf16_fp8w(const Fp8GemmArg
       asrc[j] = A + (size_t)row * K * 2 + (((lane & 7) ^ f1_swz(r)) << 4);
     }
   };
-  const uint8_t* bsrc;
+  // wave w DMAs weight rows 16 * (B_OPS * w + j) + lane / 4; lanes 0 and 1 of wave 1 the
+  // scale blocks of the two column halves
+  const uint8_t* bsrc[B_OPS];
   const float* bsrc_s;
   auto b_setup = [&](const StreamItem& it) {
-    const int r = 16 * wave + (lane >> 2);
-    bsrc = p.b + ((size_t)it.g * N + it.n0 + r) * K + (((lane & 3) ^ f2_swz_b(r)) << 4);
-    bsrc_s = p.b_s + ((size_t)it.g * (N / 128) + it.n0 / 128) * KB;
+#pragma unroll
+    for (int j = 0; j < B_OPS; j++) {
+      const int r = 16 * (B_OPS * wave + j) + (lane >> 2);
+      bsrc[j] = p.b + ((size_t)it.g * N + it.n0 + r) * K + (((lane & 3) ^ f2_swz_b(r)) << 4);
+    }
+    bsrc_s = p.b_s + ((size_t)it.g * (N / 128) + (it.n0 + (lane & 1) * WCOLS) / 128) * KB;
   };
   int a_k = 0, a_kt = 0, a_step = 0, a_st = 0;
   int b_k = 0, b_kt = 0, b_step = 0, b_st = 0;
@@ -413,8 +432,9 @@ __global__ __launch_bounds__(f2::THREADS) void k_gemm_bf16_fp8w(const Fp8GemmArg
   };
   auto issue_b = [&]() {
     uint8_t* st = ringB + b_st * B_STAGE;
-    dma16(bsrc + b_kt * BK, st + 16 * wave * BK);
-    if (wave == 1 && lane == 0) dma4(bsrc_s + (b_kt >> 1), st + BN * BK);
+#pragma unroll
+    for (int j = 0; j < B_OPS; j++) dma16(bsrc[j] + b_kt * BK, st + 16 * (B_OPS * wave + j) * BK);
+    if (wave == 1 && lane < 2) dma4(bsrc_s + (b_kt >> 1), st + BN * BK);
     b_st = b_st + 1 == SB ? 0 : b_st + 1;
     if (b_step + 1 < nsteps) {
       b_step++;
@@ -436,13 +456,16 @@ __global__ __launch_bounds__(f2::THREADS) void k_gemm_bf16_fp8w(const Fp8GemmArg
     issue_b();
   }
 
-  // acc: promoted sums; tmp: the current 128-K block, and between the end of an item and
-  // the next barrier the item's results (transposed, one row of 4 columns per lane)
-  float4_t acc[4][4], tmp[4][4];
+  // acc: the item's sums in units of the current block scale c_cur (0 before the first
+  // block with a nonzero scale); between the end of an item and the next barrier, the
+  // item's results (scaled, transposed: one row of 4 columns per lane)
+  float4_t acc[4][NBW];
 #pragma unroll
   for (int i = 0; i < 4; i++)
 #pragma unroll
-    for (int n = 0; n < 4; n++) acc[i][n] = tmp[i][n] = float4_t{0.f, 0.f, 0.f, 0.f};
+    for (int n = 0; n < NBW; n++) acc[i][n] = float4_t{0.f, 0.f, 0.f, 0.f};
+  float c_cur = 0.f;
+  bool zblk = false;
 
   StreamItem cit = item_at(0);
   int c_k = 0, c_kt = 0, c_sa = 0, c_sb = 0;
@@ -455,10 +478,10 @@ __global__ __launch_bounds__(f2::THREADS) void k_gemm_bf16_fp8w(const Fp8GemmArg
     for (int i = 0; i < 4; i++) {
       const int row = pit.m0 + 16 * wm + 64 * i + 4 * q + (lane & 3);
 #pragma unroll
-      for (int n = 0; n < 4; n++) {
-        const int col = pit.n0 + 64 * wn + 16 * n + 4 * (rr >> 2);
-        if (row < pit.mm) *(float4_t*)(O + ((size_t)pit.g * cap + row) * N + col) = tmp[i][n];
-        tmp[i][n] = float4_t{0.f, 0.f, 0.f, 0.f};
+      for (int n = 0; n < NBW; n++) {
+        const int col = pit.n0 + WCOLS * wn + 16 * n + 4 * (rr >> 2);
+        if (row < pit.mm) *(float4_t*)(O + ((size_t)pit.g * cap + row) * N + col) = acc[i][n];
+        acc[i][n] = float4_t{0.f, 0.f, 0.f, 0.f};
       }
     }
   };
@@ -475,12 +498,28 @@ __global__ __launch_bounds__(f2::THREADS) void k_gemm_bf16_fp8w(const Fp8GemmArg
     issue_b();
 
     const bool active = cit.m0 + 16 * wm < cit.mm;
-    if (active) {
+    const uint8_t* Bs = ringB + c_sb * B_STAGE;
+    if ((c_kt & 1) == 0) {  // first step of a 128-K scale block
+      const float ck = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(*(const float*)(Bs + BN * BK + 4 * wn))));
+      zblk = ck == 0.f;
+      if (!zblk) {
+        if (active && c_cur != 0.f && c_cur != ck) {
+          const float r = c_cur / ck;
+#pragma unroll
+          for (int i = 0; i < 4; i++)
+#pragma unroll
+            for (int n = 0; n < NBW; n++)
+#pragma unroll
+              for (int e = 0; e < 4; e++) acc[i][n][e] *= r;
+        }
+        c_cur = ck;
+      }
+    }
+    if (active && !zblk) {
       const uint8_t* As = ringA + c_sa * A_STAGE;
-      const uint8_t* Bs = ringB + c_sb * B_STAGE;
 #pragma unroll
       for (int ks = 0; ks < BK / 32; ks++) {
-        bf16x8_t af[4], bfr[4];
+        bf16x8_t af[4], bfr[NBW];
 #pragma unroll
         for (int i = 0; i < 4; i++) {
           if (cit.m0 + 16 * wm + 64 * i >= cit.mm) break;
@@ -488,8 +527,8 @@ __global__ __launch_bounds__(f2::THREADS) void k_gemm_bf16_fp8w(const Fp8GemmArg
           af[i] = *(const bf16x8_t*)(As + r * (BK * 2) + (((ks * 4 + q) ^ f1_swz(r)) << 4));
         }
 #pragma unroll
-        for (int n = 0; n < 4; n++) {
-          const int r = 64 * wn + 16 * n + rr;
+        for (int n = 0; n < NBW; n++) {
+          const int r = WCOLS * wn + 16 * n + rr;
           const u32x2_t raw = *(const u32x2_t*)(Bs + r * BK + (((ks * 2 + (q >> 1)) ^ f2_swz_b(r)) << 4) + (q & 1) * 8);
           const bf16x2_t w0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[0], 1.0f, false);
           const bf16x2_t w1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[0], 1.0f, true);
@@ -501,21 +540,9 @@ __global__ __launch_bounds__(f2::THREADS) void k_gemm_bf16_fp8w(const Fp8GemmArg
         for (int i = 0; i < 4; i++) {
           if (cit.m0 + 16 * wm + 64 * i >= cit.mm) break;
 #pragma unroll
-          for (int n = 0; n < 4; n++)
-            tmp[i][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[n], tmp[i][n], 0, 0, 0);
+          for (int n = 0; n < NBW; n++)
+            acc[i][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[n], acc[i][n], 0, 0, 0);
         }
-      }
-      if (c_kt & 1) {  // end of a 128-wide scale block: promote
-        const float sw = *(const float*)(Bs + BN * BK);
-#pragma unroll
-        for (int i = 0; i < 4; i++)
-#pragma unroll
-          for (int n = 0; n < 4; n++)
-#pragma unroll
-            for (int r = 0; r < 4; r++) {
-              acc[i][n][r] = __builtin_fmaf(tmp[i][n][r], sw, acc[i][n][r]);
-              tmp[i][n][r] = 0.f;
-            }
       }
     }
     c_sa ^= 1;
@@ -526,13 +553,16 @@ __global__ __launch_bounds__(f2::THREADS) void k_gemm_bf16_fp8w(const Fp8GemmArg
 #pragma unroll
         for (int i = 0; i < 4; i++)
 #pragma unroll
-          for (int n = 0; n < 4; n++) {
-            tmp[i][n] = quad_transpose(acc[i][n], lane);
-            acc[i][n] = float4_t{0.f, 0.f, 0.f, 0.f};
+          for (int n = 0; n < NBW; n++) {
+            float4_t v = acc[i][n];
+#pragma unroll
+            for (int e = 0; e < 4; e++) v[e] *= c_cur;
+            acc[i][n] = quad_transpose(v, lane);
           }
         pend = true;
         pit = cit;
       }
+      c_cur = 0.f;
       c_kt = 0;
       if (++c_k < n_items) cit = item_at(c_k);
     }
@@ -541,15 +571,24 @@ __global__ __launch_bounds__(f2::THREADS) void k_gemm_bf16_fp8w(const Fp8GemmArg
   wait_vmcnt<0>();  // the trailing re-reads land before the workgroup ends
 }
 
-hipError_t gemm_bf16_fp8w(Fp8GemmArgs p, int cu_limit, hipStream_t s) {
+template <int NBW, int DB>
+static hipError_t launch_bf16_fp8w(const Fp8GemmArgs& p, int cu_limit, hipStream_t s) {
   using namespace f2;
-  if (p.G <= 0 || p.max_m <= 0 || p.N <= 0 || p.K <= 0) return hipSuccess;
-  if (p.G > f1::MAX_G || p.N % BN != 0 || p.K % 128 != 0) return hipErrorNotSupported;
+  constexpr int BN = Cfg<NBW>::BN;
   if ((long long)p.G * ((p.max_m + BM - 1) / BM) * (p.N / BN) > 0x7FFFFFFFLL) return hipErrorNotSupported;
-  const int grid = resident_grid((const void*)k_gemm_bf16_fp8w, THREADS, cu_limit);
+  const void* k = (const void*)k_gemm_bf16_fp8w<NBW, DB>;
+  const int grid = resident_grid(k, THREADS, cu_limit);
   if (grid <= 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_gemm_bf16_fp8w, dim3(grid), dim3(THREADS), 0, s, p);
+  hipLaunchKernelGGL((k_gemm_bf16_fp8w<NBW, DB>), dim3(grid), dim3(THREADS), 0, s, p);
   return hipGetLastError();
+}
+
+hipError_t gemm_bf16_fp8w(Fp8GemmArgs p, int cu_limit, hipStream_t s) {
+  if (p.G <= 0 || p.max_m <= 0 || p.N <= 0 || p.K <= 0) return hipSuccess;
+  if (p.G > f1::MAX_G || p.N % 128 != 0 || p.K % 128 != 0) return hipErrorNotSupported;
+  // 256 columns per item where N allows it (half the h re-reads), else 128
+  if (p.N % 256 == 0) return launch_bf16_fp8w<8, 4>(p, cu_limit, s);
+  return launch_bf16_fp8w<4, 6>(p, cu_limit, s);
 }
 
 }  // namespace mxg

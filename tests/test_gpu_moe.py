@@ -172,10 +172,21 @@ def test_moe_nvfp4_prefill_full_size():
 
 
 # ----------------------------------------------------------------------------- FP8
-def _run_fp8(T, H, I, seed, n_check, n_deep=0):
+def _vary_block_scales(s, seed, zero_frac=0.1):
+    """Input variant: each 128x128 block scale times 2^u, u uniform in [-8, 8], and about
+    zero_frac of the blocks set to zero (such a block contributes nothing)."""
+    g = torch.Generator().manual_seed(seed)
+    f = torch.pow(2.0, torch.randint(-8, 9, tuple(s.shape), generator=g).float())
+    f[torch.rand(tuple(s.shape), generator=g) < zero_frac] = 0.0
+    return (s.cpu() * f).to(s.device)
+
+
+def _run_fp8(T, H, I, seed, n_check, n_deep=0, vary_w2_scales=False):
     mxg = _mxg()
     wl = datagen.moe_fp8_workload(seed, DEV, T=T, H=H, I=I)
     t = wl.tensors
+    if vary_w2_scales:
+        t["w2_s"] = _vary_block_scales(t["w2_s"], seed + 1)
     ids, w, masked_m, row, max_m = _route_dispatch(t)
     y = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
     d = mxg.make_moe_desc(mxg.MXG_MOE_FP8_BLOCK128, T, H, I, E, TOPK, max_m, t["xq"], t["w13"], t["w13_s"],
@@ -233,6 +244,14 @@ def test_moe_fp8_small_full():
 def test_moe_fp8_two_m_tiles():
     log("FP8 MoE with masked_m past 256: T=8192 H=512 I=256 E=256, 24 tokens")
     _run_fp8(8192, 512, 256, 3001, 8, n_deep=16)
+
+
+@pytest.mark.parametrize("H", [512, 384])
+def test_moe_fp8_varied_w2_scales(H):
+    # GEMM2 keeps its sum in units of the current block scale: scales that jump by up to
+    # 2^16 between blocks, zero blocks, and (H = 384) 128-column items
+    log(f"FP8 MoE with varied W2 block scales: T=256 H={H} I=384 E=256, every token")
+    _run_fp8(256, H, 384, 3002 + H, None, vary_w2_scales=True)
 
 
 def test_moe_fp8_full_size():
