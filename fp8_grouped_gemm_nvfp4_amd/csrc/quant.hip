@@ -127,23 +127,43 @@ hipError_t gather_fp8(const uint8_t* xq, const float* xs, int T, int H, const in
 }
 
 // Weighted combine: y[t, :] = bf16(sum_j w[t, j] * o[ids[t, j], row[t, j], :]),
-// fp32 sum in slot order; each thread owns 4 consecutive columns.
+// fp32 sum in slot order; each thread owns 4 consecutive columns.  All of a thread's slot
+// loads are issued before the sum (top_k <= 8), so it keeps up to eight 16-byte reads of
+// o in flight; o is read once, with nontemporal loads.
 __global__ __launch_bounds__(256) void k_combine(const float* o, const int32_t* ids, const int32_t* row,
                                                  const float* w, int T, int H, int top_k, int max_m,
                                                  uint16_t* y) {
+  constexpr int MAXK = 8;
   const int nq = H / 4;
   long c = (long)blockIdx.x * 256 + threadIdx.x;
   if (c >= (long)T * nq) return;
   int t = (int)(c / nq), q = (int)(c % nq);
-  float4_t acc = {0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < top_k; j++) {
-    int e = ids[(size_t)t * top_k + j];
-    int r = row[(size_t)t * top_k + j];
-    if (r >= max_m) continue;
-    float wj = w[(size_t)t * top_k + j];
-    float4_t v = *(const float4_t*)(o + ((size_t)e * max_m + r) * H + (size_t)q * 4);
+  int rj[MAXK];
+  float wj[MAXK];
+  float4_t v[MAXK];
 #pragma unroll
-    for (int i = 0; i < 4; i++) acc[i] = __builtin_fmaf(wj, v[i], acc[i]);
+  for (int j = 0; j < MAXK; j++) {
+    rj[j] = max_m;
+    wj[j] = 0.f;
+    if (j < top_k) {
+      rj[j] = row[(size_t)t * top_k + j];
+      wj[j] = w[(size_t)t * top_k + j];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < MAXK; j++) {
+    v[j] = float4_t{0.f, 0.f, 0.f, 0.f};
+    if (rj[j] < max_m) {
+      const int e = ids[(size_t)t * top_k + j];
+      v[j] = __builtin_nontemporal_load((const float4_t*)(o + ((size_t)e * max_m + rj[j]) * H + (size_t)q * 4));
+    }
+  }
+  float4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < MAXK; j++) {
+    if (rj[j] >= max_m) continue;
+#pragma unroll
+    for (int i = 0; i < 4; i++) acc[i] = __builtin_fmaf(wj[j], v[j][i], acc[i]);
   }
   uint32_t lo = f32_to_bf16_rne(acc[0]) | (f32_to_bf16_rne(acc[1]) << 16);
   uint32_t hi = f32_to_bf16_rne(acc[2]) | (f32_to_bf16_rne(acc[3]) << 16);
@@ -154,6 +174,7 @@ hipError_t combine(const float* o, const int32_t* ids, const int32_t* row, const
                    int H, int top_k, int max_m, uint16_t* y, hipStream_t s) {
   long n = (long)T * (H / 4);
   if (n == 0) return hipSuccess;
+  if (top_k < 1 || top_k > 8 || H % 4 != 0) return hipErrorNotSupported;
   hipLaunchKernelGGL(k_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, o, ids, row, w, T,
                      H, top_k, max_m, y);
   return hipGetLastError();
