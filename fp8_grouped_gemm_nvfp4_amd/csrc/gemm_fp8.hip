@@ -328,8 +328,11 @@ hipError_t gemm_fp8_swiglu(Fp8GemmArgs p, int cu_limit, hipStream_t s) {
 // The sum equals sum_k c_k * P_k exactly up to those fp32 roundings (about three per
 // block), and the freed registers pay for twice the columns per item, which halves the
 // re-reads of h.  A block whose scale is zero contributes nothing and is skipped.
-// LDS rows are XOR-swizzled (h: 16-byte chunk ^ (r ^ r >> 3) & 7; W2: 16-byte chunk ^
-// (r >> 2) & 3).
+// Inside a step the K order is permuted identically on both operands (only the fp32
+// summation order changes): lane quarter q takes K 16q .. 16q + 15 of the step, the first
+// 8 in the first MFMA and the rest in the second, so that a lane's W2 bytes for the step
+// are one 16-byte read and its h elements two.  LDS rows are XOR-swizzled (h: 16-byte
+// chunk ^ (r ^ r >> 3) & 7; W2: 16-byte chunk ^ 2 * (r bit 3)).
 namespace f2 {
 constexpr int BM = 256, BK = 64;
 constexpr int WAVES = 8, THREADS = WAVES * 64;
@@ -343,7 +346,11 @@ struct Cfg {
 };
 }  // namespace f2
 
-__device__ __forceinline__ int f2_swz_b(int r) { return (r >> 2) & 3; }
+// W2 rows (64 bytes): 16-byte chunk c sits at c ^ 2 * (r bit 3).  A 16-byte LDS read is
+// served in four passes of 16 lanes (same lane bit 5, same parity of lane bits 2..4);
+// with this permutation (and f1_swz on the 128-byte h rows) the lanes of a pass hit 16
+// different slots of the 256-byte bank row.
+__device__ __forceinline__ int f2_swz_b(int r) { return (r >> 2) & 2; }
 
 // 4 x 4 transpose inside each quad of lanes: lane q's v[r] (row r, column q) becomes lane
 // r's element q, so that each lane ends up with four consecutive columns of one row.
@@ -517,6 +524,12 @@ __global__ __launch_bounds__(f2::THREADS) void k_gemm_bf16_fp8w(const Fp8GemmArg
     }
     if (active && !zblk) {
       const uint8_t* As = ringA + c_sa * A_STAGE;
+      u32x4_t braw[NBW];
+#pragma unroll
+      for (int n = 0; n < NBW; n++) {
+        const int r = WCOLS * wn + 16 * n + rr;
+        braw[n] = *(const u32x4_t*)(Bs + r * BK + ((q ^ f2_swz_b(r)) << 4));
+      }
 #pragma unroll
       for (int ks = 0; ks < BK / 32; ks++) {
         bf16x8_t af[4], bfr[NBW];
@@ -524,16 +537,15 @@ __global__ __launch_bounds__(f2::THREADS) void k_gemm_bf16_fp8w(const Fp8GemmArg
         for (int i = 0; i < 4; i++) {
           if (cit.m0 + 16 * wm + 64 * i >= cit.mm) break;
           const int r = 16 * wm + 64 * i + rr;
-          af[i] = *(const bf16x8_t*)(As + r * (BK * 2) + (((ks * 4 + q) ^ f1_swz(r)) << 4));
+          af[i] = *(const bf16x8_t*)(As + r * (BK * 2) + (((2 * q + ks) ^ f1_swz(r)) << 4));
         }
 #pragma unroll
         for (int n = 0; n < NBW; n++) {
-          const int r = WCOLS * wn + 16 * n + rr;
-          const u32x2_t raw = *(const u32x2_t*)(Bs + r * BK + (((ks * 2 + (q >> 1)) ^ f2_swz_b(r)) << 4) + (q & 1) * 8);
-          const bf16x2_t w0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[0], 1.0f, false);
-          const bf16x2_t w1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[0], 1.0f, true);
-          const bf16x2_t w2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[1], 1.0f, false);
-          const bf16x2_t w3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[1], 1.0f, true);
+          const uint32_t lo = braw[n][2 * ks], hi = braw[n][2 * ks + 1];
+          const bf16x2_t w0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+          const bf16x2_t w1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+          const bf16x2_t w2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+          const bf16x2_t w3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
           bfr[n] = bf16x8_t{w0[0], w0[1], w1[0], w1[1], w2[0], w2[1], w3[0], w3[1]};
         }
 #pragma unroll

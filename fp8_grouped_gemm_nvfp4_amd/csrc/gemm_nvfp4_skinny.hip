@@ -48,7 +48,9 @@ constexpr int MAX_LIST = 512;                   // (group, M tile) entries kept 
 }
 
 // Per-lane DMA source offsets of one weight tile: codes of rows 4i + lane/16 with the
-// swizzled unit, scales of row lane/2 (lanes < 32 only).
+// swizzled unit, scales of row lane/2 (lanes < 32 only).  A row's 32 scale bytes land
+// with their 16-byte halves swapped for rows 8..15, so that the 4-byte scale reads of
+// rows n and n + 8 fall in different banks.
 struct TileSrc {
   size_t code[4];
   size_t scale;
@@ -66,7 +68,7 @@ __device__ __forceinline__ TileSrc tile_src(int first_row, int nlimit, int row_o
   int r = (lane & 31) >> 1;
   int g = first_row + r;
   g = (g < nlimit ? g : nlimit - 1) + row_off;
-  s.scale = (size_t)g * (K / 16) + (size_t)((lane & 1) * 16);
+  s.scale = (size_t)g * (K / 16) + (size_t)(((lane & 1) ^ ((r >> 3) & 1)) * 16);
   return s;
 }
 
@@ -150,7 +152,11 @@ __device__ __forceinline__ void compute_chunk(float4_t (&acc)[NT], const uint8_t
     for (int t = 0; t < NT; t++) {
       const uint8_t* st = stage + t * sk::TILE_STAGE;
       w[t] = *(const u32x4_t*)(st + n * 256 + (((4 * j + q) ^ n) * 16));
-      uint32_t sb = *(const uint16_t*)(st + sk::CODE_BYTES + n * 32 + j * 8 + q * 2);
+      // the dword holding this lane's two scale bytes (lanes q and q ^ 1 read the same
+      // dword, a broadcast; 2-byte reads of its halves would be served apart)
+      const uint32_t sw = *(const uint32_t*)(st + sk::CODE_BYTES + n * 32 + ((((j >> 1) ^ (n >> 3)) & 1) << 4) +
+                                             (j & 1) * 8 + (q >> 1) * 4);
+      const uint32_t sb = sw >> (16 * (q & 1));
       half2_t s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sb, 1.0f, false);
       sc[t][0] = half2_t{s01[0], s01[0]};
       sc[t][1] = half2_t{s01[1], s01[1]};

@@ -11,9 +11,16 @@
 // output columns or 64 gate + 64 up columns), so every weight panel is read from HBM
 // once per group whenever masked_m <= 256.  One step is 128 K: per row 64 code bytes
 // and 8 scale bytes.  Everything arrives by LDS DMA: the activation codes and scales
-// one step ahead, the weight codes and scales DB steps ahead.  Code rows are 64 bytes
-// with their 16-byte chunks XOR-permuted by ((r >> 1) ^ (r >> 3)) & 3, which keeps the
-// 16-lane MFMA operand reads free of bank conflicts.
+// one step ahead, the weight codes and scales DB steps ahead.
+//
+// LDS layouts follow how gfx950 serves 16-byte accesses (measured with the bank-conflict
+// counters): a read is served in four passes of 16 lanes, a pass being the lanes with the
+// same lane bit 5 and the same parity of lane bits 2..4, and is conflict-free when the
+// lanes of a pass hit 16 different 16-byte slots of the 256-byte bank row; a write is
+// served 8 consecutive lanes at a time over 128 bytes.  Activation code rows (64 bytes)
+// have their 16-byte chunks XOR-permuted by 2 * (row bit 3); weight code rows are plain
+// (the decode reads them 4 rows x 64 bytes per pass); the decoded fp16 weight rows (256
+// bytes) hold K chunk c at slot c ^ sigma(r), sigma flipping row bit 3 with row bit 2.
 //
 // Compute: decoding is exact (e2m1 * e4m3 fits fp16; fp16 products are exact in fp32).
 // The weight step is decoded once per workgroup into an fp16 LDS tile, one step ahead;
@@ -38,7 +45,8 @@ constexpr int B_CODE = BN * 64, B_STAGE = B_CODE + BN * 8;  // codes [128][64], 
 constexpr int DB = 4;                                       // weight steps in flight (>= 3)
 }  // namespace ns
 
-__device__ __forceinline__ int ns_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+__device__ __forceinline__ int ns_swz_a(int r) { return (r >> 2) & 2; }          // activation code rows
+__device__ __forceinline__ int ns_sigma(int r) { return (r & 15) ^ ((r & 4) << 1); }  // decoded weight rows
 
 // Operands of one work item: the group's code / scale bases (row 0), the tile origin,
 // the group's valid rows and its depth.
@@ -146,7 +154,7 @@ __global__ __launch_bounds__(ns::THREADS) void k_gemm_nvfp4_stream(const typenam
     for (int j = 0; j < 2; j++) {
       const int r = 32 * wave + 16 * j + (lane >> 2);
       const int row = it.m0 + r < it.mm ? it.m0 + r : it.mm - 1;
-      asrc[j] = it.a + (size_t)row * (K / 2) + (((lane & 3) ^ ns_swz(r)) << 4);
+      asrc[j] = it.a + (size_t)row * (K / 2) + (((lane & 3) ^ ns_swz_a(r)) << 4);
     }
     const int r = 32 * wave + (lane >> 1);
     const int row = it.m0 + r < it.mm ? it.m0 + r : it.mm - 1;
@@ -159,7 +167,7 @@ __global__ __launch_bounds__(ns::THREADS) void k_gemm_nvfp4_stream(const typenam
     const int K = it.K;
     b_KT = K / BK;
     const int r = 16 * wave + (lane >> 2);
-    bsrc = it.b + (size_t)b_row(it, r) * (K / 2) + (((lane & 3) ^ ns_swz(r)) << 4);
+    bsrc = it.b + (size_t)b_row(it, r) * (K / 2) + ((lane & 3) << 4);
     const int rs = 32 * (wave & 3) + (lane >> 1);
     bsrc_s = it.b_sf + (size_t)b_row(it, rs) * (K / 16) + (lane & 1) * 4;
   };
@@ -206,21 +214,23 @@ __global__ __launch_bounds__(ns::THREADS) void k_gemm_nvfp4_stream(const typenam
     issue_b();
   }
 
-  // The weight step is decoded once per workgroup into fp16 (thread t: row t / 4, 16-byte
-  // code chunk t % 4), one step ahead of its use; row r's 16-byte fp16 chunk c (K 8c ..
-  // 8c + 7 in the permuted order of the activation side) sits at chunk c ^ (r & 15).
+  // The weight step is decoded once per workgroup into fp16, one step ahead of its use.
+  // Wave w takes rows 16 w .. 16 w + 15, lane l row 16 w + (l & 7) + 8 (l >> 5) and
+  // 16-byte code chunk cq = (l >> 3) & 3, so that 8 consecutive lanes write 8 rows of one
+  // chunk column; row r's fp16 chunk c (K 8c .. 8c + 7 in the permuted order of the
+  // activation side) sits at slot c ^ sigma(r).
   int d_st = 0;  // raw stage of the next weight step to decode
   auto decode_b = [&](int buf) {
     const uint8_t* st = ringB + d_st * B_STAGE;
-    const int r = tid >> 2, cq = tid & 3;
-    const u32x4_t raw = *(const u32x4_t*)(st + r * 64 + ((cq ^ ns_swz(r)) << 4));
+    const int r = 16 * wave + (lane & 7) + 8 * (lane >> 5), cq = (lane >> 3) & 3;
+    const u32x4_t raw = *(const u32x4_t*)(st + r * 64 + (cq << 4));
     const uint32_t sb = *(const uint16_t*)(st + B_CODE + r * 8 + 2 * cq);
     const half2_t s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sb, 1.0f, false);
     const half2_t s0 = half2_t{s01[0], s01[0]}, s1 = half2_t{s01[1], s01[1]};
     _Float16* row = bdec[buf] + r * BK;
 #pragma unroll
     for (int ks = 0; ks < 4; ks++)
-      *(half8_t*)(row + ((((4 * cq + ks) ^ (r & 15))) << 3)) = decode8_e2m1_f16(raw[ks], ks < 2 ? s0 : s1);
+      *(half8_t*)(row + (((4 * cq + ks) ^ ns_sigma(r)) << 3)) = decode8_e2m1_f16(raw[ks], ks < 2 ? s0 : s1);
     d_st = d_st + 1 == SB ? 0 : d_st + 1;
   };
   // B(0) is followed by DB - 2 weight steps, A(0) and B(DB - 1): allowing only the weight
@@ -265,7 +275,7 @@ __global__ __launch_bounds__(ns::THREADS) void k_gemm_nvfp4_stream(const typenam
       for (int i = 0; i < 4; i++) {
         if (cit.m0 + 16 * wm + 64 * i >= cit.mm) break;
         const int r = 16 * wm + 64 * i + rr;
-        araw[i] = *(const u32x4_t*)(As + r * 64 + ((q ^ ns_swz(r)) << 4));
+        araw[i] = *(const u32x4_t*)(As + r * 64 + ((q ^ ns_swz_a(r)) << 4));
         asc[i] = *(const uint16_t*)(As + A_CODE + r * 8 + 2 * q);
       }
       half2_t as2[4][2];
@@ -283,7 +293,7 @@ __global__ __launch_bounds__(ns::THREADS) void k_gemm_nvfp4_stream(const typenam
 #pragma unroll
         for (int n = 0; n < 4; n++) {
           const int r = (SWIGLU ? (n < 2 ? 32 * wn + 16 * n : BN / 2 + 32 * wn + 16 * (n - 2)) : 64 * wn + 16 * n) + rr;
-          bf[n] = *(const half8_t*)(Bd + r * BK + (((4 * q + ks) ^ rr) << 3));
+          bf[n] = *(const half8_t*)(Bd + r * BK + (((4 * q + ks) ^ ns_sigma(rr)) << 3));
         }
 #pragma unroll
         for (int i = 0; i < 4; i++) {
