@@ -63,6 +63,7 @@ def _lib():
         "orc_gemm_nvfp4_masked": (None, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _P]),
         "orc_gemm_fp8_block": (None, [_P, _P, _P, _I, _P, _P, _I, _I, _P, _P]),
         "orc_gemm_dense_fp8w": (None, [_P, _I, _P, _P, _I, _I, _P, _P]),
+        "orc_gemv_nvfp4_w4a16": (None, [_P, _I, _P, _P, _I, _I, _D, _P, _P]),
         "orc_quantize_nvfp4": (None, [_P, _L, _I, _F, _P, _P]),
         "orc_route_noaux": (None, [_P, _P, _I, _I, _I, _I, _I, _F, _P, _P]),
         "orc_dispatch": (None, [_P, _I, _I, _I, _I, _P, _P]),
@@ -200,6 +201,20 @@ def gemm_dense_fp8w(a, qb, sb):
     y = np.empty((M, N))
     s = np.empty((M, N))
     lib.orc_gemm_dense_fp8w(_p(a), M, _p(qb), _p(sb), N, K, _p(y), _p(s))
+    return y, s
+
+
+def gemv_nvfp4_w4a16(x_bits, w, w_sf, g):
+    """bf16 activations (bits, [M, K]) times NVFP4 weights (codes [N, K/2], scales
+    [N, K/16]) with W's global scale g: y[m, n] = g * sum_k x[m, k] * dec(W)[n, k] and
+    s = |g| * sum_k |x * dec(W)|, both fp64 [M, N]."""
+    lib = _lib()
+    x_bits = _c(x_bits, np.uint16); w = _c(w, np.uint8); w_sf = _c(w_sf, np.uint8)
+    M, K = x_bits.shape
+    N = w.shape[0]
+    y = np.empty((M, N))
+    s = np.empty((M, N))
+    lib.orc_gemv_nvfp4_w4a16(_p(x_bits), M, _p(w), _p(w_sf), N, K, float(g), _p(y), _p(s))
     return y, s
 
 

@@ -251,6 +251,27 @@ void orc_gemm_dense_fp8w(const double* a, int M, const uint8_t* qb, const float*
   }
 }
 
+/* NVFP4-weight x bf16-activation GEMV (W4A16, the nvfp4_gemv row of the Helion
+ * pretuned-kernel table):
+ *   y[m,n] = g * sum_k bf16(x[m,k]) * dec(W)[n,k],  s[m,n] = |g| * sum_k |bf16(x) * dec(W)|
+ * x: bf16 bits [M, K]; W: NVFP4 codes [N, K/2], scales [N, K/16]; g: W's global
+ * dequantization scale.  fp64, unrounded. */
+void orc_gemv_nvfp4_w4a16(const uint16_t* x, int M, const uint8_t* w, const uint8_t* w_sf, int N, int K,
+                          double g, double* y, double* s) {
+#pragma omp parallel for schedule(static)
+  for (long i = 0; i < (long)M * N; i++) {
+    long m = i / N, n = i % N;
+    double acc = 0.0, accabs = 0.0;
+    for (int k = 0; k < K; k++) {
+      double p = orc_bf16_value(x[m * K + k]) * nvfp4_elem(w, w_sf, K, n, k);
+      acc += p;
+      accabs += fabs(p);
+    }
+    y[i] = g * acc;
+    if (s) s[i] = fabs(g) * accabs;
+  }
+}
+
 /* ------------------------------------------------------------------------ */
 /* NVFP4 quantizer (reading: block scale = e4m3(amax / (6 g)), block dequant   */
 /* scale d = scale * g, code = e2m1(x * (1/d)); every step an fp32 operation   */

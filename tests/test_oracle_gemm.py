@@ -236,3 +236,71 @@ def test_swiglu_closed_forms():
     # gate/up swap must change the result
     h2 = oracle.swiglu(np.concatenate([gu[:, I:], gu[:, :I]], axis=1), I)
     assert not np.array_equal(h, h2)
+
+
+# ----------------------------------------------------------------------------- W4A16 GEMV
+def _frac_bf16(bits):
+    s, e, m = (bits >> 15) & 1, (bits >> 7) & 0xFF, bits & 0x7F
+    v = Fraction(m, 128) * Fraction(2) ** -126 if e == 0 else Fraction(128 + m, 128) * Fraction(2) ** (e - 127)
+    return -v if s else v
+
+
+def _random_bf16_bits(rng, shape):
+    # finite values over a wide exponent range, subnormals included, no NaN / inf
+    e = rng.integers(0, 200, shape).astype(np.uint16)
+    m = rng.integers(0, 128, shape).astype(np.uint16)
+    s = rng.integers(0, 2, shape).astype(np.uint16)
+    return (s << 15) | (e << 7) | m
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 3, 32), (2, 4, 64)])
+def test_gemv_w4a16_bruteforce_exact(M, N, K):
+    rng = np.random.default_rng(M * 1000 + K)
+    x = _random_bf16_bits(rng, (M, K))
+    x[:, : K // 2] = (x[:, : K // 2] & 0x807F) | (rng.integers(120, 135, (M, K // 2)).astype(np.uint16) << 7)
+    w = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    w_sf = rng.integers(0, 0x7F, (N, K // 16), dtype=np.uint8)
+    w_sf[:, 0] |= 0x80  # a negative scale per row
+    g = -0.375
+    y, s = oracle.gemv_nvfp4_w4a16(x, w, w_sf, g)
+    for n in range(N):
+        wr = _frac_decode_row(w[n], w_sf[n], K)
+        for m in range(M):
+            prods = [_frac_bf16(int(x[m, k])) * wr[k] for k in range(K)]
+            exact = Fraction(g) * sum(prods)
+            exact_abs = abs(Fraction(g)) * sum(abs(p) for p in prods)
+            bound = K * 2.0 ** -52 * float(exact_abs)
+            assert abs(y[m, n] - float(exact)) <= bound, (m, n)
+            assert abs(s[m, n] - float(exact_abs)) <= bound, (m, n)
+
+
+def test_gemv_w4a16_single_element_closed_form():
+    # x is zero except x[0, k0] = -1.5: y[0, n] = g * (-1.5) * e2m1(code[n, k0]) * e4m3(sf[n, k0 / 16])
+    rng = np.random.default_rng(7)
+    N, K, k0, g = 6, 96, 37, 0.25
+    x = np.zeros((1, K), np.uint16)
+    x[0, k0] = 0xBFC0
+    w = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    w_sf = rng.integers(0, 0x7F, (N, K // 16), dtype=np.uint8)
+    y, s = oracle.gemv_nvfp4_w4a16(x, w, w_sf, g)
+    for n in range(N):
+        code = (int(w[n, k0 // 2]) >> 4) & 15  # k0 odd: high nibble
+        want = float(Fraction(g) * Fraction(-3, 2) * _frac_e2m1(code) * _frac_e4m3(int(w_sf[n, k0 // 16])))
+        assert y[0, n] == want and s[0, n] == abs(want)
+
+
+def test_gemv_w4a16_equals_w4a4_on_nvfp4_activations():
+    # activations that are exactly NVFP4 values (e2m1 * e4m3 has at most 6 significant bits,
+    # so bf16 holds them): the W4A16 GEMV equals the NVFP4 x NVFP4 row dot
+    rng = np.random.default_rng(11)
+    N, K = 9, 256
+    a = rng.integers(0, 256, (1, K // 2), dtype=np.uint8)
+    a_sf = rng.integers(0x28, 0x48, (1, K // 16), dtype=np.uint8)
+    w = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    w_sf = rng.integers(0, 0x7F, (N, K // 16), dtype=np.uint8)
+    xa = oracle.nvfp4_decode(a, a_sf)
+    x_bits = oracle.bf16_bits(xa)
+    assert np.array_equal(oracle.bf16_value(x_bits), xa)
+    y, s = oracle.gemv_nvfp4_w4a16(x_bits, w, w_sf, 0.5)
+    y4, s4 = oracle.nvfp4_row_dot(a, a_sf, 0, w, w_sf, K, alpha=0.5)
+    assert np.allclose(y[0], y4, rtol=1e-13, atol=1e-12) and np.allclose(s[0], s4, rtol=1e-13)
