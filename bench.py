@@ -322,6 +322,40 @@ def bench_hetero(dev, steps, warmup, seed=1002):
                 mfma_dtype="fp16", config=dict(workload=wl.name))
 
 
+GEMV_SHAPES = ((4096, 4096), (14336, 4096), (4096, 14336), (128256, 4096))  # Llama-3-8B (N, K): q/o, gate/up, down, LM head
+
+
+def bench_gemv_w4a16(dev, steps, warmup, seed=1005, M=1):
+    """NVFP4-weight x bf16-activation decode GEMV at batch M over Llama-3-8B (N, K) shapes,
+    each timed on its own; the row reports their total bytes over their total time."""
+    per = []
+    byts_all, ms_all, kms_all, flops_all = 0, 0.0, 0.0, 0.0
+    for i, (N, K) in enumerate(GEMV_SHAPES):
+        wl = datagen.gemv_w4a16_workload(seed + i, dev, M=M, N=N, K=K)
+        t, g_w = wl.tensors, wl.scalars["g_w"]
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+
+        def step(kt):
+            if kt:
+                kt.start()
+            mxg.mx_gemv_nvfp4_w4a16(t["x"], t["w"], t["w_sf"], g_w, out=out)
+            if kt:
+                kt.stop()
+
+        ms, kms, wall = timed_loop(step, steps, warmup)
+        byts = N * NVFP4_ROW_BYTES(K) + M * K * 2 + M * N * 2
+        per.append(dict(N=N, K=K, us=round(kms * 1e3, 2), gbs=round(byts / kms / 1e6, 1)))
+        byts_all += byts
+        ms_all += ms
+        kms_all += kms
+        flops_all += 2.0 * M * N * K
+        del t, out
+    return dict(name=f"gemv_w4a16_llama3_8b_m{M}", ms=ms_all, kernel_ms=kms_all, wall_s=0.0, bytes=byts_all,
+                kernel_bytes=byts_all, flops=flops_all, gbs=byts_all / ms_all / 1e6,
+                kernel_gbs=byts_all / kms_all / 1e6, tflops=flops_all / ms_all / 1e9, bound="hbm",
+                mfma_dtype="fp16", config=dict(workload=f"gemv_w4a16_llama3_8b_m{M}", M=M, shapes=per))
+
+
 def _moe_setup(dev, t, T, E=256, top_k=8):
     ids, w = mxg.moe_route_noaux(t["logits"], t["bias"], 8, 4, top_k, 2.5)
     mm_full, _ = mxg.moe_dispatch(ids, E, 1 << 20)
@@ -384,6 +418,7 @@ WORKLOADS = {
     "moe_fp8": lambda dev, k, w, cpu: bench_moe(dev, k, w, "fp8", 4096, 1003),
     "moe_nvfp4_decode": lambda dev, k, w, cpu: bench_moe(dev, k, w, "nvfp4", 64, 1004),
     "moe_nvfp4_prefill": lambda dev, k, w, cpu: bench_moe(dev, k, w, "nvfp4", 8192, 1004),
+    "gemv_w4a16": lambda dev, k, w, cpu: bench_gemv_w4a16(dev, k, w),
 }
 
 
@@ -442,6 +477,7 @@ def main():
                 continue
             q = fn(dev, max(5, args.steps // 5), 2, False)
             rows.append({k: q[k] for k in ("name", "ms", "kernel_ms", "gbs", "tflops") if k in q} |
+                        ({"shapes": q["config"]["shapes"]} if "shapes" in q["config"] else {}) |
                         ({"tokens_per_s": q["tokens_per_s"]} if "tokens_per_s" in q else {}) |
                         {"roofline": roofline_row(q)})
             torch.cuda.empty_cache()

@@ -151,6 +151,15 @@ def decode_gemm1_workload(seed, device, E=256, T=8, top_k=8, H=7168, I=2048, g_w
                     dict(E=E, T=T, top_k=top_k, H=H, N=2 * I, g_x=g_x, g_w=g_w))
 
 
+def gemv_w4a16_workload(seed, device, M=1, N=4096, K=4096, g_w=0.25):
+    """Decode GEMV with NVFP4 weights and bf16 activations (the nvfp4_gemv W4A16 case):
+    x [M, K] bf16 ~ N(0, 1), W codes [N, K/2] uniform bytes, scales 2^U{-4..4}."""
+    gen = generator(seed, device)
+    x = bf16_normal(gen, (M, K), device)
+    w, w_sf = nvfp4_uniform(gen, (N,), K, device)
+    return Workload(f"gemv_w4a16_m{M}_n{N}_k{K}", dict(x=x, w=w, w_sf=w_sf), dict(M=M, N=N, K=K, g_w=g_w))
+
+
 def router_inputs(gen, T, E, device):
     logits = f32_normal(gen, (T, E), device)
     bias = f32_normal(gen, (E,), device, std=0.01)

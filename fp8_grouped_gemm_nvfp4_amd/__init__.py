@@ -54,6 +54,7 @@ SIGNATURES = {
     "mxg_version": (_I, []),
     "mx_grouped_gemm_masked": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _P]),
     "mx_grouped_gemm": (_I, [_P, _I, _I, _I, _I, _I, _I, _P]),
+    "mx_gemv_nvfp4_w4a16": (_I, [_P, _I, _I, _P, _P, _F, _P, _I, _I, _I, _P]),
     "mx_quantize_nvfp4": (_I, [_P, _I, _L, _I, _F, _P, _P, _P]),
     "moe_route_noaux": (_I, [_P, _P, _I, _I, _I, _I, _I, _F, _P, _P, _P]),
     "moe_dispatch": (_I, [_P, _I, _I, _I, _I, _P, _P, _P]),
@@ -125,6 +126,19 @@ def mx_grouped_gemm(groups, out_dtype=torch.bfloat16, cu_limit=0, stream=None):
                            _ptr(g["a"]), _ptr(g["a_sf"]), _ptr(g["b"]), _ptr(g["b_sf"]), _ptr(g["out"]))
     c_dtype = {torch.bfloat16: MXG_BF16, torch.float32: MXG_F32}.get(out_dtype, 0)
     _check(lib().mx_grouped_gemm(arr, G, MXG_E2M1, MXG_E4M3, c_dtype, 16, cu_limit, _stream(stream)))
+
+
+def mx_gemv_nvfp4_w4a16(x, w, w_sf, g_w, out=None, out_dtype=torch.bfloat16, cu_limit=0, stream=None):
+    """NVFP4-weight x bf16-activation GEMV: x [M, K] bf16, w [N, K/2] u8, w_sf [N, K/16] u8,
+    g_w the weights' global scale; returns out [M, N] (bf16 or f32)."""
+    M, K = x.shape
+    N = w.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    c_dtype = {torch.bfloat16: MXG_BF16, torch.float32: MXG_F32}.get(out.dtype, 0)
+    _check(lib().mx_gemv_nvfp4_w4a16(_ptr(x), M, K, _ptr(w), _ptr(w_sf), float(g_w), _ptr(out), N, c_dtype,
+                                     cu_limit, _stream(stream)))
+    return out
 
 
 def mx_quantize_nvfp4(x, g, codes=None, sf=None, stream=None):

@@ -119,6 +119,25 @@ int mx_grouped_gemm(const mxg_group_desc* groups, int G, int ab_dtype, int sf_dt
                     "mx_grouped_gemm launch");
 }
 
+int mx_gemv_nvfp4_w4a16(const void* x, int M, int K, const uint8_t* w, const uint8_t* w_sf, float g_w,
+                        void* out, int N, int c_dtype, int cu_limit, void* stream) {
+  if (!x || !w || !w_sf || !out) return fail(MXG_ERR_INVALID_ARG, "mx_gemv_nvfp4_w4a16: null pointer");
+  if (M < 1 || K < 1 || N < 1 || cu_limit < 0)
+    return fail(MXG_ERR_INVALID_ARG, "mx_gemv_nvfp4_w4a16: bad sizes M=%d K=%d N=%d", M, K, N);
+  if (c_dtype != MXG_BF16 && c_dtype != MXG_F32)
+    return fail(MXG_ERR_UNSUPPORTED, "mx_gemv_nvfp4_w4a16: c_dtype must be BF16 or F32 (got %d)", c_dtype);
+  if (M > mxg::GEMV_MAX_M || (long long)M * K > mxg::GEMV_MAX_MK || K % 1024 != 0)
+    return fail(MXG_ERR_UNSUPPORTED, "mx_gemv_nvfp4_w4a16: needs M <= %d, M * K <= %d, K %% 1024 == 0 (M=%d K=%d)",
+                mxg::GEMV_MAX_M, mxg::GEMV_MAX_MK, M, K);
+  if (!aligned16(x) || !aligned16(w) || !aligned16(w_sf) || !aligned16(out))
+    return fail(MXG_ERR_INVALID_ARG, "mx_gemv_nvfp4_w4a16: misaligned pointer");
+  mxg::GemvArgs p{};
+  p.x = (const uint16_t*)x; p.w = w; p.w_sf = w_sf; p.out = out; p.g_w = g_w;
+  p.M = M; p.K = K; p.N = N;
+  int epi = c_dtype == MXG_BF16 ? mxg::EPI_BF16 : mxg::EPI_F32;
+  return hip_status(mxg::gemv_nvfp4_w4a16(p, epi, cu_limit, (hipStream_t)stream), "mx_gemv_nvfp4_w4a16 launch");
+}
+
 int mx_quantize_nvfp4(const void* x, int x_dtype, long rows, int K, float g, uint8_t* codes,
                       uint8_t* sf, void* stream) {
   if (!x || !codes || !sf) return fail(MXG_ERR_INVALID_ARG, "mx_quantize_nvfp4: null pointer");

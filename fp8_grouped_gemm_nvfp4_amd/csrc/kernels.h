@@ -87,6 +87,21 @@ constexpr int fp8_scale_stride(int max_m) { return (max_m + 3) / 4 * 4; }
 hipError_t gemm_fp8_swiglu(Fp8GemmArgs p, int cu_limit, hipStream_t s);
 hipError_t gemm_bf16_fp8w(Fp8GemmArgs p, int cu_limit, hipStream_t s);
 
+// NVFP4-weight x bf16-activation GEMV (W4A16) for decode batches: out[m, n] = g_w *
+// sum_k x[m, k] * dec(W)[n, k].  hipErrorNotSupported (nothing launched) unless
+// 1 <= M <= GEMV_MAX_M, M * K <= GEMV_MAX_MK and K % 1024 == 0.
+constexpr int GEMV_MAX_M = 4;
+constexpr int GEMV_MAX_MK = 32768;  // fp16 activation elements held in LDS
+struct GemvArgs {
+  const uint16_t* x;    // bf16 [M, K]
+  const uint8_t* w;     // NVFP4 codes [N, K/2]
+  const uint8_t* w_sf;  // e4m3 scales [N, K/16]
+  void* out;            // [M, N] bf16 or fp32
+  float g_w;
+  int M, K, N;
+};
+hipError_t gemv_nvfp4_w4a16(GemvArgs p, int epi, int cu_limit, hipStream_t s);
+
 // Quantization, routing, dispatch, gather and combine.
 hipError_t quantize_nvfp4(const void* x, int x_dtype, long rows, int K, float g, uint8_t* codes,
                           uint8_t* sf, hipStream_t s);

@@ -109,6 +109,27 @@ int mx_grouped_gemm(const mxg_group_desc* groups, int G, int ab_dtype, int sf_dt
                     int c_dtype, int sf_vec_size, int cu_limit, void* stream);
 
 /*
+ * NVFP4-weight x bf16-activation GEMV for decode batches (W4A16).
+ * Source: "Helion Pretuned Kernels" README, kernel table row nvfp4_gemv (NVFP4
+ * decode GEMV at M = 1, W4A4 and W4A16 variants, Llama-3 / Qwen (N, K) shapes);
+ * single-stream decode in "The CuteDSL Gamble".
+ *
+ *   out[m, n] = g_w * sum_k x[m, k] * dec(W)[n, k]   for m < M, n < N, fp32 sums
+ *
+ *   x          device bf16 [M, K], row stride K
+ *   w, w_sf    device NVFP4 weight codes [N, K/2], e4m3 scales [N, K/16]
+ *   g_w        host fp32 global dequantization scale of W
+ *   out        device [M, N] of c_dtype (MXG_BF16, round to nearest even, or MXG_F32)
+ *   cu_limit   as in mx_grouped_gemm_masked
+ * Requirements: 1 <= M <= 4, M * K <= 32768 and K % 1024 == 0 (else
+ * MXG_ERR_UNSUPPORTED); N >= 1.  The activations are used as fp16 after
+ * scaling each row by a power of two chosen from its largest magnitude, which
+ * is exact for every element at least 2^-28 times that magnitude.
+ */
+int mx_gemv_nvfp4_w4a16(const void* x, int M, int K, const uint8_t* w, const uint8_t* w_sf, float g_w,
+                        void* out, int N, int c_dtype, int cu_limit, void* stream);
+
+/*
  * NVFP4 quantization of rows of x [rows, K] (x_dtype MXG_BF16 or MXG_F32,
  * device) with global dequantization scale g > 0 (host fp32).  Per 16-element
  * block, in fp32 with round-to-nearest at every step:

@@ -26,7 +26,7 @@ def _declared_functions():
 
 def test_header_lists_entry_points():
     names = _declared_functions()
-    for want in ["mx_grouped_gemm_masked", "mx_grouped_gemm", "mx_quantize_nvfp4", "moe_route_noaux",
+    for want in ["mx_grouped_gemm_masked", "mx_grouped_gemm", "mx_gemv_nvfp4_w4a16", "mx_quantize_nvfp4", "moe_route_noaux",
                  "moe_dispatch", "moe_quantize_gather_nvfp4", "moe_expert_forward",
                  "moe_expert_forward_workspace_size", "moe_expert_forward_workspace_layout",
                  "mxg_status_string", "mxg_last_error", "mxg_version"]:
@@ -91,6 +91,19 @@ def test_hetero_rejects():
     arr[1] = mxg.GroupDesc(16, 256, 1024, 100, 1.0, FAKE, FAKE, FAKE, FAKE, FAKE)
     assert L.mx_grouped_gemm(arr, 2, 1, 2, 3, 16, 0, None) == mxg.MXG_ERR_INVALID_ARG  # ldc < N
     assert L.mx_grouped_gemm(None, 1, 1, 2, 3, 16, 0, None) == mxg.MXG_ERR_INVALID_ARG
+
+
+def test_gemv_w4a16_rejects():
+    L = mxg.lib()
+    args = dict(x=FAKE, M=1, K=4096, w=FAKE, w_sf=FAKE, g=0.5, out=FAKE, N=4096, c=mxg.MXG_BF16, cu=0, s=None)
+    for kw, status in [(dict(x=None), mxg.MXG_ERR_INVALID_ARG), (dict(M=0), mxg.MXG_ERR_INVALID_ARG),
+                       (dict(N=0), mxg.MXG_ERR_INVALID_ARG), (dict(M=5), mxg.MXG_ERR_UNSUPPORTED),
+                       (dict(K=4000), mxg.MXG_ERR_UNSUPPORTED), (dict(M=3, K=16384), mxg.MXG_ERR_UNSUPPORTED),
+                       (dict(c=mxg.MXG_E2M1), mxg.MXG_ERR_UNSUPPORTED), (dict(cu=-1), mxg.MXG_ERR_INVALID_ARG),
+                       (dict(out=P((1 << 20) + 4)), mxg.MXG_ERR_INVALID_ARG)]:
+        a = dict(args, **kw)
+        assert L.mx_gemv_nvfp4_w4a16(*a.values()) == status, kw
+        assert L.mxg_last_error().decode() != ""
 
 
 def test_route_dispatch_quant_reject():
