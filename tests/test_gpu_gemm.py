@@ -141,6 +141,25 @@ def test_masked_gemm_cu_limit_and_determinism():
     _check_masked(wl.tensors, o2, 16, 384, 1024, "cu_limit skinny")
 
 
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_masked_gemm_decode_many_groups(out_dtype):
+    """Row capacity 8 with 256 groups (valid rows 0..8), an N tail inside a 16-column
+    group, and the same bits whatever the grid."""
+    G, max_m, N, K = 256, 8, 1048, 2048
+    log(f"masked NVFP4 GEMM decode shape, many groups G={G} max_m={max_m} N={N} K={K} {out_dtype}")
+    gen = torch.Generator().manual_seed(77)
+    mm = torch.randint(0, max_m + 1, (G,), generator=gen).to(torch.int32)
+    mm[:4] = torch.tensor([8, 4, 5, 0], dtype=torch.int32)
+    wl = datagen.masked_gemm_workload(1077, DEV, G=G, max_m=max_m, N=N, K=K, masked_m=mm.tolist())
+    outs = []
+    for cu in (0, 3):
+        out = _run_masked(wl.tensors, max_m, N, out_dtype=out_dtype, cu_limit=cu)
+        outs.append(out)
+        _check_masked(wl.tensors, out, max_m, N, K, f"decode many groups cu_limit={cu}")
+    v = [np_(o.view(torch.int16 if out_dtype == torch.bfloat16 else torch.int32)) for o in outs]
+    assert np.array_equal(v[0], v[1]), "result depends on the grid"
+
+
 def test_decode_gemm1_full_size():
     """Decode-shaped MoE GEMM1 at its full size: 256 experts, 8 tokens top-8, K=7168,
     N=4096 (gate and up stacked): dispatch, on-the-fly NVFP4 quantization of the bf16
