@@ -367,15 +367,17 @@ def _moe_setup(dev, t, T, E=256, top_k=8):
 
 def bench_moe(dev, steps, warmup, precision, T, seed):
     E, H, I, top_k = 256, 7168, 2048, 8
-    if precision == "fp8":
+    fp8 = precision in ("fp8", "fp8_f32h")
+    if fp8:
         wl = datagen.moe_fp8_workload(seed, dev, T=T)
     else:
         wl = datagen.moe_nvfp4_workload(seed, dev, T=T)
     t, s = wl.tensors, wl.scalars
     ids, w, masked_m, row, cap = _moe_setup(dev, t, T)
     y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
-    if precision == "fp8":
-        d = mxg.make_moe_desc(mxg.MXG_MOE_FP8_BLOCK128, T, H, I, E, top_k, cap, t["xq"], t["w13"], t["w13_s"],
+    if fp8:
+        code = mxg.MXG_MOE_FP8_BLOCK128 if precision == "fp8" else mxg.MXG_MOE_FP8_BLOCK128_F32H
+        d = mxg.make_moe_desc(code, T, H, I, E, top_k, cap, t["xq"], t["w13"], t["w13_s"],
                               t["w2"], t["w2_s"], ids, w, masked_m, row, y, x_scale=t["xs"])
     else:
         d = mxg.make_moe_desc(mxg.MXG_MOE_NVFP4, T, H, I, E, top_k, cap, t["x"], t["w13"], t["w13_sf"],
@@ -395,7 +397,7 @@ def bench_moe(dev, steps, warmup, precision, T, seed):
     ms, kms, wall = timed_loop(step, steps, warmup)
     mm = masked_m.cpu().numpy()
     n_act, rows = int((mm > 0).sum()), int(mm.sum())
-    if precision == "fp8":
+    if fp8:
         wbytes = n_act * (2 * I * H + H * I) + n_act * ((2 * I // 128) * (H // 128) + (H // 128) * (I // 128)) * 4
         xbytes = T * H + T * (H // 128) * 4
     else:
@@ -403,8 +405,10 @@ def bench_moe(dev, steps, warmup, precision, T, seed):
         xbytes = T * H * 2
     byts = wbytes + xbytes + T * E * 4 + T * H * 2
     flops = 2.0 * rows * (2 * I * H + H * I)
-    # the FP8 GEMMs run on the fp8 MFMA, the exact NVFP4 decode on the fp16 MFMA
-    mfma_dtype = "fp8" if precision == "fp8" else "fp16"
+    # the FP8 GEMMs run on the fp8 MFMA, the exact NVFP4 decode on the fp16 MFMA (the
+    # full-precision-intermediate variant's GEMM2 runs twice on the bf16 MFMA; its
+    # algorithmic bytes and FLOPs are the layer's, as for the bf16 intermediate)
+    mfma_dtype = "fp8" if fp8 else "fp16"
     return dict(name=wl.name, ms=ms, kernel_ms=kms, wall_s=wall, bytes=byts, flops=flops,
                 gbs=byts / ms / 1e6, tflops=flops / ms / 1e9, tokens_per_s=T / ms * 1e3,
                 bound=binding_roof(byts, flops, mfma_dtype), mfma_dtype=mfma_dtype,
@@ -416,6 +420,7 @@ WORKLOADS = {
     "masked_c0": lambda dev, k, w, cpu: bench_masked_c0(dev, k, w),
     "hetero": lambda dev, k, w, cpu: bench_hetero(dev, k, w),
     "moe_fp8": lambda dev, k, w, cpu: bench_moe(dev, k, w, "fp8", 4096, 1003),
+    "moe_fp8_f32h": lambda dev, k, w, cpu: bench_moe(dev, k, w, "fp8_f32h", 4096, 1003),
     "moe_nvfp4_decode": lambda dev, k, w, cpu: bench_moe(dev, k, w, "nvfp4", 64, 1004),
     "moe_nvfp4_prefill": lambda dev, k, w, cpu: bench_moe(dev, k, w, "nvfp4", 8192, 1004),
     "gemv_w4a16": lambda dev, k, w, cpu: bench_gemv_w4a16(dev, k, w),

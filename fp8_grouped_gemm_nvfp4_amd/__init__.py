@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libmxg.so")
 
 MXG_OK, MXG_ERR_INVALID_ARG, MXG_ERR_UNSUPPORTED, MXG_ERR_WORKSPACE, MXG_ERR_HIP = range(5)
 MXG_E2M1, MXG_E4M3, MXG_BF16, MXG_F32 = 1, 2, 3, 4
-MXG_MOE_FP8_BLOCK128, MXG_MOE_NVFP4 = 1, 2
+MXG_MOE_FP8_BLOCK128, MXG_MOE_NVFP4, MXG_MOE_FP8_BLOCK128_F32H = 1, 2, 3
 MXG_MAX_GROUPS = 32
 
 

@@ -204,19 +204,21 @@ int moe_quantize_gather_nvfp4(const uint16_t* x, int T, int H, float g_x, const 
 // ----------------------------------------------------------------------------- MoE layer
 static int check_moe(const mxg_moe_desc* d) {
   if (!d) return fail(MXG_ERR_INVALID_ARG, "moe_expert_forward: null descriptor");
-  if (d->precision != MXG_MOE_FP8_BLOCK128 && d->precision != MXG_MOE_NVFP4)
+  if (d->precision != MXG_MOE_FP8_BLOCK128 && d->precision != MXG_MOE_NVFP4 &&
+      d->precision != MXG_MOE_FP8_BLOCK128_F32H)
     return fail(MXG_ERR_UNSUPPORTED, "moe_expert_forward: unknown precision %d", d->precision);
+  const bool fp8 = d->precision != MXG_MOE_NVFP4;
   if (d->T < 0 || d->H < 128 || d->I < 128 || d->E < 1 || d->top_k < 1 || d->max_m < 1)
     return fail(MXG_ERR_INVALID_ARG, "moe_expert_forward: bad sizes");
   if (d->H % 128 || d->I % 128)
     return fail(MXG_ERR_UNSUPPORTED, "moe_expert_forward: H and I must be multiples of 128");
   if (d->top_k > 8) return fail(MXG_ERR_UNSUPPORTED, "moe_expert_forward: top_k > 8");
-  if (d->precision == MXG_MOE_FP8_BLOCK128 && d->E > 1024)
+  if (fp8 && d->E > 1024)
     return fail(MXG_ERR_UNSUPPORTED, "moe_expert_forward: FP8 takes at most 1024 experts");
   if (!d->x || !d->w13 || !d->w13_scale || !d->w2 || !d->w2_scale || !d->topk_ids || !d->topk_w ||
       !d->masked_m || !d->row || !d->y)
     return fail(MXG_ERR_INVALID_ARG, "moe_expert_forward: null pointer");
-  if (d->precision == MXG_MOE_FP8_BLOCK128 && !d->x_scale)
+  if (fp8 && !d->x_scale)
     return fail(MXG_ERR_INVALID_ARG, "moe_expert_forward: FP8 needs x_scale");
   if (d->precision == MXG_MOE_NVFP4) {
     if (!d->g_w13 || !d->g_w2) return fail(MXG_ERR_INVALID_ARG, "moe_expert_forward: NVFP4 needs g_w13/g_w2");
@@ -234,10 +236,11 @@ int moe_expert_forward_workspace_layout(const mxg_moe_desc* d, size_t* off) {
   if (!off) return fail(MXG_ERR_INVALID_ARG, "moe_expert_forward_workspace_layout: null output");
   size_t rows = (size_t)d->E * d->max_m;
   size_t sz[5];
-  if (d->precision == MXG_MOE_FP8_BLOCK128) {
+  if (d->precision != MXG_MOE_NVFP4) {
+    const size_t planes = d->precision == MXG_MOE_FP8_BLOCK128_F32H ? 2 : 1;
     sz[0] = rows * d->H;                     // e4m3 activations
     sz[1] = (size_t)d->E * (d->H / 128) * mxg::fp8_scale_stride(d->max_m) * 4;  // fp32 1x128 scales
-    sz[2] = (rows + 1) * d->I * 2;           // bf16 h, plus one row that masked rows' stores land in
+    sz[2] = (rows + 1) * d->I * 2 * planes;  // bf16 h (hi, lo), plus one row that masked rows' stores land in
     sz[3] = 0;
   } else {
     sz[0] = rows * (d->H / 2);
@@ -274,7 +277,8 @@ int moe_expert_forward(const mxg_moe_desc* d, void* ws, size_t ws_bytes, void* s
   const int E = d->E, H = d->H, I = d->I, T = d->T, k = d->top_k, mm = d->max_m;
   float* o = (float*)(w + off[4]);
   hipError_t e;
-  if (d->precision == MXG_MOE_FP8_BLOCK128) {
+  if (d->precision != MXG_MOE_NVFP4) {
+    const int split = d->precision == MXG_MOE_FP8_BLOCK128_F32H;
     uint8_t* a = w + off[0];
     float* a_s = (float*)(w + off[1]);
     uint16_t* h = (uint16_t*)(w + off[2]);
@@ -284,11 +288,13 @@ int moe_expert_forward(const mxg_moe_desc* d, void* ws, size_t ws_bytes, void* s
     p1.a = a; p1.a_s = a_s; p1.b = d->w13; p1.b_s = (const float*)d->w13_scale; p1.out = h;
     p1.masked_m = d->masked_m; p1.G = E; p1.max_m = mm; p1.N = 2 * I; p1.K = H;
     p1.a_s_stride = mxg::fp8_scale_stride(mm);
+    p1.h_split = split;
     e = mxg::gemm_fp8_swiglu(p1, 0, s);
     if (e != hipSuccess) return hip_status(e, "gemm_fp8_swiglu");
     mxg::Fp8GemmArgs p2{};
     p2.a = (const uint8_t*)h; p2.b = d->w2; p2.b_s = (const float*)d->w2_scale; p2.out = o;
-    p2.masked_m = d->masked_m; p2.G = E; p2.max_m = mm; p2.N = H; p2.K = I;
+    p2.masked_m = d->masked_m; p2.G = E; p2.max_m = mm; p2.N = H; p2.K = split ? 2 * I : I;
+    p2.b_k = I; p2.h_split = split;
     e = mxg::gemm_bf16_fp8w(p2, 0, s);
     if (e != hipSuccess) return hip_status(e, "gemm_bf16_fp8w");
   } else {

@@ -64,7 +64,7 @@ constexpr int wait_count(int da, int db, int ao, int bo) {
 
 __device__ __forceinline__ int f1_swz(int r) { return (r ^ (r >> 3)) & 7; }
 
-template <int DA, int DB>
+template <int DA, int DB, bool SPLIT>
 __global__ __launch_bounds__(f1::THREADS) void k_gemm_fp8_swiglu(const Fp8GemmArgs p) {
   using namespace f1;
   constexpr int SA = DA + 1, SB = DB + 1;
@@ -181,12 +181,16 @@ __global__ __launch_bounds__(f1::THREADS) void k_gemm_fp8_swiglu(const Fp8GemmAr
   // right after its barrier, they sit in the counter just ahead of that step's
   // activation DMA and hold up no wait for a weight DMA issued before them.  Masked rows
   // store into the scratch row after the last expert.
-  uint32_t hw[4][2][2];
+  // With SPLIT, rows are 2I wide: hi = bf16(h) in columns [0, I), lo = bf16(h - hi) in
+  // [I, 2I) (h - hi is exact in fp32, so hi + lo holds h to about 16 significant bits).
+  constexpr int PL = SPLIT ? 2 : 1;
+  const int RS = PL * I;  // h row stride (elements)
+  uint32_t hw[PL][4][2][2];
   bool pend = false;
   StreamItem pit = cit;
   auto store_h = [&]() {
     uint16_t* H = (uint16_t*)p.out;
-    uint16_t* scratch_row = H + (size_t)G * cap * I;
+    uint16_t* scratch_row = H + (size_t)G * cap * RS;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       const int row0 = pit.m0 + 16 * wm + 64 * i + 4 * q;
@@ -194,10 +198,13 @@ __global__ __launch_bounds__(f1::THREADS) void k_gemm_fp8_swiglu(const Fp8GemmAr
       for (int n = 0; n < 2; n++) {
         const int c = (pit.n0 + 32 * wn + 16 * n + rr) & ~1;
         const int ra = row0 + odd, rb = row0 + 2 + odd;
-        uint16_t* pa = ra < pit.mm ? H + ((size_t)pit.g * cap + ra) * I + c : scratch_row + c;
-        uint16_t* pb = rb < pit.mm ? H + ((size_t)pit.g * cap + rb) * I + c : scratch_row + c;
-        *(uint32_t*)pa = hw[i][n][0];
-        *(uint32_t*)pb = hw[i][n][1];
+        uint16_t* pa = ra < pit.mm ? H + ((size_t)pit.g * cap + ra) * RS + c : scratch_row + c;
+        uint16_t* pb = rb < pit.mm ? H + ((size_t)pit.g * cap + rb) * RS + c : scratch_row + c;
+#pragma unroll
+        for (int pl = 0; pl < PL; pl++) {
+          *(uint32_t*)(pa + pl * I) = hw[pl][i][n][0];
+          *(uint32_t*)(pb + pl * I) = hw[pl][i][n][1];
+        }
       }
     }
   };
@@ -270,16 +277,21 @@ __global__ __launch_bounds__(f1::THREADS) void k_gemm_fp8_swiglu(const Fp8GemmAr
         for (int i = 0; i < 4; i++)
 #pragma unroll
           for (int n = 0; n < 2; n++) {
-            uint32_t b[4];
+            uint32_t b[PL][4];
 #pragma unroll
             for (int r = 0; r < 4; r++) {
               const float gt = acc[i][n][r], up = acc[i][n + 2][r];
-              b[r] = f32_to_bf16_rne(gt / (1.0f + expf(-gt)) * up);
+              const float h = gt / (1.0f + expf(-gt)) * up;
+              b[0][r] = f32_to_bf16_rne(h);
+              if constexpr (SPLIT) b[PL - 1][r] = f32_to_bf16_rne(h - __uint_as_float(b[0][r] << 16));
             }
-            const uint32_t y0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)(odd ? b[0] : b[1]), 0xB1, 0xF, 0xF, false);
-            const uint32_t y1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)(odd ? b[2] : b[3]), 0xB1, 0xF, 0xF, false);
-            hw[i][n][0] = odd ? (y0 | (b[1] << 16)) : (b[0] | (y0 << 16));
-            hw[i][n][1] = odd ? (y1 | (b[3] << 16)) : (b[2] | (y1 << 16));
+#pragma unroll
+            for (int pl = 0; pl < PL; pl++) {
+              const uint32_t y0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)(odd ? b[pl][0] : b[pl][1]), 0xB1, 0xF, 0xF, false);
+              const uint32_t y1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)(odd ? b[pl][2] : b[pl][3]), 0xB1, 0xF, 0xF, false);
+              hw[pl][i][n][0] = odd ? (y0 | (b[pl][1] << 16)) : (b[pl][0] | (y0 << 16));
+              hw[pl][i][n][1] = odd ? (y1 | (b[pl][3] << 16)) : (b[pl][2] | (y1 << 16));
+            }
           }
         pend = true;
         pit = cit;
@@ -296,23 +308,24 @@ __global__ __launch_bounds__(f1::THREADS) void k_gemm_fp8_swiglu(const Fp8GemmAr
   wait_vmcnt<0>();  // the trailing re-reads land before the workgroup ends
 }
 
-template <int DA, int DB>
+template <int DA, int DB, bool SPLIT>
 static hipError_t launch_fp8_swiglu(Fp8GemmArgs p, int cu_limit, hipStream_t s) {
   using namespace f1;
   if (p.G > MAX_G || (p.N / 2) % HN != 0 || p.K % BK != 0 || p.a_s_stride % 4 != 0 ||
       p.a_s_stride < p.max_m || p.a_s_stride < 4)
     return hipErrorNotSupported;
   if ((long long)p.G * ((p.max_m + BM - 1) / BM) * ((p.N / 2) / HN) > 0x7FFFFFFFLL) return hipErrorNotSupported;
-  const void* k = (const void*)k_gemm_fp8_swiglu<DA, DB>;
+  const void* k = (const void*)k_gemm_fp8_swiglu<DA, DB, SPLIT>;
   const int grid = resident_grid(k, THREADS, cu_limit);
   if (grid <= 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((k_gemm_fp8_swiglu<DA, DB>), dim3(grid), dim3(THREADS), 0, s, p);
+  hipLaunchKernelGGL((k_gemm_fp8_swiglu<DA, DB, SPLIT>), dim3(grid), dim3(THREADS), 0, s, p);
   return hipGetLastError();
 }
 
 hipError_t gemm_fp8_swiglu(Fp8GemmArgs p, int cu_limit, hipStream_t s) {
   if (p.G <= 0 || p.max_m <= 0 || p.N <= 0 || p.K <= 0) return hipSuccess;
-  return launch_fp8_swiglu<1, MXG_F1_DB>(p, cu_limit, s);
+  return p.h_split ? launch_fp8_swiglu<1, MXG_F1_DB, true>(p, cu_limit, s)
+                   : launch_fp8_swiglu<1, MXG_F1_DB, false>(p, cu_limit, s);
 }
 
 // ----------------------------------------------------------------------------- GEMM2
@@ -383,8 +396,10 @@ __global__ __launch_bounds__(f2::THREADS) void k_gemm_bf16_fp8w(const Fp8GemmArg
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int G = p.G, K = p.K, KB = K / 128, N = p.N, cap = p.max_m;
-  const int tiles_n = N / BN, KT = K / BK;
+  // K is the extent of A (h, or its hi and lo planes side by side); W2's K index wraps
+  // at WK (= K, or I for the two planes)
+  const int G = p.G, K = p.K, WK = p.b_k ? p.b_k : p.K, KB = WK / 128, N = p.N, cap = p.max_m;
+  const int tiles_n = N / BN, KT = K / BK, WKT = WK / BK;
 
   stream_tile_prefix(p.masked_m, p.G, p.max_m, tprefix, mm_s, tid);
   const int total = __builtin_amdgcn_readfirstlane(tprefix[G]) * tiles_n;
@@ -417,7 +432,7 @@ __global__ __launch_bounds__(f2::THREADS) void k_gemm_bf16_fp8w(const Fp8GemmArg
 #pragma unroll
     for (int j = 0; j < B_OPS; j++) {
       const int r = 16 * (B_OPS * wave + j) + (lane >> 2);
-      bsrc[j] = p.b + ((size_t)it.g * N + it.n0 + r) * K + (((lane & 3) ^ f2_swz_b(r)) << 4);
+      bsrc[j] = p.b + ((size_t)it.g * N + it.n0 + r) * WK + (((lane & 3) ^ f2_swz_b(r)) << 4);
     }
     bsrc_s = p.b_s + ((size_t)it.g * (N / 128) + (it.n0 + (lane & 1) * WCOLS) / 128) * KB;
   };
@@ -439,9 +454,10 @@ __global__ __launch_bounds__(f2::THREADS) void k_gemm_bf16_fp8w(const Fp8GemmArg
   };
   auto issue_b = [&]() {
     uint8_t* st = ringB + b_st * B_STAGE;
+    const int wkt = b_kt < WKT ? b_kt : b_kt - WKT;  // W2 step of A step b_kt
 #pragma unroll
-    for (int j = 0; j < B_OPS; j++) dma16(bsrc[j] + b_kt * BK, st + 16 * (B_OPS * wave + j) * BK);
-    if (wave == 1 && lane < 2) dma4(bsrc_s + (b_kt >> 1), st + BN * BK);
+    for (int j = 0; j < B_OPS; j++) dma16(bsrc[j] + wkt * BK, st + 16 * (B_OPS * wave + j) * BK);
+    if (wave == 1 && lane < 2) dma4(bsrc_s + (wkt >> 1), st + BN * BK);
     b_st = b_st + 1 == SB ? 0 : b_st + 1;
     if (b_step + 1 < nsteps) {
       b_step++;
@@ -598,6 +614,7 @@ static hipError_t launch_bf16_fp8w(const Fp8GemmArgs& p, int cu_limit, hipStream
 hipError_t gemm_bf16_fp8w(Fp8GemmArgs p, int cu_limit, hipStream_t s) {
   if (p.G <= 0 || p.max_m <= 0 || p.N <= 0 || p.K <= 0) return hipSuccess;
   if (p.G > f1::MAX_G || p.N % 128 != 0 || p.K % 128 != 0) return hipErrorNotSupported;
+  if (p.b_k && (p.b_k % 128 != 0 || (p.K != p.b_k && p.K != 2 * p.b_k))) return hipErrorNotSupported;
   // 256 columns per item where N allows it (half the h re-reads), else 128
   if (p.N % 256 == 0) return launch_bf16_fp8w<8, 4>(p, cu_limit, s);
   return launch_bf16_fp8w<4, 6>(p, cu_limit, s);

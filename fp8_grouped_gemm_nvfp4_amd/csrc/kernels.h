@@ -82,6 +82,10 @@ struct Fp8GemmArgs {
   int G, max_m, N, K;
   int a_s_stride;       // GEMM1: max_m rounded up to a multiple of 4
   int tiles_m, tiles_n, total_tiles;
+  // h kept as two bf16 planes (hi = bf16(h), lo = bf16(h - hi)) in rows of 2 * (N/2):
+  // GEMM1 writes both, GEMM2 runs over K = 2I with W2's K index wrapping at b_k = I
+  int h_split;
+  int b_k;              // GEMM2: K extent of W2 when h_split (else K)
 };
 constexpr int fp8_scale_stride(int max_m) { return (max_m + 3) / 4 * 4; }
 hipError_t gemm_fp8_swiglu(Fp8GemmArgs p, int cu_limit, hipStream_t s);

@@ -189,7 +189,7 @@ int moe_quantize_gather_nvfp4(const uint16_t* x, int T, int H, float g_x,
                               int max_m, uint8_t* a, uint8_t* a_sf, void* stream);
 
 /* Precision of moe_expert_forward. */
-typedef enum { MXG_MOE_FP8_BLOCK128 = 1, MXG_MOE_NVFP4 = 2 } mxg_moe_precision;
+typedef enum { MXG_MOE_FP8_BLOCK128 = 1, MXG_MOE_NVFP4 = 2, MXG_MOE_FP8_BLOCK128_F32H = 3 } mxg_moe_precision;
 
 /*
  * The routed expert computation of one MoE layer: gather -> GEMM1 (W13, gate
@@ -204,6 +204,12 @@ typedef enum { MXG_MOE_FP8_BLOCK128 = 1, MXG_MOE_NVFP4 = 2 } mxg_moe_precision;
  *   w13      e4m3 [E, 2I, H], w13_scale fp32 [E, 2I/128, H/128]
  *   w2       e4m3 [E, H, I],  w2_scale fp32 [E, H/128, I/128]
  *   h        = bf16 (round to nearest even) of silu(gate) * up
+ * MXG_MOE_FP8_BLOCK128_F32H: as MXG_MOE_FP8_BLOCK128 with a full-precision
+ *   intermediate: the fp32 h is kept as hi = bf16(h) and lo = bf16(h - hi)
+ *   (about 16 significant bits) and GEMM2 runs over both planes, o = (hi + lo) W2,
+ *   at about twice GEMM2's cost.  Source: "llm-assisted-kernel-dev" README,
+ *   moe_fibench_ref.py (experts in full precision) and the fp32 expert variants of
+ *   moe_fp8fpX_fused.py; the hi/lo split is this library's reading of it.
  * MXG_MOE_NVFP4:
  *   x        bf16 [T, H], quantized in the layer with global scale g_x
  *   w13      codes [E, 2I, H/2], w13_scale e4m3 [E, 2I, H/16], g_w13 fp32 [E]
@@ -216,8 +222,8 @@ typedef enum { MXG_MOE_FP8_BLOCK128 = 1, MXG_MOE_NVFP4 = 2 } mxg_moe_precision;
  *   dbg_h    optional device fp32 [E, max_m, I]: NVFP4 only, receives the
  *            pre-quantization intermediate for the rows it computes (NULL in
  *            production; y is bit-identical either way).
- * Requirements: H % 128 == 0, I % 128 == 0, 1 <= top_k <= 8, max_m >= 1; FP8 also
- * E <= 1024 (else MXG_ERR_UNSUPPORTED).
+ * Requirements: H % 128 == 0, I % 128 == 0, 1 <= top_k <= 8, max_m >= 1; both FP8
+ * precisions also E <= 1024 (else MXG_ERR_UNSUPPORTED).
  * Workspace: ws of at least moe_expert_forward_workspace_size(desc) bytes,
  * 256-byte aligned, device; its regions hold the gathered activations, h and
  * the GEMM2 output (offsets from moe_expert_forward_workspace_layout).
@@ -251,7 +257,8 @@ size_t moe_expert_forward_workspace_size(const mxg_moe_desc* desc);
  *   [0] gathered activations (FP8: e4m3 [E, max_m, H]; NVFP4: codes [E, max_m, H/2])
  *   [1] their scales (FP8: fp32 [E, H/128, max_m rounded up to a multiple of 4], i.e.
  *       transposed; NVFP4: e4m3 [E, max_m, H/16])
- *   [2] h (FP8: bf16 [E, max_m, I] followed by one scratch row; NVFP4: codes [E, max_m, I/2])
+ *   [2] h (FP8: bf16 [E, max_m, I] followed by one scratch row; FP8 F32H: bf16 [E, max_m, 2I],
+ *       hi in columns [0, I) and lo in [I, 2I), then one scratch row; NVFP4: codes [E, max_m, I/2])
  *   [3] h scales (FP8: unused; NVFP4: e4m3 [E, max_m, I/16])
  *   [4] GEMM2 output fp32 [E, max_m, H]
  *   [5] total size

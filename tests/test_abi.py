@@ -145,6 +145,11 @@ def test_moe_fp8_workspace_layout_and_expert_limit():
     assert off[2] - off[1] >= 256 * (7168 // 128) * 244 * 4      # transposed scales, stride 244
     assert off[3] - off[2] >= (rows + 1) * 2048 * 2              # h plus the scratch row
     assert off[5] - off[4] >= rows * 7168 * 4
+    d2 = _desc(precision=mxg.MXG_MOE_FP8_BLOCK128_F32H, max_m=241)
+    off2 = (ctypes.c_size_t * 6)()
+    assert L.moe_expert_forward_workspace_layout(ctypes.byref(d2), off2) == mxg.MXG_OK
+    assert off2[3] - off2[2] >= (rows + 1) * 2 * 2048 * 2                  # hi and lo planes
+    assert off2[1] - off2[0] == off[1] - off[0] and off2[2] - off2[1] == off[2] - off[1]
     for E, want in ((1024, mxg.MXG_OK), (1025, mxg.MXG_ERR_UNSUPPORTED)):
         d = _desc(precision=mxg.MXG_MOE_FP8_BLOCK128, E=E)
         assert L.moe_expert_forward_workspace_layout(ctypes.byref(d), off) == want, E

@@ -181,15 +181,22 @@ def _vary_block_scales(s, seed, zero_frac=0.1):
     return (s.cpu() * f).to(s.device)
 
 
-def _run_fp8(T, H, I, seed, n_check, n_deep=0, vary_w2_scales=False):
+def _run_fp8(T, H, I, seed, n_check, n_deep=0, vary_w2_scales=False, f32h=False):
+    """FP8 layer, checked stage by stage on the GPU's own intermediates.  With f32h the
+    intermediate is kept as bf16 hi and lo planes (h = hi + lo to about 16 bits): h is
+    checked against the oracle's unrounded SwiGLU, GEMM2 and the combine against the
+    oracle on hi + lo, and y also against the oracle's whole layer on the unrounded h
+    with the h tolerance carried through GEMM2."""
     mxg = _mxg()
+    prec = mxg.MXG_MOE_FP8_BLOCK128_F32H if f32h else mxg.MXG_MOE_FP8_BLOCK128
+    planes = 2 if f32h else 1
     wl = datagen.moe_fp8_workload(seed, DEV, T=T, H=H, I=I)
     t = wl.tensors
     if vary_w2_scales:
         t["w2_s"] = _vary_block_scales(t["w2_s"], seed + 1)
     ids, w, masked_m, row, max_m = _route_dispatch(t)
     y = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
-    d = mxg.make_moe_desc(mxg.MXG_MOE_FP8_BLOCK128, T, H, I, E, TOPK, max_m, t["xq"], t["w13"], t["w13_s"],
+    d = mxg.make_moe_desc(prec, T, H, I, E, TOPK, max_m, t["xq"], t["w13"], t["w13_s"],
                           t["w2"], t["w2_s"], ids, w, masked_m, row, y, x_scale=t["xs"])
     off = mxg.moe_expert_forward_workspace_layout(d)
     ws = torch.empty((off[5],), dtype=torch.uint8, device=DEV)
@@ -203,7 +210,8 @@ def _run_fp8(T, H, I, seed, n_check, n_deep=0, vary_w2_scales=False):
     cap_s = (max_m + 3) // 4 * 4  # the row scales are stored transposed: [E, H/128, cap_s]
     a_s = np_(ws[off[1]:off[1] + E * (H // 128) * cap_s * 4].view(torch.float32)).reshape(E, H // 128, cap_s)
     a_s = np.ascontiguousarray(a_s[:, :, :max_m].transpose(0, 2, 1))
-    hb = np_(ws[off[2]:off[2] + E * max_m * I * 2].view(torch.int16)).view(np.uint16).reshape(E, max_m, I)
+    hb = np_(ws[off[2]:off[2] + E * max_m * planes * I * 2].view(torch.int16)).view(np.uint16)
+    hb = hb.reshape(E, max_m, planes * I)
     ids_h, w_h, row_h = np_(ids), np_(w), np_(row)
     xq, xs = np_(t["xq"]), np_(t["xs"])
     yb = bf16_from_bits_np(bf16_tensor_bits(y))
@@ -214,8 +222,12 @@ def _run_fp8(T, H, I, seed, n_check, n_deep=0, vary_w2_scales=False):
         assert len(deep) >= n_deep, "workload has too few rows past 256"
         toks = sorted(set(toks) | set(deep[np.linspace(0, len(deep) - 1, n_deep).astype(int)].tolist()))
     touched = set()
+    if f32h:
+        o_gpu = np_(ws[off[4]:off[4] + E * max_m * H * 4].view(torch.float32)).reshape(E, max_m, H)
+        err2 = {"split": 0.0, "bf16": 0.0}
     for tt in toks:
         o_list, so_list, wj = [], [], []
+        ox_list, sx_list, px_list = [], [], []
         for j in range(TOPK):
             e, r = int(ids_h[tt, j]), int(row_h[tt, j])
             touched.add(e)
@@ -225,14 +237,38 @@ def _run_fp8(T, H, I, seed, n_check, n_deep=0, vary_w2_scales=False):
             gu, S1 = gu[0], S1[0]
             g, u = gu[:I], gu[I:]
             hstar = oracle.swiglu(gu[None], I)[0]
-            tol = _swiglu_tol(g, u, S1[:I], S1[I:], hstar) + ulp_bf16(hstar)
-            hv = bf16_from_bits_np(hb[e, r])
+            if f32h:
+                tol_h = _swiglu_tol(g, u, S1[:I], S1[I:], hstar)
+                tol = tol_h + 2.0 ** -17 * np.abs(hstar)
+                hv = bf16_from_bits_np(hb[e, r, :I]) + bf16_from_bits_np(hb[e, r, I:])
+            else:
+                tol = _swiglu_tol(g, u, S1[:I], S1[I:], hstar) + ulp_bf16(hstar)
+                hv = bf16_from_bits_np(hb[e, r])
             err = np.abs(hv - hstar)
             assert np.all(err <= tol), f"h token {tt} slot {j}: max excess {np.max(err - tol)}"
             o, So = oracle.gemm_dense_fp8w(hv[None], np_(t["w2"][e]), np_(t["w2_s"][e]))
             o_list.append(o[0]); so_list.append(So[0]); wj.append(w_h[tt, j])
+            if f32h:
+                # the whole layer on the unrounded h, and how far the GPU's h may sit from it
+                ox, Sx = oracle.gemm_dense_fp8w(hstar[None], np_(t["w2"][e]), np_(t["w2_s"][e]))
+                w2_abs = np_(t["w2"][e]) & 0x7F  # |W2| codes (sign bit cleared)
+                px, _ = oracle.gemm_dense_fp8w(tol[None], w2_abs, np.abs(np_(t["w2_s"][e])))
+                ox_list.append(ox[0]); sx_list.append(Sx[0]); px_list.append(np.abs(px[0]))
+                # GEMM2's fp32 output against the unrounded h, next to what a bf16 h gives
+                ob, _ = oracle.gemm_dense_fp8w(oracle.bf16_value(oracle.bf16_bits(hstar))[None], np_(t["w2"][e]),
+                                               np_(t["w2_s"][e]))
+                err2["split"] += float(np.sum((o_gpu[e, r] - ox[0]) ** 2))
+                err2["bf16"] += float(np.sum((ob[0] - ox[0]) ** 2))
         ystar, S = oracle.combine(np.array(o_list), np.array(so_list), np.array(wj))
         assert_within(yb[tt], ystar, S, f"y token {tt}")
+        if f32h:
+            yx, Sxx = oracle.combine(np.array(ox_list), np.array(sx_list), np.array(wj))
+            carry = np.abs(np.array(wj)) @ np.array(px_list)
+            assert_within(yb[tt], yx, Sxx + carry / 1e-5, f"y token {tt} against the unrounded h")
+    if f32h:
+        ratio = (err2["split"] / err2["bf16"]) ** 0.5
+        log(f"GEMM2 rms error against the unrounded h: hi/lo planes / bf16 h = {ratio:.4f}")
+        assert ratio < 0.05, f"the hi/lo intermediate is not much closer to the unrounded h ({ratio:.3f})"
     log(f"FP8 MoE T={T} H={H} I={I} max_m={max_m}: {len(toks)} tokens, {len(touched)} experts")
 
 
@@ -252,6 +288,16 @@ def test_moe_fp8_varied_w2_scales(H):
     # 2^16 between blocks, zero blocks, and (H = 384) 128-column items
     log(f"FP8 MoE with varied W2 block scales: T=256 H={H} I=384 E=256, every token")
     _run_fp8(256, H, 384, 3002 + H, None, vary_w2_scales=True)
+
+
+def test_moe_fp8_full_precision_intermediate():
+    log("FP8 MoE with hi/lo bf16 intermediate: T=256 H=512 I=384 E=256, every token")
+    _run_fp8(256, 512, 384, 3010, None, f32h=True)
+
+
+def test_moe_fp8_full_precision_intermediate_full_size():
+    log("FP8 MoE with hi/lo bf16 intermediate: T=4096 H=7168 I=2048, 3 tokens checked")
+    _run_fp8(4096, 7168, 2048, 1003, 3, f32h=True)
 
 
 def test_moe_fp8_full_size():
