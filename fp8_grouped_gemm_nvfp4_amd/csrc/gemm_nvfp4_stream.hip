@@ -30,8 +30,10 @@
 // the fp32 sum.  The MFMA computes the transposed tile D = B A^T, so each lane ends
 // with four consecutive output columns of one row: 16-byte fp32 stores, and the
 // 16-column NVFP4 blocks of the SwiGLU epilogue sit in 4 lanes (quantize_block_x4).
-// Waves: 4 (M) x 2 (N); wave (wm, wn) owns the 16-row groups 16 wm + 64 i, so both
-// waves of a SIMD compute when masked_m <= 128.
+// Waves: MW (M) x 8 / MW (N); wave (wm, wn) owns the 16-row groups 16 wm + 16 MW i, so
+// both waves of a SIMD compute when masked_m <= 128.  With MW = 8 every wave decodes
+// activation rows no other wave decodes (with MW = 4 the two N waves of a row block
+// decode the same rows) and reads twice the fp16 weight fragments from LDS.
 #include "kernels.h"
 #include "stream_common.h"
 
@@ -55,9 +57,14 @@ struct NsJob {
   int g, m0, mm, n0, K;
 };
 
-template <int EPI, int MODE>
+template <int EPI, int MODE, int MW>
 __global__ __launch_bounds__(ns::THREADS) void k_gemm_nvfp4_stream(const typename ArgsOf<MODE>::type p) {
   using namespace ns;
+  static_assert(MW == 4 || MW == 8, "waves along M");
+  constexpr int NW = WAVES / MW;        // waves along N
+  constexpr int RG = BM / 16 / MW;      // 16-row groups per wave
+  constexpr int NB = BN / 16 / NW;      // 16-column groups per wave
+  constexpr int WC = BN / NW;           // weight rows (output columns) per wave
   constexpr bool SWIGLU = (EPI == EPI_SWIGLU_NVFP4);
   constexpr bool MASKED = (MODE == MODE_MASKED);
   static_assert(MASKED || !SWIGLU, "the SwiGLU epilogue is the MoE GEMM1's (masked)");
@@ -72,7 +79,7 @@ __global__ __launch_bounds__(ns::THREADS) void k_gemm_nvfp4_stream(const typenam
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: branches on it are scalar
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / NW, wn = wave % NW;
   const int G = p.G;
   int N = 0, cap = 0, tiles_n = 0, total = 0;  // masked: common N, row capacity, N tiles
   const int ncols = SWIGLU ? BN / 2 : BN;      // output (h) columns per item
@@ -240,11 +247,11 @@ __global__ __launch_bounds__(ns::THREADS) void k_gemm_nvfp4_stream(const typenam
   __syncthreads();
   decode_b(0);
 
-  float4_t acc[4][4];
+  float4_t acc[RG][NB];
 #pragma unroll
-  for (int i = 0; i < 4; i++)
+  for (int i = 0; i < RG; i++)
 #pragma unroll
-    for (int n = 0; n < 4; n++) acc[i][n] = float4_t{0.f, 0.f, 0.f, 0.f};
+    for (int n = 0; n < NB; n++) acc[i][n] = float4_t{0.f, 0.f, 0.f, 0.f};
 
   NsJob cit = job_at(0);
   int c_k = 0, c_kt = 0, c_sa = 0;
@@ -269,18 +276,18 @@ __global__ __launch_bounds__(ns::THREADS) void k_gemm_nvfp4_stream(const typenam
     if (active) {
       const uint8_t* As = ringA + c_sa * A_STAGE;
       const _Float16* Bd = bdec[s & 1];
-      u32x4_t araw[4];
-      uint32_t asc[4];
+      u32x4_t araw[RG];
+      uint32_t asc[RG];
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
-        if (cit.m0 + 16 * wm + 64 * i >= cit.mm) break;
-        const int r = 16 * wm + 64 * i + rr;
+      for (int i = 0; i < RG; i++) {
+        if (cit.m0 + 16 * wm + 16 * MW * i >= cit.mm) break;
+        const int r = 16 * wm + 16 * MW * i + rr;
         araw[i] = *(const u32x4_t*)(As + r * 64 + ((q ^ ns_swz_a(r)) << 4));
         asc[i] = *(const uint16_t*)(As + A_CODE + r * 8 + 2 * q);
       }
-      half2_t as2[4][2];
+      half2_t as2[RG][2];
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
+      for (int i = 0; i < RG; i++) {
         const half2_t s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(asc[i], 1.0f, false);
         as2[i][0] = half2_t{s01[0], s01[0]};
         as2[i][1] = half2_t{s01[1], s01[1]};
@@ -289,25 +296,26 @@ __global__ __launch_bounds__(ns::THREADS) void k_gemm_nvfp4_stream(const typenam
       for (int ks = 0; ks < 4; ks++) {
         // dword ks of a lane's chunk q holds K elements 32 q + 8 ks .. +7 of the step,
         // in 16-block 2 q + ks / 2
-        half8_t bf[4];
+        half8_t bf[NB];
 #pragma unroll
-        for (int n = 0; n < 4; n++) {
-          const int r = (SWIGLU ? (n < 2 ? 32 * wn + 16 * n : BN / 2 + 32 * wn + 16 * (n - 2)) : 64 * wn + 16 * n) + rr;
+        for (int n = 0; n < NB; n++) {
+          const int r = (SWIGLU ? (n < NB / 2 ? WC / 2 * wn + 16 * n : BN / 2 + WC / 2 * wn + 16 * (n - NB / 2))
+                                : WC * wn + 16 * n) + rr;
           bf[n] = *(const half8_t*)(Bd + r * BK + (((4 * q + ks) ^ ns_sigma(rr)) << 3));
         }
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-          if (cit.m0 + 16 * wm + 64 * i >= cit.mm) break;
+        for (int i = 0; i < RG; i++) {
+          if (cit.m0 + 16 * wm + 16 * MW * i >= cit.mm) break;
           const half8_t af = decode8_e2m1_f16(araw[i][ks], as2[i][ks >> 1]);
 #pragma unroll
-          for (int n = 0; n < 4; n++) acc[i][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bf[n], af, acc[i][n], 0, 0, 0);
+          for (int n = 0; n < NB; n++) acc[i][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bf[n], af, acc[i][n], 0, 0, 0);
         }
       }
     }
     c_sa ^= 1;
 
     if (++c_kt == cit.K / BK) {
-      // lane (rr, q) holds, for row group i, output row 16 wm + 64 i + rr and the four
+      // lane (rr, q) holds, for row group i, output row 16 wm + 16 MW i + rr and the four
       // columns 4 q .. 4 q + 3 of each 16-column group n
       if (active) {
         float alpha;
@@ -323,20 +331,20 @@ __global__ __launch_bounds__(ns::THREADS) void k_gemm_nvfp4_stream(const typenam
           ldo = p.grp[cit.g].ldc;
         }
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-          const int m = cit.m0 + 16 * wm + 64 * i + rr;
+        for (int i = 0; i < RG; i++) {
+          const int m = cit.m0 + 16 * wm + 16 * MW * i + rr;
           const bool ok = m < cit.mm;
           const size_t orow = MASKED ? (size_t)cit.g * cap + m : (size_t)m;
           if constexpr (SWIGLU) {
 #pragma unroll
-            for (int n = 0; n < 2; n++) {
+            for (int n = 0; n < NB / 2; n++) {
               float h[4];
 #pragma unroll
               for (int r = 0; r < 4; r++) {
-                const float gt = alpha * acc[i][n][r], up = alpha * acc[i][n + 2][r];
+                const float gt = alpha * acc[i][n][r], up = alpha * acc[i][n + NB / 2][r];
                 h[r] = gt / (1.0f + expf(-gt)) * up;
               }
-              const int hc0 = cit.n0 + 32 * wn + 16 * n;  // first column of this lane's 16-block
+              const int hc0 = cit.n0 + WC / 2 * wn + 16 * n;  // first column of this lane's 16-block
               if (p.dbg_h && ok) *(float4_t*)(p.dbg_h + orow * I + hc0 + 4 * q) = float4_t{h[0], h[1], h[2], h[3]};
               uint32_t sbyte;
               const uint32_t bits = quantize_block_x4(h, p.g_h, 6.0f * p.g_h, sbyte);
@@ -348,8 +356,8 @@ __global__ __launch_bounds__(ns::THREADS) void k_gemm_nvfp4_stream(const typenam
             }
           } else {
 #pragma unroll
-            for (int n = 0; n < 4; n++) {
-              const int c = cit.n0 + 64 * wn + 16 * n + 4 * q;
+            for (int n = 0; n < NB; n++) {
+              const int c = cit.n0 + WC * wn + 16 * n + 4 * q;
               const float4_t v = acc[i][n] * alpha;
               if (!ok) continue;
               if constexpr (EPI == EPI_BF16) {
@@ -364,9 +372,9 @@ __global__ __launch_bounds__(ns::THREADS) void k_gemm_nvfp4_stream(const typenam
         }
       }
 #pragma unroll
-      for (int i = 0; i < 4; i++)
+      for (int i = 0; i < RG; i++)
 #pragma unroll
-        for (int n = 0; n < 4; n++) acc[i][n] = float4_t{0.f, 0.f, 0.f, 0.f};
+        for (int n = 0; n < NB; n++) acc[i][n] = float4_t{0.f, 0.f, 0.f, 0.f};
       c_kt = 0;
       if (++c_k < n_items) cit = job_at(c_k);
     }
@@ -376,10 +384,11 @@ __global__ __launch_bounds__(ns::THREADS) void k_gemm_nvfp4_stream(const typenam
 
 template <int EPI, int MODE>
 static hipError_t launch_stream(const typename ArgsOf<MODE>::type& p, int cu_limit, hipStream_t s) {
-  const void* k = (const void*)k_gemm_nvfp4_stream<EPI, MODE>;
+  constexpr int MW = 8;  // 8 x 1 waves: measured about 1% ahead of 4 x 2 (T=8192 layer, hetero)
+  const void* k = (const void*)k_gemm_nvfp4_stream<EPI, MODE, MW>;
   const int grid = resident_grid(k, ns::THREADS, cu_limit);
   if (grid <= 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((k_gemm_nvfp4_stream<EPI, MODE>), dim3(grid), dim3(ns::THREADS), 0, s, p);
+  hipLaunchKernelGGL((k_gemm_nvfp4_stream<EPI, MODE, MW>), dim3(grid), dim3(ns::THREADS), 0, s, p);
   return hipGetLastError();
 }
 
