@@ -356,6 +356,42 @@ def bench_gemv_w4a16(dev, steps, warmup, seed=1005, M=1):
                 mfma_dtype="fp16", config=dict(workload=f"gemv_w4a16_llama3_8b_m{M}", M=M, shapes=per))
 
 
+def bench_contiguous(dev, steps, warmup, seed=1004, T=8192, align=128):
+    """GEMM1 of the T=8192 NVFP4 layer over the contiguous (expert-sorted, 128-row aligned)
+    layout: routing and contiguous dispatch, then the grouped GEMM on NVFP4 activation
+    rows (synthetic codes) against W13, bf16 output."""
+    E, H, I, top_k = 256, 7168, 2048, 8
+    wl = datagen.moe_nvfp4_workload(seed, dev, T=T)
+    t = wl.tensors
+    ids, w = mxg.moe_route_noaux(t["logits"], t["bias"], 8, 4, top_k, 2.5)
+    gs, cnt, row = mxg.moe_dispatch_contiguous(ids, E, align)
+    mm_full, _ = mxg.moe_dispatch(ids, E, 1 << 20)
+    torch.cuda.synchronize()
+    M_total = int(gs[-1].item())
+    cap = max(16, -(-int(mm_full.max().item()) // 16) * 16)
+    gen = datagen.generator(seed + 50, dev)
+    a, a_sf = datagen.nvfp4_uniform(gen, (M_total,), H, dev)
+    alpha = t["g_w13"] * float(datagen.global_scale_from_amax(t["x"]))
+    out = torch.empty((M_total, 2 * I), dtype=torch.bfloat16, device=dev)
+
+    def step(kt):
+        if kt:
+            kt.start()
+        mxg.mx_grouped_gemm_contiguous(a, a_sf, t["w13"], t["w13_sf"], alpha, gs, cnt, out)
+        if kt:
+            kt.stop()
+
+    ms, kms, wall = timed_loop(step, steps, warmup)
+    rows = int(cnt.sum().item())
+    byts = E * 2 * I * NVFP4_ROW_BYTES(H) + rows * NVFP4_ROW_BYTES(H) + rows * 2 * I * 2
+    flops = 2.0 * rows * 2 * I * H
+    return dict(name=f"contiguous_gemm1_nvfp4_t{T}", ms=ms, kernel_ms=kms, wall_s=wall, bytes=byts,
+                kernel_bytes=byts, flops=flops, gbs=byts / ms / 1e6, tflops=flops / ms / 1e9,
+                kernel_tflops=flops / kms / 1e9, bound="mfma", mfma_dtype="fp16",
+                config=dict(workload=f"contiguous_gemm1_nvfp4_t{T}", tokens=T, rows=rows, contiguous_rows=M_total,
+                            masked_rows=E * cap, align=align))
+
+
 def _moe_setup(dev, t, T, E=256, top_k=8):
     ids, w = mxg.moe_route_noaux(t["logits"], t["bias"], 8, 4, top_k, 2.5)
     mm_full, _ = mxg.moe_dispatch(ids, E, 1 << 20)
@@ -424,6 +460,7 @@ WORKLOADS = {
     "moe_nvfp4_decode": lambda dev, k, w, cpu: bench_moe(dev, k, w, "nvfp4", 64, 1004),
     "moe_nvfp4_prefill": lambda dev, k, w, cpu: bench_moe(dev, k, w, "nvfp4", 8192, 1004),
     "gemv_w4a16": lambda dev, k, w, cpu: bench_gemv_w4a16(dev, k, w),
+    "contiguous_gemm1": lambda dev, k, w, cpu: bench_contiguous(dev, k, w),
 }
 
 

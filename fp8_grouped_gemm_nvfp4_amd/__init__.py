@@ -54,6 +54,8 @@ SIGNATURES = {
     "mxg_version": (_I, []),
     "mx_grouped_gemm_masked": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _P]),
     "mx_grouped_gemm": (_I, [_P, _I, _I, _I, _I, _I, _I, _P]),
+    "mx_grouped_gemm_contiguous": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _P]),
+    "moe_dispatch_contiguous": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P]),
     "mx_gemv_nvfp4_w4a16": (_I, [_P, _I, _I, _P, _P, _F, _P, _I, _I, _I, _P]),
     "mx_quantize_nvfp4": (_I, [_P, _I, _L, _I, _F, _P, _P, _P]),
     "moe_route_noaux": (_I, [_P, _P, _I, _I, _I, _I, _I, _F, _P, _P, _P]),
@@ -116,6 +118,20 @@ def mx_grouped_gemm_masked(a, a_sf, b, b_sf, alpha, masked_m, out, cu_limit=0, s
     return out
 
 
+def mx_grouped_gemm_contiguous(a, a_sf, b, b_sf, alpha, group_start, count, out, cu_limit=0, stream=None):
+    """Contiguous-layout grouped NVFP4 NT GEMM.  a [M_total, K/2] u8, a_sf [M_total, K/16] u8,
+    b [G, N, K/2], b_sf [G, N, K/16], alpha [G] f32 or None, group_start [G + 1] i32,
+    count [G] i32, out [M_total, N] bf16 or f32."""
+    M_total, half_k = a.shape
+    G, N = b.shape[0], b.shape[1]
+    c_dtype = {torch.bfloat16: MXG_BF16, torch.float32: MXG_F32}.get(out.dtype, 0)
+    _check(lib().mx_grouped_gemm_contiguous(_ptr(a), _ptr(a_sf), _ptr(b), _ptr(b_sf), _ptr(alpha),
+                                            _ptr(group_start), _ptr(count), _ptr(out), G, M_total, N,
+                                            2 * half_k, MXG_E2M1, MXG_E4M3, c_dtype, 16, cu_limit,
+                                            _stream(stream)))
+    return out
+
+
 def mx_grouped_gemm(groups, out_dtype=torch.bfloat16, cu_limit=0, stream=None):
     """Heterogeneous grouped NVFP4 NT GEMM.  groups: list of dicts with M, N, K, alpha,
     a, a_sf, b, b_sf, out (tensors) and optional ldc."""
@@ -174,6 +190,19 @@ def moe_dispatch(ids, E, max_m, masked_m=None, row=None, stream=None):
         row = torch.empty((T, k), dtype=torch.int32, device=ids.device)
     _check(lib().moe_dispatch(_ptr(ids), T, E, k, max_m, _ptr(masked_m), _ptr(row), _stream(stream)))
     return masked_m, row
+
+
+def moe_dispatch_contiguous(ids, E, align, group_start=None, count=None, row=None, stream=None):
+    T, k = ids.shape
+    if group_start is None:
+        group_start = torch.empty((E + 1,), dtype=torch.int32, device=ids.device)
+    if count is None:
+        count = torch.empty((E,), dtype=torch.int32, device=ids.device)
+    if row is None:
+        row = torch.empty((T, k), dtype=torch.int32, device=ids.device)
+    _check(lib().moe_dispatch_contiguous(_ptr(ids), T, E, k, align, _ptr(group_start), _ptr(count), _ptr(row),
+                                         _stream(stream)))
+    return group_start, count, row
 
 
 def moe_quantize_gather_nvfp4(x, g_x, ids, row, E, max_m, a=None, a_sf=None, stream=None):

@@ -89,6 +89,31 @@ int mx_grouped_gemm_masked(const uint8_t* a, const uint8_t* a_sf, const uint8_t*
                     "mx_grouped_gemm_masked launch");
 }
 
+int mx_grouped_gemm_contiguous(const uint8_t* a, const uint8_t* a_sf, const uint8_t* b, const uint8_t* b_sf,
+                               const float* alpha, const int32_t* group_start, const int32_t* count, void* out,
+                               int G, int M_total, int N, int K, int ab_dtype, int sf_dtype, int c_dtype,
+                               int sf_vec_size, int cu_limit, void* stream) {
+  if (!a || !a_sf || !b || !b_sf || !group_start || !count || !out)
+    return fail(MXG_ERR_INVALID_ARG, "mx_grouped_gemm_contiguous: null pointer");
+  if (G < 1 || M_total < 1 || N < 1 || K < 1 || cu_limit < 0)
+    return fail(MXG_ERR_INVALID_ARG, "mx_grouped_gemm_contiguous: bad sizes G=%d M_total=%d N=%d K=%d", G,
+                M_total, N, K);
+  int st = check_nvfp4_types(ab_dtype, sf_dtype, c_dtype, sf_vec_size);
+  if (st) return st;
+  if (G > mxg::STREAM_CONTIG_MAX_G || N % 128 != 0 || K % 128 != 0)
+    return fail(MXG_ERR_UNSUPPORTED, "mx_grouped_gemm_contiguous: needs G <= %d, N %% 128 == 0, K %% 128 == 0",
+                mxg::STREAM_CONTIG_MAX_G);
+  if (!aligned16(a) || !aligned16(b) || !aligned16(out) || !aligned16(a_sf) || !aligned16(b_sf))
+    return fail(MXG_ERR_INVALID_ARG, "mx_grouped_gemm_contiguous: misaligned pointer");
+  mxg::MaskedGemmArgs p{};
+  p.a = a; p.a_sf = a_sf; p.b = b; p.b_sf = b_sf; p.out = out;
+  p.masked_m = count; p.alpha = alpha; p.alpha_scale = 1.0f; p.row_start = group_start;
+  p.G = G; p.max_m = M_total; p.N = N; p.K = K;
+  int epi = c_dtype == MXG_BF16 ? mxg::EPI_BF16 : mxg::EPI_F32;
+  return hip_status(mxg::gemm_nvfp4_contiguous(p, epi, cu_limit, (hipStream_t)stream),
+                    "mx_grouped_gemm_contiguous launch");
+}
+
 int mx_grouped_gemm(const mxg_group_desc* groups, int G, int ab_dtype, int sf_dtype, int c_dtype,
                     int sf_vec_size, int cu_limit, void* stream) {
   if (!groups) return fail(MXG_ERR_INVALID_ARG, "mx_grouped_gemm: null descriptor array");
@@ -182,6 +207,19 @@ int moe_dispatch(const int32_t* topk_ids, int T, int E, int top_k, int max_m, in
   if ((long long)T * top_k >= (1LL << 31)) return fail(MXG_ERR_UNSUPPORTED, "moe_dispatch: too many slots");
   return hip_status(mxg::dispatch(topk_ids, T, E, top_k, max_m, masked_m, row, (hipStream_t)stream),
                     "moe_dispatch launch");
+}
+
+int moe_dispatch_contiguous(const int32_t* topk_ids, int T, int E, int top_k, int align, int32_t* group_start,
+                            int32_t* count, int32_t* row, void* stream) {
+  if (!topk_ids || !group_start || !count || !row)
+    return fail(MXG_ERR_INVALID_ARG, "moe_dispatch_contiguous: null pointer");
+  if (T < 0 || E < 1 || top_k < 1 || E > 65535 || align < 1 || align > 4096)
+    return fail(MXG_ERR_INVALID_ARG, "moe_dispatch_contiguous: bad sizes");
+  if ((long long)T * top_k + (long long)E * align >= (1LL << 31))
+    return fail(MXG_ERR_UNSUPPORTED, "moe_dispatch_contiguous: too many rows");
+  return hip_status(mxg::dispatch_contiguous(topk_ids, T, E, top_k, align, group_start, count, row,
+                                             (hipStream_t)stream),
+                    "moe_dispatch_contiguous launch");
 }
 
 int moe_quantize_gather_nvfp4(const uint16_t* x, int T, int H, float g_x, const int32_t* topk_ids,

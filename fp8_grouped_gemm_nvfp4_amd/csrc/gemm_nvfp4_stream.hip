@@ -66,16 +66,20 @@ __global__ __launch_bounds__(ns::THREADS) void k_gemm_nvfp4_stream(const typenam
   constexpr int NB = BN / 16 / NW;      // 16-column groups per wave
   constexpr int WC = BN / NW;           // weight rows (output columns) per wave
   constexpr bool SWIGLU = (EPI == EPI_SWIGLU_NVFP4);
-  constexpr bool MASKED = (MODE == MODE_MASKED);
+  // the contiguous layout is the masked one with each group's rows starting at row_start[g]
+  constexpr bool CONTIG = (MODE == MODE_CONTIG);
+  constexpr bool MASKED = (MODE == MODE_MASKED) || CONTIG;
+  constexpr int MAXG = CONTIG ? STREAM_CONTIG_MAX_G : STREAM_MAX_G;
   static_assert(MASKED || !SWIGLU, "the SwiGLU epilogue is the MoE GEMM1's (masked)");
   constexpr int SA = 2, SB = DB + 1;
   static_assert(DB >= 3, "B(s + 1) must be issued before A(s)");
   __shared__ __attribute__((aligned(16))) uint8_t ringA[SA * A_STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t ringB[SB * B_STAGE];
   __shared__ __attribute__((aligned(16))) _Float16 bdec[2][BN * BK];
-  __shared__ int tprefix[STREAM_MAX_G + 1];
-  __shared__ int mm_s[STREAM_MAX_G];
-  __shared__ float alpha_s[STREAM_MAX_G];
+  __shared__ int tprefix[MAXG + 1];
+  __shared__ int mm_s[MAXG];
+  __shared__ float alpha_s[MAXG];
+  __shared__ int rs_s[CONTIG ? MAXG + 1 : 1];  // group row starts, clamped to [0, max_m] and non-decreasing
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: branches on it are scalar
@@ -88,7 +92,34 @@ __global__ __launch_bounds__(ns::THREADS) void k_gemm_nvfp4_stream(const typenam
     cap = p.max_m;
     tiles_n = SWIGLU ? (N / 2) / ncols : N / ncols;
     for (int g = tid; g < G; g += THREADS) alpha_s[g] = (p.alpha ? p.alpha[g] : 1.0f) * p.alpha_scale;
-    stream_tile_prefix(p.masked_m, G, cap, tprefix, mm_s, tid);
+    if constexpr (CONTIG) {
+      // starts clamped to [0, max_m] and made non-decreasing (a running maximum, by wave
+      // 0's shuffle scan), so every access stays inside the max_m rows whatever they hold
+      for (int g = tid; g <= G; g += THREADS) {
+        const int v = p.row_start[g];
+        rs_s[g] = v < 0 ? 0 : (v > cap ? cap : v);
+      }
+      __syncthreads();
+      if (tid < 64) {
+        int run = 0;
+        for (int base = 0; base <= G; base += 64) {
+          const int g = base + tid;
+          int x = g <= G ? rs_s[g] : 0;
+#pragma unroll
+          for (int d = 1; d < 64; d <<= 1) {
+            const int y = __shfl_up(x, d);
+            if (tid >= d) x = x > y ? x : y;
+          }
+          x = x > run ? x : run;
+          if (g <= G) rs_s[g] = x;
+          run = __shfl(x, 63);
+        }
+      }
+      __syncthreads();
+      stream_tile_prefix(p.masked_m, G, cap, tprefix, mm_s, tid, rs_s);
+    } else {
+      stream_tile_prefix(p.masked_m, G, cap, tprefix, mm_s, tid);
+    }
     total = __builtin_amdgcn_readfirstlane(tprefix[G]) * tiles_n;
   } else {
     // heterogeneous groups: tprefix counts items (M tiles x N tiles) per group
@@ -114,8 +145,9 @@ __global__ __launch_bounds__(ns::THREADS) void k_gemm_nvfp4_stream(const typenam
     if constexpr (MASKED) {
       const StreamItem it = stream_item(bx + k * grid, tiles_n, G, tprefix, mm_s, ncols);
       j.g = it.g; j.m0 = it.m0; j.mm = it.mm; j.n0 = it.n0; j.K = p.K;
-      j.a = p.a + (size_t)it.g * cap * (p.K / 2);
-      j.a_sf = p.a_sf + (size_t)it.g * cap * (p.K / 16);
+      const size_t r0 = CONTIG ? (size_t)__builtin_amdgcn_readfirstlane(rs_s[it.g]) : (size_t)it.g * cap;
+      j.a = p.a + r0 * (p.K / 2);
+      j.a_sf = p.a_sf + r0 * (p.K / 16);
       j.b = p.b + (size_t)it.g * N * (p.K / 2);
       j.b_sf = p.b_sf + (size_t)it.g * N * (p.K / 16);
     } else {
@@ -334,7 +366,8 @@ __global__ __launch_bounds__(ns::THREADS) void k_gemm_nvfp4_stream(const typenam
         for (int i = 0; i < RG; i++) {
           const int m = cit.m0 + 16 * wm + 16 * MW * i + rr;
           const bool ok = m < cit.mm;
-          const size_t orow = MASKED ? (size_t)cit.g * cap + m : (size_t)m;
+          const size_t orow = CONTIG ? (size_t)__builtin_amdgcn_readfirstlane(rs_s[cit.g]) + m
+                              : MASKED ? (size_t)cit.g * cap + m : (size_t)m;
           if constexpr (SWIGLU) {
 #pragma unroll
             for (int n = 0; n < NB / 2; n++) {
@@ -405,6 +438,19 @@ hipError_t gemm_nvfp4_stream(MaskedGemmArgs p, int epi, int cu_limit, hipStream_
     case EPI_F32: return launch_stream<EPI_F32, MODE_MASKED>(p, cu_limit, s);
     case EPI_SWIGLU_NVFP4: return launch_stream<EPI_SWIGLU_NVFP4, MODE_MASKED>(p, cu_limit, s);
     default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t gemm_nvfp4_contiguous(MaskedGemmArgs p, int epi, int cu_limit, hipStream_t s) {
+  using namespace ns;
+  if (p.G <= 0 || p.G > STREAM_CONTIG_MAX_G || p.K % BK != 0 || p.K <= 0 || p.N % BN != 0 || p.N <= 0 ||
+      p.max_m <= 0 || !p.row_start)
+    return hipErrorNotSupported;
+  if ((long long)((p.max_m + BM - 1) / BM + p.G) * (p.N / BN) > 0x7FFFFFFFLL) return hipErrorNotSupported;
+  switch (epi) {
+    case EPI_BF16: return launch_stream<EPI_BF16, MODE_CONTIG>(p, cu_limit, s);
+    case EPI_F32: return launch_stream<EPI_F32, MODE_CONTIG>(p, cu_limit, s);
+    default: return hipErrorNotSupported;
   }
 }
 

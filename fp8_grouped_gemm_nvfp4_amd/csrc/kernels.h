@@ -10,7 +10,7 @@
 namespace mxg {
 
 enum { EPI_BF16 = 0, EPI_F32 = 1, EPI_SWIGLU_NVFP4 = 2, EPI_SWIGLU_BF16 = 3 };
-enum { MODE_MASKED = 0, MODE_HETERO = 1 };
+enum { MODE_MASKED = 0, MODE_HETERO = 1, MODE_CONTIG = 2 };
 
 // Masked layout: A [G, max_m, K], B [G, N, K], C [G, max_m, N].  For the fused
 // SwiGLU epilogue N = 2I (W13 rows: gate [0, I), up [I, 2I)) and the outputs
@@ -30,6 +30,9 @@ struct MaskedGemmArgs {
   uint8_t* h_sf;
   float* dbg_h;
   float g_h;
+  // contiguous layout (MODE_CONTIG): A [max_m, K] and C [max_m, N] hold every group's rows,
+  // group g from row row_start[g] (row_start [G + 1]); masked_m[g] counts its valid rows
+  const int32_t* row_start;
 };
 
 struct HeteroGroup {
@@ -52,6 +55,7 @@ struct HeteroGemmArgs {
 template <int MODE> struct ArgsOf;
 template <> struct ArgsOf<MODE_MASKED> { typedef MaskedGemmArgs type; };
 template <> struct ArgsOf<MODE_HETERO> { typedef HeteroGemmArgs type; };
+template <> struct ArgsOf<MODE_CONTIG> { typedef MaskedGemmArgs type; };
 
 hipError_t gemm_nvfp4_masked(MaskedGemmArgs p, int epi, int cu_limit, hipStream_t s);
 hipError_t gemm_nvfp4_hetero(HeteroGemmArgs p, int epi, int cu_limit, hipStream_t s);
@@ -62,6 +66,10 @@ constexpr int SKINNY_MAX_M = 32;  // row capacity up to which the skinny kernel 
 // Larger masked groups (prefill): persistent weight-streaming kernel, 256-row M tiles;
 // returns hipErrorNotSupported without launching for shapes it does not take.
 hipError_t gemm_nvfp4_stream(MaskedGemmArgs p, int epi, int cu_limit, hipStream_t s);
+// The same kernel over the contiguous layout (bf16 / fp32 outputs, N and K multiples of
+// 128, at most STREAM_CONTIG_MAX_G groups); hipErrorNotSupported otherwise.
+constexpr int STREAM_CONTIG_MAX_G = 512;
+hipError_t gemm_nvfp4_contiguous(MaskedGemmArgs p, int epi, int cu_limit, hipStream_t s);
 // The same kernel over heterogeneous groups (bf16 / fp32 outputs); hipErrorNotSupported for
 // groups it does not take (N or K not a multiple of 128, unaligned output rows).
 hipError_t gemm_nvfp4_stream_hetero(HeteroGemmArgs p, int epi, int cu_limit, hipStream_t s);
@@ -114,6 +122,10 @@ hipError_t route_noaux(const float* logits, const float* bias, int T, int E, int
                        hipStream_t s);
 hipError_t dispatch(const int32_t* ids, int T, int E, int top_k, int max_m, int32_t* masked_m,
                     int32_t* row, hipStream_t s);
+// contiguous layout: count[e] tokens of expert e from row start[e] (start[E + 1], each
+// start a multiple of align), row[t, j] the absolute row of slot (t, j)
+hipError_t dispatch_contiguous(const int32_t* ids, int T, int E, int top_k, int align, int32_t* start,
+                               int32_t* count, int32_t* row, hipStream_t s);
 hipError_t quantize_gather_nvfp4(const uint16_t* x, int T, int H, float g_x, const int32_t* ids,
                                  const int32_t* row, int top_k, int max_m, uint8_t* a,
                                  uint8_t* a_sf, hipStream_t s);

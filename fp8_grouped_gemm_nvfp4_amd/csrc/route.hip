@@ -148,6 +148,45 @@ __global__ __launch_bounds__(256) void k_dispatch(const int32_t* ids, int n, int
   if (tid == 0) masked_m[e] = base < max_m ? base : max_m;
 }
 
+// Contiguous layout: start[e + 1] = start[e] + count[e] rounded up to a multiple of
+// align (one wave, shuffle scans over 64 experts at a time), start[0] = 0.
+__global__ __launch_bounds__(64) void k_contig_starts(const int32_t* count, int E, int align, int32_t* start) {
+  const int lane = threadIdx.x;
+  int run = 0;
+  for (int base = 0; base < E; base += 64) {
+    const int e = base + lane;
+    const int c = e < E ? (count[e] + align - 1) / align * align : 0;
+    int x = c;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(x, d);
+      if (lane >= d) x += y;
+    }
+    if (e < E) start[e + 1] = run + x;
+    run += __shfl(x, 63);
+  }
+  if (lane == 0) start[0] = 0;
+}
+
+// row[f] (rank of slot f among its expert's slots) becomes its absolute row.
+__global__ __launch_bounds__(256) void k_contig_rows(const int32_t* ids, int n, const int32_t* start, int32_t* row) {
+  const int f = blockIdx.x * 256 + threadIdx.x;
+  if (f < n) row[f] += start[ids[f]];
+}
+
+hipError_t dispatch_contiguous(const int32_t* ids, int T, int E, int top_k, int align, int32_t* start,
+                               int32_t* count, int32_t* row, hipStream_t s) {
+  const int n = T * top_k;
+  hipLaunchKernelGGL(k_dispatch, dim3((unsigned)E), dim3(256), 0, s, ids, n, 0x7FFFFFFF, count, row);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_contig_starts, dim3(1), dim3(64), 0, s, count, E, align, start);
+  e = hipGetLastError();
+  if (e != hipSuccess || n == 0) return e;
+  hipLaunchKernelGGL(k_contig_rows, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, ids, n, start, row);
+  return hipGetLastError();
+}
+
 hipError_t dispatch(const int32_t* ids, int T, int E, int top_k, int max_m, int32_t* masked_m,
                     int32_t* row, hipStream_t s) {
   hipLaunchKernelGGL(k_dispatch, dim3((unsigned)E), dim3(256), 0, s, ids, T * top_k, max_m, masked_m,

@@ -21,11 +21,12 @@ struct StreamItem {
 };
 
 // tprefix[g] = sum over g' < g of ceil(clamped masked_m[g'] / STREAM_BM); tprefix[G] = the
-// number of units; mm_s[g] = masked_m[g] clamped to [0, max_m].  Wave 0 builds both with
+// number of units; mm_s[g] = masked_m[g] clamped to [0, max_m], or with `seg` (group row
+// starts in LDS, seg[G] = the end) to [0, seg[g + 1] - seg[g]].  Wave 0 builds both with
 // shuffle scans.  They live in LDS because a global load inside a main loop would make the
 // compiler drain the DMA queue (vmcnt(0)) to wait for it.
 __device__ __forceinline__ void stream_tile_prefix(const int32_t* masked_m, int G, int max_m, int* tprefix,
-                                                   int* mm_s, int tid) {
+                                                   int* mm_s, int tid, const int* seg = nullptr) {
   if (tid < 64) {
     const int lane = tid;
     int run = 0;
@@ -34,7 +35,8 @@ __device__ __forceinline__ void stream_tile_prefix(const int32_t* masked_m, int 
       int c = 0;
       if (g < G) {
         int mm = masked_m[g];
-        mm = mm < 0 ? 0 : (mm > max_m ? max_m : mm);
+        const int lim = seg ? seg[g + 1] - seg[g] : max_m;
+        mm = mm < 0 ? 0 : (mm > lim ? lim : mm);
         c = (mm + STREAM_BM - 1) / STREAM_BM;
         mm_s[g] = mm;
       }

@@ -77,6 +77,34 @@ int mx_grouped_gemm_masked(const uint8_t* a, const uint8_t* a_sf, const uint8_t*
                            void* stream);
 
 /*
+ * Grouped NVFP4 NT GEMM over the contiguous (expert-sorted) layout for prefill:
+ * the rows of all groups sit in one A [M_total, K], group g's from row
+ * group_start[g], with aligned padding between groups.
+ * Source: "Helion Pretuned Kernels" README, kernel table row grouped_gemm_deepgemm
+ * (DeepGEMM's packed contiguous A layout, heterogeneous per-group M, aligned
+ * padding excluded from the result).
+ *
+ *   out[r, n] = alpha[g] * sum_k dec(A)[r, k] * dec(B)[g, n, k]
+ *   for r in [group_start[g], group_start[g] + count[g]), n < N, fp32 sums
+ *
+ *   a, a_sf      device A codes [M_total, K/2], scales [M_total, K/16]
+ *   b, b_sf      device B codes [G, N, K/2], scales [G, N, K/16]
+ *   alpha        device fp32 [G], or NULL = 1
+ *   group_start  device int32 [G + 1], non-decreasing, group_start[G] <= M_total
+ *   count        device int32 [G], valid rows of each group
+ *   out          device [M_total, N] of c_dtype; padding rows are never written
+ * The kernel clamps group_start to [0, M_total] and to a running maximum, and
+ * count[g] to [0, group_start[g + 1] - group_start[g]], so no access leaves the
+ * M_total rows whatever those arrays hold.  Requirements: G <= 512, N % 128 == 0,
+ * K % 128 == 0 (else MXG_ERR_UNSUPPORTED); dtypes as in mx_grouped_gemm_masked.
+ */
+int mx_grouped_gemm_contiguous(const uint8_t* a, const uint8_t* a_sf, const uint8_t* b,
+                               const uint8_t* b_sf, const float* alpha, const int32_t* group_start,
+                               const int32_t* count, void* out, int G, int M_total, int N, int K,
+                               int ab_dtype, int sf_dtype, int c_dtype, int sf_vec_size, int cu_limit,
+                               void* stream);
+
+/*
  * One group of a heterogeneous grouped GEMM: its own (M, N, K), operand and
  * output pointers (device), alpha by value, and the output row stride ldc in
  * elements (0 = N).
@@ -163,6 +191,20 @@ int mx_quantize_nvfp4(const void* x, int x_dtype, long rows, int K, float g, uin
 int moe_route_noaux(const float* logits, const float* bias, int T, int E, int n_group,
                     int topk_group, int top_k, float rsf, int32_t* topk_ids, float* topk_w,
                     void* stream);
+
+/*
+ * Token-to-expert permutation for the contiguous layout (stable counting sort in
+ * token order, each expert's rows starting at a multiple of align).
+ *   count[e]        = number of tokens routed to e
+ *   group_start[e]  = sum over e' < e of count[e'] rounded up to a multiple of align;
+ *                     group_start[E] = the total rows (with padding)
+ *   row[t, j]       = group_start[e] + number of tokens t' < t routed to e, e = topk_ids[t, j]
+ * topk_ids device int32 [T, top_k] (distinct per token, in [0, E)); group_start
+ * device int32 [E + 1]; count device int32 [E]; row device int32 [T, top_k].
+ * 1 <= align <= 4096; T * top_k + E * align < 2^31.
+ */
+int moe_dispatch_contiguous(const int32_t* topk_ids, int T, int E, int top_k, int align,
+                            int32_t* group_start, int32_t* count, int32_t* row, void* stream);
 
 /*
  * Token-to-expert permutation for the masked layout (stable counting sort in

@@ -254,6 +254,19 @@ def dispatch(ids, E, max_m):
     return masked_m, row
 
 
+def dispatch_contiguous(ids, E, align):
+    """Contiguous layout: counts per expert, starts = exclusive sum of the counts rounded up
+    to a multiple of align ([E + 1], the last the total rows), absolute rows of the slots
+    (the expert's start plus the slot's rank in token order, from dispatch)."""
+    ids = _c(ids, np.int32)
+    T, k = ids.shape
+    count, rank = dispatch(ids, E, T * k + 1)
+    padded = (count.astype(np.int64) + align - 1) // align * align
+    start = np.zeros(E + 1, np.int64)
+    start[1:] = np.cumsum(padded)
+    return start.astype(np.int32), count, (start[ids] + rank).astype(np.int32)
+
+
 def swiglu(gate_up, I):
     lib = _lib()
     gu = _c(gate_up, np.float64)

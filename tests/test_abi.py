@@ -26,7 +26,8 @@ def _declared_functions():
 
 def test_header_lists_entry_points():
     names = _declared_functions()
-    for want in ["mx_grouped_gemm_masked", "mx_grouped_gemm", "mx_gemv_nvfp4_w4a16", "mx_quantize_nvfp4", "moe_route_noaux",
+    for want in ["mx_grouped_gemm_masked", "mx_grouped_gemm", "mx_grouped_gemm_contiguous", "moe_dispatch_contiguous",
+                 "mx_gemv_nvfp4_w4a16", "mx_quantize_nvfp4", "moe_route_noaux",
                  "moe_dispatch", "moe_quantize_gather_nvfp4", "moe_expert_forward",
                  "moe_expert_forward_workspace_size", "moe_expert_forward_workspace_layout",
                  "mxg_status_string", "mxg_last_error", "mxg_version"]:
@@ -104,6 +105,21 @@ def test_gemv_w4a16_rejects():
         a = dict(args, **kw)
         assert L.mx_gemv_nvfp4_w4a16(*a.values()) == status, kw
         assert L.mxg_last_error().decode() != ""
+
+
+def test_contiguous_rejects():
+    L = mxg.lib()
+    args = dict(a=FAKE, a_sf=FAKE, b=FAKE, b_sf=FAKE, alpha=None, gs=FAKE, cnt=FAKE, out=FAKE, G=8, M=4096, N=512,
+                K=1024, ab=mxg.MXG_E2M1, sf=mxg.MXG_E4M3, c=mxg.MXG_BF16, vec=16, cu=0, s=None)
+    for kw, status in [(dict(gs=None), mxg.MXG_ERR_INVALID_ARG), (dict(G=0), mxg.MXG_ERR_INVALID_ARG),
+                       (dict(M=0), mxg.MXG_ERR_INVALID_ARG), (dict(G=513), mxg.MXG_ERR_UNSUPPORTED),
+                       (dict(N=520), mxg.MXG_ERR_UNSUPPORTED), (dict(K=1088), mxg.MXG_ERR_UNSUPPORTED),
+                       (dict(vec=32), mxg.MXG_ERR_UNSUPPORTED), (dict(a=P((1 << 20) + 8)), mxg.MXG_ERR_INVALID_ARG)]:
+        a = dict(args, **kw)
+        assert L.mx_grouped_gemm_contiguous(*a.values()) == status, kw
+    assert L.moe_dispatch_contiguous(FAKE, 8, 256, 8, 0, FAKE, FAKE, FAKE, None) == mxg.MXG_ERR_INVALID_ARG
+    assert L.moe_dispatch_contiguous(FAKE, 8, 256, 8, 8192, FAKE, FAKE, FAKE, None) == mxg.MXG_ERR_INVALID_ARG
+    assert L.moe_dispatch_contiguous(None, 8, 256, 8, 16, FAKE, FAKE, FAKE, None) == mxg.MXG_ERR_INVALID_ARG
 
 
 def test_route_dispatch_quant_reject():

@@ -278,3 +278,53 @@ def test_hetero_gemm_tails_full(shapes):
                                            np_(q["b_sf"])[None], np.array([q["alpha"]], np.float32),
                                            [q["M"]], q["M"], q["N"], q["K"])
         assert_within(bf16_from_bits_np(bits), y[0], S[0], f"group {gi}")
+
+
+# ----------------------------------------------------------------------------- contiguous layout
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_contiguous_gemm_groups_and_padding(out_dtype):
+    """Expert-sorted rows with aligned padding: groups of 0 to 300 rows (several 256-row M
+    tiles, tails inside 16-row groups), every valid row against the oracle, the padding
+    rows and the rows past the last group left untouched."""
+    counts = [0, 1, 130, 256, 300, 17, 64, 129]
+    G, N, K, align = len(counts), 384, 512, 16
+    start = [0]
+    for c in counts:
+        start.append(start[-1] + -(-c // align) * align)
+    M_total = start[-1] + 32
+    log(f"contiguous grouped NVFP4 GEMM G={G} M_total={M_total} N={N} K={K} {out_dtype}")
+    gen = datagen.generator(2024, DEV)
+    a, a_sf = datagen.nvfp4_uniform(gen, (M_total,), K, DEV)
+    b, b_sf = datagen.nvfp4_uniform(gen, (G, N), K, DEV)
+    alpha = torch.linspace(0.05, 0.4, G, device=DEV, dtype=torch.float32)
+    gs = torch.tensor(start, dtype=torch.int32, device=DEV)
+    cnt = torch.tensor(counts, dtype=torch.int32, device=DEV)
+    out = (sentinel_bf16 if out_dtype == torch.bfloat16 else sentinel_f32)((M_total, N), DEV)
+    _mxg().mx_grouped_gemm_contiguous(a, a_sf, b, b_sf, alpha, gs, cnt, out)
+    torch.cuda.synchronize()
+    if out_dtype == torch.bfloat16:
+        bits, sent, kw = bf16_tensor_bits(out), SENT_BF16, {}
+        vals = bf16_from_bits_np(bits)
+    else:
+        bits, sent, kw = np_(out.view(torch.int32)).view(np.uint32), SENT_F32 & 0xFFFFFFFF, dict(ulp=ulp_f32)
+        vals = np_(out).astype(np.float64)
+    a_h, asf_h, b_h, bsf_h, al = np_(a), np_(a_sf), np_(b), np_(b_sf), np_(alpha)
+    valid = np.zeros(M_total, bool)
+    for g, c in enumerate(counts):
+        r0 = start[g]
+        valid[r0:r0 + c] = True
+        for m in range(c):
+            y, S = oracle.nvfp4_row_dot(a_h, asf_h, r0 + m, b_h[g], bsf_h[g], K, float(al[g]))
+            assert_within(vals[r0 + m], y, S, f"contiguous group {g} row {m}", **kw)
+    assert (bits[~valid] == sent).all(), "padding or trailing rows were written"
+
+
+@pytest.mark.parametrize("T,E,align", [(37, 16, 8), (4096, 256, 128)])
+def test_dispatch_contiguous_matches_oracle(T, E, align):
+    log(f"contiguous dispatch T={T} E={E} align={align}")
+    gen = datagen.generator(3300 + T, DEV)
+    ids = datagen.distinct_topk_ids(gen, T, E, 8, DEV)
+    gs, cnt, row = _mxg().moe_dispatch_contiguous(ids, E, align)
+    torch.cuda.synchronize()
+    s_o, c_o, r_o = oracle.dispatch_contiguous(np_(ids), E, align)
+    assert np.array_equal(np_(cnt), c_o) and np.array_equal(np_(gs), s_o) and np.array_equal(np_(row), r_o)

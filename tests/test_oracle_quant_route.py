@@ -198,3 +198,26 @@ def test_dispatch_bruteforce_and_invariants():
     assert mm.sum() == T * k
     pairs = {(int(ids[t, j]), int(row[t, j])) for t in range(T) for j in range(k)}
     assert len(pairs) == T * k
+
+
+@pytest.mark.parametrize("T,E,k,align", [(1, 8, 2, 16), (37, 16, 4, 8), (200, 256, 8, 128)])
+def test_dispatch_contiguous_invariants(T, E, k, align):
+    # brute force in token order: each slot takes the next free row of its expert's
+    # aligned segment; segments follow each other in expert order
+    rng = np.random.default_rng(T * 7 + E)
+    ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    start, count, row = oracle.dispatch_contiguous(ids, E, align)
+    want_count = np.bincount(ids.ravel(), minlength=E)
+    assert np.array_equal(count, want_count)
+    pos = 0
+    for e in range(E):
+        assert start[e] == pos and start[e] % align == 0
+        pos += -(-int(want_count[e]) // align) * align
+    assert start[E] == pos
+    nxt = start[:E].astype(np.int64).copy()
+    for t in range(T):
+        for j in range(k):
+            e = ids[t, j]
+            assert row[t, j] == nxt[e]
+            nxt[e] += 1
+    assert len(np.unique(row)) == T * k
