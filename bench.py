@@ -445,10 +445,11 @@ def bench_moe(dev, steps, warmup, precision, T, seed):
     # full-precision-intermediate variant's GEMM2 runs twice on the bf16 MFMA; its
     # algorithmic bytes and FLOPs are the layer's, as for the bf16 intermediate)
     mfma_dtype = "fp8" if fp8 else "fp16"
-    return dict(name=wl.name, ms=ms, kernel_ms=kms, wall_s=wall, bytes=byts, flops=flops,
+    name = wl.name + ("_f32h" if precision == "fp8_f32h" else "")
+    return dict(name=name, ms=ms, kernel_ms=kms, wall_s=wall, bytes=byts, flops=flops,
                 gbs=byts / ms / 1e6, tflops=flops / ms / 1e9, tokens_per_s=T / ms * 1e3,
                 bound=binding_roof(byts, flops, mfma_dtype), mfma_dtype=mfma_dtype,
-                config=dict(workload=wl.name, tokens=T, active_experts=n_act, max_m=cap))
+                config=dict(workload=name, tokens=T, active_experts=n_act, max_m=cap))
 
 
 WORKLOADS = {
