@@ -324,23 +324,29 @@ __global__ __launch_bounds__(ns::THREADS) void k_gemm_nvfp4_stream(const typenam
         as2[i][0] = half2_t{s01[0], s01[0]};
         as2[i][1] = half2_t{s01[1], s01[1]};
       }
-#pragma unroll
-      for (int ks = 0; ks < 4; ks++) {
-        // dword ks of a lane's chunk q holds K elements 32 q + 8 ks .. +7 of the step,
-        // in 16-block 2 q + ks / 2
-        half8_t bf[NB];
+      // dword ks of a lane's chunk q holds K elements 32 q + 8 ks .. +7 of the step, in
+      // 16-block 2 q + ks / 2.  The weight fragments of sub-step ks + 1 are read while the
+      // MFMAs of sub-step ks run (two register sets), so no MFMA waits on a fresh LDS read.
+      half8_t bf[2][NB];
+      auto load_bf = [&](half8_t* dst, int ks) {
 #pragma unroll
         for (int n = 0; n < NB; n++) {
           const int r = (SWIGLU ? (n < NB / 2 ? WC / 2 * wn + 16 * n : BN / 2 + WC / 2 * wn + 16 * (n - NB / 2))
                                 : WC * wn + 16 * n) + rr;
-          bf[n] = *(const half8_t*)(Bd + r * BK + (((4 * q + ks) ^ ns_sigma(rr)) << 3));
+          dst[n] = *(const half8_t*)(Bd + r * BK + (((4 * q + ks) ^ ns_sigma(rr)) << 3));
         }
+      };
+      load_bf(bf[0], 0);
+#pragma unroll
+      for (int ks = 0; ks < 4; ks++) {
+        if (ks + 1 < 4) load_bf(bf[(ks + 1) & 1], ks + 1);
 #pragma unroll
         for (int i = 0; i < RG; i++) {
           if (cit.m0 + 16 * wm + 16 * MW * i >= cit.mm) break;
           const half8_t af = decode8_e2m1_f16(araw[i][ks], as2[i][ks >> 1]);
 #pragma unroll
-          for (int n = 0; n < NB; n++) acc[i][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bf[n], af, acc[i][n], 0, 0, 0);
+          for (int n = 0; n < NB; n++)
+            acc[i][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bf[ks & 1][n], af, acc[i][n], 0, 0, 0);
         }
       }
     }
