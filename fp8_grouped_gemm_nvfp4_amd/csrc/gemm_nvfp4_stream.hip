@@ -259,18 +259,33 @@ __global__ __launch_bounds__(ns::THREADS) void k_gemm_nvfp4_stream(const typenam
   // chunk column; row r's fp16 chunk c (K 8c .. 8c + 7 in the permuted order of the
   // activation side) sits at slot c ^ sigma(r).
   int d_st = 0;  // raw stage of the next weight step to decode
-  auto decode_b = [&](int buf) {
+  struct DecB {
+    u32x4_t raw;
+    half2_t s0, s1;
+    _Float16* row;
+    int r, cq;
+  };
+  auto decode_b_begin = [&](int buf) {
     const uint8_t* st = ringB + d_st * B_STAGE;
-    const int r = 16 * wave + (lane & 7) + 8 * (lane >> 5), cq = (lane >> 3) & 3;
-    const u32x4_t raw = *(const u32x4_t*)(st + r * 64 + (cq << 4));
-    const uint32_t sb = *(const uint16_t*)(st + B_CODE + r * 8 + 2 * cq);
+    DecB d;
+    d.r = 16 * wave + (lane & 7) + 8 * (lane >> 5);
+    d.cq = (lane >> 3) & 3;
+    d.raw = *(const u32x4_t*)(st + d.r * 64 + (d.cq << 4));
+    const uint32_t sb = *(const uint16_t*)(st + B_CODE + d.r * 8 + 2 * d.cq);
     const half2_t s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sb, 1.0f, false);
-    const half2_t s0 = half2_t{s01[0], s01[0]}, s1 = half2_t{s01[1], s01[1]};
-    _Float16* row = bdec[buf] + r * BK;
-#pragma unroll
-    for (int ks = 0; ks < 4; ks++)
-      *(half8_t*)(row + (((4 * cq + ks) ^ ns_sigma(r)) << 3)) = decode8_e2m1_f16(raw[ks], ks < 2 ? s0 : s1);
+    d.s0 = half2_t{s01[0], s01[0]};
+    d.s1 = half2_t{s01[1], s01[1]};
+    d.row = bdec[buf] + d.r * BK;
     d_st = d_st + 1 == SB ? 0 : d_st + 1;
+    return d;
+  };
+  auto decode_b_part = [&](const DecB& d, int ks) {
+    *(half8_t*)(d.row + (((4 * d.cq + ks) ^ ns_sigma(d.r)) << 3)) = decode8_e2m1_f16(d.raw[ks], ks < 2 ? d.s0 : d.s1);
+  };
+  auto decode_b = [&](int buf) {
+    const DecB d = decode_b_begin(buf);
+#pragma unroll
+    for (int ks = 0; ks < 4; ks++) decode_b_part(d, ks);
   };
   // B(0) is followed by DB - 2 weight steps, A(0) and B(DB - 1): allowing only the weight
   // DMAs behind it outstanding is enough
@@ -301,11 +316,15 @@ __global__ __launch_bounds__(ns::THREADS) void k_gemm_nvfp4_stream(const typenam
     issue_b();
     // weight step s + 1 (issued before A(s), so it has landed) into the other fp16 buffer,
     // whose readers finished step s - 1 before the barrier; past the end it re-decodes
-    // a stage that is not read again
-    decode_b((s + 1) & 1);
+    // a stage that is not read again.  Its four 16-byte chunks are decoded one per
+    // sub-step, after that sub-step's MFMAs (all at once in a wave without valid rows).
+    const DecB db = decode_b_begin((s + 1) & 1);
 
     const bool active = cit.m0 + 16 * wm < cit.mm;
-    if (active) {
+    if (!active) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ks++) decode_b_part(db, ks);
+    } else {
       const uint8_t* As = ringA + c_sa * A_STAGE;
       const _Float16* Bd = bdec[s & 1];
       u32x4_t araw[RG];
@@ -348,6 +367,7 @@ __global__ __launch_bounds__(ns::THREADS) void k_gemm_nvfp4_stream(const typenam
           for (int n = 0; n < NB; n++)
             acc[i][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bf[ks & 1][n], af, acc[i][n], 0, 0, 0);
         }
+        decode_b_part(db, ks);
       }
     }
     c_sa ^= 1;
