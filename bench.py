@@ -191,6 +191,33 @@ def timed_loop(step, steps, warmup):
     return t0.elapsed_time(t1) / steps, kt.mean_ms(), wall
 
 
+def graph_loop(step, steps):
+    """Mean time of one step replayed from a captured HIP graph (the pages' grouped
+    benchmarks replay pre-captured graphs): the step is captured once after an eager call
+    on the capture stream, then replayed `steps` times back to back between two events."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step(None)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(None)
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    gpu_head_start(5.0 + 0.05 * steps)
+    t0.record()
+    for _ in range(steps):
+        g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    del g
+    return t0.elapsed_time(t1) / steps
+
+
 def binding_roof(byts, flops, mfma_dtype):
     """'hbm' or 'mfma': whichever floor (bytes at the HBM peak, flops at the MFMA peak of
     the dtype the path computes in) is longer."""
@@ -230,6 +257,7 @@ def bench_decode_gemm1(dev, steps, warmup, seed=1001, cpu=True):
             kt.stop()
 
     ms, kms, wall = timed_loop(step, steps, warmup)
+    graph_ms = graph_loop(step, steps)
     mm = masked_m.cpu().numpy()
     n_act, rows = int((mm > 0).sum()), int(mm.sum())
     w_bytes = n_act * N * NVFP4_ROW_BYTES(H)
@@ -238,7 +266,7 @@ def bench_decode_gemm1(dev, steps, warmup, seed=1001, cpu=True):
     flops = 2.0 * rows * N * H
     res = dict(name=wl.name, ms=ms, kernel_ms=kms, wall_s=wall, bytes=step_bytes, kernel_bytes=gemm_bytes,
                flops=flops, gbs=step_bytes / ms / 1e6, kernel_gbs=gemm_bytes / kms / 1e6,
-               tflops=flops / ms / 1e9, tokens_per_s=T / ms * 1e3, bound="hbm",
+               tflops=flops / ms / 1e9, tokens_per_s=T / ms * 1e3, bound="hbm", graph_ms=graph_ms,
                config=dict(workload=wl.name, experts=E, tokens=T, top_k=top_k, K=H, N=N, max_m=max_m,
                            active_experts=n_act, sum_masked_m=rows))
     if cpu:
@@ -431,6 +459,7 @@ def bench_moe(dev, steps, warmup, precision, T, seed):
             kt.stop()
 
     ms, kms, wall = timed_loop(step, steps, warmup)
+    graph_ms = graph_loop(step, steps) if T <= 64 else None
     mm = masked_m.cpu().numpy()
     n_act, rows = int((mm > 0).sum()), int(mm.sum())
     if fp8:
@@ -448,7 +477,7 @@ def bench_moe(dev, steps, warmup, precision, T, seed):
     name = wl.name + ("_f32h" if precision == "fp8_f32h" else "")
     return dict(name=name, ms=ms, kernel_ms=kms, wall_s=wall, bytes=byts, flops=flops,
                 gbs=byts / ms / 1e6, tflops=flops / ms / 1e9, tokens_per_s=T / ms * 1e3,
-                bound=binding_roof(byts, flops, mfma_dtype), mfma_dtype=mfma_dtype,
+                bound=binding_roof(byts, flops, mfma_dtype), mfma_dtype=mfma_dtype, graph_ms=graph_ms,
                 config=dict(workload=name, tokens=T, active_experts=n_act, max_m=cap))
 
 
@@ -512,6 +541,8 @@ def main():
         line["tokens_per_s"] = r["tokens_per_s"]
     line["tflops"] = r["tflops"]
     line["kernel_ms"] = r["kernel_ms"]
+    if r.get("graph_ms") is not None:
+        line["graph_ms_per_step"] = r["graph_ms"]
     line["cpu_baseline"] = r.get("cpu_baseline")
     if args.all:
         rows = []
@@ -519,7 +550,8 @@ def main():
             if name == args.workload:
                 continue
             q = fn(dev, max(5, args.steps // 5), 2, False)
-            rows.append({k: q[k] for k in ("name", "ms", "kernel_ms", "gbs", "tflops") if k in q} |
+            rows.append({k: q[k] for k in ("name", "ms", "kernel_ms", "graph_ms", "gbs", "tflops")
+                         if q.get(k) is not None} |
                         ({"shapes": q["config"]["shapes"]} if "shapes" in q["config"] else {}) |
                         ({"tokens_per_s": q["tokens_per_s"]} if "tokens_per_s" in q else {}) |
                         {"roofline": roofline_row(q)})
