@@ -429,7 +429,7 @@ def _moe_setup(dev, t, T, E=256, top_k=8):
     return ids, w, masked_m, row, cap
 
 
-def bench_moe(dev, steps, warmup, precision, T, seed):
+def bench_moe(dev, steps, warmup, precision, T, seed, w13_layout=0):
     E, H, I, top_k = 256, 7168, 2048, 8
     fp8 = precision in ("fp8", "fp8_f32h")
     if fp8:
@@ -444,9 +444,14 @@ def bench_moe(dev, steps, warmup, precision, T, seed):
         d = mxg.make_moe_desc(code, T, H, I, E, top_k, cap, t["xq"], t["w13"], t["w13_s"],
                               t["w2"], t["w2_s"], ids, w, masked_m, row, y, x_scale=t["xs"])
     else:
-        d = mxg.make_moe_desc(mxg.MXG_MOE_NVFP4, T, H, I, E, top_k, cap, t["x"], t["w13"], t["w13_sf"],
+        w13, w13_sf = t["w13"], t["w13_sf"]
+        if w13_layout:  # the same weights with gate and up rows interleaved in 16-row blocks
+            w13, w13_sf = mxg.moe_interleave_w13(w13), mxg.moe_interleave_w13(w13_sf)
+            del t["w13"], t["w13_sf"]
+            torch.cuda.synchronize()
+        d = mxg.make_moe_desc(mxg.MXG_MOE_NVFP4, T, H, I, E, top_k, cap, t["x"], w13, w13_sf,
                               t["w2"], t["w2_sf"], ids, w, masked_m, row, y, g_x=s["g_x"], g_w13=t["g_w13"],
-                              g_w2=t["g_w2"], g_h=s["g_h"])
+                              g_w2=t["g_w2"], g_h=s["g_h"], w13_layout=w13_layout)
     ws = torch.empty((mxg.moe_expert_forward_workspace_size(d),), dtype=torch.uint8, device=dev)
 
     def step(kt):
@@ -474,7 +479,7 @@ def bench_moe(dev, steps, warmup, precision, T, seed):
     # full-precision-intermediate variant's GEMM2 runs twice on the bf16 MFMA; its
     # algorithmic bytes and FLOPs are the layer's, as for the bf16 intermediate)
     mfma_dtype = "fp8" if fp8 else "fp16"
-    name = wl.name + ("_f32h" if precision == "fp8_f32h" else "")
+    name = wl.name + ("_f32h" if precision == "fp8_f32h" else "") + ("_w13il16" if w13_layout else "")
     return dict(name=name, ms=ms, kernel_ms=kms, wall_s=wall, bytes=byts, flops=flops,
                 gbs=byts / ms / 1e6, tflops=flops / ms / 1e9, tokens_per_s=T / ms * 1e3,
                 bound=binding_roof(byts, flops, mfma_dtype), mfma_dtype=mfma_dtype, graph_ms=graph_ms,
@@ -489,6 +494,8 @@ WORKLOADS = {
     "moe_fp8_f32h": lambda dev, k, w, cpu: bench_moe(dev, k, w, "fp8_f32h", 4096, 1003),
     "moe_nvfp4_decode": lambda dev, k, w, cpu: bench_moe(dev, k, w, "nvfp4", 64, 1004),
     "moe_nvfp4_prefill": lambda dev, k, w, cpu: bench_moe(dev, k, w, "nvfp4", 8192, 1004),
+    "moe_nvfp4_decode_w13il16": lambda dev, k, w, cpu: bench_moe(dev, k, w, "nvfp4", 64, 1004, 16),
+    "moe_nvfp4_prefill_w13il16": lambda dev, k, w, cpu: bench_moe(dev, k, w, "nvfp4", 8192, 1004, 16),
     "gemv_w4a16": lambda dev, k, w, cpu: bench_gemv_w4a16(dev, k, w),
     "contiguous_gemm1": lambda dev, k, w, cpu: bench_contiguous(dev, k, w),
 }

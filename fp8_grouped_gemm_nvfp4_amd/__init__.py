@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libmxg.so")
 MXG_OK, MXG_ERR_INVALID_ARG, MXG_ERR_UNSUPPORTED, MXG_ERR_WORKSPACE, MXG_ERR_HIP = range(5)
 MXG_E2M1, MXG_E4M3, MXG_BF16, MXG_F32 = 1, 2, 3, 4
 MXG_MOE_FP8_BLOCK128, MXG_MOE_NVFP4, MXG_MOE_FP8_BLOCK128_F32H = 1, 2, 3
+MXG_W13_STACKED, MXG_W13_INTERLEAVED16 = 0, 16
 MXG_MAX_GROUPS = 32
 
 
@@ -42,7 +43,8 @@ class MoeDesc(ctypes.Structure):
                 ("w2", ctypes.c_void_p), ("w2_scale", ctypes.c_void_p), ("g_w2", ctypes.c_void_p),
                 ("g_h", ctypes.c_float),
                 ("topk_ids", ctypes.c_void_p), ("topk_w", ctypes.c_void_p), ("masked_m", ctypes.c_void_p),
-                ("row", ctypes.c_void_p), ("y", ctypes.c_void_p), ("dbg_h", ctypes.c_void_p)]
+                ("row", ctypes.c_void_p), ("y", ctypes.c_void_p), ("dbg_h", ctypes.c_void_p),
+                ("w13_layout", ctypes.c_int)]
 
 
 _LIB = None
@@ -61,6 +63,7 @@ SIGNATURES = {
     "moe_route_noaux": (_I, [_P, _P, _I, _I, _I, _I, _I, _F, _P, _P, _P]),
     "moe_dispatch": (_I, [_P, _I, _I, _I, _I, _P, _P, _P]),
     "moe_quantize_gather_nvfp4": (_I, [_P, _I, _I, _F, _P, _P, _I, _I, _I, _P, _P, _P]),
+    "moe_interleave_w13": (_I, [_P, _P, _I, _I, _I, _P]),
     "moe_expert_forward_workspace_size": (_SZ, [_P]),
     "moe_expert_forward_workspace_layout": (_I, [_P, _P]),
     "moe_expert_forward": (_I, [_P, _P, _SZ, _P]),
@@ -220,11 +223,21 @@ def moe_quantize_gather_nvfp4(x, g_x, ids, row, E, max_m, a=None, a_sf=None, str
 
 def make_moe_desc(precision, T, H, I, E, top_k, max_m, x, w13, w13_scale, w2, w2_scale,
                   topk_ids, topk_w, masked_m, row, y, x_scale=None, g_x=0.0, g_w13=None, g_w2=None,
-                  g_h=0.0, dbg_h=None):
+                  g_h=0.0, dbg_h=None, w13_layout=0):
     return MoeDesc(precision, T, H, I, E, top_k, max_m, _ptr(x), _ptr(x_scale), float(g_x),
                    _ptr(w13), _ptr(w13_scale), _ptr(g_w13), _ptr(w2), _ptr(w2_scale), _ptr(g_w2),
                    float(g_h), _ptr(topk_ids), _ptr(topk_w), _ptr(masked_m), _ptr(row), _ptr(y),
-                   _ptr(dbg_h))
+                   _ptr(dbg_h), int(w13_layout))
+
+
+def moe_interleave_w13(src, dst=None, stream=None):
+    """Stacked W13 rows (codes [E, 2I, H/2] or scales [E, 2I, H/16], uint8) into the
+    16-row gate/up-interleaved order (MXG_W13_INTERLEAVED16)."""
+    E, two_i, row_bytes = src.shape
+    if dst is None:
+        dst = torch.empty_like(src)
+    _check(lib().moe_interleave_w13(_ptr(src), _ptr(dst), E, two_i // 2, row_bytes, _stream(stream)))
+    return dst
 
 
 def moe_expert_forward_workspace_size(desc: MoeDesc) -> int:

@@ -239,6 +239,19 @@ int moe_quantize_gather_nvfp4(const uint16_t* x, int T, int H, float g_x, const 
                     "moe_quantize_gather_nvfp4 launch");
 }
 
+int moe_interleave_w13(const uint8_t* src, uint8_t* dst, int E, int I, int row_bytes, void* stream) {
+  if (!src || !dst) return fail(MXG_ERR_INVALID_ARG, "moe_interleave_w13: null pointer");
+  if (E < 0 || I < 0 || row_bytes < 0) return fail(MXG_ERR_INVALID_ARG, "moe_interleave_w13: bad sizes");
+  if (I % 16 != 0 || row_bytes % 4 != 0)
+    return fail(MXG_ERR_UNSUPPORTED, "moe_interleave_w13: needs I %% 16 == 0 and row_bytes %% 4 == 0");
+  if (((uintptr_t)src & 3u) || ((uintptr_t)dst & 3u))
+    return fail(MXG_ERR_INVALID_ARG, "moe_interleave_w13: misaligned pointer");
+  const size_t n = (size_t)E * 2 * I * row_bytes;
+  if ((uintptr_t)src < (uintptr_t)dst + n && (uintptr_t)dst < (uintptr_t)src + n && n > 0)
+    return fail(MXG_ERR_INVALID_ARG, "moe_interleave_w13: src and dst overlap");
+  return hip_status(mxg::interleave_w13(src, dst, E, I, row_bytes, (hipStream_t)stream), "moe_interleave_w13 launch");
+}
+
 // ----------------------------------------------------------------------------- MoE layer
 static int check_moe(const mxg_moe_desc* d) {
   if (!d) return fail(MXG_ERR_INVALID_ARG, "moe_expert_forward: null descriptor");
@@ -258,6 +271,10 @@ static int check_moe(const mxg_moe_desc* d) {
     return fail(MXG_ERR_INVALID_ARG, "moe_expert_forward: null pointer");
   if (fp8 && !d->x_scale)
     return fail(MXG_ERR_INVALID_ARG, "moe_expert_forward: FP8 needs x_scale");
+  if (d->w13_layout != MXG_W13_STACKED && d->w13_layout != MXG_W13_INTERLEAVED16)
+    return fail(MXG_ERR_INVALID_ARG, "moe_expert_forward: unknown w13_layout %d", d->w13_layout);
+  if (fp8 && d->w13_layout != MXG_W13_STACKED)
+    return fail(MXG_ERR_UNSUPPORTED, "moe_expert_forward: the interleaved W13 layout is NVFP4 only");
   if (d->precision == MXG_MOE_NVFP4) {
     if (!d->g_w13 || !d->g_w2) return fail(MXG_ERR_INVALID_ARG, "moe_expert_forward: NVFP4 needs g_w13/g_w2");
     if (!(d->g_x > 0.0f) || !(d->g_h > 0.0f) || d->g_x == __builtin_inff() || d->g_h == __builtin_inff())
@@ -348,6 +365,7 @@ int moe_expert_forward(const mxg_moe_desc* d, void* ws, size_t ws_bytes, void* s
     p1.out = nullptr; p1.masked_m = d->masked_m; p1.alpha = d->g_w13; p1.alpha_scale = d->g_x;
     p1.G = E; p1.max_m = mm; p1.N = 2 * I; p1.K = H;
     p1.h_codes = hc; p1.h_sf = hsf; p1.dbg_h = d->dbg_h; p1.g_h = d->g_h;
+    p1.w13_il16 = d->w13_layout == MXG_W13_INTERLEAVED16;
     e = mxg::gemm_nvfp4_masked(p1, mxg::EPI_SWIGLU_NVFP4, 0, s);
     if (e != hipSuccess) return hip_status(e, "gemm1 nvfp4 swiglu");
     mxg::MaskedGemmArgs p2{};

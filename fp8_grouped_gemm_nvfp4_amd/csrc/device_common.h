@@ -160,6 +160,16 @@ __device__ __forceinline__ uint32_t quantize_block_x4(const float h[4], float g,
   return bits;
 }
 
+// Physical row of logical W13 row r (gate rows [0, I), up rows [I, 2I)): r itself in
+// the stacked layout; with gate and up interleaved in 16-row blocks, gate row j sits at
+// 32 (j / 16) + j % 16 and up row j 16 rows after it.
+__device__ __forceinline__ int w13_row(int r, int I, bool il16) {
+  if (!il16) return r;
+  const bool up = r >= I;
+  const int j = up ? r - I : r;
+  return ((j >> 4) << 5) + (up ? 16 : 0) + (j & 15);
+}
+
 // LDS DMA (global_load_lds_*): 64 lanes each copy 16 (or 4) bytes from their own global
 // address into LDS at base + lane * 16 (or 4), without passing through registers.  The
 // streaming kernels issue every asynchronous operation of their main loops this way and

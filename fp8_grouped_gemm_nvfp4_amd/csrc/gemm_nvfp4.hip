@@ -182,7 +182,7 @@ __global__ __launch_bounds__(256) void k_gemm_nvfp4(const typename ArgsOf<MODE>:
         const int half_n = j.N / 2;  // I
         int hc = j.n0 + (r < BN / 2 ? r : r - BN / 2);
         hc = hc < half_n ? hc : half_n - 1;
-        gr = r < BN / 2 ? hc : half_n + hc;
+        gr = w13_row(r < BN / 2 ? hc : half_n + hc, half_n, p.w13_il16 != 0);
       } else {
         gr = (j.n0 + r < j.N) ? j.n0 + r : j.N - 1;
       }

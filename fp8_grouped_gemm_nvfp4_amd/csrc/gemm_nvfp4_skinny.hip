@@ -56,18 +56,23 @@ struct TileSrc {
   size_t scale;
 };
 
-__device__ __forceinline__ TileSrc tile_src(int first_row, int nlimit, int row_off, int K, int lane) {
+// With il16 (SwiGLU tiles only, nlimit = I) the logical W13 row is mapped to its place
+// in the gate/up-interleaved layout.
+__device__ __forceinline__ TileSrc tile_src(int first_row, int nlimit, int row_off, int K, int lane,
+                                            bool il16 = false) {
   TileSrc s;
 #pragma unroll
   for (int i = 0; i < 4; i++) {
     int r = 4 * i + (lane >> 4);
     int g = first_row + r;
     g = (g < nlimit ? g : nlimit - 1) + row_off;  // rows past the end re-read a valid row (never stored)
+    g = w13_row(g, nlimit, il16);
     s.code[i] = (size_t)g * (K / 2) + (size_t)(((lane & 15) ^ r) * 16);
   }
   int r = (lane & 31) >> 1;
   int g = first_row + r;
   g = (g < nlimit ? g : nlimit - 1) + row_off;
+  g = w13_row(g, nlimit, il16);
   s.scale = (size_t)g * (K / 16) + (size_t)(((lane & 1) ^ ((r >> 3) & 1)) * 16);
   return s;
 }
@@ -291,11 +296,11 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_nvfp4_skinny(const MaskedGe
     const int c0 = ncol0_of(un.nt);
     if constexpr (PAIRED) {
       const int I = p.N / 2;
-      src[0] = tile_src(c0, I, (wave & 1) ? I : 0, K, lane);
+      src[0] = tile_src(c0, I, (wave & 1) ? I : 0, K, lane, p.w13_il16 != 0);
     } else if constexpr (SWIGLU) {
       const int I = p.N / 2;
-      src[0] = tile_src(c0, I, 0, K, lane);
-      src[1] = tile_src(c0, I, I, K, lane);
+      src[0] = tile_src(c0, I, 0, K, lane, p.w13_il16 != 0);
+      src[1] = tile_src(c0, I, I, K, lane, p.w13_il16 != 0);
     } else {
 #pragma unroll
       for (int t = 0; t < NT; t++) src[t] = tile_src(c0 + 16 * t, p.N, 0, K, lane);

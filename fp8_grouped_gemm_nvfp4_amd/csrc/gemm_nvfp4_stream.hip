@@ -174,7 +174,7 @@ __global__ __launch_bounds__(ns::THREADS) void k_gemm_nvfp4_stream(const typenam
   // B row r of an item (stage row): SwiGLU rows [0, 64) are gate rows n0 + r, [64, 128)
   // the matching up rows I + n0 + r - 64
   auto b_row = [&](const NsJob& it, int r) {
-    if constexpr (SWIGLU) return r < BN / 2 ? it.n0 + r : I + it.n0 + (r - BN / 2);
+    if constexpr (SWIGLU) return w13_row(r < BN / 2 ? it.n0 + r : I + it.n0 + (r - BN / 2), I, p.w13_il16 != 0);
     else return it.n0 + r;
   };
 

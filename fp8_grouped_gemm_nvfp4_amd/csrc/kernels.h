@@ -33,6 +33,9 @@ struct MaskedGemmArgs {
   // contiguous layout (MODE_CONTIG): A [max_m, K] and C [max_m, N] hold every group's rows,
   // group g from row row_start[g] (row_start [G + 1]); masked_m[g] counts its valid rows
   const int32_t* row_start;
+  // SwiGLU epilogue: B holds W13 with gate and up rows interleaved in 16-row blocks
+  // (gate rows [16 j, 16 j + 16) at [32 j, 32 j + 16), the matching up rows after them)
+  int w13_il16;
 };
 
 struct HeteroGroup {
@@ -133,6 +136,7 @@ hipError_t quantize_gather_nvfp4(const uint16_t* x, int T, int H, float g_x, con
 hipError_t gather_fp8(const uint8_t* xq, const float* xs, int T, int H, const int32_t* ids,
                       const int32_t* row, int top_k, int max_m, uint8_t* a, float* a_s,
                       hipStream_t s);
+hipError_t interleave_w13(const uint8_t* src, uint8_t* dst, int E, int I, int row_bytes, hipStream_t s);
 hipError_t combine(const float* o, const int32_t* ids, const int32_t* row, const float* w, int T,
                    int H, int top_k, int max_m, uint16_t* y, hipStream_t s);
 

@@ -170,6 +170,29 @@ __global__ __launch_bounds__(256) void k_combine(const float* o, const int32_t* 
   *(u32x2_t*)(y + (size_t)t * H + (size_t)q * 4) = u32x2_t{lo, hi};
 }
 
+// Stacked -> interleaved W13 rows, one dword per thread (grid-stride).
+__global__ __launch_bounds__(256) void k_interleave_w13(const uint32_t* src, uint32_t* dst, int E, int I,
+                                                        int row_dw) {
+  const long total = (long)E * 2 * I * row_dw;
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < total; i += (long)gridDim.x * 256) {
+    const long prow = i / row_dw;
+    const int c = (int)(i - prow * row_dw);
+    const int e = (int)(prow / (2 * I)), r = (int)(prow - (long)e * 2 * I);
+    const int j = 16 * (r >> 5) + (r & 15);  // gate / up index of physical row r
+    const int lrow = (r & 16) ? I + j : j;
+    dst[i] = src[((long)e * 2 * I + lrow) * row_dw + c];
+  }
+}
+
+hipError_t interleave_w13(const uint8_t* src, uint8_t* dst, int E, int I, int row_bytes, hipStream_t s) {
+  const long dw = (long)E * 2 * I * (row_bytes / 4);
+  if (dw == 0) return hipSuccess;
+  const long blocks = (dw + 255) / 256;
+  hipLaunchKernelGGL(k_interleave_w13, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), 0, s,
+                     (const uint32_t*)src, (uint32_t*)dst, E, I, row_bytes / 4);
+  return hipGetLastError();
+}
+
 hipError_t combine(const float* o, const int32_t* ids, const int32_t* row, const float* w, int T,
                    int H, int top_k, int max_m, uint16_t* y, hipStream_t s) {
   long n = (long)T * (H / 4);

@@ -233,6 +233,26 @@ int moe_quantize_gather_nvfp4(const uint16_t* x, int T, int H, float g_x,
 /* Precision of moe_expert_forward. */
 typedef enum { MXG_MOE_FP8_BLOCK128 = 1, MXG_MOE_NVFP4 = 2, MXG_MOE_FP8_BLOCK128_F32H = 3 } mxg_moe_precision;
 
+/* Row order of W13 (and of its scale rows).
+ *   MXG_W13_STACKED: gate rows [0, I), then up rows [I, 2I).
+ *   MXG_W13_INTERLEAVED16: gate and up rows interleaved in blocks of 16: rows
+ *     [32 j, 32 j + 16) hold gate rows [16 j, 16 j + 16) and rows [32 j + 16, 32 j + 32)
+ *     the matching up rows, so every 32-row slice holds the gate and up columns of
+ *     the same 16 h columns.
+ * Source: Helion "pretuned_kernels" README, interleaved_swiglu row (a projection
+ * with interleaved gate/value columns feeding a compact SwiGLU epilogue).  The
+ * block of 16 rows (one MFMA tile) is this library's reading of "interleaved". */
+typedef enum { MXG_W13_STACKED = 0, MXG_W13_INTERLEAVED16 = 16 } mxg_w13_layout;
+
+/* Reorders the rows of a stacked W13 array (codes [E, 2I, H/2] or scales
+ * [E, 2I, H/16], row_bytes = H/2 or H/16) into the MXG_W13_INTERLEAVED16 order:
+ * dst row r of expert e is src row (r mod 32 < 16 ? 16 (r / 32) + r mod 32 :
+ * I + 16 (r / 32) + r mod 32 - 16).  src and dst are device arrays of E * 2I *
+ * row_bytes bytes that must not overlap.  Requires I % 16 == 0, row_bytes % 4 == 0,
+ * 4-byte aligned pointers (else MXG_ERR_INVALID_ARG / MXG_ERR_UNSUPPORTED).
+ * Asynchronous on `stream`; a one-off weight preparation, not part of a layer step. */
+int moe_interleave_w13(const uint8_t* src, uint8_t* dst, int E, int I, int row_bytes, void* stream);
+
 /*
  * The routed expert computation of one MoE layer: gather -> GEMM1 (W13, gate
  * rows [0, I) and up rows [I, 2I)) -> SwiGLU h = silu(gate) * up -> GEMM2 (W2)
@@ -264,6 +284,10 @@ typedef enum { MXG_MOE_FP8_BLOCK128 = 1, MXG_MOE_NVFP4 = 2, MXG_MOE_FP8_BLOCK128
  *   dbg_h    optional device fp32 [E, max_m, I]: NVFP4 only, receives the
  *            pre-quantization intermediate for the rows it computes (NULL in
  *            production; y is bit-identical either way).
+ *   w13_layout  mxg_w13_layout of w13 and its scales; MXG_W13_INTERLEAVED16 is
+ *            NVFP4 only (MXG_ERR_UNSUPPORTED for the FP8 precisions).  The layer's
+ *            result does not depend on the layout: y is bit-identical for the same
+ *            logical weights.
  * Requirements: H % 128 == 0, I % 128 == 0, 1 <= top_k <= 8, max_m >= 1; both FP8
  * precisions also E <= 1024 (else MXG_ERR_UNSUPPORTED).
  * Workspace: ws of at least moe_expert_forward_workspace_size(desc) bytes,
@@ -289,6 +313,7 @@ typedef struct {
   const int32_t* row;
   uint16_t* y;
   float* dbg_h;
+  int w13_layout;
 } mxg_moe_desc;
 
 /* Bytes of workspace moe_expert_forward needs for this descriptor (0 on a bad

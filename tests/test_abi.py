@@ -192,6 +192,28 @@ def test_moe_workspace_layout_and_rejects():
     assert L.moe_expert_forward(ctypes.byref(d8), FAKE, 1 << 40, None) == mxg.MXG_ERR_INVALID_ARG
 
 
+def test_w13_layout_rejects():
+    L = mxg.lib()
+    off = (ctypes.c_size_t * 6)()
+    d = _desc(w13_layout=mxg.MXG_W13_INTERLEAVED16)
+    assert L.moe_expert_forward_workspace_layout(ctypes.byref(d), off) == mxg.MXG_OK
+    for bad, want in [(dict(w13_layout=8), mxg.MXG_ERR_INVALID_ARG),
+                      (dict(w13_layout=mxg.MXG_W13_INTERLEAVED16, precision=mxg.MXG_MOE_FP8_BLOCK128),
+                       mxg.MXG_ERR_UNSUPPORTED),
+                      (dict(w13_layout=mxg.MXG_W13_INTERLEAVED16, precision=mxg.MXG_MOE_FP8_BLOCK128_F32H),
+                       mxg.MXG_ERR_UNSUPPORTED)]:
+        db = _desc(**bad)
+        assert L.moe_expert_forward(ctypes.byref(db), FAKE, 1 << 40, None) == want, bad
+    # the weight re-layout: null, sizes, alignment and overlap are refused before any launch
+    A, B = P(1 << 20), P(1 << 30)
+    assert L.moe_interleave_w13(None, B, 4, 64, 512, None) == mxg.MXG_ERR_INVALID_ARG
+    assert L.moe_interleave_w13(A, B, 4, 24, 512, None) == mxg.MXG_ERR_UNSUPPORTED   # I % 16
+    assert L.moe_interleave_w13(A, B, 4, 64, 510, None) == mxg.MXG_ERR_UNSUPPORTED   # row_bytes % 4
+    assert L.moe_interleave_w13(P((1 << 20) + 2), B, 4, 64, 512, None) == mxg.MXG_ERR_INVALID_ARG
+    assert L.moe_interleave_w13(A, P((1 << 20) + 4096), 4, 64, 512, None) == mxg.MXG_ERR_INVALID_ARG
+    assert L.moe_interleave_w13(A, B, -1, 64, 512, None) == mxg.MXG_ERR_INVALID_ARG
+
+
 def test_product_path_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(mxg, "LIB_PATH", str(tmp_path / "missing.so"))
     monkeypatch.setattr(mxg, "_LIB", None)
