@@ -61,7 +61,7 @@ __global__ __launch_bounds__(256) void k_route_noaux(const float* logits, const 
   }
   const bool keep = rank < topk_group;
 
-  bool taken[4] = {false, false, false, false};
+  uint32_t taken = 0;  // bit i: this lane's expert 4 lane + i already selected (a mask, not an array: no scratch)
   int my_id = -1;
   float my_s = 0.0f;
   for (int j = 0; j < top_k; j++) {
@@ -72,7 +72,7 @@ __global__ __launch_bounds__(256) void k_route_noaux(const float* logits, const 
 #pragma unroll
       for (int i = 0; i < 4; i++) {
         int e = lane * 4 + i;
-        if (!taken[i] && (bi == 0x7FFFFFFF || better(sb[i], e, bv, bi))) { bv = sb[i]; bi = e; bsv = s[i]; }
+        if (!((taken >> i) & 1u) && (bi == 0x7FFFFFFF || better(sb[i], e, bv, bi))) { bv = sb[i]; bi = e; bsv = s[i]; }
       }
     }
     for (int off = 32; off >= 1; off >>= 1) {
@@ -82,7 +82,7 @@ __global__ __launch_bounds__(256) void k_route_noaux(const float* logits, const 
       bool take_other = (oi != 0x7FFFFFFF) && (bi == 0x7FFFFFFF || better(ov, oi, bv, bi));
       if (take_other) { bv = ov; bi = oi; bsv = os; }
     }
-    if ((bi >> 2) == lane) taken[bi & 3] = true;
+    if ((bi >> 2) == lane) taken |= 1u << (bi & 3);
     if (lane == j) { my_id = bi; my_s = bsv; }
   }
   // denominator: fp32 sum of the selected s in slot order
