@@ -172,6 +172,41 @@ def gpu_head_start(ms):
     torch.cuda._sleep(int(ms * _SLEEP_CYCLES_PER_MS))
 
 
+# Cold-cache samples of the main workload: each sample is preceded by a 1 GiB scratch
+# pass that evicts the L2s and the 256 MB Infinity Cache, then one step is timed alone.
+COLD = {"samples": 0, "result": None}
+
+
+def cold_samples(step, n, nbytes=1 << 30):
+    """n samples of one step each after a scrub, with a GPU head start so that the events
+    bracket GPU work only.  "dirty": the scrub writes the buffer (the caches then hold
+    dirty lines that the step's reads must evict, as after a memset clear of L2);
+    "clean": the scrub only reads it."""
+    scrub = torch.empty((nbytes,), dtype=torch.uint8, device="cuda")
+    scrub.fill_(1)
+    out = {"samples": n, "scrub_bytes": nbytes}
+    for kind in ("dirty", "clean"):
+        times = []
+        for _ in range(n):
+            if kind == "dirty":
+                scrub.zero_()
+            else:
+                scrub.view(torch.int64).max()
+            gpu_head_start(1.0)
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            step(None)
+            b.record()
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b))
+        t = np.array(times)
+        out[kind] = {"median_ms": float(np.median(t)), "min_ms": float(t.min()),
+                     "p90_ms": float(np.percentile(t, 90))}
+    del scrub
+    return out
+
+
 def timed_loop(step, steps, warmup):
     for _ in range(warmup):
         step(None)
@@ -188,6 +223,8 @@ def timed_loop(step, steps, warmup):
     t1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    if COLD["samples"] > 0 and COLD["result"] is None:
+        COLD["result"] = cold_samples(step, COLD["samples"])
     return t0.elapsed_time(t1) / steps, kt.mean_ms(), wall
 
 
@@ -509,6 +546,8 @@ def main():
     ap.add_argument("--workload", default="decode_gemm1", choices=sorted(WORKLOADS))
     ap.add_argument("--all", action="store_true", help="also time every other workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold", type=int, default=10,
+                    help="cold-cache samples of the main workload (each after a 1 GiB scrub); 0 = none")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration under rocprofv3 --pmc)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -524,7 +563,9 @@ def main():
     _ensure_built()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    COLD["samples"] = max(0, args.cold)
     r = WORKLOADS[args.workload](dev, args.steps, args.warmup, not args.no_cpu_baseline)
+    COLD["samples"] = 0
 
     line = {
         "metric": "masked grouped GEMM GB/s & TFLOP/s (% roofline); MoE layer tokens/s, 1 GPU",
@@ -550,6 +591,8 @@ def main():
     line["kernel_ms"] = r["kernel_ms"]
     if r.get("graph_ms") is not None:
         line["graph_ms_per_step"] = r["graph_ms"]
+    if COLD["result"] is not None:
+        line["cold"] = COLD["result"]
     line["cpu_baseline"] = r.get("cpu_baseline")
     if args.all:
         rows = []
