@@ -142,13 +142,15 @@ __device__ __forceinline__ void decode_a_chunk(_Float16* As, const uint8_t* raw,
 
 // MFMA over one staged chunk.  Lane (n = l%16, q = l/16) reads unit 4j + q of row n (at
 // swizzled position (4j+q) ^ n) and the two scale bytes of its elements' 16-blocks.
-// Activation lanes of padding rows read row rows-1 (their output columns are never
-// stored).
+// Activation lanes of padding rows read the buffer's zero row zrow (their output columns
+// are never stored): most decode tiles hold one valid row, and zero operands in the other
+// fifteen MFMA columns draw less power than copies of a valid row, which matters once
+// back-to-back launches run into the power limit.
 template <int NT>
 __device__ __forceinline__ void compute_chunk(float4_t (&acc)[NT], const uint8_t* stage, const _Float16* As,
-                                              int lane, int rows) {
+                                              int lane, int rows, int zrow) {
   const int n = lane & 15, q = lane >> 4;
-  const int ma = n < rows ? n : rows - 1;
+  const int ma = n < rows ? n : zrow;
 #pragma unroll
   for (int j = 0; j < 4; j++) {
     u32x4_t w[NT];
@@ -268,7 +270,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_nvfp4_skinny(const MaskedGe
   constexpr int WAIT_0 = WAIT_0a < WAIT_0b ? WAIT_0a : WAIT_0b;
   constexpr int WAIT_PRO = (DA - 2) * A_OPS + (S - 1) * W_OPS;  // activation chunk 0 in the prologue
 
-  __shared__ __attribute__((aligned(16))) _Float16 As[2][MR * sk::APITCH];
+  __shared__ __attribute__((aligned(16))) _Float16 As[2][(MR + 1) * sk::APITCH];  // row MR: zeros
   __shared__ __attribute__((aligned(16))) uint8_t Araw[DA][ARaw<MR>::BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t Bst[WAVES][S][NT * sk::TILE_STAGE];
   __shared__ uint16_t list[sk::MAX_LIST];
@@ -281,6 +283,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_nvfp4_skinny(const MaskedGe
   const int K = p.K, nchunks = K / sk::KC;
   const int tiles_n = p.tiles_n;
 
+  for (int i = tid; i < 2 * (sk::APITCH / 8); i += THREADS)  // the zero rows (never written again)
+    *(half8_t*)(&As[i / (sk::APITCH / 8)][MR * sk::APITCH + (i % (sk::APITCH / 8)) * 8]) = half8_t{};
   build_unit_list<MR>(p, list, &list_n, alpha_s, tid, THREADS);
   const int total = list_n * tiles_n;
   if ((int)blockIdx.x >= total) return;  // uniform over the workgroup
@@ -382,7 +386,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_nvfp4_skinny(const MaskedGe
     // and the raw stage of chunk f+DA may be rewritten), activation buffer f&1 is
     // complete and activation chunk f+1 is in LDS.
     __syncthreads();
-    compute_chunk<NT>(acc, &Bst[wave][f % S][0], As[f & 1], lane, cu.rows);
+    compute_chunk<NT>(acc, &Bst[wave][f % S][0], As[f & 1], lane, cu.rows, MR);
 
     if (cc == nchunks - 1) {
       // epilogue of the unit
