@@ -186,7 +186,7 @@ def cold_samples(step, n, nbytes=1 << 30):
     scrub.fill_(1)
     out = {"samples": n, "scrub_bytes": nbytes}
     for kind in ("dirty", "clean"):
-        times = []
+        times, ktimes = [], []
         for _ in range(n):
             if kind == "dirty":
                 scrub.zero_()
@@ -195,14 +195,16 @@ def cold_samples(step, n, nbytes=1 << 30):
             gpu_head_start(1.0)
             a = torch.cuda.Event(enable_timing=True)
             b = torch.cuda.Event(enable_timing=True)
+            kt = Timer()
             a.record()
-            step(None)
+            step(kt)
             b.record()
             torch.cuda.synchronize()
             times.append(a.elapsed_time(b))
-        t = np.array(times)
+            ktimes.append(kt.mean_ms())
+        t, k = np.array(times), np.array(ktimes)
         out[kind] = {"median_ms": float(np.median(t)), "min_ms": float(t.min()),
-                     "p90_ms": float(np.percentile(t, 90))}
+                     "p90_ms": float(np.percentile(t, 90)), "kernel_median_ms": float(np.median(k))}
     del scrub
     return out
 
