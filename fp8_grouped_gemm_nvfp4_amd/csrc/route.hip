@@ -105,25 +105,42 @@ hipError_t route_noaux(const float* logits, const float* bias, int T, int E, int
   return hipGetLastError();
 }
 
-// One workgroup per expert e.  Each pass covers 1024 flattened slots (4 per
+// One workgroup per expert e.  Each pass covers 4096 flattened slots (16 per
 // thread, in order); the rank of a matching slot is the number of matches at
 // smaller flat index, which equals the number of earlier tokens routed to e
 // because a token's ids are distinct.
 __global__ __launch_bounds__(256) void k_dispatch(const int32_t* ids, int n, int max_m,
                                                   int32_t* masked_m, int32_t* row) {
+  constexpr int PT = 16, PASS = 256 * PT;  // slots per thread and per pass
   const int e = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   __shared__ int wave_tot[4];
+  // the next pass's ids are loaded while the current pass is scanned (the passes would
+  // otherwise each wait a full memory latency)
+  const bool vec = ((uintptr_t)ids & 15u) == 0;
+  auto load = [&](int f, int (&v)[PT]) {
+#pragma unroll
+    for (int c = 0; c < PT; c += 4) {
+      if (vec && f + c + 3 < n) {
+        const int4 q = *(const int4*)(ids + f + c);
+        v[c] = q.x; v[c + 1] = q.y; v[c + 2] = q.z; v[c + 3] = q.w;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; i++) v[c + i] = f + c + i < n ? ids[f + c + i] : -1;
+      }
+    }
+  };
+  int cur[PT], nxt[PT];
+#pragma unroll
+  for (int i = 0; i < PT; i++) nxt[i] = -1;
+  load(tid * PT, cur);
   int base = 0;
-  for (int f0 = 0; f0 < n; f0 += 1024) {
-    int f = f0 + tid * 4;
-    int match[4];
+  for (int f0 = 0; f0 < n; f0 += PASS) {
+    const int f = f0 + tid * PT;
+    if (f0 + PASS < n) load(f + PASS, nxt);
     int cnt = 0;
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-      match[i] = (f + i < n) && ids[f + i] == e;
-      cnt += match[i];
-    }
+    for (int i = 0; i < PT; i++) cnt += (f + i < n) && cur[i] == e;
     // inclusive wave scan of cnt
     int inc = cnt;
     for (int off = 1; off < 64; off <<= 1) {
@@ -140,9 +157,11 @@ __global__ __launch_bounds__(256) void k_dispatch(const int32_t* ids, int n, int
     }
     int r = base + before + inc - cnt;
 #pragma unroll
-    for (int i = 0; i < 4; i++)
-      if (match[i]) row[f + i] = r++;
+    for (int i = 0; i < PT; i++)
+      if ((f + i < n) && cur[i] == e) row[f + i] = r++;
     base += total;
+#pragma unroll
+    for (int i = 0; i < PT; i++) cur[i] = nxt[i];
     __syncthreads();
   }
   if (tid == 0) masked_m[e] = base < max_m ? base : max_m;
