@@ -6,10 +6,12 @@ of the bf16 activations into the masked layout -> masked grouped NVFP4 GEMM1 aga
 W13 [256, 4096, 7168] with bf16 output.  Inputs are resident in HBM before timing.
 
 Prints ONE JSON line with the metric, a roofline object for the dominant kernel
-(algorithmic bytes / its HIP-event-timed average duration) and the oracle's CPU
-baseline on a bounded sample.  Other workloads: --workload {decode_gemm1, masked_c0,
-hetero, moe_fp8, moe_nvfp4_decode, moe_nvfp4_prefill}; --all adds a per-workload
-table under "workloads".
+(algorithmic bytes / its HIP-event-timed average duration), cold-cache samples, the
+captured-graph replay time of the decode workloads and the oracle's CPU baseline on a
+bounded sample.  Other workloads: --workload (see WORKLOADS: the masked GEMM of 4 groups,
+the heterogeneous GEMM, the FP8 layer and its full-precision-intermediate variant, the
+NVFP4 layer at decode and prefill sizes with stacked or interleaved W13, the W4A16 GEMV,
+the contiguous-layout GEMM1); --all adds a per-workload table under "workloads".
 """
 from __future__ import annotations
 

@@ -1,0 +1,65 @@
+"""Host-side logic of bench.py that needs no GPU: the one-GPU guard, the roofline
+arithmetic, and the counter-based traffic record (scaling by a copy of known size, and
+the source hash that voids a record taken from other kernel sources)."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def test_binding_roof_and_roofline_row():
+    # 8 GB at 8 TB/s = 1 ms; 1 TFLOP at 2.5 PFLOP/s = 0.4 ms: HBM-bound
+    assert bench.binding_roof(8e9, 1e12, "fp16") == "hbm"
+    # 5 TFLOP at 2.5 PFLOP/s = 2 ms > 1 ms
+    assert bench.binding_roof(8e9, 5e12, "fp16") == "mfma"
+    # the same 5 TFLOP at the fp8 rate take exactly the 1 ms of the bytes: not above it
+    assert bench.binding_roof(8e9, 5e12, "fp8") == "hbm"
+    row = bench.roofline_row({"bytes": 8e9, "flops": 1e12, "ms": 2.0, "mfma_dtype": "fp16"})
+    assert row["bound"] == "hbm" and row["floor_ms"] == pytest.approx(1.0) and row["frac"] == pytest.approx(0.5)
+    row = bench.roofline_row({"bytes": 8e9, "flops": 5e12, "ms": 4.0, "mfma_dtype": "fp16"})
+    assert row["bound"] == "mfma" and row["floor_ms"] == pytest.approx(2.0) and row["frac"] == pytest.approx(0.5)
+
+
+def _csv(path, counter, rows):
+    with open(path, "w") as f:
+        f.write("Kernel_Name,Counter_Name,Counter_Value\n")
+        for name, value in rows:
+            f.write(f"\"{name}\",{counter},{value}\n")
+
+
+def test_summarize_counters_scales_by_the_copy(tmp_path):
+    kern = "void mxg::k_gemm_nvfp4_skinny<8, 1, 0, 8, 3, 4>(mxg::MaskedGemmArgs)"
+    copy = "__amd_rocclr_copyBuffer"
+    fetch, write = tmp_path / "fetch.csv", tmp_path / "write.csv"
+    # FETCH_SIZE reads half of the 1 GiB copy (factor 2), WRITE_SIZE all of it (factor 1);
+    # a small copy below a quarter of the known size is ignored
+    _csv(fetch, "FETCH_SIZE", [(kern, 1000), (kern, 1002), (copy, 524288), (copy, 100), (kern, 998)])
+    _csv(write, "WRITE_SIZE", [(kern, 10), (copy, 1048576), (kern, 10), (kern, 10)])
+    text = bench.summarize_counters(str(fetch), str(write))
+    assert "traffic_bytes_per_launch: 2058240" in text          # (1000 * 2 + 10 * 1) KiB
+    files = bench.TRAFFIC_RECORDS["decode_gemm1"][1]
+    assert f"source_sha256: {bench.kernel_source_hash(files)}" in text
+
+
+def test_recorded_traffic_follows_the_source_hash(tmp_path, monkeypatch):
+    files = bench.TRAFFIC_RECORDS["decode_gemm1"][1]
+    good = tmp_path / "good.md"
+    bad = tmp_path / "bad.md"
+    good.write_text(f"traffic_bytes_per_launch: 123456\nsource_sha256: {bench.kernel_source_hash(files)}\n")
+    bad.write_text("traffic_bytes_per_launch: 123456\nsource_sha256: " + "0" * 64 + "\n")
+    monkeypatch.setattr(bench, "TRAFFIC_RECORDS", {"decode_gemm1": (str(good), files)})
+    assert bench.recorded_traffic("decode_gemm1") == 123456
+    monkeypatch.setattr(bench, "TRAFFIC_RECORDS", {"decode_gemm1": (str(bad), files)})
+    assert bench.recorded_traffic("decode_gemm1") is None
+    assert bench.recorded_traffic("hetero") is None
