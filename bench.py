@@ -289,8 +289,9 @@ def bench_decode_gemm1(dev, steps, warmup, seed=1001, cpu=True):
     out = torch.empty((E, max_m, N), dtype=torch.bfloat16, device=dev)
 
     def step(kt):
-        mxg.moe_dispatch(t["ids"], E, max_m, masked_m=masked_m, row=row)
-        mxg.moe_quantize_gather_nvfp4(t["x"], s["g_x"], t["ids"], row, E, max_m, a=a, a_sf=a_sf)
+        # dispatch and quantize-gather in one launch (the batch has 64 slots)
+        mxg.moe_dispatch_quantize_gather_nvfp4(t["x"], s["g_x"], t["ids"], E, max_m, masked_m=masked_m, row=row,
+                                               a=a, a_sf=a_sf)
         if kt:
             kt.start()
         mxg.mx_grouped_gemm_masked(a, a_sf, t["w13"], t["w13_sf"], alpha, masked_m, out)

@@ -63,6 +63,7 @@ SIGNATURES = {
     "moe_route_noaux": (_I, [_P, _P, _I, _I, _I, _I, _I, _F, _P, _P, _P]),
     "moe_dispatch": (_I, [_P, _I, _I, _I, _I, _P, _P, _P]),
     "moe_quantize_gather_nvfp4": (_I, [_P, _I, _I, _F, _P, _P, _I, _I, _I, _P, _P, _P]),
+    "moe_dispatch_quantize_gather_nvfp4": (_I, [_P, _I, _I, _F, _P, _I, _I, _I, _P, _P, _P, _P, _P]),
     "moe_interleave_w13": (_I, [_P, _P, _I, _I, _I, _P]),
     "moe_expert_forward_workspace_size": (_SZ, [_P]),
     "moe_expert_forward_workspace_layout": (_I, [_P, _P]),
@@ -219,6 +220,25 @@ def moe_quantize_gather_nvfp4(x, g_x, ids, row, E, max_m, a=None, a_sf=None, str
                                            T, H, float(g_x), _ptr(ids), _ptr(row), k, E, max_m,
                                            _ptr(a), _ptr(a_sf), _stream(stream)))
     return a, a_sf
+
+
+def moe_dispatch_quantize_gather_nvfp4(x, g_x, ids, E, max_m, masked_m=None, row=None, a=None, a_sf=None,
+                                       stream=None):
+    """moe_dispatch followed by moe_quantize_gather_nvfp4 (one launch for small batches)."""
+    T, H = x.shape
+    k = ids.shape[1]
+    if masked_m is None:
+        masked_m = torch.empty((E,), dtype=torch.int32, device=x.device)
+    if row is None:
+        row = torch.empty((T, k), dtype=torch.int32, device=x.device)
+    if a is None:
+        a = torch.empty((E, max_m, H // 2), dtype=torch.uint8, device=x.device)
+    if a_sf is None:
+        a_sf = torch.empty((E, max_m, H // 16), dtype=torch.uint8, device=x.device)
+    _check(lib().moe_dispatch_quantize_gather_nvfp4(_ptr(x.view(torch.uint16) if x.dtype == torch.bfloat16 else x),
+                                                    T, H, float(g_x), _ptr(ids), k, E, max_m, _ptr(masked_m),
+                                                    _ptr(row), _ptr(a), _ptr(a_sf), _stream(stream)))
+    return masked_m, row, a, a_sf
 
 
 def make_moe_desc(precision, T, H, I, E, top_k, max_m, x, w13, w13_scale, w2, w2_scale,

@@ -252,6 +252,25 @@ int moe_interleave_w13(const uint8_t* src, uint8_t* dst, int E, int I, int row_b
   return hip_status(mxg::interleave_w13(src, dst, E, I, row_bytes, (hipStream_t)stream), "moe_interleave_w13 launch");
 }
 
+int moe_dispatch_quantize_gather_nvfp4(const uint16_t* x, int T, int H, float g_x, const int32_t* topk_ids,
+                                       int top_k, int E, int max_m, int32_t* masked_m, int32_t* row, uint8_t* a,
+                                       uint8_t* a_sf, void* stream) {
+  if (!x || !topk_ids || !masked_m || !row || !a || !a_sf)
+    return fail(MXG_ERR_INVALID_ARG, "moe_dispatch_quantize_gather_nvfp4: null pointer");
+  if (T < 0 || H < 64 || top_k < 1 || E < 1 || max_m < 1 || E > 65535)
+    return fail(MXG_ERR_INVALID_ARG, "moe_dispatch_quantize_gather_nvfp4: bad sizes");
+  if (H % 64 != 0) return fail(MXG_ERR_UNSUPPORTED, "moe_dispatch_quantize_gather_nvfp4: H %% 64 != 0");
+  if ((long long)T * top_k >= (1LL << 31))
+    return fail(MXG_ERR_UNSUPPORTED, "moe_dispatch_quantize_gather_nvfp4: too many slots");
+  if (!(g_x > 0.0f) || g_x == __builtin_inff())
+    return fail(MXG_ERR_INVALID_ARG, "moe_dispatch_quantize_gather_nvfp4: g_x must be finite and > 0");
+  if (!aligned16(x) || !aligned16(a))
+    return fail(MXG_ERR_INVALID_ARG, "moe_dispatch_quantize_gather_nvfp4: misaligned pointer");
+  return hip_status(mxg::dispatch_quantize_gather_nvfp4(x, T, H, g_x, topk_ids, top_k, E, max_m, masked_m, row, a,
+                                                        a_sf, (hipStream_t)stream),
+                    "moe_dispatch_quantize_gather_nvfp4 launch");
+}
+
 // ----------------------------------------------------------------------------- MoE layer
 static int check_moe(const mxg_moe_desc* d) {
   if (!d) return fail(MXG_ERR_INVALID_ARG, "moe_expert_forward: null descriptor");

@@ -129,6 +129,9 @@ hipError_t dispatch(const int32_t* ids, int T, int E, int top_k, int max_m, int3
 // start a multiple of align), row[t, j] the absolute row of slot (t, j)
 hipError_t dispatch_contiguous(const int32_t* ids, int T, int E, int top_k, int align, int32_t* start,
                                int32_t* count, int32_t* row, hipStream_t s);
+hipError_t dispatch_quantize_gather_nvfp4(const uint16_t* x, int T, int H, float g_x, const int32_t* ids,
+                                          int top_k, int E, int max_m, int32_t* masked_m, int32_t* row,
+                                          uint8_t* a, uint8_t* a_sf, hipStream_t s);
 hipError_t quantize_gather_nvfp4(const uint16_t* x, int T, int H, float g_x, const int32_t* ids,
                                  const int32_t* row, int top_k, int max_m, uint8_t* a,
                                  uint8_t* a_sf, hipStream_t s);

@@ -93,6 +93,67 @@ hipError_t quantize_gather_nvfp4(const uint16_t* x, int T, int H, float g_x, con
   return hipGetLastError();
 }
 
+// Dispatch and quantize-gather in one launch for small batches (T * top_k <= 256): every
+// workgroup reads all ids into LDS and gives each slot its row, the number of earlier
+// tokens routed to the same expert (a token's ids are distinct), exactly as k_dispatch;
+// then it quantizes its (token, 16-block) items as k_quantize_gather.  Workgroup 0 also
+// writes row[] and masked_m[] (one thread per expert counts its slots).
+constexpr int DQ_MAX_SLOTS = 256;
+__global__ __launch_bounds__(256) void k_dispatch_quantize_gather(const uint16_t* x, int T, int H, float g,
+                                                                  const int32_t* ids, int top_k, int E,
+                                                                  int max_m, int32_t* masked_m, int32_t* row,
+                                                                  uint8_t* a, uint8_t* a_sf) {
+  __shared__ int id_s[DQ_MAX_SLOTS];
+  __shared__ int row_s[DQ_MAX_SLOTS];
+  const int n = T * top_k, tid = threadIdx.x;
+  if (tid < n) id_s[tid] = ids[tid];
+  __syncthreads();
+  if (tid < n) {
+    const int e = id_s[tid], t = tid / top_k;
+    int r = 0;
+    for (int f = 0; f < t * top_k; f++) r += id_s[f] == e;
+    row_s[tid] = r;
+    if (blockIdx.x == 0) row[tid] = r;
+  }
+  if (blockIdx.x == 0)
+    for (int e = tid; e < E; e += 256) {
+      int c = 0;
+      for (int f = 0; f < n; f++) c += id_s[f] == e;
+      masked_m[e] = c < max_m ? c : max_m;
+    }
+  __syncthreads();
+  const int nb = H / 16;
+  const long b = (long)blockIdx.x * 256 + tid;
+  if (b >= (long)T * nb) return;
+  const int t = (int)(b / nb), blk = (int)(b % nb);
+  float v[16];
+  load_block16<true>(x, (size_t)t * H + (size_t)blk * 16, v);
+  uint32_t w[2];
+  const uint32_t sc = quantize_block16(v, g, 6.0f * g, w);
+  for (int j = 0; j < top_k; j++) {
+    const int e = id_s[t * top_k + j], r = row_s[t * top_k + j];
+    if (r >= max_m) continue;
+    const size_t dst = (size_t)e * max_m + r;
+    *(u32x2_t*)(a + dst * (H / 2) + (size_t)blk * 8) = u32x2_t{w[0], w[1]};
+    a_sf[dst * nb + blk] = (uint8_t)sc;
+  }
+}
+
+hipError_t dispatch_quantize_gather_nvfp4(const uint16_t* x, int T, int H, float g_x, const int32_t* ids,
+                                          int top_k, int E, int max_m, int32_t* masked_m, int32_t* row,
+                                          uint8_t* a, uint8_t* a_sf, hipStream_t s) {
+  if ((long)T * top_k > DQ_MAX_SLOTS) {
+    const hipError_t e = dispatch(ids, T, E, top_k, max_m, masked_m, row, s);
+    if (e != hipSuccess) return e;
+    return quantize_gather_nvfp4(x, T, H, g_x, ids, row, top_k, max_m, a, a_sf, s);
+  }
+  const long items = (long)T * (H / 16);
+  const long blocks = items > 0 ? (items + 255) / 256 : 1;  // at least one, for masked_m
+  hipLaunchKernelGGL(k_dispatch_quantize_gather, dim3((unsigned)blocks), dim3(256), 0, s, x, T, H, g_x, ids, top_k,
+                     E, max_m, masked_m, row, a, a_sf);
+  return hipGetLastError();
+}
+
 // FP8 rows: copy the e4m3 codes (16 bytes per thread) and the 1x128 scales of
 // token t to every dispatched expert row.  The scales are stored transposed, one
 // contiguous column of rows per (expert, 128-block), as the GEMM streams them.

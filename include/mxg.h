@@ -230,6 +230,16 @@ int moe_quantize_gather_nvfp4(const uint16_t* x, int T, int H, float g_x,
                               const int32_t* topk_ids, const int32_t* row, int top_k, int E,
                               int max_m, uint8_t* a, uint8_t* a_sf, void* stream);
 
+/* moe_dispatch followed by moe_quantize_gather_nvfp4, in one launch when T * top_k
+ * <= 256 (the decode batches; larger batches run the two kernels).  Outputs, layouts
+ * and requirements are those of the two calls (masked_m [E], row [T, top_k], a, a_sf),
+ * bit for bit.  For callers of small decode steps, which save a launch and the wait
+ * between the two. */
+int moe_dispatch_quantize_gather_nvfp4(const uint16_t* x, int T, int H, float g_x,
+                                       const int32_t* topk_ids, int top_k, int E, int max_m,
+                                       int32_t* masked_m, int32_t* row, uint8_t* a, uint8_t* a_sf,
+                                       void* stream);
+
 /* Precision of moe_expert_forward. */
 typedef enum { MXG_MOE_FP8_BLOCK128 = 1, MXG_MOE_NVFP4 = 2, MXG_MOE_FP8_BLOCK128_F32H = 3 } mxg_moe_precision;
 

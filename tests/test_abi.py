@@ -214,6 +214,19 @@ def test_w13_layout_rejects():
     assert L.moe_interleave_w13(A, B, -1, 64, 512, None) == mxg.MXG_ERR_INVALID_ARG
 
 
+def test_dispatch_quantize_gather_rejects():
+    L = mxg.lib()
+    f = L.moe_dispatch_quantize_gather_nvfp4
+    args = [FAKE, 8, 7168, 0.01, FAKE, 8, 256, 8, FAKE, FAKE, FAKE, FAKE, None]
+    for i, v, want in [(0, None, mxg.MXG_ERR_INVALID_ARG), (1, -1, mxg.MXG_ERR_INVALID_ARG),
+                       (2, 7168 + 32, mxg.MXG_ERR_UNSUPPORTED), (3, 0.0, mxg.MXG_ERR_INVALID_ARG),
+                       (5, 0, mxg.MXG_ERR_INVALID_ARG), (7, 0, mxg.MXG_ERR_INVALID_ARG),
+                       (10, P((1 << 20) + 4), mxg.MXG_ERR_INVALID_ARG)]:
+        a = list(args)
+        a[i] = v
+        assert f(*a) == want, (i, v)
+
+
 def test_product_path_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(mxg, "LIB_PATH", str(tmp_path / "missing.so"))
     monkeypatch.setattr(mxg, "_LIB", None)

@@ -114,3 +114,28 @@ def test_quantize_gather_bit_exact():
                 filled[e, r] = True
     assert (a_h[~filled] == 0xEE).all() and (asf_h[~filled] == 0xEE).all()
     assert filled.sum() == mm_o.sum()
+
+
+@pytest.mark.parametrize("T,k,max_m,H", [(8, 8, 8, 7168), (1, 8, 4, 1024), (32, 8, 16, 512), (37, 4, 3, 256),
+                                         (64, 8, 16, 512)])
+def test_dispatch_quantize_gather_fused_matches_two_calls(T, k, max_m, H):
+    """The one-launch small-batch path (T * k <= 256) and the two-kernel path it falls back
+    to (T * k = 512) give masked_m, row and every dispatched row bit for bit as
+    moe_dispatch + moe_quantize_gather_nvfp4."""
+    import fp8_grouped_gemm_nvfp4_amd as mxg
+    E = 256
+    log(f"fused dispatch + quantize-gather: T={T} k={k} max_m={max_m} H={H}")
+    gen = datagen.generator(77 + T, DEV)
+    ids = datagen.distinct_topk_ids(gen, T, E, k, DEV)
+    x = datagen.bf16_normal(gen, (T, H), DEV)
+    g = datagen.global_scale_from_amax(x)
+    mm0, row0 = mxg.moe_dispatch(ids, E, max_m)
+    a0, sf0 = mxg.moe_quantize_gather_nvfp4(x, g, ids, row0, E, max_m)
+    mm1, row1, a1, sf1 = mxg.moe_dispatch_quantize_gather_nvfp4(x, g, ids, E, max_m)
+    torch.cuda.synchronize()
+    assert torch.equal(mm0, mm1) and torch.equal(row0, row1)
+    mm = mm0.cpu().numpy()
+    a0, a1, sf0, sf1 = a0.cpu().numpy(), a1.cpu().numpy(), sf0.cpu().numpy(), sf1.cpu().numpy()
+    for e in np.nonzero(mm)[0]:
+        m = int(mm[e])
+        assert np.array_equal(a0[e, :m], a1[e, :m]) and np.array_equal(sf0[e, :m], sf1[e, :m]), f"expert {e}"
