@@ -83,13 +83,56 @@ __global__ __launch_bounds__(256) void k_quantize_gather(const uint16_t* x, int 
   }
 }
 
+// The same with one wave per 64 blocks of a token (H % 1024 == 0) and top_k fixed at
+// compile time: the token's experts and rows are wave-uniform and come in through scalar
+// loads once per wave, ahead of the row read, instead of as vector loads inside the loop.
+template <int K>
+__global__ __launch_bounds__(256) void k_quantize_gather_wave(const uint16_t* __restrict__ x, int T, int H,
+                                                              float g, const int32_t* __restrict__ ids,
+                                                              const int32_t* __restrict__ row, int max_m,
+                                                              uint8_t* __restrict__ a, uint8_t* __restrict__ a_sf) {
+  const int nb = H / 16, per_t = nb / 64;
+  const long wv = (long)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (wv >= (long)T * per_t) return;
+  const int t = (int)(wv / per_t);
+  const int blk = (int)(wv - (long)t * per_t) * 64 + (threadIdx.x & 63);
+  int ej[K], rj[K];
+#pragma unroll
+  for (int j = 0; j < K; j++) {
+    ej[j] = ids[(size_t)t * K + j];
+    rj[j] = row[(size_t)t * K + j];
+  }
+  float v[16];
+  load_block16<true>(x, (size_t)t * H + (size_t)blk * 16, v);
+  uint32_t w[2];
+  const uint32_t sc = quantize_block16(v, g, 6.0f * g, w);
+#pragma unroll
+  for (int j = 0; j < K; j++) {
+    if (rj[j] >= max_m) continue;
+    const size_t dst = (size_t)ej[j] * max_m + rj[j];
+    *(u32x2_t*)(a + dst * (H / 2) + (size_t)blk * 8) = u32x2_t{w[0], w[1]};
+    a_sf[dst * nb + blk] = (uint8_t)sc;
+  }
+}
+
 hipError_t quantize_gather_nvfp4(const uint16_t* x, int T, int H, float g_x, const int32_t* ids,
                                  const int32_t* row, int top_k, int max_m, uint8_t* a,
                                  uint8_t* a_sf, hipStream_t s) {
   long n = (long)T * (H / 16);
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_quantize_gather, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, x, T, H,
-                     g_x, ids, row, top_k, max_m, a, a_sf);
+  const dim3 grid((unsigned)((n + 255) / 256));
+  if (H % 1024 == 0 && (top_k == 8 || top_k == 6 || top_k == 4 || top_k == 2)) {
+    if (top_k == 8)
+      hipLaunchKernelGGL(k_quantize_gather_wave<8>, grid, dim3(256), 0, s, x, T, H, g_x, ids, row, max_m, a, a_sf);
+    else if (top_k == 6)
+      hipLaunchKernelGGL(k_quantize_gather_wave<6>, grid, dim3(256), 0, s, x, T, H, g_x, ids, row, max_m, a, a_sf);
+    else if (top_k == 4)
+      hipLaunchKernelGGL(k_quantize_gather_wave<4>, grid, dim3(256), 0, s, x, T, H, g_x, ids, row, max_m, a, a_sf);
+    else
+      hipLaunchKernelGGL(k_quantize_gather_wave<2>, grid, dim3(256), 0, s, x, T, H, g_x, ids, row, max_m, a, a_sf);
+  } else {
+    hipLaunchKernelGGL(k_quantize_gather, grid, dim3(256), 0, s, x, T, H, g_x, ids, row, top_k, max_m, a, a_sf);
+  }
   return hipGetLastError();
 }
 
@@ -231,6 +274,48 @@ __global__ __launch_bounds__(256) void k_combine(const float* o, const int32_t* 
   *(u32x2_t*)(y + (size_t)t * H + (size_t)q * 4) = u32x2_t{lo, hi};
 }
 
+// The same sum with one wave per 256 columns of a token (H % 256 == 0) and top_k fixed at
+// compile time: a token's slot rows, experts and weights are then wave-uniform and come in
+// through a few wide scalar loads, once per wave, so the vector memory instructions are the
+// eight 16-byte row reads and the store.
+template <int K>
+__global__ __launch_bounds__(256) void k_combine_wave(const float* __restrict__ o,
+                                                      const int32_t* __restrict__ ids,
+                                                      const int32_t* __restrict__ row,
+                                                      const float* __restrict__ w, int T, int H,
+                                                      int max_m, uint16_t* __restrict__ y) {
+  const int per_t = H / 256;
+  const long wv = (long)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (wv >= (long)T * per_t) return;
+  const int t = (int)(wv / per_t);
+  const int q = (int)(wv - (long)t * per_t) * 64 + (threadIdx.x & 63);
+  int rj[K], ej[K];
+  float wj[K];
+#pragma unroll
+  for (int j = 0; j < K; j++) {
+    rj[j] = row[(size_t)t * K + j];
+    ej[j] = ids[(size_t)t * K + j];
+    wj[j] = w[(size_t)t * K + j];
+  }
+  float4_t v[K];
+#pragma unroll
+  for (int j = 0; j < K; j++) {
+    v[j] = float4_t{0.f, 0.f, 0.f, 0.f};
+    if (rj[j] < max_m)
+      v[j] = __builtin_nontemporal_load((const float4_t*)(o + ((size_t)ej[j] * max_m + rj[j]) * H + (size_t)q * 4));
+  }
+  float4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < K; j++) {
+    if (rj[j] >= max_m) continue;
+#pragma unroll
+    for (int i = 0; i < 4; i++) acc[i] = __builtin_fmaf(wj[j], v[j][i], acc[i]);
+  }
+  uint32_t lo = f32_to_bf16_rne(acc[0]) | (f32_to_bf16_rne(acc[1]) << 16);
+  uint32_t hi = f32_to_bf16_rne(acc[2]) | (f32_to_bf16_rne(acc[3]) << 16);
+  *(u32x2_t*)(y + (size_t)t * H + (size_t)q * 4) = u32x2_t{lo, hi};
+}
+
 // Stacked -> interleaved W13 rows, one dword per thread (grid-stride).
 __global__ __launch_bounds__(256) void k_interleave_w13(const uint32_t* src, uint32_t* dst, int E, int I,
                                                         int row_dw) {
@@ -259,8 +344,11 @@ hipError_t combine(const float* o, const int32_t* ids, const int32_t* row, const
   long n = (long)T * (H / 4);
   if (n == 0) return hipSuccess;
   if (top_k < 1 || top_k > 8 || H % 4 != 0) return hipErrorNotSupported;
-  hipLaunchKernelGGL(k_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, o, ids, row, w, T,
-                     H, top_k, max_m, y);
+  const dim3 grid((unsigned)((n + 255) / 256));
+  if (H % 256 == 0 && top_k == 8)
+    hipLaunchKernelGGL(k_combine_wave<8>, grid, dim3(256), 0, s, o, ids, row, w, T, H, max_m, y);
+  else
+    hipLaunchKernelGGL(k_combine, grid, dim3(256), 0, s, o, ids, row, w, T, H, top_k, max_m, y);
   return hipGetLastError();
 }
 

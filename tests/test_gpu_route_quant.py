@@ -89,10 +89,14 @@ def test_quantize_all_bf16_values():
         assert np.array_equal(np_(codes), c_o), g
 
 
-def test_quantize_gather_bit_exact():
-    log("quantize + gather into the masked layout, T=300 top8 H=7168 max_m=12 (some slots dropped)")
-    gen = datagen.generator(19, DEV)
-    T, H, E, k, max_m = 300, 7168, 256, 8, 12
+@pytest.mark.parametrize("T,H,k,max_m", [(300, 7168, 8, 12), (77, 2048, 6, 5), (50, 1024, 4, 3), (40, 1024, 2, 2),
+                                         (300, 512, 8, 12), (60, 1024, 3, 4)])
+def test_quantize_gather_bit_exact(T, H, k, max_m):
+    """Both launch shapes: one wave per 64 blocks of a token with top_k fixed at compile time
+    (H % 1024 == 0, top_k in {2, 4, 6, 8}) and one thread per block otherwise."""
+    log(f"quantize + gather into the masked layout, T={T} top{k} H={H} max_m={max_m} (some slots dropped)")
+    gen = datagen.generator(19 + T + k, DEV)
+    E = 256
     ids = datagen.distinct_topk_ids(gen, T, E, k, DEV)
     x = datagen.bf16_normal(gen, (T, H), DEV)
     g_x = datagen.global_scale_from_amax(x)
