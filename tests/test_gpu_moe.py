@@ -277,6 +277,12 @@ def test_moe_fp8_small_full():
     _run_fp8(128, 512, 256, 3000, None)
 
 
+def test_moe_fp8_wide_rows_full():
+    # top-8 with H % 256 == 0: the combine runs one wave per 256 columns of a token
+    log("FP8 MoE: T=128 H=1024 I=256 E=256, every token")
+    _run_fp8(128, 1024, 256, 3004, None)
+
+
 def test_moe_fp8_two_m_tiles():
     log("FP8 MoE with masked_m past 256: T=8192 H=512 I=256 E=256, 24 tokens")
     _run_fp8(8192, 512, 256, 3001, 8, n_deep=16)
