@@ -4,8 +4,9 @@
 // sigmoid(logits) + bias, grouped top-k, routed_scaling_factor).  One
 // wavefront per token; with E = 256 each lane owns 4 consecutive experts, so
 // a group of E / n_group experts is a run of 64 / n_group lanes.  Group top-2
-// sums and the top-k rounds are wave reductions (xor shuffles); ties resolve to
-// the lower index at every comparison.  All value arithmetic is fp32 with
+// sums are xor-shuffle reductions and each top-k round a DPP row reduction plus
+// readlanes; ties resolve to the lower index at every comparison.  All value
+// arithmetic is fp32 with
 // round to nearest; the sigmoid is evaluated in fp64 and rounded once.
 //
 // Dispatch (per-expert valid row count masked_m of the masked grouped GEMM,
@@ -19,6 +20,18 @@ namespace mxg {
 
 __device__ __forceinline__ bool better(float v, int i, float w, int j) {
   return v > w || (v == w && i < j);
+}
+
+constexpr int NONE = 0x7FFFFFFF;  // no candidate
+
+// Combine this lane's candidate with the one DPP control CTRL brings in from its row
+// (a rotation: every source lane is valid).
+template <int CTRL>
+__device__ __forceinline__ void row_best(float& bv, int& bi, float& bsv) {
+  const float ov = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(bv), CTRL, 0xF, 0xF, false));
+  const int oi = __builtin_amdgcn_update_dpp(0, bi, CTRL, 0xF, 0xF, false);
+  const float os = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(bsv), CTRL, 0xF, 0xF, false));
+  if (oi != NONE && (bi == NONE || better(ov, oi, bv, bi))) { bv = ov; bi = oi; bsv = os; }
 }
 
 __global__ __launch_bounds__(256) void k_route_noaux(const float* logits, const float* bias, int T,
@@ -61,33 +74,44 @@ __global__ __launch_bounds__(256) void k_route_noaux(const float* logits, const 
   }
   const bool keep = rank < topk_group;
 
+  float den = 0.0f;  // fp32 sum of the selected s in slot order
   uint32_t taken = 0;  // bit i: this lane's expert 4 lane + i already selected (a mask, not an array: no scratch)
   int my_id = -1;
   float my_s = 0.0f;
   for (int j = 0; j < top_k; j++) {
     float bv = -INFINITY;
-    int bi = 0x7FFFFFFF;
+    int bi = NONE;
     float bsv = 0.0f;
     if (keep) {
 #pragma unroll
       for (int i = 0; i < 4; i++) {
         int e = lane * 4 + i;
-        if (!((taken >> i) & 1u) && (bi == 0x7FFFFFFF || better(sb[i], e, bv, bi))) { bv = sb[i]; bi = e; bsv = s[i]; }
+        if (!((taken >> i) & 1u) && (bi == NONE || better(sb[i], e, bv, bi))) { bv = sb[i]; bi = e; bsv = s[i]; }
       }
     }
-    for (int off = 32; off >= 1; off >>= 1) {
-      float ov = __shfl_xor(bv, off);
-      int oi = __shfl_xor(bi, off);
-      float os = __shfl_xor(bsv, off);
-      bool take_other = (oi != 0x7FFFFFFF) && (bi == 0x7FFFFFFF || better(ov, oi, bv, bi));
-      if (take_other) { bv = ov; bi = oi; bsv = os; }
+    // the wave's best candidate: rotations inside each 16-lane row (DPP, VALU latency), then
+    // the four row winners read into uniform registers; the order is total over the
+    // distinct expert indices, so any reduction order picks the same expert
+    row_best<0x128>(bv, bi, bsv);  // row_ror:8
+    row_best<0x124>(bv, bi, bsv);  // row_ror:4
+    row_best<0x122>(bv, bi, bsv);  // row_ror:2
+    row_best<0x121>(bv, bi, bsv);  // row_ror:1
+    float wv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 0));
+    int wi = __builtin_amdgcn_readlane(bi, 0);
+    float ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bsv), 0));
+#pragma unroll
+    for (int r = 1; r < 4; r++) {
+      const float ov = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 16 * r));
+      const int oi = __builtin_amdgcn_readlane(bi, 16 * r);
+      const float os = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bsv), 16 * r));
+      if (oi != NONE && (wi == NONE || better(ov, oi, wv, wi))) { wv = ov; wi = oi; ws = os; }
     }
+    bi = wi;
+    bsv = ws;
     if ((bi >> 2) == lane) taken |= 1u << (bi & 3);
     if (lane == j) { my_id = bi; my_s = bsv; }
+    den = den + bsv;
   }
-  // denominator: fp32 sum of the selected s in slot order
-  float den = 0.0f;
-  for (int j = 0; j < top_k; j++) den = den + __shfl(my_s, j);
   if (lane < top_k) {
     ids[(size_t)t * top_k + lane] = my_id;
     float q = my_s / den;
