@@ -60,6 +60,7 @@ def _lib():
         "orc_encode_e2m1_array": (None, [_P, _L, _P]),
         "orc_encode_e4m3_array": (None, [_P, _L, _P]),
         "orc_nvfp4_row_dot": (None, [_P, _P, _L, _P, _P, _I, _I, _D, _P, _P]),
+        "orc_gemm_nvfp4_rows": (None, [_P, _P, _P, _I, _P, _P, _I, _I, _D, _P, _P]),
         "orc_gemm_nvfp4_masked": (None, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _P]),
         "orc_gemm_fp8_block": (None, [_P, _P, _P, _I, _P, _P, _I, _I, _P, _P]),
         "orc_gemm_dense_fp8w": (None, [_P, _I, _P, _P, _I, _I, _P, _P]),
@@ -177,6 +178,22 @@ def nvfp4_row_dot(a, a_sf, a_row, b, b_sf, K, alpha=1.0):
     return y, s
 
 
+def gemm_nvfp4_rows(a, a_sf, rows, b, b_sf, K, alpha=1.0):
+    """Rows ``rows`` of an NVFP4 A ([rows, K] codes/scales) against every row of B:
+    y[m, n] = alpha * sum_k dec(A)[rows[m], k] * dec(B)[n, k] and s the same sum of
+    |terms|, both fp64 [len(rows), nb]; the same sums as nvfp4_row_dot row by row."""
+    lib = _lib()
+    a = _c(a, np.uint8); a_sf = _c(a_sf, np.uint8); b = _c(b, np.uint8); b_sf = _c(b_sf, np.uint8)
+    r = _c(rows, np.int32)
+    nb = b.size // (K // 2)
+    y = np.empty((len(r), nb))
+    s = np.empty((len(r), nb))
+    if len(r):
+        lib.orc_gemm_nvfp4_rows(_p(a), _p(a_sf), _p(r), len(r), _p(b), _p(b_sf), nb, K, float(alpha),
+                                _p(y), _p(s))
+    return y, s
+
+
 def gemm_fp8_block(qa, sa, qb, sb, rows=None):
     """FP8 1x128-activation / 128x128-weight block-scaled GEMM in fp64.
     qa [Ma, K] uint8 e4m3, sa [Ma, K/128] f32, qb [N, K], sb [N/128, K/128];
@@ -285,3 +302,106 @@ def combine(o, s_o, w):
 
 def num_threads() -> int:
     return int(_lib().orc_num_threads())
+
+
+# ----------------------------------------------------------------------------- MoE layer
+def _expert_slots(ids, row, max_m, tokens):
+    """For each expert, the (subset position, slot) pairs of the given tokens routed to it
+    whose row fits the capacity, in token order."""
+    sub_ids = ids[tokens]
+    keep = row[tokens] < max_m
+    slots = {}
+    for p, j in zip(*np.nonzero(keep)):
+        slots.setdefault(int(sub_ids[p, j]), []).append((int(p), int(j)))
+    return slots
+
+
+def _combine_tokens(o, so, w, kept):
+    """y*[p] = sum over kept slots j (in slot order) of w[p, j] * o[p, j] in fp64, S likewise
+    of |w| * S_o (the weighted combine of the mixture-of-experts row)."""
+    n, k, H = o.shape
+    ystar = np.zeros((n, H))
+    S = np.zeros((n, H))
+    for j in range(k):
+        wj = np.where(kept[:, j], w[:, j].astype(np.float64), 0.0)[:, None]
+        ystar = ystar + np.where(kept[:, j][:, None], wj * o[:, j], 0.0)
+        S = S + np.where(kept[:, j][:, None], np.abs(wj) * so[:, j], 0.0)
+    return ystar, S
+
+
+def moe_layer_nvfp4(x, g_x, ids, w, max_m, weights, g_w13, g_w2, g_h, I, tokens=None):
+    """The NVFP4 expert path of one MoE layer for the given tokens (default: all), step by
+    step in the order of the mixture-of-experts row ("llm-assisted-kernel-dev" README):
+    dispatch into the masked layout (capacity max_m; slots past it are dropped), NVFP4
+    quantization of the token rows with g_x, GEMM1 against W13 (gate rows [0, I), up rows
+    [I, 2I)) with alpha = g_w13[e] * g_x, SwiGLU in fp64, requantization of the fp32 of h*
+    with g_h, GEMM2 against W2 with alpha = g_w2[e] * g_h, then the weighted combine.
+
+    x: fp32 [T, H] (bf16 values widened); ids [T, k] int32; w [T, k] fp32; weights(e) ->
+    (w13 codes [2I, H/2], w13 scales [2I, H/16], w2 codes [H, I/2], w2 scales [H, I/16]).
+    Returns a dict of fp64 / integer arrays over the subset positions p (tokens[p]):
+    y (bf16 bits), ystar, S [n, H]; kept [n, k]; xq/xsf; per slot h (fp64 h*), hq/hsf,
+    o/so (GEMM2 fp64 outputs and their |.| sums), g1/s1 (GEMM1 outputs) [n, k, ...]."""
+    ids = np.asarray(ids, np.int32)
+    T, k = ids.shape
+    E = len(g_w13)
+    tokens = np.arange(T) if tokens is None else np.asarray(tokens)
+    n = len(tokens)
+    _, row = dispatch(ids, E, max_m)
+    xq, xsf = quantize_nvfp4(np.asarray(x, np.float32)[tokens], g_x)
+    H = xq.shape[1] * 2
+    out = dict(xq=xq, xsf=xsf, kept=row[tokens] < max_m, row=row[tokens],
+               g1=np.full((n, k, 2 * I), np.nan), s1=np.full((n, k, 2 * I), np.nan),
+               h=np.full((n, k, I), np.nan), hq=np.zeros((n, k, I // 2), np.uint8),
+               hsf=np.zeros((n, k, I // 16), np.uint8), o=np.zeros((n, k, H)), so=np.zeros((n, k, H)))
+    for e, sl in sorted(_expert_slots(ids, row, max_m, tokens).items()):
+        w13, w13_sf, w2, w2_sf = weights(e)
+        pos = np.array([p for p, _ in sl])
+        js = np.array([j for _, j in sl])
+        gu, s1 = gemm_nvfp4_rows(xq, xsf, pos, w13, w13_sf, H, float(g_w13[e]) * float(g_x))
+        hstar = swiglu(gu, I)
+        hq, hsf = quantize_nvfp4(hstar.astype(np.float32), g_h)
+        o, so = gemm_nvfp4_rows(hq, hsf, np.arange(len(sl)), w2, w2_sf, I, float(g_w2[e]) * float(g_h))
+        out["g1"][pos, js], out["s1"][pos, js], out["h"][pos, js] = gu, s1, hstar
+        out["hq"][pos, js], out["hsf"][pos, js] = hq, hsf
+        out["o"][pos, js], out["so"][pos, js] = o, so
+    out["ystar"], out["S"] = _combine_tokens(out["o"], out["so"], np.asarray(w)[tokens], out["kept"])
+    out["y"] = bf16_bits(out["ystar"])
+    return out
+
+
+def moe_layer_fp8(xq, xs, ids, w, max_m, weights, I, tokens=None, full_precision_h=False):
+    """The FP8 block-scaled expert path of one MoE layer for the given tokens (default:
+    all), in the order of the mixture-of-experts row ("llm-assisted-kernel-dev" README):
+    dispatch (capacity max_m), GEMM1 of the 1x128-scaled e4m3 token rows against the
+    128x128-scaled W13, SwiGLU in fp64, h rounded to bf16 (the optimized kernel's BF16
+    default; with full_precision_h the unrounded h* is kept, as the reference's full
+    precision experts), GEMM2 against the 128x128-scaled W2, then the weighted combine.
+
+    xq e4m3 [T, H], xs fp32 [T, H/128]; weights(e) -> (w13 [2I, H], w13 scales
+    [2I/128, H/128], w2 [H, I], w2 scales [H/128, I/128]).  Returns a dict as
+    moe_layer_nvfp4 (h holds h*, hb the bf16 h actually multiplied)."""
+    ids = np.asarray(ids, np.int32)
+    T, k = ids.shape
+    tokens = np.arange(T) if tokens is None else np.asarray(tokens)
+    n = len(tokens)
+    H = xq.shape[1]
+    E = int(ids.max()) + 1 if ids.size else 1
+    _, row = dispatch(ids, max(E, 1), max_m)
+    out = dict(kept=row[tokens] < max_m, row=row[tokens],
+               g1=np.full((n, k, 2 * I), np.nan), s1=np.full((n, k, 2 * I), np.nan),
+               h=np.full((n, k, I), np.nan), hb=np.full((n, k, I), np.nan),
+               o=np.zeros((n, k, H)), so=np.zeros((n, k, H)))
+    for e, sl in sorted(_expert_slots(ids, row, max_m, tokens).items()):
+        w13, w13_s, w2, w2_s = weights(e)
+        pos = np.array([p for p, _ in sl])
+        js = np.array([j for _, j in sl])
+        gu, s1 = gemm_fp8_block(xq, xs, w13, w13_s, rows=np.asarray(tokens)[pos])
+        hstar = swiglu(gu, I)
+        hb = hstar if full_precision_h else bf16_value(bf16_bits(hstar))
+        o, so = gemm_dense_fp8w(hb, w2, w2_s)
+        out["g1"][pos, js], out["s1"][pos, js], out["h"][pos, js], out["hb"][pos, js] = gu, s1, hstar, hb
+        out["o"][pos, js], out["so"][pos, js] = o, so
+    out["ystar"], out["S"] = _combine_tokens(out["o"], out["so"], np.asarray(w)[tokens], out["kept"])
+    out["y"] = bf16_bits(out["ystar"])
+    return out

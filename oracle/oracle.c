@@ -165,6 +165,39 @@ void orc_nvfp4_row_dot(const uint8_t* a, const uint8_t* a_sf, long a_row,
   free(ad);
 }
 
+/* Selected A rows against rows [0, nb) of B: for m < M,
+ *   y[m, n] = alpha * sum_k dec(A)[a_rows[m], k] * dec(B)[n, k],  s[m, n] likewise of |.|,
+ * the same fp64 sums in k order as orc_nvfp4_row_dot, with each operand row decoded
+ * once (a subset of tokens routed to one expert, evaluated together). */
+void orc_gemm_nvfp4_rows(const uint8_t* a, const uint8_t* a_sf, const int32_t* a_rows, int M,
+                         const uint8_t* b, const uint8_t* b_sf, int nb, int K, double alpha,
+                         double* y, double* s) {
+  double* ad = (double*)malloc(sizeof(double) * (size_t)M * (size_t)K);
+  for (int m = 0; m < M; m++)
+    for (int k = 0; k < K; k++) ad[(size_t)m * K + k] = nvfp4_elem(a, a_sf, K, a_rows[m], k);
+#pragma omp parallel
+  {
+    double* bd = (double*)malloc(sizeof(double) * (size_t)K);
+#pragma omp for schedule(static)
+    for (int n = 0; n < nb; n++) {
+      for (int k = 0; k < K; k++) bd[k] = nvfp4_elem(b, b_sf, K, n, k);
+      for (int m = 0; m < M; m++) {
+        const double* av = ad + (size_t)m * K;
+        double acc = 0.0, accabs = 0.0;
+        for (int k = 0; k < K; k++) {
+          double p = av[k] * bd[k];
+          acc += p;
+          accabs += fabs(p);
+        }
+        if (y) y[(size_t)m * nb + n] = alpha * acc;
+        if (s) s[(size_t)m * nb + n] = fabs(alpha) * accabs;
+      }
+    }
+    free(bd);
+  }
+  free(ad);
+}
+
 /* Masked grouped NT GEMM over NVFP4 operands (the masked batched GEMM with
  * scale factors and alpha at output of "The CuteDSL Gamble", "The Message").
  *   A [G, max_m, K], B [G, N, K] (NVFP4 as above), alpha [G] (NULL -> 1),
@@ -212,42 +245,71 @@ void orc_gemm_nvfp4_masked(const uint8_t* a, const uint8_t* a_sf, const uint8_t*
 
 /* y[m,n] = sum_k (e4m3(qa[m,k]) * sa[m,k/128]) * (e4m3(qb[n,k]) * sb[n/128,k/128])
  * s[m,n] = the same sum of absolute values.  Rows of qa/sa are given by a
- * row-index list (NULL -> rows 0..M-1) so one token subset can be evaluated. */
+ * row-index list (NULL -> rows 0..M-1) so one token subset can be evaluated.
+ * Each selected A row and each B row is decoded once into exact doubles; every
+ * (m, n) is then the plain fp64 sum over k = 0..K-1 in order. */
 void orc_gemm_fp8_block(const uint8_t* qa, const float* sa, const int32_t* a_rows, int M,
                         const uint8_t* qb, const float* sb, int N, int K, double* y, double* s) {
   int KB = K / 128;
-#pragma omp parallel for schedule(static)
-  for (int i = 0; i < M * N; i++) {
-    int m = i / N, n = i % N;
+  double* ad = (double*)malloc(sizeof(double) * (size_t)M * (size_t)K);
+  for (int m = 0; m < M; m++) {
     long ar = a_rows ? a_rows[m] : m;
-    double acc = 0.0, accabs = 0.0;
-    for (int k = 0; k < K; k++) {
-      double av = E4M3[qa[ar * K + k]] * (double)sa[ar * KB + k / 128];
-      double bv = E4M3[qb[(long)n * K + k]] * (double)sb[(n / 128) * KB + k / 128];
-      acc += av * bv;
-      accabs += fabs(av * bv);
-    }
-    y[i] = acc;
-    if (s) s[i] = accabs;
+    for (int k = 0; k < K; k++)
+      ad[(size_t)m * K + k] = E4M3[qa[ar * K + k]] * (double)sa[ar * KB + k / 128];
   }
+#pragma omp parallel
+  {
+    double* bd = (double*)malloc(sizeof(double) * (size_t)K);
+#pragma omp for schedule(static)
+    for (int n = 0; n < N; n++) {
+      for (int k = 0; k < K; k++) bd[k] = E4M3[qb[(long)n * K + k]] * (double)sb[(n / 128) * KB + k / 128];
+      for (int m = 0; m < M; m++) {
+        const double* av = ad + (size_t)m * K;
+        double acc = 0.0, accabs = 0.0;
+        for (int k = 0; k < K; k++) {
+          double p = av[k] * bd[k];
+          acc += p;
+          accabs += fabs(p);
+        }
+        y[(size_t)m * N + n] = acc;
+        if (s) s[(size_t)m * N + n] = accabs;
+      }
+    }
+    free(bd);
+  }
+  free(ad);
 }
 
 /* Dense activations (given as exact doubles, e.g. bf16 values) times FP8
- * 128x128-block-scaled weights: y[m,n] = sum_k a[m,k] * e4m3(qb[n,k]) * sb[n/128,k/128]. */
+ * 128x128-block-scaled weights: y[m,n] = sum_k a[m,k] * e4m3(qb[n,k]) * sb[n/128,k/128],
+ * each term evaluated as (a * e4m3) * scale, summed in k order. */
 void orc_gemm_dense_fp8w(const double* a, int M, const uint8_t* qb, const float* sb, int N, int K,
                          double* y, double* s) {
   int KB = K / 128;
-#pragma omp parallel for schedule(static)
-  for (int i = 0; i < M * N; i++) {
-    int m = i / N, n = i % N;
-    double acc = 0.0, accabs = 0.0;
-    for (int k = 0; k < K; k++) {
-      double p = a[(long)m * K + k] * E4M3[qb[(long)n * K + k]] * (double)sb[(n / 128) * KB + k / 128];
-      acc += p;
-      accabs += fabs(p);
+#pragma omp parallel
+  {
+    double* be = (double*)malloc(sizeof(double) * (size_t)K);
+    double* bs = (double*)malloc(sizeof(double) * (size_t)K);
+#pragma omp for schedule(static)
+    for (int n = 0; n < N; n++) {
+      for (int k = 0; k < K; k++) {
+        be[k] = E4M3[qb[(long)n * K + k]];
+        bs[k] = (double)sb[(n / 128) * KB + k / 128];
+      }
+      for (int m = 0; m < M; m++) {
+        const double* av = a + (long)m * K;
+        double acc = 0.0, accabs = 0.0;
+        for (int k = 0; k < K; k++) {
+          double p = av[k] * be[k] * bs[k];
+          acc += p;
+          accabs += fabs(p);
+        }
+        y[(size_t)m * N + n] = acc;
+        if (s) s[(size_t)m * N + n] = accabs;
+      }
     }
-    y[i] = acc;
-    if (s) s[i] = accabs;
+    free(be);
+    free(bs);
   }
 }
 

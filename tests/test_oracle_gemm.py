@@ -304,3 +304,18 @@ def test_gemv_w4a16_equals_w4a4_on_nvfp4_activations():
     y, s = oracle.gemv_nvfp4_w4a16(x_bits, w, w_sf, 0.5)
     y4, s4 = oracle.nvfp4_row_dot(a, a_sf, 0, w, w_sf, K, alpha=0.5)
     assert np.allclose(y[0], y4, rtol=1e-13, atol=1e-12) and np.allclose(s[0], s4, rtol=1e-13)
+
+
+def test_rows_form_matches_row_dot():
+    # the row-subset form used for token subsets gives the row dot's sums bit for bit
+    rng = np.random.default_rng(13)
+    K, nb = 96, 11
+    a = rng.integers(0, 256, (7, K // 2), dtype=np.uint8)
+    a_sf = rng.integers(0, 0x7F, (7, K // 16), dtype=np.uint8)
+    b = rng.integers(0, 256, (nb, K // 2), dtype=np.uint8)
+    b_sf = rng.integers(0, 0x7F, (nb, K // 16), dtype=np.uint8)
+    rows = [6, 0, 3, 3]
+    y, s = oracle.gemm_nvfp4_rows(a, a_sf, rows, b, b_sf, K, alpha=-0.375)
+    for i, r in enumerate(rows):
+        yr, sr = oracle.nvfp4_row_dot(a, a_sf, r, b, b_sf, K, alpha=-0.375)
+        assert np.array_equal(y[i], yr) and np.array_equal(s[i], sr)

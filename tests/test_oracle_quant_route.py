@@ -221,3 +221,126 @@ def test_dispatch_contiguous_invariants(T, E, k, align):
             assert row[t, j] == nxt[e]
             nxt[e] += 1
     assert len(np.unique(row)) == T * k
+
+
+# ----------------------------------------------------------------------------- quantizer steps in exact arithmetic
+def _rnd32(q):
+    """Nearest IEEE binary32 value to the rational q (ties to even), subnormals included."""
+    from fractions import Fraction
+    if q == 0:
+        return Fraction(0)
+    a = abs(q)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    quantum = Fraction(2) ** (max(e, -126) - 23)
+    n = a / quantum
+    fl = n.numerator // n.denominator
+    rem = n - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    r = fl * quantum
+    return r if q > 0 else -r
+
+
+def _frac_e4m3_mag(c):
+    from fractions import Fraction
+    e, m = (c >> 3) & 15, c & 7
+    return Fraction(m, 512) if e == 0 else Fraction(8 + m, 8) * Fraction(2) ** (e - 7)
+
+
+def _nearest_e4m3_code(q):
+    """Nearest finite non-negative e4m3fn code to q >= 0 (ties to the even code), saturating."""
+    if q > 448:
+        return 0x7E
+    best = min(range(0x7F), key=lambda c: (abs(_frac_e4m3_mag(c) - q), c & 1))
+    return best
+
+
+def _nearest_e2m1_frac(v):
+    """Nearest e2m1 code of a rational v (sign kept, ties to the code with LSB 0, |v| > 6 -> 6)."""
+    from fractions import Fraction
+    mags = [Fraction(x) for x in (0, 0.5, 1, 1.5, 2, 3, 4, 6)]
+    a = abs(v)
+    c = 7 if a > 6 else min(range(8), key=lambda i: (abs(mags[i] - a), i & 1))
+    return c | (8 if v < 0 else 0)
+
+
+def _quantize_block_exact(xb, g):
+    """The quantizer's reading step by step, each fp32 operation rounded from the exact
+    rational result: S = e4m3(fl(amax / fl(6 g))), d = fl(S g), r = fl(1 / d),
+    code = e2m1(fl(x r)).  Also returns the codes the other reading, e2m1(fl(x / d)), gives."""
+    from fractions import Fraction
+    xs = [Fraction(float(v)) for v in xb]
+    gf = Fraction(float(g))
+    six_g = _rnd32(6 * gf)
+    amax = max(abs(v) for v in xs)
+    sc = _nearest_e4m3_code(_rnd32(amax / six_g))
+    sval = _frac_e4m3_mag(sc)
+    if sval == 0:
+        codes = [8 if np.signbit(v) else 0 for v in xb]
+        return sc, codes, codes
+    d = _rnd32(sval * gf)
+    r = _rnd32(1 / d)
+    by_rcp = [_nearest_e2m1_frac(_rnd32(v * r)) | (8 if np.signbit(xb[i]) else 0) for i, v in enumerate(xs)]
+    by_div = [_nearest_e2m1_frac(_rnd32(v / d)) | (8 if np.signbit(xb[i]) else 0) for i, v in enumerate(xs)]
+    return sc, by_rcp, by_div
+
+
+def _codes_of(q):
+    return np.stack([q & 15, q >> 4], -1).reshape(q.shape[0], -1)
+
+
+def test_quantize_multiplies_by_rounded_reciprocal():
+    """Blocks where multiplying by fl(1/d) and dividing by d give different codes: the
+    oracle must follow the reciprocal reading.  Among them, the block with g = 1.6267272,
+    x = 36.601364 beside a block maximum that gives scale code 0x49."""
+    rng = np.random.default_rng(90)
+    cand_x, cand_g = [], []
+    # named case: the scale code 0x49 (= 1.125 * 2^2) from a block maximum of 6 * 4.5 * g
+    g0 = np.float32(1.6267272)
+    xb = np.zeros(16, np.float32)
+    xb[0] = np.float32(6.0 * 4.5) * g0
+    xb[1] = np.float32(36.601364)
+    cand_x.append(xb); cand_g.append(g0)
+    # searched cases: values near e2m1 midpoints in units of d
+    for _ in range(4000):
+        g = np.float32(np.exp(rng.uniform(-6, 3)))
+        sc = rng.integers(0x20, 0x70)
+        d = np.float32(np.float32(_frac_e4m3_mag(int(sc))) * g)
+        mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+        xb = (rng.choice(mids, 16) * (1 + rng.integers(-4, 5, 16) * 2.0 ** -23) * float(d)).astype(np.float32)
+        xb *= np.where(rng.random(16) < 0.5, -1, 1).astype(np.float32)
+        xb[0] = np.float32(6.0 * float(_frac_e4m3_mag(int(sc)))) * g
+        r = np.float32(1.0) / d
+        if np.any(oracle.encode_e2m1(xb * r) != oracle.encode_e2m1(xb / d)):
+            cand_x.append(xb); cand_g.append(g)
+        if len(cand_x) >= 24:
+            break
+    differ = 0
+    for xb, g in zip(cand_x, cand_g):
+        sc, by_rcp, by_div = _quantize_block_exact(xb, g)
+        q, sf = oracle.quantize_nvfp4(xb[None], float(g))
+        assert sf[0, 0] == sc, (g, xb)
+        assert _codes_of(q)[0].tolist() == by_rcp, (g, xb)
+        differ += by_rcp != by_div
+    assert differ >= 20, "too few blocks separate the two readings"
+    sc, by_rcp, by_div = _quantize_block_exact(cand_x[0], cand_g[0])
+    assert sc == 0x49 and by_rcp[1] == 6 and by_div[1] == 7
+
+
+def test_quantize_scale_step_exact_rational():
+    """The scale code comes from fl(amax / fl(6 g)) with g a general fp32 value: checked in
+    exact arithmetic over random blocks, including maxima near e4m3 midpoints."""
+    rng = np.random.default_rng(91)
+    for i in range(300):
+        g = np.float32(np.exp(rng.uniform(-8, 4)))
+        xb = (rng.standard_normal(16) * np.exp(rng.uniform(-3, 3))).astype(np.float32) * g
+        if i % 3 == 0:   # block maximum at 6 g times an e4m3 midpoint
+            c = int(rng.integers(0x10, 0x76))
+            mid = (_frac_e4m3_mag(c) + _frac_e4m3_mag(c + 1)) / 2
+            xb[int(rng.integers(16))] = np.float32(6.0 * float(mid)) * g
+        sc, by_rcp, _ = _quantize_block_exact(xb, g)
+        q, sf = oracle.quantize_nvfp4(xb[None], float(g))
+        assert sf[0, 0] == sc, (i, g)
+        assert _codes_of(q)[0].tolist() == by_rcp, (i, g)
