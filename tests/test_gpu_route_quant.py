@@ -143,3 +143,13 @@ def test_dispatch_quantize_gather_fused_matches_two_calls(T, k, max_m, H):
     for e in np.nonzero(mm)[0]:
         m = int(mm[e])
         assert np.array_equal(a0[e, :m], a1[e, :m]) and np.array_equal(sf0[e, :m], sf1[e, :m]), f"expert {e}"
+    # and the one-launch path against the oracle itself
+    ids_h = np_(ids)
+    mm_o, row_o = oracle.dispatch(ids_h, E, max_m)
+    assert np.array_equal(np_(mm1), mm_o) and np.array_equal(np_(row1), row_o)
+    c_o, s_o = oracle.quantize_nvfp4(np_(x.float()), g)
+    for t in range(T):
+        for j in range(k):
+            e, r = ids_h[t, j], row_o[t, j]
+            if r < max_m:
+                assert np.array_equal(a1[e, r], c_o[t]) and np.array_equal(sf1[e, r], s_o[t]), (t, j)

@@ -97,3 +97,47 @@ def test_moe_nvfp4_interleaved_w13_tiled_kernel():
     g = torch.Generator(device=DEV).manual_seed(11)
     w = (torch.rand((T, TOPK), generator=g, device=DEV) + 0.1).float().contiguous()
     _check(wl, T, H, I, E, ids, w, 48, "tiled kernel")
+
+
+@pytest.mark.parametrize("T,H,I", [(16, 512, 256), (512, 512, 256), (64, 7168, 2048)])
+def test_moe_nvfp4_interleaved_w13_against_oracle(T, H, I):
+    """The interleaved-W13 layer checked against the oracle directly: the GPU runs on the
+    interleaved copy, the oracle on the logical (stacked) weights, stage by stage."""
+    import oracle
+    from _helpers import bf16_tensor_bits, np_
+    from _moe_check import check_nvfp4_layer
+    mxg = _mxg()
+    E = 256
+    log(f"interleaved W13 against the oracle: T={T} H={H} I={I}")
+    wl = datagen.moe_nvfp4_workload(1004, DEV, T=T, H=H, I=I)
+    t, s = wl.tensors, wl.scalars
+    ids, w = mxg.moe_route_noaux(t["logits"], t["bias"], 8, 4, TOPK, 2.5)
+    mm, _ = mxg.moe_dispatch(ids, E, 1 << 20)
+    cap = max(16, -(-int(mm.max().item()) // 16) * 16)
+    masked_m, row = mxg.moe_dispatch(ids, E, cap)
+    w13_il = mxg.moe_interleave_w13(t["w13"])
+    sf_il = mxg.moe_interleave_w13(t["w13_sf"])
+    y = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
+    dbg_h = torch.full((E, cap, I), float("nan"), dtype=torch.float32, device=DEV)
+    d = mxg.make_moe_desc(mxg.MXG_MOE_NVFP4, T, H, I, E, TOPK, cap, t["x"], w13_il, sf_il, t["w2"], t["w2_sf"],
+                          ids, w, masked_m, row, y, g_x=s["g_x"], g_w13=t["g_w13"], g_w2=t["g_w2"],
+                          g_h=s["g_h"], w13_layout=mxg.MXG_W13_INTERLEAVED16, dbg_h=dbg_h)
+    off = mxg.moe_expert_forward_workspace_layout(d)
+    ws = torch.empty((off[5],), dtype=torch.uint8, device=DEV)
+    mxg.moe_expert_forward(d, ws)
+    torch.cuda.synchronize()
+    ids_h, row_h = np_(ids), np_(row)
+    ids_o, w_o = oracle.route_noaux(np_(t["logits"]), np_(t["bias"]), 8, 4, TOPK, 2.5)
+    assert np.array_equal(ids_h, ids_o)
+
+    def region(i, shape):
+        n = int(np.prod(shape))
+        return lambda e: np_(ws[off[i] + e * n: off[i] + (e + 1) * n]).reshape(shape)
+    ga, gs = region(0, (cap, H // 2)), region(1, (cap, H // 16))
+    hc, hs = region(2, (cap, I // 2)), region(3, (cap, I // 16))
+    check_nvfp4_layer(
+        x=np_(t["x"].float()), g_x=s["g_x"], ids=ids_h, w=np_(w), row=row_h, max_m=cap, I=I,
+        weights=lambda e: (np_(t["w13"][e]), np_(t["w13_sf"][e]), np_(t["w2"][e]), np_(t["w2_sf"][e])),
+        g_w13=np_(t["g_w13"]), g_w2=np_(t["g_w2"]), g_h=s["g_h"],
+        gathered=lambda e: (ga(e), gs(e), hc(e), hs(e)), h_pre=lambda e: np_(dbg_h[e]),
+        y_bits=bf16_tensor_bits(y), toks=np.arange(T), what=f"interleaved W13 T={T} H={H}")
