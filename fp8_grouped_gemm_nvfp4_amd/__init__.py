@@ -44,7 +44,7 @@ class MoeDesc(ctypes.Structure):
                 ("g_h", ctypes.c_float),
                 ("topk_ids", ctypes.c_void_p), ("topk_w", ctypes.c_void_p), ("masked_m", ctypes.c_void_p),
                 ("row", ctypes.c_void_p), ("y", ctypes.c_void_p), ("dbg_h", ctypes.c_void_p),
-                ("w13_layout", ctypes.c_int)]
+                ("w13_layout", ctypes.c_int), ("dbg_g1", ctypes.c_void_p)]
 
 
 _LIB = None
@@ -61,7 +61,7 @@ SIGNATURES = {
     "mx_gemv_nvfp4_w4a16": (_I, [_P, _I, _I, _P, _P, _F, _P, _I, _I, _I, _P]),
     "mx_quantize_nvfp4": (_I, [_P, _I, _L, _I, _F, _P, _P, _P]),
     "moe_route_noaux": (_I, [_P, _P, _I, _I, _I, _I, _I, _F, _P, _P, _P]),
-    "moe_dispatch": (_I, [_P, _I, _I, _I, _I, _P, _P, _P]),
+    "moe_dispatch": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P]),
     "moe_quantize_gather_nvfp4": (_I, [_P, _I, _I, _F, _P, _P, _I, _I, _I, _P, _P, _P]),
     "moe_dispatch_quantize_gather_nvfp4": (_I, [_P, _I, _I, _F, _P, _I, _I, _I, _P, _P, _P, _P, _P]),
     "moe_interleave_w13": (_I, [_P, _P, _I, _I, _I, _P]),
@@ -186,14 +186,19 @@ def moe_route_noaux(logits, bias, n_group, topk_group, top_k, rsf, ids=None, w=N
     return ids, w
 
 
-def moe_dispatch(ids, E, max_m, masked_m=None, row=None, stream=None):
+def moe_dispatch(ids, E, max_m, masked_m=None, row=None, stream=None, offsets=None, with_offsets=False):
+    """Masked-layout dispatch: returns (masked_m, row), or (masked_m, row, offsets) when
+    with_offsets or an offsets tensor [E + 1] is given."""
     T, k = ids.shape
     if masked_m is None:
         masked_m = torch.empty((E,), dtype=torch.int32, device=ids.device)
     if row is None:
         row = torch.empty((T, k), dtype=torch.int32, device=ids.device)
-    _check(lib().moe_dispatch(_ptr(ids), T, E, k, max_m, _ptr(masked_m), _ptr(row), _stream(stream)))
-    return masked_m, row
+    if offsets is None and with_offsets:
+        offsets = torch.empty((E + 1,), dtype=torch.int32, device=ids.device)
+    _check(lib().moe_dispatch(_ptr(ids), T, E, k, max_m, _ptr(masked_m), _ptr(row), _ptr(offsets),
+                              _stream(stream)))
+    return (masked_m, row) if offsets is None else (masked_m, row, offsets)
 
 
 def moe_dispatch_contiguous(ids, E, align, group_start=None, count=None, row=None, stream=None):
@@ -243,11 +248,11 @@ def moe_dispatch_quantize_gather_nvfp4(x, g_x, ids, E, max_m, masked_m=None, row
 
 def make_moe_desc(precision, T, H, I, E, top_k, max_m, x, w13, w13_scale, w2, w2_scale,
                   topk_ids, topk_w, masked_m, row, y, x_scale=None, g_x=0.0, g_w13=None, g_w2=None,
-                  g_h=0.0, dbg_h=None, w13_layout=0):
+                  g_h=0.0, dbg_h=None, w13_layout=0, dbg_g1=None):
     return MoeDesc(precision, T, H, I, E, top_k, max_m, _ptr(x), _ptr(x_scale), float(g_x),
                    _ptr(w13), _ptr(w13_scale), _ptr(g_w13), _ptr(w2), _ptr(w2_scale), _ptr(g_w2),
                    float(g_h), _ptr(topk_ids), _ptr(topk_w), _ptr(masked_m), _ptr(row), _ptr(y),
-                   _ptr(dbg_h), int(w13_layout))
+                   _ptr(dbg_h), int(w13_layout), _ptr(dbg_g1))
 
 
 def moe_interleave_w13(src, dst=None, stream=None):
@@ -276,3 +281,4 @@ def moe_expert_forward_workspace_layout(desc: MoeDesc):
 def moe_expert_forward(desc: MoeDesc, ws, stream=None):
     _check(lib().moe_expert_forward(ctypes.byref(desc), _ptr(ws), ws.numel() * ws.element_size(),
                                     _stream(stream)))
+

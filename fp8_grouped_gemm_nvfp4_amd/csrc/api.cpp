@@ -200,12 +200,12 @@ int moe_route_noaux(const float* logits, const float* bias, int T, int E, int n_
 }
 
 int moe_dispatch(const int32_t* topk_ids, int T, int E, int top_k, int max_m, int32_t* masked_m,
-                 int32_t* row, void* stream) {
+                 int32_t* row, int32_t* offsets, void* stream) {
   if (!topk_ids || !masked_m || !row) return fail(MXG_ERR_INVALID_ARG, "moe_dispatch: null pointer");
   if (T < 0 || E < 1 || top_k < 1 || max_m < 1 || E > 65535)
     return fail(MXG_ERR_INVALID_ARG, "moe_dispatch: bad sizes");
   if ((long long)T * top_k >= (1LL << 31)) return fail(MXG_ERR_UNSUPPORTED, "moe_dispatch: too many slots");
-  return hip_status(mxg::dispatch(topk_ids, T, E, top_k, max_m, masked_m, row, (hipStream_t)stream),
+  return hip_status(mxg::dispatch(topk_ids, T, E, top_k, max_m, masked_m, row, offsets, (hipStream_t)stream),
                     "moe_dispatch launch");
 }
 
@@ -363,6 +363,7 @@ int moe_expert_forward(const mxg_moe_desc* d, void* ws, size_t ws_bytes, void* s
     p1.masked_m = d->masked_m; p1.G = E; p1.max_m = mm; p1.N = 2 * I; p1.K = H;
     p1.a_s_stride = mxg::fp8_scale_stride(mm);
     p1.h_split = split;
+    p1.dbg_g1 = d->dbg_g1;
     e = mxg::gemm_fp8_swiglu(p1, 0, s);
     if (e != hipSuccess) return hip_status(e, "gemm_fp8_swiglu");
     mxg::Fp8GemmArgs p2{};
@@ -383,7 +384,7 @@ int moe_expert_forward(const mxg_moe_desc* d, void* ws, size_t ws_bytes, void* s
     p1.a = a; p1.a_sf = a_sf; p1.b = d->w13; p1.b_sf = (const uint8_t*)d->w13_scale;
     p1.out = nullptr; p1.masked_m = d->masked_m; p1.alpha = d->g_w13; p1.alpha_scale = d->g_x;
     p1.G = E; p1.max_m = mm; p1.N = 2 * I; p1.K = H;
-    p1.h_codes = hc; p1.h_sf = hsf; p1.dbg_h = d->dbg_h; p1.g_h = d->g_h;
+    p1.h_codes = hc; p1.h_sf = hsf; p1.dbg_h = d->dbg_h; p1.dbg_g1 = d->dbg_g1; p1.g_h = d->g_h;
     p1.w13_il16 = d->w13_layout == MXG_W13_INTERLEAVED16;
     e = mxg::gemm_nvfp4_masked(p1, mxg::EPI_SWIGLU_NVFP4, 0, s);
     if (e != hipSuccess) return hip_status(e, "gemm1 nvfp4 swiglu");

@@ -180,11 +180,11 @@ __device__ __forceinline__ int w13_row(int r, int I, bool il16) {
 __device__ __forceinline__ void dma16(const void* g, void* lds) {
   // the LDS base is wave-uniform; readfirstlane puts it in an SGPR for M0
   uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0) : "memory");
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0) : "memory", "m0");
 }
 __device__ __forceinline__ void dma4(const void* g, void* lds) {
   uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(m0) : "memory");
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(m0) : "memory", "m0");
 }
 
 // Wait until at most N of this wave's vector memory operations are outstanding (they

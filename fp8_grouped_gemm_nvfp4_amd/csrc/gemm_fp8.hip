@@ -64,7 +64,7 @@ constexpr int wait_count(int da, int db, int ao, int bo) {
 
 __device__ __forceinline__ int f1_swz(int r) { return (r ^ (r >> 3)) & 7; }
 
-template <int DA, int DB, bool SPLIT>
+template <int DA, int DB, bool SPLIT, bool DBG>
 __global__ __launch_bounds__(f1::THREADS) void k_gemm_fp8_swiglu(const Fp8GemmArgs p) {
   using namespace f1;
   constexpr int SA = DA + 1, SB = DB + 1;
@@ -281,6 +281,15 @@ __global__ __launch_bounds__(f1::THREADS) void k_gemm_fp8_swiglu(const Fp8GemmAr
 #pragma unroll
             for (int r = 0; r < 4; r++) {
               const float gt = acc[i][n][r], up = acc[i][n + 2][r];
+              if constexpr (DBG) {  // the promoted GEMM1 sums, for stage checks only
+                const int row = cit.m0 + 16 * wm + 64 * i + 4 * q + r;
+                if (row < cit.mm) {
+                  float* d = p.dbg_g1 + ((size_t)cit.g * cap + row) * N;
+                  const int c = cit.n0 + 32 * wn + 16 * n + rr;
+                  d[c] = gt;
+                  d[I + c] = up;
+                }
+              }
               const float h = gt / (1.0f + expf(-gt)) * up;
               b[0][r] = f32_to_bf16_rne(h);
               if constexpr (SPLIT) b[PL - 1][r] = f32_to_bf16_rne(h - __uint_as_float(b[0][r] << 16));
@@ -308,24 +317,27 @@ __global__ __launch_bounds__(f1::THREADS) void k_gemm_fp8_swiglu(const Fp8GemmAr
   wait_vmcnt<0>();  // the trailing re-reads land before the workgroup ends
 }
 
-template <int DA, int DB, bool SPLIT>
+template <int DA, int DB, bool SPLIT, bool DBG>
 static hipError_t launch_fp8_swiglu(Fp8GemmArgs p, int cu_limit, hipStream_t s) {
   using namespace f1;
   if (p.G > MAX_G || (p.N / 2) % HN != 0 || p.K % BK != 0 || p.a_s_stride % 4 != 0 ||
       p.a_s_stride < p.max_m || p.a_s_stride < 4)
     return hipErrorNotSupported;
   if ((long long)p.G * ((p.max_m + BM - 1) / BM) * ((p.N / 2) / HN) > 0x7FFFFFFFLL) return hipErrorNotSupported;
-  const void* k = (const void*)k_gemm_fp8_swiglu<DA, DB, SPLIT>;
+  const void* k = (const void*)k_gemm_fp8_swiglu<DA, DB, SPLIT, DBG>;
   const int grid = resident_grid(k, THREADS, cu_limit);
   if (grid <= 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((k_gemm_fp8_swiglu<DA, DB, SPLIT>), dim3(grid), dim3(THREADS), 0, s, p);
+  hipLaunchKernelGGL((k_gemm_fp8_swiglu<DA, DB, SPLIT, DBG>), dim3(grid), dim3(THREADS), 0, s, p);
   return hipGetLastError();
 }
 
 hipError_t gemm_fp8_swiglu(Fp8GemmArgs p, int cu_limit, hipStream_t s) {
   if (p.G <= 0 || p.max_m <= 0 || p.N <= 0 || p.K <= 0) return hipSuccess;
-  return p.h_split ? launch_fp8_swiglu<1, MXG_F1_DB, true>(p, cu_limit, s)
-                   : launch_fp8_swiglu<1, MXG_F1_DB, false>(p, cu_limit, s);
+  if (p.dbg_g1)
+    return p.h_split ? launch_fp8_swiglu<1, MXG_F1_DB, true, true>(p, cu_limit, s)
+                     : launch_fp8_swiglu<1, MXG_F1_DB, false, true>(p, cu_limit, s);
+  return p.h_split ? launch_fp8_swiglu<1, MXG_F1_DB, true, false>(p, cu_limit, s)
+                   : launch_fp8_swiglu<1, MXG_F1_DB, false, false>(p, cu_limit, s);
 }
 
 // ----------------------------------------------------------------------------- GEMM2

@@ -313,6 +313,13 @@ __global__ __launch_bounds__(256) void k_gemm_nvfp4(const typename ArgsOf<MODE>:
 #pragma unroll
           for (int e = 0; e < 16; e++) dbg[hrow * I + hc0 + e] = h[e];
         }
+        if (float* g1 = p.dbg_g1) {
+#pragma unroll
+          for (int e = 0; e < 16; e++) {
+            g1[hrow * 2 * I + hc0 + e] = cs[rr * CP + cb * 16 + e];
+            g1[hrow * 2 * I + I + hc0 + e] = cs[rr * CP + HN + cb * 16 + e];
+          }
+        }
         uint32_t w[2];
         uint32_t s = quantize_block16(h, gh, six_gh, w);
         *(u32x2_t*)(p.h_codes + hrow * (I / 2) + hc0 / 2) = u32x2_t{w[0], w[1]};

@@ -432,15 +432,21 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_nvfp4_skinny(const MaskedGe
         } else {
           upv = acc[1];
         }
-        float h[4];
+        float h[4], gv[4], uv[4];
 #pragma unroll
         for (int r = 0; r < 4; r++) {
           float gt = alpha * acc[0][r], up = alpha * upv[r];
+          gv[r] = gt;
+          uv[r] = up;
           h[r] = gt / (1.0f + expf(-gt)) * up;
         }
         const int hc = ncol0 + q * 4;  // this lane's first h column
         if (p.dbg_h && m < cu.rows && hc < I && !(PAIRED && (wave & 1)))
           *(float4_t*)(p.dbg_h + orow * I + hc) = float4_t{h[0], h[1], h[2], h[3]};
+        if (p.dbg_g1 && m < cu.rows && hc < I && !(PAIRED && (wave & 1))) {
+          *(float4_t*)(p.dbg_g1 + orow * 2 * I + hc) = float4_t{gv[0], gv[1], gv[2], gv[3]};
+          *(float4_t*)(p.dbg_g1 + orow * 2 * I + I + hc) = float4_t{uv[0], uv[1], uv[2], uv[3]};
+        }
         uint32_t sbyte;
         uint32_t bits = quantize_block_x4(h, p.g_h, 6.0f * p.g_h, sbyte);
         uint32_t b1 = __shfl_xor(bits, 16);  // q ^ 1

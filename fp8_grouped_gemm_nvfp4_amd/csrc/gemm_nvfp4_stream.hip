@@ -397,14 +397,20 @@ __global__ __launch_bounds__(ns::THREADS) void k_gemm_nvfp4_stream(const typenam
           if constexpr (SWIGLU) {
 #pragma unroll
             for (int n = 0; n < NB / 2; n++) {
-              float h[4];
+              float h[4], gv[4], uv[4];
 #pragma unroll
               for (int r = 0; r < 4; r++) {
                 const float gt = alpha * acc[i][n][r], up = alpha * acc[i][n + NB / 2][r];
+                gv[r] = gt;
+                uv[r] = up;
                 h[r] = gt / (1.0f + expf(-gt)) * up;
               }
               const int hc0 = cit.n0 + WC / 2 * wn + 16 * n;  // first column of this lane's 16-block
               if (p.dbg_h && ok) *(float4_t*)(p.dbg_h + orow * I + hc0 + 4 * q) = float4_t{h[0], h[1], h[2], h[3]};
+              if (p.dbg_g1 && ok) {
+                *(float4_t*)(p.dbg_g1 + orow * 2 * I + hc0 + 4 * q) = float4_t{gv[0], gv[1], gv[2], gv[3]};
+                *(float4_t*)(p.dbg_g1 + orow * 2 * I + I + hc0 + 4 * q) = float4_t{uv[0], uv[1], uv[2], uv[3]};
+              }
               uint32_t sbyte;
               const uint32_t bits = quantize_block_x4(h, p.g_h, 6.0f * p.g_h, sbyte);
               const uint32_t b1 = __shfl_xor(bits, 16), b2 = __shfl_xor(bits, 32), b3 = __shfl_xor(bits, 48);

@@ -29,6 +29,7 @@ struct MaskedGemmArgs {
   uint8_t* h_codes;
   uint8_t* h_sf;
   float* dbg_h;
+  float* dbg_g1;        // SwiGLU epilogue: optional fp32 GEMM1 outputs [G, max_m, N] (gate | up)
   float g_h;
   // contiguous layout (MODE_CONTIG): A [max_m, K] and C [max_m, N] hold every group's rows,
   // group g from row row_start[g] (row_start [G + 1]); masked_m[g] counts its valid rows
@@ -97,6 +98,7 @@ struct Fp8GemmArgs {
   // GEMM1 writes both, GEMM2 runs over K = 2I with W2's K index wrapping at b_k = I
   int h_split;
   int b_k;              // GEMM2: K extent of W2 when h_split (else K)
+  float* dbg_g1;        // GEMM1: optional fp32 outputs [G, max_m, N] (gate | up), promoted sums
 };
 constexpr int fp8_scale_stride(int max_m) { return (max_m + 3) / 4 * 4; }
 hipError_t gemm_fp8_swiglu(Fp8GemmArgs p, int cu_limit, hipStream_t s);
@@ -124,7 +126,7 @@ hipError_t route_noaux(const float* logits, const float* bias, int T, int E, int
                        int topk_group, int top_k, float rsf, int32_t* ids, float* w,
                        hipStream_t s);
 hipError_t dispatch(const int32_t* ids, int T, int E, int top_k, int max_m, int32_t* masked_m,
-                    int32_t* row, hipStream_t s);
+                    int32_t* row, int32_t* offsets, hipStream_t s);
 // contiguous layout: count[e] tokens of expert e from row start[e] (start[E + 1], each
 // start a multiple of align), row[t, j] the absolute row of slot (t, j)
 hipError_t dispatch_contiguous(const int32_t* ids, int T, int E, int top_k, int align, int32_t* start,

@@ -186,7 +186,7 @@ hipError_t dispatch_quantize_gather_nvfp4(const uint16_t* x, int T, int H, float
                                           int top_k, int E, int max_m, int32_t* masked_m, int32_t* row,
                                           uint8_t* a, uint8_t* a_sf, hipStream_t s) {
   if ((long)T * top_k > DQ_MAX_SLOTS) {
-    const hipError_t e = dispatch(ids, T, E, top_k, max_m, masked_m, row, s);
+    const hipError_t e = dispatch(ids, T, E, top_k, max_m, masked_m, row, nullptr, s);
     if (e != hipSuccess) return e;
     return quantize_gather_nvfp4(x, T, H, g_x, ids, row, top_k, max_m, a, a_sf, s);
   }

@@ -231,9 +231,13 @@ hipError_t dispatch_contiguous(const int32_t* ids, int T, int E, int top_k, int 
 }
 
 hipError_t dispatch(const int32_t* ids, int T, int E, int top_k, int max_m, int32_t* masked_m,
-                    int32_t* row, hipStream_t s) {
+                    int32_t* row, int32_t* offsets, hipStream_t s) {
   hipLaunchKernelGGL(k_dispatch, dim3((unsigned)E), dim3(256), 0, s, ids, T * top_k, max_m, masked_m,
                      row);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !offsets) return e;
+  // offsets = exclusive scan of masked_m (the scan of the contiguous layout with align 1)
+  hipLaunchKernelGGL(k_contig_starts, dim3(1), dim3(64), 0, s, masked_m, E, 1, offsets);
   return hipGetLastError();
 }
 

@@ -132,6 +132,11 @@ typedef struct {
  * launch arguments, so nothing is read from device metadata); the pointers
  * inside are device pointers.  G in [1, MXG_MAX_GROUPS]; each group needs
  * M >= 0, N >= 1, K % 64 == 0.  Same dtype rules as mx_grouped_gemm_masked.
+ * The descriptors travel by value in the launch arguments, which a captured graph
+ * records with the launch: the table the pages set up on the device before graph
+ * capture is, here, part of the captured kernel node, and the cap of 32 groups keeps
+ * it inside the kernel-argument space.  Larger group counts with one shared N and K
+ * are the masked (mx_grouped_gemm_masked) or contiguous layouts.
  */
 int mx_grouped_gemm(const mxg_group_desc* groups, int G, int ab_dtype, int sf_dtype,
                     int c_dtype, int sf_vec_size, int cu_limit, void* stream);
@@ -195,6 +200,10 @@ int moe_route_noaux(const float* logits, const float* bias, int T, int E, int n_
 /*
  * Token-to-expert permutation for the contiguous layout (stable counting sort in
  * token order, each expert's rows starting at a multiple of align).
+ * Source: "Helion Pretuned Kernels" README, kernel table row grouped_gemm_deepgemm
+ * (DeepGEMM's packed contiguous A layout with aligned padding per group); the
+ * permutation is the one the masked layout's masked_m implies ("The CuteDSL
+ * Gamble", "The Message"), with the groups packed one after another.
  *   count[e]        = number of tokens routed to e
  *   group_start[e]  = sum over e' < e of count[e'] rounded up to a multiple of align;
  *                     group_start[E] = the total rows (with padding)
@@ -212,12 +221,15 @@ int moe_dispatch_contiguous(const int32_t* topk_ids, int T, int E, int top_k, in
  * grouped_gemm_nt_masked ("The CuteDSL Gamble", "The Message").
  *   row[t, j]   = number of tokens t' < t routed to expert topk_ids[t, j]
  *   masked_m[e] = min(number of tokens routed to e, max_m)
+ *   offsets[e]  = sum over e' < e of masked_m[e'] (exclusive scan; offsets[E] =
+ *                 the number of slots kept), or nothing when offsets is NULL
  * A slot whose row is >= max_m does not fit the capacity and is dropped by the
  * later stages.  topk_ids device int32 [T, top_k] (distinct per token, in
- * [0, E)); masked_m device int32 [E]; row device int32 [T, top_k].
+ * [0, E)); masked_m device int32 [E]; row device int32 [T, top_k]; offsets
+ * device int32 [E + 1] or NULL.
  */
 int moe_dispatch(const int32_t* topk_ids, int T, int E, int top_k, int max_m, int32_t* masked_m,
-                 int32_t* row, void* stream);
+                 int32_t* row, int32_t* offsets, void* stream);
 
 /*
  * NVFP4-quantize the bf16 activations x [T, H] (global scale g_x, same recipe
@@ -225,13 +237,20 @@ int moe_dispatch(const int32_t* topk_ids, int T, int E, int top_k, int max_m, in
  * row it was dispatched to: a[e, row, :], a_sf[e, row, :] for each slot with
  * row < max_m.  a [E, max_m, H/2], a_sf [E, max_m, H/16] (device).
  * H % 64 == 0 required.
+ * Source: activations "quantized on the fly" to NVFP4 ahead of the masked grouped
+ * GEMM ("The CuteDSL Gamble", "Input Knowledge Required": NVFP4 as 4-bit values
+ * with block scale factors; "The Message": the per-expert masked layout that
+ * grouped_gemm_nt_masked reads).
  */
 int moe_quantize_gather_nvfp4(const uint16_t* x, int T, int H, float g_x,
                               const int32_t* topk_ids, const int32_t* row, int top_k, int E,
                               int max_m, uint8_t* a, uint8_t* a_sf, void* stream);
 
-/* moe_dispatch followed by moe_quantize_gather_nvfp4, in one launch when T * top_k
- * <= 256 (the decode batches; larger batches run the two kernels).  Outputs, layouts
+/* moe_dispatch (without offsets) followed by moe_quantize_gather_nvfp4, in one launch
+ * when T * top_k <= 256 (the decode batches; larger batches run the two kernels).
+ * Source: as those two calls ("The CuteDSL Gamble", "The Message" and "Input Knowledge
+ * Required"); a single-stream decode step is where launch count matters ("Context: The
+ * Performance Crisis").  Outputs, layouts
  * and requirements are those of the two calls (masked_m [E], row [T, top_k], a, a_sf),
  * bit for bit.  For callers of small decode steps, which save a launch and the wait
  * between the two. */
@@ -294,6 +313,9 @@ int moe_interleave_w13(const uint8_t* src, uint8_t* dst, int E, int I, int row_b
  *   dbg_h    optional device fp32 [E, max_m, I]: NVFP4 only, receives the
  *            pre-quantization intermediate for the rows it computes (NULL in
  *            production; y is bit-identical either way).
+ *   dbg_g1   optional device fp32 [E, max_m, 2I]: receives GEMM1's fp32 outputs (alpha
+ *            applied) for the rows it computes, gate in columns [0, I) and up in [I, 2I)
+ *            whatever the W13 layout (NULL in production; y is bit-identical either way)
  *   w13_layout  mxg_w13_layout of w13 and its scales; MXG_W13_INTERLEAVED16 is
  *            NVFP4 only (MXG_ERR_UNSUPPORTED for the FP8 precisions).  The layer's
  *            result does not depend on the layout: y is bit-identical for the same
@@ -324,6 +346,7 @@ typedef struct {
   uint16_t* y;
   float* dbg_h;
   int w13_layout;
+  float* dbg_g1;
 } mxg_moe_desc;
 
 /* Bytes of workspace moe_expert_forward needs for this descriptor (0 on a bad

@@ -51,11 +51,18 @@ def _slots_by_expert(ids, row, max_m, toks):
     return by_e
 
 
+def _check_g1(g1_gpu, gu, S1, what):
+    """GEMM1 debug stage: the GPU's fp32 gate/up sums against the oracle's, 1e-5 S + 1 fp32 ulp."""
+    if g1_gpu is not None:
+        assert_within(g1_gpu.astype(np.float64), gu, S1, what, ulp=ulp_f32)
+
+
 def check_nvfp4_layer(*, x, g_x, ids, w, row, max_m, I, weights, g_w13, g_w2, g_h, gathered, h_pre,
-                      y_bits, toks, what, e2e_tokens=0):
+                      y_bits, toks, what, e2e_tokens=0, g1=None):
     """gathered(e) -> (a codes [max_m, H/2], a scales, h codes [max_m, I/2], h scales) from the
     GPU workspace; h_pre(e) -> GPU fp32 pre-quantization h [max_m, I]; weights(e) -> the
-    logical (stacked) W13 and W2 codes/scales; y_bits [T, H] bf16 bits of the GPU output."""
+    logical (stacked) W13 and W2 codes/scales; y_bits [T, H] bf16 bits of the GPU output;
+    g1(e) -> the GPU's fp32 GEMM1 debug output [max_m, 2I] (gate | up), or None."""
     xq, xsf = oracle.quantize_nvfp4(np.asarray(x, np.float32)[toks], g_x)
     H = xq.shape[1] * 2
     n, k = len(toks), ids.shape[1]
@@ -69,6 +76,7 @@ def check_nvfp4_layer(*, x, g_x, ids, w, row, max_m, I, weights, g_w13, g_w2, g_
         assert np.array_equal(a[rows], xq[pos]) and np.array_equal(a_sf[rows], xsf[pos]), \
             f"{what}: quantized x rows of expert {e}"
         gu, S1 = oracle.gemm_nvfp4_rows(a, a_sf, rows, w13, w13_sf, H, float(g_w13[e]) * float(g_x))
+        _check_g1(None if g1 is None else g1(e)[rows], gu, S1, f"{what}: GEMM1 of expert {e}")
         g, u = gu[:, :I], gu[:, I:]
         hstar = oracle.swiglu(gu, I)
         tol = swiglu_tol(g, u, S1[:, :I], S1[:, I:], hstar)
@@ -94,7 +102,7 @@ def check_nvfp4_layer(*, x, g_x, ids, w, row, max_m, I, weights, g_w13, g_w2, g_
 
 
 def check_fp8_layer(*, xq, xs, ids, w, row, max_m, I, weights, gathered, h_planes, y_bits, toks, what,
-                    f32h=False, o_gpu=None, e2e_tokens=0):
+                    f32h=False, o_gpu=None, e2e_tokens=0, g1=None):
     """gathered(e) -> (a e4m3 [max_m, H], a scales [max_m, H/128]); h_planes(e) -> GPU bf16
     bits [max_m, planes * I]; weights(e) -> (w13, w13 scales, w2, w2 scales).  With f32h
     the intermediate is bf16 hi + lo: h is checked against the unrounded SwiGLU, GEMM2 and
@@ -116,6 +124,7 @@ def check_fp8_layer(*, xq, xs, ids, w, row, max_m, I, weights, gathered, h_plane
         assert np.array_equal(a[rows], xq[toks[pos]]) and np.array_equal(a_s[rows], xs[toks[pos]]), \
             f"{what}: gathered x of expert {e}"
         gu, S1 = oracle.gemm_fp8_block(xq, xs, w13, w13_s, rows=toks[pos])
+        _check_g1(None if g1 is None else g1(e)[rows], gu, S1, f"{what}: GEMM1 of expert {e}")
         g, u = gu[:, :I], gu[:, I:]
         hstar = oracle.swiglu(gu, I)
         hb = h_planes(e)[rows]

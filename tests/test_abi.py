@@ -129,8 +129,8 @@ def test_route_dispatch_quant_reject():
     assert L.moe_route_noaux(FAKE, FAKE, 8, 256, 8, 9, 8, 2.5, FAKE, FAKE, None) == mxg.MXG_ERR_INVALID_ARG
     assert L.moe_route_noaux(FAKE, FAKE, 8, 256, 8, 4, 9, 2.5, FAKE, FAKE, None) == mxg.MXG_ERR_UNSUPPORTED
     assert L.moe_route_noaux(None, FAKE, 8, 256, 8, 4, 8, 2.5, FAKE, FAKE, None) == mxg.MXG_ERR_INVALID_ARG
-    assert L.moe_dispatch(FAKE, 8, 256, 8, 0, FAKE, FAKE, None) == mxg.MXG_ERR_INVALID_ARG
-    assert L.moe_dispatch(None, 8, 256, 8, 8, FAKE, FAKE, None) == mxg.MXG_ERR_INVALID_ARG
+    assert L.moe_dispatch(FAKE, 8, 256, 8, 0, FAKE, FAKE, None, None) == mxg.MXG_ERR_INVALID_ARG
+    assert L.moe_dispatch(None, 8, 256, 8, 8, FAKE, FAKE, FAKE, None) == mxg.MXG_ERR_INVALID_ARG
     assert L.mx_quantize_nvfp4(FAKE, mxg.MXG_BF16, 4, 24, 1.0, FAKE, FAKE, None) == mxg.MXG_ERR_UNSUPPORTED
     assert L.mx_quantize_nvfp4(FAKE, mxg.MXG_BF16, 4, 32, 0.0, FAKE, FAKE, None) == mxg.MXG_ERR_INVALID_ARG
     assert L.mx_quantize_nvfp4(FAKE, mxg.MXG_E2M1, 4, 32, 1.0, FAKE, FAKE, None) == mxg.MXG_ERR_UNSUPPORTED

@@ -72,11 +72,12 @@ def _run_nvfp4(T, H, I, seed, n_check, cap=None, n_deep=0, e2e=0, report_h_scale
     y_dbg = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
     y = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
     dbg_h = torch.full((E, max_m, I), float("nan"), dtype=torch.float32, device=DEV)
+    dbg_g1 = torch.full((E, max_m, 2 * I), float("nan"), dtype=torch.float32, device=DEV)
     common = dict(precision=mxg.MXG_MOE_NVFP4, T=T, H=H, I=I, E=E, top_k=TOPK, max_m=max_m,
                   x=t["x"], w13=t["w13"], w13_scale=t["w13_sf"], w2=t["w2"], w2_scale=t["w2_sf"],
                   topk_ids=ids, topk_w=w, masked_m=masked_m, row=row, g_x=s["g_x"], g_w13=t["g_w13"],
                   g_w2=t["g_w2"], g_h=s["g_h"])
-    d_dbg = mxg.make_moe_desc(y=y_dbg, dbg_h=dbg_h, **common)
+    d_dbg = mxg.make_moe_desc(y=y_dbg, dbg_h=dbg_h, dbg_g1=dbg_g1, **common)
     d = mxg.make_moe_desc(y=y, **common)
     off = mxg.moe_expert_forward_workspace_layout(d)
     ws = torch.empty((off[5],), dtype=torch.uint8, device=DEV)
@@ -105,7 +106,8 @@ def _run_nvfp4(T, H, I, seed, n_check, cap=None, n_deep=0, e2e=0, report_h_scale
         weights=_cached(lambda e: (np_(t["w13"][e]), np_(t["w13_sf"][e]), np_(t["w2"][e]), np_(t["w2_sf"][e]))),
         g_w13=np_(t["g_w13"]), g_w2=np_(t["g_w2"]), g_h=s["g_h"],
         gathered=lambda e: (ga(e), gs(e), hc(e), hs(e)), h_pre=lambda e: np_(dbg_h[e]),
-        y_bits=bf16_tensor_bits(y), toks=toks, what=f"NVFP4 T={T} H={H}", e2e_tokens=e2e)
+        y_bits=bf16_tensor_bits(y), toks=toks, what=f"NVFP4 T={T} H={H}", e2e_tokens=e2e,
+        g1=lambda e: np_(dbg_g1[e]))
 
 
 def test_moe_nvfp4_small_full():
@@ -167,12 +169,18 @@ def _run_fp8(T, H, I, seed, n_check, n_deep=0, vary_w2_scales=False, f32h=False,
                           t["w2"], t["w2_s"], ids, w, masked_m, row, y, x_scale=t["xs"])
     off = mxg.moe_expert_forward_workspace_layout(d)
     ws = torch.empty((off[5],), dtype=torch.uint8, device=DEV)
+    dbg_g1 = torch.full((E, max_m, 2 * I), float("nan"), dtype=torch.float32, device=DEV)
+    y_dbg = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
+    d_dbg = mxg.make_moe_desc(prec, T, H, I, E, TOPK, max_m, t["xq"], t["w13"], t["w13_s"],
+                              t["w2"], t["w2_s"], ids, w, masked_m, row, y_dbg, x_scale=t["xs"], dbg_g1=dbg_g1)
+    mxg.moe_expert_forward(d_dbg, ws)
     mxg.moe_expert_forward(d, ws)
     torch.cuda.synchronize()
     y1 = y.clone()
     mxg.moe_expert_forward(d, ws)
     torch.cuda.synchronize()
     assert torch.equal(y.view(torch.int16), y1.view(torch.int16)), "two runs differ"
+    assert torch.equal(y.view(torch.int16), y_dbg.view(torch.int16)), "timed run differs from debug run"
     cap_s = (max_m + 3) // 4 * 4  # the row scales are stored transposed: [E, H/128, cap_s]
     ga = _region(ws, off, 0, (max_m, H))
     gs_t = _region(ws, off, 1, (H // 128, cap_s), torch.float32)
@@ -186,7 +194,8 @@ def _run_fp8(T, H, I, seed, n_check, n_deep=0, vary_w2_scales=False, f32h=False,
         weights=_cached(lambda e: (np_(t["w13"][e]), np_(t["w13_s"][e]), np_(t["w2"][e]), np_(t["w2_s"][e]))),
         gathered=lambda e: (ga(e), np.ascontiguousarray(gs_t(e)[:, :max_m].T)),
         h_planes=lambda e: hp(e).view(np.uint16), y_bits=bf16_tensor_bits(y), toks=toks,
-        what=f"FP8{' hi/lo h' if f32h else ''} T={T} H={H}", f32h=f32h, o_gpu=og, e2e_tokens=e2e)
+        what=f"FP8{' hi/lo h' if f32h else ''} T={T} H={H}", f32h=f32h, o_gpu=og, e2e_tokens=e2e,
+        g1=lambda e: np_(dbg_g1[e]))
 
 
 def test_moe_fp8_small_full():

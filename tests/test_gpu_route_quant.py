@@ -41,11 +41,13 @@ def test_dispatch_bit_exact(T, k, max_m):
     log(f"dispatch T={T} top_k={k} max_m={max_m}")
     gen = datagen.generator(T + k, DEV)
     ids = datagen.distinct_topk_ids(gen, T, 256, k, DEV)
-    mm, row = _mxg().moe_dispatch(ids, 256, max_m)
+    mm, row, offs = _mxg().moe_dispatch(ids, 256, max_m, with_offsets=True)
     torch.cuda.synchronize()
     mm_o, row_o = oracle.dispatch(np_(ids), 256, max_m)
     assert np.array_equal(np_(mm), mm_o)
     assert np.array_equal(np_(row), row_o)
+    # offsets: exclusive prefix sum of masked_m (closed form from the oracle's counts)
+    assert np.array_equal(np_(offs), np.concatenate([[0], np.cumsum(mm_o)]))
 
 
 def _quant_inputs(gen, rows, K):

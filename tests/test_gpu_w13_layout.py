@@ -119,9 +119,10 @@ def test_moe_nvfp4_interleaved_w13_against_oracle(T, H, I):
     sf_il = mxg.moe_interleave_w13(t["w13_sf"])
     y = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
     dbg_h = torch.full((E, cap, I), float("nan"), dtype=torch.float32, device=DEV)
+    dbg_g1 = torch.full((E, cap, 2 * I), float("nan"), dtype=torch.float32, device=DEV)
     d = mxg.make_moe_desc(mxg.MXG_MOE_NVFP4, T, H, I, E, TOPK, cap, t["x"], w13_il, sf_il, t["w2"], t["w2_sf"],
                           ids, w, masked_m, row, y, g_x=s["g_x"], g_w13=t["g_w13"], g_w2=t["g_w2"],
-                          g_h=s["g_h"], w13_layout=mxg.MXG_W13_INTERLEAVED16, dbg_h=dbg_h)
+                          g_h=s["g_h"], w13_layout=mxg.MXG_W13_INTERLEAVED16, dbg_h=dbg_h, dbg_g1=dbg_g1)
     off = mxg.moe_expert_forward_workspace_layout(d)
     ws = torch.empty((off[5],), dtype=torch.uint8, device=DEV)
     mxg.moe_expert_forward(d, ws)
@@ -140,4 +141,5 @@ def test_moe_nvfp4_interleaved_w13_against_oracle(T, H, I):
         weights=lambda e: (np_(t["w13"][e]), np_(t["w13_sf"][e]), np_(t["w2"][e]), np_(t["w2_sf"][e])),
         g_w13=np_(t["g_w13"]), g_w2=np_(t["g_w2"]), g_h=s["g_h"],
         gathered=lambda e: (ga(e), gs(e), hc(e), hs(e)), h_pre=lambda e: np_(dbg_h[e]),
-        y_bits=bf16_tensor_bits(y), toks=np.arange(T), what=f"interleaved W13 T={T} H={H}")
+        y_bits=bf16_tensor_bits(y), toks=np.arange(T), what=f"interleaved W13 T={T} H={H}",
+        g1=lambda e: np_(dbg_g1[e]))
