@@ -68,6 +68,7 @@ SIGNATURES = {
     "moe_expert_forward_workspace_size": (_SZ, [_P]),
     "moe_expert_forward_workspace_layout": (_I, [_P, _P]),
     "moe_expert_forward": (_I, [_P, _P, _SZ, _P]),
+    "moe_expert_forward_noalloc": (_I, [_P, _P]),
 }
 
 
@@ -282,3 +283,7 @@ def moe_expert_forward(desc: MoeDesc, ws, stream=None):
     _check(lib().moe_expert_forward(ctypes.byref(desc), _ptr(ws), ws.numel() * ws.element_size(),
                                     _stream(stream)))
 
+
+def moe_expert_forward_noalloc(desc: MoeDesc, stream=None):
+    """moe_expert_forward on the library's own device scratch (no workspace argument)."""
+    _check(lib().moe_expert_forward_noalloc(ctypes.byref(desc), _stream(stream)))

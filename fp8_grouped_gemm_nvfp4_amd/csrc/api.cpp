@@ -7,7 +7,16 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "kernels.h"
+
+// Device scratch of moe_expert_forward_noalloc: one copy on every GPU the library runs
+// on, held until the process ends.  Its name is a host-side stand-in in host code, never
+// a device address: the address on each device comes from hipGetSymbolAddress, taken
+// once per device with that device current.  The array holds MXG_NOALLOC_SCRATCH_BYTES
+// of workspace plus a 64 KiB tail that no region reaches.
+static __device__ __align__(256) uint8_t scratch[MXG_NOALLOC_SCRATCH_BYTES + (64u << 10)];
 
 namespace {
 
@@ -44,6 +53,28 @@ int check_nvfp4_types(int ab_dtype, int sf_dtype, int c_dtype, int sf_vec_size) 
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // address of `scratch` on each device, once looked up
+
+// The scratch array's address on the current device (looked up on the first call there).
+int scratch_on_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "moe_expert_forward_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MXG_ERR_UNSUPPORTED, "moe_expert_forward_noalloc: device %d", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "moe_expert_forward_noalloc: hipGetSymbolAddress(scratch)");
+    if (!p) return fail(MXG_ERR_HIP, "moe_expert_forward_noalloc: no device address for the scratch array");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MXG_OK;
+}
 
 }  // namespace
 
@@ -397,6 +428,20 @@ int moe_expert_forward(const mxg_moe_desc* d, void* ws, size_t ws_bytes, void* s
   }
   e = mxg::combine(o, d->topk_ids, d->row, d->topk_w, T, H, k, mm, d->y, s);
   return hip_status(e, "combine");
+}
+
+int moe_expert_forward_noalloc(const mxg_moe_desc* d, void* stream) {
+  size_t off[6];
+  int st = moe_expert_forward_workspace_layout(d, off);
+  if (st) return st;
+  if (off[5] > MXG_NOALLOC_SCRATCH_BYTES)
+    return fail(MXG_ERR_WORKSPACE,
+                "moe_expert_forward_noalloc: the layer needs %zu bytes of workspace; the device scratch holds %zu",
+                off[5], (size_t)MXG_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  st = scratch_on_current_device(&ws);
+  if (st) return st;
+  return moe_expert_forward(d, ws, off[5], stream);
 }
 
 }  // extern "C"

@@ -367,6 +367,29 @@ int moe_expert_forward_workspace_layout(const mxg_moe_desc* desc, size_t* offset
 
 int moe_expert_forward(const mxg_moe_desc* desc, void* ws, size_t ws_bytes, void* stream);
 
+/* Workspace bytes moe_expert_forward_noalloc can serve (192 MiB per GPU). */
+#define MXG_NOALLOC_SCRATCH_BYTES ((size_t)192 << 20)
+
+/*
+ * moe_expert_forward with no workspace argument, for callers that cannot allocate
+ * device memory: code under graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The same kernels run on the same workspace regions
+ * (moe_expert_forward_workspace_layout), placed in a device array the library holds on
+ * every GPU it runs on until the process ends (MXG_NOALLOC_SCRATCH_BYTES of workspace;
+ * its address is looked up once per device, on the first call there).  Nothing is
+ * allocated or freed in the call.  y and every output are those of moe_expert_forward,
+ * bit for bit.
+ *   A layer whose workspace exceeds MXG_NOALLOC_SCRATCH_BYTES returns MXG_ERR_WORKSPACE
+ *   with nothing launched.  At E = 256, H = 7168, I = 2048 it serves max_m up to 16
+ *   (132 MiB for NVFP4, 157 MiB for FP8): decode batches.  The fp32 GEMM2 output alone
+ *   takes E * max_m * H * 4 bytes.
+ *   All calls on one GPU share its array, which keeps the last call's contents; no
+ *   region needs to start at zero (each call writes every row it later reads).  Calls
+ *   that overlap on one GPU (other streams, or host threads without ordering) race on
+ *   the array and corrupt each other's results: order them on one stream.
+ */
+int moe_expert_forward_noalloc(const mxg_moe_desc* desc, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
