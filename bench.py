@@ -1,6 +1,6 @@
 """Benchmark of the block-scaled grouped-GEMM / MoE hot path on one MI355X.
 
-Default workload (one "step" = the whole decode GEMM1 path): 8 tokens routed top-8
+Headline workload (one "step" = the whole decode GEMM1 path): 8 tokens routed top-8
 to 256 experts (ids from the seed) -> dispatch (masked_m, rows) -> NVFP4 quantization
 of the bf16 activations into the masked layout -> masked grouped NVFP4 GEMM1 against
 W13 [256, 4096, 7168] with bf16 output.  Inputs are resident in HBM before timing.
@@ -8,10 +8,12 @@ W13 [256, 4096, 7168] with bf16 output.  Inputs are resident in HBM before timin
 Prints ONE JSON line with the metric, a roofline object for the dominant kernel
 (algorithmic bytes / its HIP-event-timed average duration), cold-cache samples, the
 captured-graph replay time of the decode workloads and the oracle's CPU baseline on a
-bounded sample.  Other workloads: --workload (see WORKLOADS: the masked GEMM of 4 groups,
-the heterogeneous GEMM, the FP8 layer and its full-precision-intermediate variant, the
-NVFP4 layer at decode and prefill sizes with stacked or interleaved W13, the W4A16 GEMV,
-the contiguous-layout GEMM1); --all adds a per-workload table under "workloads".
+bounded sample.  The default run adds the other four configurations under "workloads"
+(the masked GEMM of 4 groups, the heterogeneous GEMM, the FP8 layer at T=4096 and the
+NVFP4 layer at T=64 and T=8192), each with its roofline against HBM and the MFMA peaks,
+tokens/s for the layers and an oracle baseline (token subsets for the prefill layers).
+--all adds the rows beyond the configurations (full-precision FP8 intermediate,
+interleaved W13, W4A16 GEMV, contiguous layout); --workload X makes X the main line.
 """
 from __future__ import annotations
 
@@ -266,14 +268,25 @@ def binding_roof(byts, flops, mfma_dtype):
 
 
 def roofline_row(r):
-    """Floor of a workload at its binding roof, and the fraction of it achieved (floor
-    over the measured step time)."""
+    """Roofline view of one workload.  The floor is the longer of its algorithmic bytes at
+    the HBM peak and its FLOPs at the MFMA peak of its operand format (fp4 for NVFP4
+    operands, fp8 for the FP8 path): `frac` = floor / measured step time.  `of_peak` gives
+    the step's rate against each roof separately, and `implementation` the floor at the
+    MFMA dtype the kernels actually compute in (the exact NVFP4 decode feeds the fp16
+    MFMA, which caps an MFMA-bound NVFP4 workload at 25% of the fp4 peak)."""
     hbm_ms = r["bytes"] / HBM_PEAK_GBS / 1e6
-    dt = r.get("mfma_dtype", "fp16")
-    mfma_ms = r["flops"] / PEAK_TFLOPS[dt] / 1e9
-    floor = max(hbm_ms, mfma_ms)
-    return dict(bound="mfma" if mfma_ms > hbm_ms else "hbm", mfma_dtype=dt, floor_ms=floor,
-                frac=floor / r["ms"])
+    fmt = r.get("format_dtype", r.get("mfma_dtype", "fp16"))
+    impl = r.get("mfma_dtype", fmt)
+    fmt_ms = r["flops"] / PEAK_TFLOPS[fmt] / 1e9
+    impl_ms = r.get("impl_mfma_ms", r["flops"] / PEAK_TFLOPS[impl] / 1e9)
+    floor = max(hbm_ms, fmt_ms)
+    of_peak = {"hbm": hbm_ms / r["ms"]}
+    for dt in ("fp4", "fp8", "fp16"):
+        of_peak[dt] = r["flops"] / PEAK_TFLOPS[dt] / 1e9 / r["ms"]
+    return dict(bound="mfma" if fmt_ms > hbm_ms else "hbm", format_dtype=fmt, floor_ms=floor,
+                frac=floor / r["ms"], of_peak=of_peak,
+                implementation=dict(mfma_dtype=impl, floor_ms=max(hbm_ms, impl_ms),
+                                    frac=max(hbm_ms, impl_ms) / r["ms"]))
 
 
 # ----------------------------------------------------------------------------- workloads
@@ -309,6 +322,7 @@ def bench_decode_gemm1(dev, steps, warmup, seed=1001, cpu=True):
     res = dict(name=wl.name, ms=ms, kernel_ms=kms, wall_s=wall, bytes=step_bytes, kernel_bytes=gemm_bytes,
                flops=flops, gbs=step_bytes / ms / 1e6, kernel_gbs=gemm_bytes / kms / 1e6,
                tflops=flops / ms / 1e9, tokens_per_s=T / ms * 1e3, bound="hbm", graph_ms=graph_ms,
+               format_dtype="fp4", mfma_dtype="fp16",
                config=dict(workload=wl.name, experts=E, tokens=T, top_k=top_k, K=H, N=N, max_m=max_m,
                            active_experts=n_act, sum_masked_m=rows))
     if cpu:
@@ -346,7 +360,7 @@ def cpu_baseline_decode_gemm1(t, s, step_bytes, min_seconds=10.0):
                 seconds_per_step=el / reps)
 
 
-def bench_masked_c0(dev, steps, warmup, seed=1000):
+def bench_masked_c0(dev, steps, warmup, seed=1000, cpu=False):
     wl = datagen.masked_gemm_workload(seed, dev)
     t = wl.tensors
     out = torch.empty((4, 64, 512), dtype=torch.bfloat16, device=dev)
@@ -363,12 +377,23 @@ def bench_masked_c0(dev, steps, warmup, seed=1000):
     rows, ng = int(mm.sum()), int((mm > 0).sum())
     byts = ng * 512 * NVFP4_ROW_BYTES(1024) + rows * NVFP4_ROW_BYTES(1024) + rows * 512 * 2
     flops = 2.0 * rows * 512 * 1024
-    return dict(name=wl.name, ms=ms, kernel_ms=kms, wall_s=wall, bytes=byts, kernel_bytes=byts, flops=flops,
-                gbs=byts / ms / 1e6, kernel_gbs=byts / kms / 1e6, tflops=flops / ms / 1e9, bound="launch",
-                config=dict(workload=wl.name, masked_m=mm.tolist()))
+    res = dict(name=wl.name, ms=ms, kernel_ms=kms, wall_s=wall, bytes=byts, kernel_bytes=byts, flops=flops,
+               gbs=byts / ms / 1e6, kernel_gbs=byts / kms / 1e6, tflops=flops / ms / 1e9, bound="launch",
+               format_dtype="fp4", mfma_dtype="fp16", config=dict(workload=wl.name, masked_m=mm.tolist()))
+    if cpu:
+        import oracle
+        h = {k: v.cpu().numpy() for k, v in t.items()}
+        reps, t0 = 0, time.perf_counter()
+        while reps == 0 or time.perf_counter() - t0 < 2.0:
+            oracle.gemm_nvfp4_masked(h["a"], h["a_sf"], h["b"], h["b_sf"], h["alpha"], h["masked_m"], 64, 512, 1024)
+            reps += 1
+        el = time.perf_counter() - t0
+        res["cpu_baseline"] = dict(value=byts * reps / el / 1e9, unit="GB/s", cores=oracle.num_threads(),
+                                   kind="oracle", sample=f"the whole masked GEMM ({rows} valid rows) x {reps}")
+    return res
 
 
-def bench_hetero(dev, steps, warmup, seed=1002):
+def bench_hetero(dev, steps, warmup, seed=1002, cpu=False):
     wl = datagen.hetero_gemm_workload(seed, dev)
     groups = []
     byts, flops = 0, 0.0
@@ -387,9 +412,21 @@ def bench_hetero(dev, steps, warmup, seed=1002):
             kt.stop()
 
     ms, kms, wall = timed_loop(step, steps, warmup)
-    return dict(name=wl.name, ms=ms, kernel_ms=kms, wall_s=wall, bytes=byts, kernel_bytes=byts, flops=flops,
-                gbs=byts / ms / 1e6, tflops=flops / ms / 1e9, kernel_tflops=flops / kms / 1e9, bound="mfma",
-                mfma_dtype="fp16", config=dict(workload=wl.name))
+    res = dict(name=wl.name, ms=ms, kernel_ms=kms, wall_s=wall, bytes=byts, kernel_bytes=byts, flops=flops,
+               gbs=byts / ms / 1e6, tflops=flops / ms / 1e9, kernel_tflops=flops / kms / 1e9, bound="mfma",
+               format_dtype="fp4", mfma_dtype="fp16", config=dict(workload=wl.name))
+    if cpu:
+        import oracle
+        host = [{k: (v.cpu().numpy() if torch.is_tensor(v) else v) for k, v in q.items() if k != "out"}
+                for q in groups]
+        t0 = time.perf_counter()
+        for q in host:
+            oracle.gemm_nvfp4_rows(q["a"], q["a_sf"], np.arange(q["M"]), q["b"], q["b_sf"], q["K"], q["alpha"])
+        el = time.perf_counter() - t0
+        res["cpu_baseline"] = dict(value=flops / el / 1e12, unit="TFLOP/s", cores=oracle.num_threads(),
+                                   kind="oracle", sample=f"every output of the 4 groups ({flops / 2e9:.1f} GMAC), "
+                                   f"once, {el:.1f} s")
+    return res
 
 
 GEMV_SHAPES = ((4096, 4096), (14336, 4096), (4096, 14336), (128256, 4096))  # Llama-3-8B (N, K): q/o, gate/up, down, LM head
@@ -423,7 +460,8 @@ def bench_gemv_w4a16(dev, steps, warmup, seed=1005, M=1):
     return dict(name=f"gemv_w4a16_llama3_8b_m{M}", ms=ms_all, kernel_ms=kms_all, wall_s=0.0, bytes=byts_all,
                 kernel_bytes=byts_all, flops=flops_all, gbs=byts_all / ms_all / 1e6,
                 kernel_gbs=byts_all / kms_all / 1e6, tflops=flops_all / ms_all / 1e9, bound="hbm",
-                mfma_dtype="fp16", config=dict(workload=f"gemv_w4a16_llama3_8b_m{M}", M=M, shapes=per))
+                format_dtype="fp16", mfma_dtype="fp16",
+                config=dict(workload=f"gemv_w4a16_llama3_8b_m{M}", M=M, shapes=per))
 
 
 def bench_contiguous(dev, steps, warmup, seed=1004, T=8192, align=128):
@@ -457,7 +495,7 @@ def bench_contiguous(dev, steps, warmup, seed=1004, T=8192, align=128):
     flops = 2.0 * rows * 2 * I * H
     return dict(name=f"contiguous_gemm1_nvfp4_t{T}", ms=ms, kernel_ms=kms, wall_s=wall, bytes=byts,
                 kernel_bytes=byts, flops=flops, gbs=byts / ms / 1e6, tflops=flops / ms / 1e9,
-                kernel_tflops=flops / kms / 1e9, bound="mfma", mfma_dtype="fp16",
+                kernel_tflops=flops / kms / 1e9, bound="mfma", format_dtype="fp4", mfma_dtype="fp16",
                 config=dict(workload=f"contiguous_gemm1_nvfp4_t{T}", tokens=T, rows=rows, contiguous_rows=M_total,
                             masked_rows=E * cap, align=align))
 
@@ -471,7 +509,43 @@ def _moe_setup(dev, t, T, E=256, top_k=8):
     return ids, w, masked_m, row, cap
 
 
-def bench_moe(dev, steps, warmup, precision, T, seed, w13_layout=0):
+def cpu_baseline_moe(precision, t, s, ids, w, cap, T, n_sub, seed):
+    """The oracle's layer on a seeded subset of n_sub tokens (all tokens when n_sub >= T):
+    its routing and dispatch run over every token, the expert path (quantize, GEMM1,
+    SwiGLU, intermediate, GEMM2, combine) over the subset, which is exact for those tokens
+    because the layer is token-separable.  Weights of the touched experts are copied to the
+    host before the clock starts."""
+    import oracle
+    E, I = 256, 2048
+    logits, bias = t["logits"].cpu().numpy(), t["bias"].cpu().numpy()
+    t0 = time.perf_counter()
+    ids_o, w_o = oracle.route_noaux(logits, bias, 8, 4, 8, 2.5)
+    mm_o, row_o = oracle.dispatch(ids_o, E, cap)
+    t_route = time.perf_counter() - t0
+    toks = np.arange(T) if n_sub >= T else np.sort(np.random.default_rng(seed).choice(T, n_sub, replace=False))
+    touched = sorted(set(ids_o[toks].ravel().tolist()))
+    if precision == "nvfp4":
+        W = {e: (t["w13"][e].cpu().numpy(), t["w13_sf"][e].cpu().numpy(), t["w2"][e].cpu().numpy(),
+                 t["w2_sf"][e].cpu().numpy()) for e in touched}
+        x = t["x"].float().cpu().numpy()
+        g13, g2 = t["g_w13"].cpu().numpy(), t["g_w2"].cpu().numpy()
+        t0 = time.perf_counter()
+        oracle.moe_layer_nvfp4(x, s["g_x"], ids_o, w_o, cap, W.__getitem__, g13, g2, s["g_h"], I, tokens=toks)
+    else:
+        W = {e: (t["w13"][e].cpu().numpy(), t["w13_s"][e].cpu().numpy(), t["w2"][e].cpu().numpy(),
+                 t["w2_s"][e].cpu().numpy()) for e in touched}
+        xq, xs = t["xq"].cpu().numpy(), t["xs"].cpu().numpy()
+        t0 = time.perf_counter()
+        oracle.moe_layer_fp8(xq, xs, ids_o, w_o, cap, W.__getitem__, I, tokens=toks,
+                             full_precision_h=precision == "fp8_f32h")
+    el = time.perf_counter() - t0
+    return dict(value=len(toks) / (el + t_route * len(toks) / T), unit="tokens/s", cores=oracle.num_threads(),
+                kind="oracle",
+                sample=f"expert path of {len(toks)} of {T} tokens ({len(touched)} experts) in {el:.1f} s; "
+                       f"routing + dispatch of all {T} tokens in {t_route:.2f} s, charged pro rata")
+
+
+def bench_moe(dev, steps, warmup, precision, T, seed, w13_layout=0, cpu=False):
     E, H, I, top_k = 256, 7168, 2048, 8
     fp8 = precision in ("fp8", "fp8_f32h")
     if fp8:
@@ -521,26 +595,56 @@ def bench_moe(dev, steps, warmup, precision, T, seed, w13_layout=0):
     # full-precision-intermediate variant's GEMM2 runs twice on the bf16 MFMA; its
     # algorithmic bytes and FLOPs are the layer's, as for the bf16 intermediate)
     mfma_dtype = "fp8" if fp8 else "fp16"
+    g1_flops, g2_flops = 2.0 * rows * 2 * I * H, 2.0 * rows * H * I
+    if fp8:  # GEMM1 on the scaled fp8 MFMA, GEMM2 on the bf16 MFMA (twice for the hi/lo planes)
+        impl_ms = (g1_flops / PEAK_TFLOPS["fp8"] + g2_flops * (2 if precision == "fp8_f32h" else 1)
+                   / PEAK_TFLOPS["bf16"]) / 1e9
+    else:
+        impl_ms = flops / PEAK_TFLOPS["fp16"] / 1e9
     name = wl.name + ("_f32h" if precision == "fp8_f32h" else "") + ("_w13il16" if w13_layout else "")
-    return dict(name=name, ms=ms, kernel_ms=kms, wall_s=wall, bytes=byts, flops=flops,
-                gbs=byts / ms / 1e6, tflops=flops / ms / 1e9, tokens_per_s=T / ms * 1e3,
-                bound=binding_roof(byts, flops, mfma_dtype), mfma_dtype=mfma_dtype, graph_ms=graph_ms,
-                config=dict(workload=name, tokens=T, active_experts=n_act, max_m=cap))
+    res = dict(name=name, ms=ms, kernel_ms=kms, wall_s=wall, bytes=byts, flops=flops,
+               gbs=byts / ms / 1e6, tflops=flops / ms / 1e9, tokens_per_s=T / ms * 1e3,
+               bound=binding_roof(byts, flops, mfma_dtype), mfma_dtype=mfma_dtype,
+               format_dtype="fp8" if fp8 else "fp4", impl_mfma_ms=impl_ms, graph_ms=graph_ms,
+               config=dict(workload=name, tokens=T, active_experts=n_act, max_m=cap))
+    if cpu:
+        res["cpu_baseline"] = cpu_baseline_moe(precision, t, s, ids, w, cap, T, 64 if T <= 64 else 128, seed + 7)
+    return res
 
 
 WORKLOADS = {
     "decode_gemm1": lambda dev, k, w, cpu: bench_decode_gemm1(dev, k, w, cpu=cpu),
-    "masked_c0": lambda dev, k, w, cpu: bench_masked_c0(dev, k, w),
-    "hetero": lambda dev, k, w, cpu: bench_hetero(dev, k, w),
-    "moe_fp8": lambda dev, k, w, cpu: bench_moe(dev, k, w, "fp8", 4096, 1003),
-    "moe_fp8_f32h": lambda dev, k, w, cpu: bench_moe(dev, k, w, "fp8_f32h", 4096, 1003),
-    "moe_nvfp4_decode": lambda dev, k, w, cpu: bench_moe(dev, k, w, "nvfp4", 64, 1004),
-    "moe_nvfp4_prefill": lambda dev, k, w, cpu: bench_moe(dev, k, w, "nvfp4", 8192, 1004),
+    "masked_c0": lambda dev, k, w, cpu: bench_masked_c0(dev, k, w, cpu=cpu),
+    "hetero": lambda dev, k, w, cpu: bench_hetero(dev, k, w, cpu=cpu),
+    "moe_fp8": lambda dev, k, w, cpu: bench_moe(dev, k, w, "fp8", 4096, 1003, cpu=cpu),
+    "moe_fp8_f32h": lambda dev, k, w, cpu: bench_moe(dev, k, w, "fp8_f32h", 4096, 1003, cpu=cpu),
+    "moe_nvfp4_decode": lambda dev, k, w, cpu: bench_moe(dev, k, w, "nvfp4", 64, 1004, cpu=cpu),
+    "moe_nvfp4_prefill": lambda dev, k, w, cpu: bench_moe(dev, k, w, "nvfp4", 8192, 1004, cpu=cpu),
     "moe_nvfp4_decode_w13il16": lambda dev, k, w, cpu: bench_moe(dev, k, w, "nvfp4", 64, 1004, 16),
     "moe_nvfp4_prefill_w13il16": lambda dev, k, w, cpu: bench_moe(dev, k, w, "nvfp4", 8192, 1004, 16),
     "gemv_w4a16": lambda dev, k, w, cpu: bench_gemv_w4a16(dev, k, w),
     "contiguous_gemm1": lambda dev, k, w, cpu: bench_contiguous(dev, k, w),
 }
+
+# The five configurations of the metric: the headline line is the decode GEMM1 (config 1,
+# the largest single-GPU configuration the GEMM half of the metric is quoted on); the
+# default run adds the other four as rows of "workloads", with the MoE layers' tokens/s.
+CONFIG_ROWS = ["masked_c0", "hetero", "moe_fp8", "moe_nvfp4_decode", "moe_nvfp4_prefill"]
+# The rows beyond the configurations (--all).
+NEXT_ROWS = ["moe_fp8_f32h", "moe_nvfp4_decode_w13il16", "moe_nvfp4_prefill_w13il16", "gemv_w4a16",
+             "contiguous_gemm1"]
+
+
+def table_row(q):
+    row = {k: q[k] for k in ("name", "ms", "kernel_ms", "graph_ms", "gbs", "tflops", "tokens_per_s")
+           if q.get(k) is not None}
+    if "shapes" in q["config"]:
+        row["shapes"] = q["config"]["shapes"]
+    row["config"] = q["config"]
+    row["roofline"] = roofline_row(q)
+    if q.get("cpu_baseline") is not None:
+        row["cpu_baseline"] = q["cpu_baseline"]
+    return row
 
 
 def main():
@@ -549,7 +653,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_gemm1", choices=sorted(WORKLOADS))
-    ap.add_argument("--all", action="store_true", help="also time every other workload")
+    ap.add_argument("--all", action="store_true", help="also time the rows beyond the five configurations")
+    ap.add_argument("--no-table", action="store_true", help="time the main workload only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold", type=int, default=10,
                     help="cold-cache samples of the main workload (each after a 1 GiB scrub); 0 = none")
@@ -580,10 +685,14 @@ def main():
     }
     dt = r.get("mfma_dtype", "fp16")
     if r["bound"] == "mfma":
+        # against the MFMA peak of the operand format (fp4 for NVFP4, fp8 for FP8); the
+        # peak of the dtype the kernels compute in is reported beside it
+        fmt = r.get("format_dtype", dt)
         line.update(value=r["tflops"], unit="TFLOP/s", dtype=f"{dt}-mfma/fp32-acc")
         achieved = r["flops"] / r["kernel_ms"] / 1e9
-        line["roofline"] = dict(bound="mfma", achieved=achieved, peak=PEAK_TFLOPS[dt], unit="TFLOP/s",
-                                frac=achieved / PEAK_TFLOPS[dt], traffic=None)
+        line["roofline"] = dict(bound="mfma", achieved=achieved, peak=PEAK_TFLOPS[fmt], unit="TFLOP/s",
+                                frac=achieved / PEAK_TFLOPS[fmt], traffic=None, peak_dtype=fmt,
+                                implementation_peak=PEAK_TFLOPS[dt], implementation_frac=achieved / PEAK_TFLOPS[dt])
     else:
         line.update(value=r["gbs"], unit="GB/s", dtype=f"{dt}-mfma/fp32-acc")
         kb = r.get("kernel_bytes", r["bytes"])
@@ -599,17 +708,15 @@ def main():
     if COLD["result"] is not None:
         line["cold"] = COLD["result"]
     line["cpu_baseline"] = r.get("cpu_baseline")
-    if args.all:
+    line["main_roofline"] = roofline_row(r)
+    names = [] if args.no_table else [n for n in CONFIG_ROWS + (NEXT_ROWS if args.all else []) if n != args.workload]
+    if names:
         rows = []
-        for name, fn in WORKLOADS.items():
-            if name == args.workload:
-                continue
-            q = fn(dev, max(5, args.steps // 5), 2, False)
-            rows.append({k: q[k] for k in ("name", "ms", "kernel_ms", "graph_ms", "gbs", "tflops")
-                         if q.get(k) is not None} |
-                        ({"shapes": q["config"]["shapes"]} if "shapes" in q["config"] else {}) |
-                        ({"tokens_per_s": q["tokens_per_s"]} if "tokens_per_s" in q else {}) |
-                        {"roofline": roofline_row(q)})
+        for name in names:
+            q = WORKLOADS[name](dev, max(10, args.steps // 5), 3, not args.no_cpu_baseline and name in CONFIG_ROWS)
+            rows.append(table_row(q))
+            print(f"[bench] {name}: {q['ms']:.4f} ms/step", file=sys.stderr, flush=True)
+            del q
             torch.cuda.empty_cache()
         line["workloads"] = rows
     if args.copy_calibration:

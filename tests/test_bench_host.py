@@ -29,6 +29,13 @@ def test_binding_roof_and_roofline_row():
     assert row["bound"] == "hbm" and row["floor_ms"] == pytest.approx(1.0) and row["frac"] == pytest.approx(0.5)
     row = bench.roofline_row({"bytes": 8e9, "flops": 5e12, "ms": 4.0, "mfma_dtype": "fp16"})
     assert row["bound"] == "mfma" and row["floor_ms"] == pytest.approx(2.0) and row["frac"] == pytest.approx(0.5)
+    # NVFP4 operands computed on the fp16 MFMA: the floor is at the fp4 peak, the
+    # implementation floor at the fp16 one
+    row = bench.roofline_row({"bytes": 8e9, "flops": 40.4e12, "ms": 32.0, "format_dtype": "fp4",
+                              "mfma_dtype": "fp16"})
+    assert row["bound"] == "mfma" and row["floor_ms"] == pytest.approx(4.0) and row["frac"] == pytest.approx(0.125)
+    assert row["implementation"]["floor_ms"] == pytest.approx(16.16) and row["of_peak"]["hbm"] == pytest.approx(1 / 32)
+    assert row["of_peak"]["fp8"] == pytest.approx(40.4e12 / 5000e9 / 32.0)
 
 
 def _csv(path, counter, rows):
