@@ -393,8 +393,11 @@ def bench_masked_c0(dev, steps, warmup, seed=1000, cpu=False):
     return res
 
 
-def bench_hetero(dev, steps, warmup, seed=1002, cpu=False):
+def bench_hetero(dev, steps, warmup, seed=1002, cpu=False, pow2=False):
+    """Config 2.  With pow2 the caller declares the scales (2^u by construction) powers of
+    two, and the groups run on the scaled fp4 MFMA."""
     wl = datagen.hetero_gemm_workload(seed, dev)
+    sf = mxg.MXG_E4M3_POW2 if pow2 else mxg.MXG_E4M3
     groups = []
     byts, flops = 0, 0.0
     for q in wl.tensors["groups"]:
@@ -407,14 +410,17 @@ def bench_hetero(dev, steps, warmup, seed=1002, cpu=False):
     def step(kt):
         if kt:
             kt.start()
-        mxg.mx_grouped_gemm(groups)
+        mxg.mx_grouped_gemm(groups, sf_dtype=sf)
         if kt:
             kt.stop()
 
     ms, kms, wall = timed_loop(step, steps, warmup)
-    res = dict(name=wl.name, ms=ms, kernel_ms=kms, wall_s=wall, bytes=byts, kernel_bytes=byts, flops=flops,
+    name = wl.name + ("_pow2" if pow2 else "")
+    # the power-of-two path: two fp4 MFMAs per 128-K block, i.e. the fp8 rate
+    res = dict(name=name, ms=ms, kernel_ms=kms, wall_s=wall, bytes=byts, kernel_bytes=byts, flops=flops,
                gbs=byts / ms / 1e6, tflops=flops / ms / 1e9, kernel_tflops=flops / kms / 1e9, bound="mfma",
-               format_dtype="fp4", mfma_dtype="fp16", config=dict(workload=wl.name))
+               format_dtype="fp4", mfma_dtype="fp8" if pow2 else "fp16",
+               config=dict(workload=name, scales="declared powers of two (fp4 MFMA)" if pow2 else "general e4m3"))
     if cpu:
         import oracle
         host = [{k: (v.cpu().numpy() if torch.is_tensor(v) else v) for k, v in q.items() if k != "out"}
@@ -616,6 +622,7 @@ WORKLOADS = {
     "decode_gemm1": lambda dev, k, w, cpu: bench_decode_gemm1(dev, k, w, cpu=cpu),
     "masked_c0": lambda dev, k, w, cpu: bench_masked_c0(dev, k, w, cpu=cpu),
     "hetero": lambda dev, k, w, cpu: bench_hetero(dev, k, w, cpu=cpu),
+    "hetero_pow2": lambda dev, k, w, cpu: bench_hetero(dev, k, w, cpu=False, pow2=True),
     "moe_fp8": lambda dev, k, w, cpu: bench_moe(dev, k, w, "fp8", 4096, 1003, cpu=cpu),
     "moe_fp8_f32h": lambda dev, k, w, cpu: bench_moe(dev, k, w, "fp8_f32h", 4096, 1003, cpu=cpu),
     "moe_nvfp4_decode": lambda dev, k, w, cpu: bench_moe(dev, k, w, "nvfp4", 64, 1004, cpu=cpu),
@@ -629,7 +636,7 @@ WORKLOADS = {
 # The five configurations of the metric: the headline line is the decode GEMM1 (config 1,
 # the largest single-GPU configuration the GEMM half of the metric is quoted on); the
 # default run adds the other four as rows of "workloads", with the MoE layers' tokens/s.
-CONFIG_ROWS = ["masked_c0", "hetero", "moe_fp8", "moe_nvfp4_decode", "moe_nvfp4_prefill"]
+CONFIG_ROWS = ["masked_c0", "hetero", "hetero_pow2", "moe_fp8", "moe_nvfp4_decode", "moe_nvfp4_prefill"]
 # The rows beyond the configurations (--all).
 NEXT_ROWS = ["moe_fp8_f32h", "moe_nvfp4_decode_w13il16", "moe_nvfp4_prefill_w13il16", "gemv_w4a16",
              "contiguous_gemm1"]

@@ -17,7 +17,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmxg.so")
 
 MXG_OK, MXG_ERR_INVALID_ARG, MXG_ERR_UNSUPPORTED, MXG_ERR_WORKSPACE, MXG_ERR_HIP = range(5)
-MXG_E2M1, MXG_E4M3, MXG_BF16, MXG_F32 = 1, 2, 3, 4
+MXG_E2M1, MXG_E4M3, MXG_BF16, MXG_F32, MXG_E4M3_POW2 = 1, 2, 3, 4, 5
 MXG_MOE_FP8_BLOCK128, MXG_MOE_NVFP4, MXG_MOE_FP8_BLOCK128_F32H = 1, 2, 3
 MXG_W13_STACKED, MXG_W13_INTERLEAVED16 = 0, 16
 MXG_MAX_GROUPS = 32
@@ -137,16 +137,17 @@ def mx_grouped_gemm_contiguous(a, a_sf, b, b_sf, alpha, group_start, count, out,
     return out
 
 
-def mx_grouped_gemm(groups, out_dtype=torch.bfloat16, cu_limit=0, stream=None):
+def mx_grouped_gemm(groups, out_dtype=torch.bfloat16, cu_limit=0, stream=None, sf_dtype=MXG_E4M3):
     """Heterogeneous grouped NVFP4 NT GEMM.  groups: list of dicts with M, N, K, alpha,
-    a, a_sf, b, b_sf, out (tensors) and optional ldc."""
+    a, a_sf, b, b_sf, out (tensors) and optional ldc.  sf_dtype=MXG_E4M3_POW2 declares
+    every scale byte a positive power of two (the fp4-MFMA path)."""
     G = len(groups)
     arr = (GroupDesc * max(G, 1))()
     for i, g in enumerate(groups):
         arr[i] = GroupDesc(g["M"], g["N"], g["K"], g.get("ldc", 0), float(g["alpha"]),
                            _ptr(g["a"]), _ptr(g["a_sf"]), _ptr(g["b"]), _ptr(g["b_sf"]), _ptr(g["out"]))
     c_dtype = {torch.bfloat16: MXG_BF16, torch.float32: MXG_F32}.get(out_dtype, 0)
-    _check(lib().mx_grouped_gemm(arr, G, MXG_E2M1, MXG_E4M3, c_dtype, 16, cu_limit, _stream(stream)))
+    _check(lib().mx_grouped_gemm(arr, G, MXG_E2M1, sf_dtype, c_dtype, 16, cu_limit, _stream(stream)))
 
 
 def mx_gemv_nvfp4_w4a16(x, w, w_sf, g_w, out=None, out_dtype=torch.bfloat16, cu_limit=0, stream=None):

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libmxg.so")
 OBJDIR = os.path.join(HERE, "_build")
 
-SOURCES = ["api.cpp", "gemm_nvfp4.hip", "gemm_nvfp4_skinny.hip", "gemm_nvfp4_stream.hip", "gemm_fp8.hip",
+SOURCES = ["api.cpp", "gemm_nvfp4.hip", "gemm_nvfp4_skinny.hip", "gemm_nvfp4_stream.hip", "gemm_nvfp4_mx.hip", "gemm_fp8.hip",
            "gemv_w4a16.hip", "quant.hip", "route.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

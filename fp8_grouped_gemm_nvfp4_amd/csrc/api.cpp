@@ -43,9 +43,9 @@ int hip_status(hipError_t e, const char* what) {
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 int check_nvfp4_types(int ab_dtype, int sf_dtype, int c_dtype, int sf_vec_size) {
-  if (ab_dtype != MXG_E2M1 || sf_dtype != MXG_E4M3 || sf_vec_size != 16)
+  if (ab_dtype != MXG_E2M1 || (sf_dtype != MXG_E4M3 && sf_dtype != MXG_E4M3_POW2) || sf_vec_size != 16)
     return fail(MXG_ERR_UNSUPPORTED,
-                "only ab_dtype=E2M1, sf_dtype=E4M3, sf_vec_size=16 is supported (got %d, %d, %d)",
+                "only ab_dtype=E2M1, sf_dtype=E4M3 or E4M3_POW2, sf_vec_size=16 is supported (got %d, %d, %d)",
                 ab_dtype, sf_dtype, sf_vec_size);
   if (c_dtype != MXG_BF16 && c_dtype != MXG_F32)
     return fail(MXG_ERR_UNSUPPORTED, "c_dtype must be BF16 or F32 (got %d)", c_dtype);
@@ -171,6 +171,10 @@ int mx_grouped_gemm(const mxg_group_desc* groups, int G, int ab_dtype, int sf_dt
     q.M = d.M; q.N = d.N; q.K = d.K; q.ldc = ldc; q.alpha = d.alpha;
   }
   int epi = c_dtype == MXG_BF16 ? mxg::EPI_BF16 : mxg::EPI_F32;
+  if (sf_dtype == MXG_E4M3_POW2) {
+    const hipError_t e = mxg::gemm_nvfp4_mx_hetero(p, epi, cu_limit, (hipStream_t)stream);
+    if (e != hipErrorNotSupported) return hip_status(e, "mx_grouped_gemm launch (power-of-two scales)");
+  }
   return hip_status(mxg::gemm_nvfp4_hetero(p, epi, cu_limit, (hipStream_t)stream),
                     "mx_grouped_gemm launch");
 }

@@ -56,6 +56,19 @@ struct HeteroGemmArgs {
   int total_tiles;
 };
 
+// Heterogeneous groups on the scaled fp4 MFMA (power-of-two e4m3 scales): the groups in
+// schedule order (tiles_m, tiles_n and tile_base filled in) and the item schedule, either
+// npat > 0 patterns (workgroups [pat_start[p], pat_start[p + 1]) take pat_cnt[p][g] items
+// of group g each, as contiguous ranges in workgroup order) or npat = 0 (round robin).
+constexpr int MX_MAX_PAT = 16;
+struct MxGemmArgs {
+  HeteroGroup grp[MXG_MAX_GROUPS];
+  int G, npat;
+  int pat_start[MX_MAX_PAT + 1];
+  unsigned char pat_cnt[MX_MAX_PAT][MXG_MAX_GROUPS];
+};
+hipError_t gemm_nvfp4_mx_hetero(HeteroGemmArgs p, int epi, int cu_limit, hipStream_t s);
+
 template <int MODE> struct ArgsOf;
 template <> struct ArgsOf<MODE_MASKED> { typedef MaskedGemmArgs type; };
 template <> struct ArgsOf<MODE_HETERO> { typedef HeteroGemmArgs type; };

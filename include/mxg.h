@@ -38,7 +38,10 @@ typedef enum {
   MXG_ERR_HIP = 4          /* a HIP launch or runtime call failed             */
 } mxg_status;
 
-typedef enum { MXG_E2M1 = 1, MXG_E4M3 = 2, MXG_BF16 = 3, MXG_F32 = 4 } mxg_dtype;
+/* MXG_E4M3_POW2 (sf_dtype only): e4m3 scale bytes that the caller declares to be positive
+ * powers of two, 2^-9 .. 2^8 (codes (u + 7) << 3 for u in [-6, 8], and 0x01, 0x02, 0x04);
+ * see mx_grouped_gemm. */
+typedef enum { MXG_E2M1 = 1, MXG_E4M3 = 2, MXG_BF16 = 3, MXG_F32 = 4, MXG_E4M3_POW2 = 5 } mxg_dtype;
 
 /* Static text for a status code ("unknown status" for anything else). */
 const char* mxg_status_string(int status);
@@ -63,8 +66,8 @@ int mxg_version(void);
  *   masked_m   device int32 [G], valid rows per group; clamped to [0, max_m]
  *   out        device [G, max_m, N] of c_dtype (bf16, round to nearest even, or
  *              fp32); rows at or beyond masked_m[g] are never written
- *   ab_dtype = MXG_E2M1, sf_dtype = MXG_E4M3, sf_vec_size = 16 (the only
- *   supported combination); c_dtype = MXG_BF16 or MXG_F32.
+ *   ab_dtype = MXG_E2M1, sf_dtype = MXG_E4M3 or MXG_E4M3_POW2 (same kernels here),
+ *   sf_vec_size = 16; c_dtype = MXG_BF16 or MXG_F32.
  *   cu_limit   0 = use the whole GPU; > 0 caps the number of resident
  *              workgroups to about that many CUs (sm_count analog)
  * Requirements: G in [1, 65535], max_m >= 1, N >= 1, K % 64 == 0 (else
@@ -137,6 +140,18 @@ typedef struct {
  * capture is, here, part of the captured kernel node, and the cap of 32 groups keeps
  * it inside the kernel-argument space.  Larger group counts with one shared N and K
  * are the masked (mx_grouped_gemm_masked) or contiguous layouts.
+ * sf_dtype = MXG_E4M3_POW2 declares that every scale byte of every group is a positive
+ * power of two.  Groups whose N and K are multiples of 128 (with 8-byte aligned bf16 or
+ * 16-byte aligned fp32 output rows) then run on the scaled fp4 MFMA: each power-of-two
+ * scale is exactly an e8m0 MFMA scale, so the result is the same exact-product fp32 sum
+ * as with general scales, at up to four times the rate of the fp16 MFMA the general
+ * decode uses (two fp4 MFMAs per 128-K block, one per 16-element half of each 32-element
+ * MFMA scale block).  Other shapes run the general kernels.  Scale bytes outside the
+ * declared set give wrong results (a zero scale counts as 2^-127, a mantissa is
+ * dropped), never an out-of-bounds access.
+ * Source for the power-of-two path: the per-16 e4m3 scales of NVFP4 do not map onto the
+ * per-32 e8m0 scales of the MX MFMA in general; a K split around the scaled MFMA does
+ * when the scales are powers of two.
  */
 int mx_grouped_gemm(const mxg_group_desc* groups, int G, int ab_dtype, int sf_dtype,
                     int c_dtype, int sf_vec_size, int cu_limit, void* stream);

@@ -207,23 +207,27 @@ def test_decode_gemm1_full_size(path):
 HETERO = ((128, 4096, 7168), (1000, 2048, 7168), (4096, 7168, 2048), (37, 4096, 4096))
 
 
-def _run_hetero(shapes, seed):
+def _run_hetero(shapes, seed, sf_dtype=None):
     wl = datagen.hetero_gemm_workload(seed, DEV, shapes)
     groups = []
     for q in wl.tensors["groups"]:
         q = dict(q)
         q["out"] = sentinel_bf16((q["M"], q["N"]), DEV)
         groups.append(q)
-    _mxg().mx_grouped_gemm(groups)
+    mxg = _mxg()
+    mxg.mx_grouped_gemm(groups, sf_dtype=mxg.MXG_E4M3 if sf_dtype is None else sf_dtype)
     torch.cuda.synchronize()
     return groups
 
 
-def test_hetero_gemm_full_size_rows():
+@pytest.mark.parametrize("pow2", [False, True])
+def test_hetero_gemm_full_size_rows(pow2):
     """Every row of the 37- and 128-row groups, and in the others every row on either side of
-    each 256-row M-tile boundary plus a seeded sample, all N columns of each."""
-    log("heterogeneous NVFP4 grouped GEMM (128,4096,7168) (1000,2048,7168) (4096,7168,2048) (37,4096,4096)")
-    groups = _run_hetero(HETERO, 1002)
+    each 256-row M-tile boundary plus a seeded sample, all N columns of each.  With pow2 the
+    caller declares the (power-of-two) scales as such and the fp4-MFMA path runs."""
+    log(f"heterogeneous NVFP4 grouped GEMM (128,4096,7168) (1000,2048,7168) (4096,7168,2048) (37,4096,4096)"
+        f"{' with power-of-two scales declared' if pow2 else ''}")
+    groups = _run_hetero(HETERO, 1002, _mxg().MXG_E4M3_POW2 if pow2 else None)
     rng = np.random.default_rng(5)
     for gi, q in enumerate(groups):
         M, N, K = q["M"], q["N"], q["K"]
@@ -339,3 +343,72 @@ def test_dispatch_contiguous_matches_oracle(T, E, align):
     torch.cuda.synchronize()
     s_o, c_o, r_o = oracle.dispatch_contiguous(np_(ids), E, align)
     assert np.array_equal(np_(cnt), c_o) and np.array_equal(np_(gs), s_o) and np.array_equal(np_(row), r_o)
+
+
+# ----------------------------------------------------------------------------- power-of-two scales
+def _pow2_groups(shapes, seed, out_dtype, ldc_pad=0, extreme=False):
+    gen = datagen.generator(seed, DEV)
+    groups = []
+    for gi, (M, N, K) in enumerate(shapes):
+        a, a_sf = datagen.nvfp4_uniform(gen, (M,), K, DEV)
+        b, b_sf = datagen.nvfp4_uniform(gen, (N,), K, DEV)
+        if extreme:
+            # every power-of-two e4m3 scale: subnormal 2^-9, 2^-8, 2^-7 and 2^-6 .. 2^8
+            codes = torch.tensor([0x01, 0x02, 0x04] + [(u + 7) << 3 for u in range(-6, 9)], dtype=torch.uint8,
+                                 device=DEV)
+            a_sf = codes[torch.randint(0, len(codes), tuple(a_sf.shape), generator=gen, device=DEV)]
+            b_sf = codes[torch.randint(0, len(codes), tuple(b_sf.shape), generator=gen, device=DEV)]
+        ldc = N + ldc_pad
+        mk = sentinel_bf16 if out_dtype == torch.bfloat16 else sentinel_f32
+        groups.append(dict(M=M, N=N, K=K, ldc=ldc, a=a, a_sf=a_sf, b=b, b_sf=b_sf, alpha=0.125 * (gi + 1),
+                           out=mk((max(M, 1), ldc), DEV)))
+    return groups
+
+
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("case", ["tails", "extreme_scales", "many_groups"])
+def test_hetero_gemm_pow2_against_oracle(out_dtype, case):
+    """The fp4-MFMA path (scales declared powers of two) against the oracle on every output:
+    M tails inside and past the first 128 rows of a tile, an empty group, K from one step up,
+    padded output rows, every power-of-two scale including the e4m3 subnormals, and more
+    groups than one item each."""
+    mxg = _mxg()
+    if case == "tails":
+        shapes, pad, extreme = ((300, 256, 384), (0, 128, 128), (37, 384, 1024), (513, 128, 256), (128, 128, 128)), 68, False
+    elif case == "extreme_scales":
+        shapes, pad, extreme = ((200, 256, 512), (16, 128, 896)), 0, True
+    else:
+        shapes, pad, extreme = tuple((17 * g + 1, 128 * (1 + g % 3), 128 * (1 + g % 5)) for g in range(12)), 4, False
+    log(f"power-of-two scales on the fp4 MFMA: {case} {shapes} {out_dtype}")
+    groups = _pow2_groups(shapes, 4242 + len(case), out_dtype, pad, extreme)
+    mxg.mx_grouped_gemm(groups, out_dtype=out_dtype, sf_dtype=mxg.MXG_E4M3_POW2)
+    torch.cuda.synchronize()
+    for gi, q in enumerate(groups):
+        M, N, K = q["M"], q["N"], q["K"]
+        if M == 0:
+            continue
+        if out_dtype == torch.bfloat16:
+            bits = bf16_tensor_bits(q["out"])
+            assert (bits[:, N:] == SENT_BF16).all(), f"group {gi}: padding columns written"
+            got, kw = bf16_from_bits_np(bits[:, :N]), {}
+        else:
+            o = np_(q["out"])
+            assert (o[:, N:].view(np.uint32) == np.uint32(SENT_F32 & 0xFFFFFFFF)).all(), f"group {gi}: padding written"
+            got, kw = o[:, :N].astype(np.float64), dict(ulp=ulp_f32)
+        y, S = oracle.gemm_nvfp4_rows(np_(q["a"]), np_(q["a_sf"]), np.arange(M), np_(q["b"]), np_(q["b_sf"]), K,
+                                      q["alpha"])
+        assert_within(got, y, S, f"pow2 {case} group {gi} ({M},{N},{K})", **kw)
+
+
+def test_hetero_gemm_pow2_grid_independent():
+    """The fp4-MFMA path gives the same bits whatever the grid (cu_limit) and schedule."""
+    mxg = _mxg()
+    shapes = ((300, 256, 384), (1000, 512, 1024), (64, 768, 256))
+    outs = []
+    for cu in (0, 7, 64):
+        groups = _pow2_groups(shapes, 77, torch.float32)
+        mxg.mx_grouped_gemm(groups, out_dtype=torch.float32, sf_dtype=mxg.MXG_E4M3_POW2, cu_limit=cu)
+        torch.cuda.synchronize()
+        outs.append([np_(q["out"]).view(np.uint32) for q in groups])
+    for o in outs[1:]:
+        assert all(np.array_equal(x, y) for x, y in zip(outs[0], o))
