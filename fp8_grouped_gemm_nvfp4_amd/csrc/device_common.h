@@ -19,6 +19,7 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef int int8v_t __attribute__((ext_vector_type(8)));
+typedef int int4v_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
@@ -185,6 +186,19 @@ __device__ __forceinline__ void dma16(const void* g, void* lds) {
 __device__ __forceinline__ void dma4(const void* g, void* lds) {
   uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(m0) : "memory", "m0");
+}
+
+// The same DMAs with a wave-uniform 64-bit base in SGPRs and a per-lane 32-bit byte
+// offset (the saddr form), which keeps per-lane addresses to one VGPR each.
+__device__ __forceinline__ void dma16_s(const void* sbase, uint32_t voff, void* lds) {
+  uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(m0)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4_s(const void* sbase, uint32_t voff, void* lds) {
+  uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(m0)
+               : "memory", "m0");
 }
 
 // Wait until at most N of this wave's vector memory operations are outstanding (they

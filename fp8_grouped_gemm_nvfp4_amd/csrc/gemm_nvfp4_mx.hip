@@ -15,16 +15,18 @@
 // the fp8 rate, twice the fp16 MFMA that the exact decode of general e4m3 scales needs.
 // The operands go from LDS to the MFMA as stored: no per-element decode.
 //
-// Tiles.  An item is (group, 256-row M tile, 128 output columns); a step is 128 K: per
-// row 64 code bytes and 8 scale bytes, for 256 activation and 128 weight rows (27 KB),
-// streamed by LDS DMA through a ring of five stages (three steps in flight).  Eight waves
-// as 2 (M) x 4 (N), each 128 rows x 32 columns: per step 8 activation and 2 weight
-// fragments, 16 MFMA tiles, 32 MFMAs.  The fragments of step s + 1 are read from LDS while
-// the MFMAs of step s run.  The MFMA computes D = B A^T, so each lane ends with four
-// consecutive output columns of one row.  A wave whose 128 rows all lie past M skips its
-// MFMAs and stores; activation rows past M inside a tile re-read row M - 1, and their
-// outputs (equal to row M - 1's bit for bit) are stored to row M - 1, so every active wave
-// issues the same number of stores per item.
+// Tiles.  An item is (group, M tile of 256 or 128 rows, 256 output columns); a step is
+// 128 K: per row 64 code bytes and 8 scale bytes, for 256 activation and 256 weight rows
+// (36 KB), streamed by LDS DMA through a ring of four stages (three steps in flight).
+// Eight waves as 2 (M) x 4 (N), each 128 (or 64) rows x 64 columns: per step 8 (4)
+// activation and 4 weight fragments, 32 (16) MFMA tiles, 64 (32) MFMAs; the two waves of a
+// SIMD cover each other's LDS reads.  The MFMA computes D = B A^T, so each lane ends with
+// four consecutive output columns of one row; bf16 outputs pair lanes to store 8.  A wave
+// whose rows or columns all lie past M or N skips its MFMAs and stores; activation rows
+// past M inside a tile re-read row M - 1, and their outputs (equal to row M - 1's bit for
+// bit) are stored to row M - 1, so every active wave issues a fixed number of stores per
+// item, which the DMA waits count.  Groups of at most 128 rows or of 40 steps and more
+// take 128-row tiles, so that no item is longer than a balanced share of the work.
 //
 // Schedule.  The host orders the groups by decreasing cost per item and deals the items
 // longest-first to the least-loaded workgroup; workgroups with the same count of items per
@@ -32,6 +34,7 @@
 // derived from its pattern (at most MX_MAX_PAT patterns, else a round-robin deal).
 #include <string.h>
 
+#include <type_traits>
 #include <vector>
 
 #include "device_common.h"
@@ -40,13 +43,14 @@
 namespace mxg {
 
 namespace mx {
-constexpr int BM = 256, BN = 128, BK = 128;
+constexpr int BM = 256, BN = 256, BK = 128;
 constexpr int WAVES = 8, THREADS = WAVES * 64;
-constexpr int RG = 8, NB = 2;                              // per wave: 16-row groups, 16-column groups
+constexpr int RG = 8, NB = 4;                              // per wave: 16-row groups (BM rows), 16-column groups
 constexpr int A_CODE = BM * 64, A_STAGE = A_CODE + BM * 8;  // codes [256][64], scales [256][8]
-constexpr int B_CODE = BN * 64, B_STAGE = B_CODE + BN * 8;  // codes [128][64], scales [128][8]
+constexpr int B_CODE = BN * 64, B_STAGE = B_CODE + BN * 8;  // codes [256][64], scales [256][8]
 constexpr int STAGE = A_STAGE + B_STAGE;
-constexpr int NST = 5;                                     // ring stages; steps in flight NST - 2
+constexpr int NST = 4;                                     // ring stages; three steps in flight
+constexpr int NDMA = 6;                                    // DMA instructions per wave and step
 }  // namespace mx
 
 // 16-byte chunk c of code row r sits at slot c ^ mx_swz(r) (conflict-free fragment reads)
@@ -63,9 +67,25 @@ __device__ __forceinline__ uint32_t mx_e8m0_pair(uint32_t w) {
 struct MxJob {
   const uint8_t *a, *a_sf, *b, *b_sf;
   void* out;
-  int m0, M, n0, K, ldc;
+  int m0, M, n0, N, K, ldc, bm;
   float alpha;
 };
+
+// Wait until the DMAs of the current step have landed: at most `later` vector memory
+// operations (the DMAs of the two later steps and the stores of the item ends since) may
+// still be outstanding.  `later` is 12 plus up to three store counts of 0, 8, 16 or 32,
+// capped at the counter's 63; the wait takes the largest listed count not above it
+// (waiting for fewer is always safe).
+__device__ __forceinline__ void mx_wait(int later) {
+  if (later >= 63) wait_vmcnt<63>();
+  else if (later >= 60) wait_vmcnt<60>();
+  else if (later >= 52) wait_vmcnt<52>();
+  else if (later >= 44) wait_vmcnt<44>();
+  else if (later >= 36) wait_vmcnt<36>();
+  else if (later >= 28) wait_vmcnt<28>();
+  else if (later >= 20) wait_vmcnt<20>();
+  else wait_vmcnt<12>();
+}
 
 template <int EPI>
 __global__ __launch_bounds__(mx::THREADS) void k_gemm_nvfp4_mx(const MxGemmArgs p) {
@@ -88,10 +108,9 @@ __global__ __launch_bounds__(mx::THREADS) void k_gemm_nvfp4_mx(const MxGemmArgs 
       if (p.npat > 0) {
         int pp = 0;
         while (pp + 1 < p.npat && p.pat_start[pp + 1] <= bx) pp++;
-        for (int q = 0; q < pp; q++) base += (p.pat_start[q + 1] - p.pat_start[q]) * p.pat_cnt[q][g];
-        cnt = p.pat_cnt[pp][g];
+        for (int t = 0; t < pp; t++) base += (p.pat_start[t + 1] - p.pat_start[t]) * p.pat_cnt[t][g];
+        cnt = bx < p.pat_start[p.npat] ? p.pat_cnt[pp][g] : 0;
         base += (bx - p.pat_start[pp]) * cnt;
-        if (bx >= p.pat_start[p.npat]) cnt = 0;
       } else {
         // round robin over the items in group order: item t goes to workgroup t % grid
         const int t0 = p.grp[g].tile_base, n = p.grp[g].tiles_m * p.grp[g].tiles_n;
@@ -120,68 +139,78 @@ __global__ __launch_bounds__(mx::THREADS) void k_gemm_nvfp4_mx(const MxGemmArgs 
       if (k < c) break;
       k -= c;
     }
-    if (g == G) g = G - 1, k = 0;  // past the last item: the last group's first (never computed)
+    if (g == G) g = G - 1, k = 0;  // past the last item (not reached)
     const HeteroGroup& q = p.grp[g];
     const int local = __builtin_amdgcn_readfirstlane(my_base[g]) + k * stride;
     const int mt = local / q.tiles_n;
     MxJob j;
     j.a = q.a; j.a_sf = q.a_sf; j.b = q.b; j.b_sf = q.b_sf; j.out = q.out;
-    j.m0 = mt * BM; j.M = q.M; j.n0 = (local - mt * q.tiles_n) * BN; j.K = q.K; j.ldc = q.ldc;
+    j.bm = p.bm[g];
+    j.m0 = mt * j.bm; j.M = q.M; j.n0 = (local - mt * q.tiles_n) * BN; j.N = q.N; j.K = q.K; j.ldc = q.ldc;
     j.alpha = q.alpha;
     return j;
   };
 
-  // ---- DMA: per step and wave, 2 activation code DMAs (rows 32 w ..), 1 weight code DMA
-  // (rows 16 w ..), 1 activation scale DMA (rows 32 w ..) and, for waves 0-3, 1 weight
-  // scale DMA (rows 32 w ..).  Rows past M re-read row M - 1.
-  const int n_dma = wave < 4 ? 5 : 4;
-  const uint8_t* asrc[2];
-  const uint8_t* asrc_s;
-  const uint8_t* bsrc;
-  const uint8_t* bsrc_s;
+  // ---- DMA: per step and wave, 2 activation and 2 weight code DMAs (rows 32 w ..) and 1
+  // activation and 1 weight scale DMA (rows 32 w ..).  Activation rows past M re-read row
+  // M - 1; with 128-row tiles rows 128 .. 255 of the stage re-read rows 0 .. 127; weight
+  // rows past N re-read row N - 1.  Per-lane byte offsets from the item's operand bases
+  // (uniform, in SGPRs).
+  uint32_t aoff[2], aoff_s, boff[2], boff_s;
+  const uint8_t *abase = nullptr, *abase_s = nullptr, *bbase = nullptr, *bbase_s = nullptr;
   auto dma_setup = [&](const MxJob& j) {
     const int K = j.K;
+    auto arow = [&](int r) {
+      const int rt = r < j.bm ? r : r - j.bm;
+      return j.m0 + rt < j.M ? j.m0 + rt : j.M - 1;
+    };
+    auto brow = [&](int r) { return j.n0 + r < j.N ? j.n0 + r : j.N - 1; };
 #pragma unroll
     for (int h = 0; h < 2; h++) {
       const int r = 32 * wave + 16 * h + (lane >> 2);
-      const int row = j.m0 + r < j.M ? j.m0 + r : j.M - 1;
-      asrc[h] = j.a + (size_t)row * (K / 2) + (((lane & 3) ^ mx_swz(r)) << 4);
+      const int sw = (((lane & 3) ^ mx_swz(r)) << 4);
+      aoff[h] = (uint32_t)arow(r) * (uint32_t)(K / 2) + sw;
+      boff[h] = (uint32_t)brow(r) * (uint32_t)(K / 2) + sw;
     }
-    {
-      const int r = 32 * wave + (lane >> 1);
-      const int row = j.m0 + r < j.M ? j.m0 + r : j.M - 1;
-      asrc_s = j.a_sf + (size_t)row * (K / 16) + (lane & 1) * 4;
-    }
-    {
-      const int r = 16 * wave + (lane >> 2);
-      bsrc = j.b + (size_t)(j.n0 + r) * (K / 2) + (((lane & 3) ^ mx_swz(r)) << 4);
-    }
-    {
-      const int r = 32 * (wave & 3) + (lane >> 1);
-      bsrc_s = j.b_sf + (size_t)(j.n0 + r) * (K / 16) + (lane & 1) * 4;
-    }
+    const int r = 32 * wave + (lane >> 1);
+    aoff_s = (uint32_t)arow(r) * (uint32_t)(K / 16) + (lane & 1) * 4;
+    boff_s = (uint32_t)brow(r) * (uint32_t)(K / 16) + (lane & 1) * 4;
+    abase = j.a; abase_s = j.a_sf; bbase = j.b; bbase_s = j.b_sf;
   };
   int d_k = 0, d_kt = 0, d_KT = 0, d_step = 0, d_st = 0;
-  auto dma_issue = [&]() {
+  // the DMAs of one step in three parts (interleaved with the MFMAs of the current step):
+  // activation codes, weight codes, both scale rows; the last part advances the cursor
+  auto dma_part = [&](int part) {
     uint8_t* st = ring + d_st * STAGE;
-    const int ko = d_kt;
+    if (part == 0) {
+      const uint8_t* ab = abase + d_kt * (BK / 2);
 #pragma unroll
-    for (int h = 0; h < 2; h++) dma16(asrc[h] + ko * (BK / 2), st + (32 * wave + 16 * h) * 64);
-    dma4(asrc_s + ko * (BK / 16), st + A_CODE + 32 * wave * 8);
-    dma16(bsrc + ko * (BK / 2), st + A_STAGE + 16 * wave * 64);
-    if (wave < 4) dma4(bsrc_s + ko * (BK / 16), st + A_STAGE + B_CODE + 32 * wave * 8);
-    d_st = d_st + 1 == NST ? 0 : d_st + 1;
-    // past the last step the cursor stays on it: the extra DMAs re-read it into stages
-    // that are not read again
-    if (d_step + 1 < nsteps) {
-      d_step++;
-      if (++d_kt == d_KT) {
-        d_kt = 0;
-        const MxJob j = job_at(++d_k);
-        d_KT = j.K / BK;
-        dma_setup(j);
+      for (int h = 0; h < 2; h++) dma16_s(ab, aoff[h], st + (32 * wave + 16 * h) * 64);
+    } else if (part == 1) {
+      const uint8_t* bb = bbase + d_kt * (BK / 2);
+#pragma unroll
+      for (int h = 0; h < 2; h++) dma16_s(bb, boff[h], st + A_STAGE + (32 * wave + 16 * h) * 64);
+    } else {
+      dma4_s(abase_s + d_kt * (BK / 16), aoff_s, st + A_CODE + 32 * wave * 8);
+      dma4_s(bbase_s + d_kt * (BK / 16), boff_s, st + A_STAGE + B_CODE + 32 * wave * 8);
+      d_st = d_st + 1 == NST ? 0 : d_st + 1;
+      // past the last step the cursor stays on it: the extra DMAs re-read it into stages
+      // that are not read again
+      if (d_step + 1 < nsteps) {
+        d_step++;
+        if (++d_kt == d_KT) {
+          d_kt = 0;
+          const MxJob j = job_at(++d_k);
+          d_KT = j.K / BK;
+          dma_setup(j);
+        }
       }
     }
+  };
+  auto dma_issue = [&]() {
+    dma_part(0);
+    dma_part(1);
+    dma_part(2);
   };
   {
     const MxJob j = job_at(0);
@@ -193,156 +222,153 @@ __global__ __launch_bounds__(mx::THREADS) void k_gemm_nvfp4_mx(const MxGemmArgs 
 
   // ---- compute state
   const int q = lane >> 4, rr = lane & 15;
-  float4_t acc[RG][NB];
-#pragma unroll
-  for (int i = 0; i < RG; i++)
-#pragma unroll
-    for (int n = 0; n < NB; n++) acc[i][n] = float4_t{0.f, 0.f, 0.f, 0.f};
-  struct Frag {
-    u32x4_t a[RG];
-    u32x4_t b[NB];
-    u32x2_t as[RG];
-    u32x2_t bs[NB];
-  };
-  Frag F[2];
-  auto load_frags = [&](Frag& f, int stage) {
+  int st_h[3] = {0, 0, 0};  // stores issued at the ends of the last three steps
+  int s = 0;                // global step
+
+  // Fragments of a step, read at its start: activation row group i (16 rows), weight
+  // column group n (16 columns); codes as stored and the two scale bytes of this lane's
+  // 32-element slice.
+  u32x4_t fa[RG], fb[NB];
+  uint32_t fas[RG], fbs[NB];
+  auto load_frags = [&](int rga, int bm, int stage) {
     const uint8_t* As = ring + stage * STAGE;
     const uint8_t* Bs = As + A_STAGE;
 #pragma unroll
-    for (int i = 0; i < RG; i++) {
-      const int r = 128 * wm + 16 * i + rr;
-      f.a[i] = *(const u32x4_t*)(As + r * 64 + ((q ^ mx_swz(r)) << 4));
-      f.as[i] = *(const u32x2_t*)(As + A_CODE + r * 8);
-    }
-#pragma unroll
     for (int n = 0; n < NB; n++) {
-      const int r = 32 * wn + 16 * n + rr;
-      f.b[n] = *(const u32x4_t*)(Bs + r * 64 + ((q ^ mx_swz(r)) << 4));
-      f.bs[n] = *(const u32x2_t*)(Bs + B_CODE + r * 8);
+      const int r = 64 * wn + 16 * n + rr;
+      fb[n] = *(const u32x4_t*)(Bs + r * 64 + ((q ^ mx_swz(r)) << 4));
+      fbs[n] = *(const uint32_t*)(Bs + B_CODE + r * 8 + 4 * (q >> 1));
     }
-  };
-
-  // stores issued at the last three item ends (0 or RG * NB each), for the DMA waits
-  int st_hist = 0;  // bit k: an item ended k + 1 iterations ago
-  auto wait_next = [&]() {
-    // the DMAs of step s + 1 have landed once at most the later ones are outstanding:
-    // two steps of DMAs and the stores of the item ends since then
-    const int ends = __builtin_popcount(st_hist & 7);
-    if (n_dma == 5) {
-      switch (ends) {
-        case 0: wait_vmcnt<10>(); break;
-        case 1: wait_vmcnt<10 + RG * NB>(); break;
-        case 2: wait_vmcnt<10 + 2 * RG * NB>(); break;
-        default: wait_vmcnt<10 + 3 * RG * NB>(); break;
-      }
-    } else {
-      switch (ends) {
-        case 0: wait_vmcnt<8>(); break;
-        case 1: wait_vmcnt<8 + RG * NB>(); break;
-        case 2: wait_vmcnt<8 + 2 * RG * NB>(); break;
-        default: wait_vmcnt<8 + 3 * RG * NB>(); break;
+#pragma unroll
+    for (int i = 0; i < RG; i++) {
+      if (i < rga) {
+        const int r = (bm / 2) * wm + 16 * i + rr;
+        fa[i] = *(const u32x4_t*)(As + r * 64 + ((q ^ mx_swz(r)) << 4));
+        fas[i] = *(const uint32_t*)(As + A_CODE + r * 8 + 4 * (q >> 1));
       }
     }
   };
 
-  // step 0's DMAs: the three later steps may be outstanding
-  if (n_dma == 5) wait_vmcnt<15>();
-  else wait_vmcnt<12>();
-  __syncthreads();
-  load_frags(F[0], 0);
-
-  MxJob cit = job_at(0);
-  int c_k = 0, c_kt = 0;
-  const int zero = 0;
-
-  auto step = [&](int s, Frag& cur, Frag& nxt) {
-    wait_next();
-    // every wave's DMAs of step s + 1 have landed and every wave is past its reads of
-    // step s - 1's stage, which the next DMA overwrites
-    __syncthreads();
-    dma_issue();
-    load_frags(nxt, (s + 1) % NST);
-    st_hist <<= 1;
-
-    const bool active = cit.m0 + 128 * wm < cit.M;
-    if (active) {
-      uint32_t sa[RG], sb[NB];
+  // One item over its KT steps with RGA 16-row groups per wave (0: the item has no rows or
+  // columns for this wave, which only keeps the DMA pipeline going), then its stores.
+  auto run_item = [&](auto rga_c, const MxJob& it) {
+    constexpr int RGA = decltype(rga_c)::value;
+    const int KT = it.K / BK, bmh = it.bm / 2;
+    float4_t acc[RGA > 0 ? RGA : 1][NB];
 #pragma unroll
-      for (int i = 0; i < RG; i++) sa[i] = mx_e8m0_pair(cur.as[i][q >> 1] >> (16 * (q & 1)));
+    for (int i = 0; i < RGA; i++)
 #pragma unroll
-      for (int n = 0; n < NB; n++) sb[n] = mx_e8m0_pair(cur.bs[n][q >> 1] >> (16 * (q & 1)));
-      // first 16-blocks of every lane's 32 elements, then the second ones
+      for (int n = 0; n < NB; n++) acc[i][n] = float4_t{0.f, 0.f, 0.f, 0.f};
+    for (int kt = 0; kt < KT; kt++) {
+      // step s's DMAs have landed for every wave, and every wave is past its reads of step
+      // s - 1's stage, which the next DMA overwrites
+      mx_wait(2 * NDMA + st_h[0] + st_h[1] + st_h[2]);
+      __syncthreads();
+      st_h[2] = st_h[1];
+      st_h[1] = st_h[0];
+      st_h[0] = 0;
+      if constexpr (RGA > 0) {
+        load_frags(RGA, it.bm, s % NST);
+        uint32_t sa[RGA], sb[NB];
 #pragma unroll
-      for (int n = 0; n < NB; n++) {
-        const int8v_t blo = {(int)cur.b[n][0], (int)cur.b[n][1], zero, zero, 0, 0, 0, 0};
+        for (int i = 0; i < RGA; i++) sa[i] = mx_e8m0_pair(fas[i] >> (16 * (q & 1)));
 #pragma unroll
-        for (int i = 0; i < RG; i++) {
-          const int8v_t av = {(int)cur.a[i][0], (int)cur.a[i][1], (int)cur.a[i][2], (int)cur.a[i][3], 0, 0, 0, 0};
-          acc[i][n] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(blo, av, acc[i][n], 4, 4, 0, sb[n], 0, sa[i]);
-        }
-      }
+        for (int n = 0; n < NB; n++) sb[n] = mx_e8m0_pair(fbs[n] >> (16 * (q & 1)));
+        // per pair of 16-row groups: the first 16-blocks of every lane's 32 elements for
+        // their tiles, then the second ones (each hi MFMA 2 NB MFMAs after its lo MFMA);
+        // a part of the next step's DMAs after each of the first three pairs, so that
+        // their issue overlaps the MFMAs already queued
 #pragma unroll
-      for (int n = 0; n < NB; n++) {
-        const int8v_t bhi = {zero, zero, (int)cur.b[n][2], (int)cur.b[n][3], 0, 0, 0, 0};
+        for (int i0 = 0; i0 < RGA; i0 += 2) {
+          if (i0 > 0 && i0 / 2 <= 3) {
+            __builtin_amdgcn_sched_barrier(0);
+            dma_part(i0 / 2 - 1);
+            __builtin_amdgcn_sched_barrier(0);
+          }
 #pragma unroll
-        for (int i = 0; i < RG; i++) {
-          const int8v_t av = {(int)cur.a[i][0], (int)cur.a[i][1], (int)cur.a[i][2], (int)cur.a[i][3], 0, 0, 0, 0};
-          acc[i][n] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bhi, av, acc[i][n], 4, 4, 1, sb[n], 1, sa[i]);
-        }
-      }
-    }
-
-    if (++c_kt == cit.K / BK) {
-      if (active) {
-        // lane (rr, q): row 128 wm + 16 i + rr of the tile, columns 4 q .. 4 q + 3 of the
-        // wave's 16-column group n; rows past M hold row M - 1's values and go there
+          for (int i = i0; i < i0 + 2; i++) {
+            const int8v_t alo = __builtin_shufflevector((int4v_t)fa[i], int4v_t{0, 0, 0, 0}, 0, 1, 4, 5, -1, -1, -1, -1);
 #pragma unroll
-        for (int i = 0; i < RG; i++) {
-          int m = cit.m0 + 128 * wm + 16 * i + rr;
-          m = m < cit.M ? m : cit.M - 1;
+            for (int n = 0; n < NB; n++) {
+              const int8v_t bv = __builtin_shufflevector((int4v_t)fb[n], (int4v_t)fb[n], 0, 1, 2, 3, -1, -1, -1, -1);
+              acc[i][n] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bv, alo, acc[i][n], 4, 4, 0, sb[n], 0, sa[i]);
+            }
+          }
 #pragma unroll
-          for (int n = 0; n < NB; n++) {
-            const int c = cit.n0 + 32 * wn + 16 * n + 4 * q;
-            const float4_t v = acc[i][n] * cit.alpha;
-            if constexpr (EPI == EPI_BF16) {
-              const uint32_t lo = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
-              const uint32_t hi = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
-              *(u32x2_t*)((uint16_t*)cit.out + (size_t)m * cit.ldc + c) = u32x2_t{lo, hi};
-            } else {
-              *(float4_t*)((float*)cit.out + (size_t)m * cit.ldc + c) = v;
+          for (int i = i0; i < i0 + 2; i++) {
+            const int8v_t ahi = __builtin_shufflevector((int4v_t)fa[i], int4v_t{0, 0, 0, 0}, 4, 5, 2, 3, -1, -1, -1, -1);
+#pragma unroll
+            for (int n = 0; n < NB; n++) {
+              const int8v_t bv = __builtin_shufflevector((int4v_t)fb[n], (int4v_t)fb[n], 0, 1, 2, 3, -1, -1, -1, -1);
+              acc[i][n] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bv, ahi, acc[i][n], 4, 4, 1, sb[n], 1, sa[i]);
             }
           }
         }
-        st_hist |= 1;
+        // with fewer than 8 row groups, the DMA parts not issued yet
+#pragma unroll
+        for (int part = RGA / 2 - 1; part < 3; part++) dma_part(part);
+      } else {
+        dma_issue();
       }
+      s++;
+    }
+    if constexpr (RGA > 0) {
+      // lane (rr, q): row (bm / 2) wm + 16 i + rr of the tile, columns 4 q .. 4 q + 3 of
+      // each 16-column group n; rows past M hold row M - 1's values and go there
 #pragma unroll
-      for (int i = 0; i < RG; i++)
+      for (int i = 0; i < RGA; i++) {
+        int m = it.m0 + bmh * wm + 16 * i + rr;
+        m = m < it.M ? m : it.M - 1;
+        if constexpr (EPI == EPI_BF16) {
+          // lanes q and q ^ 1 trade halves so that each holds 8 consecutive columns:
+          // even q columns 8 (q / 2) .. + 7 of group n, odd q those of group n + 1
+          const bool odd = q & 1;
 #pragma unroll
-        for (int n = 0; n < NB; n++) acc[i][n] = float4_t{0.f, 0.f, 0.f, 0.f};
-      c_kt = 0;
-      if (++c_k < n_items) cit = job_at(c_k);
+          for (int n = 0; n < NB; n += 2) {
+            const float4_t v0 = acc[i][n] * it.alpha, v1 = acc[i][n + 1] * it.alpha;
+            const uint32_t a0 = f32_to_bf16_rne(v0[0]) | (f32_to_bf16_rne(v0[1]) << 16);
+            const uint32_t a1 = f32_to_bf16_rne(v0[2]) | (f32_to_bf16_rne(v0[3]) << 16);
+            const uint32_t b0 = f32_to_bf16_rne(v1[0]) | (f32_to_bf16_rne(v1[1]) << 16);
+            const uint32_t b1 = f32_to_bf16_rne(v1[2]) | (f32_to_bf16_rne(v1[3]) << 16);
+            const uint32_t s0 = __shfl_xor(odd ? a0 : b0, 16), s1 = __shfl_xor(odd ? a1 : b1, 16);
+            const u32x4_t w = odd ? u32x4_t{s0, s1, b0, b1} : u32x4_t{a0, a1, s0, s1};
+            const int c = it.n0 + 64 * wn + 16 * (n + (odd ? 1 : 0)) + 8 * (q >> 1);
+            *(u32x4_t*)((uint16_t*)it.out + (size_t)m * it.ldc + c) = w;
+          }
+        } else {
+#pragma unroll
+          for (int n = 0; n < NB; n++) {
+            const int c = it.n0 + 64 * wn + 16 * n + 4 * q;
+            *(float4_t*)((float*)it.out + (size_t)m * it.ldc + c) = acc[i][n] * it.alpha;
+          }
+        }
+      }
+      st_h[0] = RGA * (EPI == EPI_BF16 ? NB / 2 : NB);  // stores issued at this step's end
     }
   };
 
-  int s = 0;
-  for (; s + 1 < nsteps; s += 2) {
-    step(s, F[0], F[1]);
-    step(s + 1, F[1], F[0]);
+  for (int k = 0; k < n_items; k++) {
+    const MxJob it = job_at(k);
+    const bool active = it.m0 + (it.bm / 2) * wm < it.M && it.n0 + 64 * wn < it.N;
+    if (!active) run_item(std::integral_constant<int, 0>{}, it);
+    else if (it.bm == BM) run_item(std::integral_constant<int, RG>{}, it);
+    else run_item(std::integral_constant<int, RG / 2>{}, it);
   }
-  if (s < nsteps) step(s, F[0], F[1]);
   wait_vmcnt<0>();  // the trailing DMAs land before the workgroup ends
 }
 
 // ---------------------------------------------------------------------------- host side
 namespace {
 
-// Cost of one item of group q in the units of the schedule: steps times the waves per
-// SIMD that compute (one when the tile's rows fit the first 128, else two), plus a fixed
-// per-step share for the DMA issue and the barrier.
-double mx_item_cost(const HeteroGroup& q) {
-  const int rows = q.M < mx::BM ? q.M : mx::BM;  // the fullest tile of the group
-  return (q.K / mx::BK) * ((rows > 128 ? 2.0 : 1.0) + 0.5);
-}
+// M tile of a group: 128 rows for groups of at most 128 rows (the other half of a 256-row
+// tile would idle two of the four SIMDs) and for deep groups (K >= 40 steps), whose
+// 256 x 256 items would be longer than a balanced share of the work; 256 otherwise.
+int mx_bm(const HeteroGroup& q) { return (q.M <= 128 || q.K / mx::BK >= 40) ? 128 : 256; }
+
+// Cost of one item of group q in the units of the schedule: steps times the share of a
+// full 256 x 256 tile the waves compute, plus a per-step share for the barrier, the
+// fragment reads and the DMA issue (measured: about 0.6 of a full step's MFMA time).
+double mx_item_cost(const HeteroGroup& q) { return (q.K / mx::BK) * (mx_bm(q) / 256.0 + 0.6); }
 
 // Longest-first deal of the items (groups in schedule order, every item of a group at the
 // group's cost) to the least-loaded of W workgroups, ties to the lower index; the count
@@ -395,20 +421,22 @@ struct MxSchedCache {
 
 }  // namespace
 
-// Groups with rows need N % 128 == 0, K % 128 == 0 and aligned output rows; returns
-// hipErrorNotSupported (nothing launched) otherwise.  The groups are reordered by
+// Groups with rows need N % 128 == 0, K % 128 == 0 and 16-byte aligned output rows;
+// returns hipErrorNotSupported (nothing launched) otherwise.  The groups are reordered by
 // decreasing item cost and the items dealt longest-first (see the file comment).
 hipError_t gemm_nvfp4_mx_hetero(HeteroGemmArgs in, int epi, int cu_limit, hipStream_t s) {
   using namespace mx;
   if (epi != EPI_BF16 && epi != EPI_F32) return hipErrorNotSupported;
-  const uintptr_t out_align = epi == EPI_BF16 ? 8 : 16;
+  const int ldc_mult = epi == EPI_BF16 ? 8 : 4;  // 16-byte row starts
   MxGemmArgs p{};
   int order[MXG_MAX_GROUPS], n = 0;
   for (int g = 0; g < in.G; g++) {
     const HeteroGroup& q = in.grp[g];
     if (q.M == 0) continue;
-    if (q.N % BN != 0 || q.K % BK != 0 || q.K <= 0 || q.ldc % 4 != 0 ||
-        ((uintptr_t)q.out & (out_align - 1)) != 0)
+    if (q.N % 128 != 0 || q.K % BK != 0 || q.K <= 0 || q.ldc % ldc_mult != 0 || ((uintptr_t)q.out & 15u) != 0)
+      return hipErrorNotSupported;
+    // the DMAs address operand rows by 32-bit byte offsets from the group's bases
+    if ((long long)q.M * (q.K / 2) >= (1LL << 32) || (long long)q.N * (q.K / 2) >= (1LL << 32))
       return hipErrorNotSupported;
     order[n++] = g;
   }
@@ -425,8 +453,9 @@ hipError_t gemm_nvfp4_mx_hetero(HeteroGemmArgs in, int epi, int cu_limit, hipStr
   long long items = 0;
   for (int i = 0; i < n; i++) {
     HeteroGroup q = in.grp[order[i]];
-    q.tiles_m = (q.M + BM - 1) / BM;
-    q.tiles_n = q.N / BN;
+    p.bm[i] = mx_bm(q);
+    q.tiles_m = (q.M + p.bm[i] - 1) / p.bm[i];
+    q.tiles_n = (q.N + BN - 1) / BN;
     q.tile_base = (int)items;
     items += (long long)q.tiles_m * q.tiles_n;
     p.grp[i] = q;

@@ -63,6 +63,7 @@ struct HeteroGemmArgs {
 constexpr int MX_MAX_PAT = 16;
 struct MxGemmArgs {
   HeteroGroup grp[MXG_MAX_GROUPS];
+  int bm[MXG_MAX_GROUPS];  // M tile of each group (128 or 256 rows)
   int G, npat;
   int pat_start[MX_MAX_PAT + 1];
   unsigned char pat_cnt[MX_MAX_PAT][MXG_MAX_GROUPS];
