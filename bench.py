@@ -130,6 +130,74 @@ def summarize_counters(fetch_csv, write_csv, workload="decode_gemm1", kernel_sub
     return "\n".join(lines)
 
 
+# Sources of the MFMA kernels whose counters the MFMA record summarizes.
+MFMA_KERNEL_SOURCES = ["fp8_grouped_gemm_nvfp4_amd/csrc/gemm_nvfp4_stream.hip",
+                       "fp8_grouped_gemm_nvfp4_amd/csrc/gemm_nvfp4_mx.hip",
+                       "fp8_grouped_gemm_nvfp4_amd/csrc/gemm_fp8.hip",
+                       "fp8_grouped_gemm_nvfp4_amd/csrc/stream_common.h",
+                       "fp8_grouped_gemm_nvfp4_amd/csrc/device_common.h",
+                       "fp8_grouped_gemm_nvfp4_amd/csrc/kernels.h"]
+MFMA_KERNELS = {  # kernel name substring -> (MFMA dtype, the instruction's peak), for the record
+    "k_gemm_nvfp4_stream": ("fp16", "v_mfma_f32_16x16x32_f16"),
+    "k_gemm_nvfp4_mx": ("fp4", "v_mfma_scale_f32_16x16x128_f8f6f4, e2m1 operands"),
+    "k_gemm_fp8_swiglu": ("fp8", "v_mfma_scale_f32_16x16x128_f8f6f4, e4m3 operands"),
+    "k_gemm_bf16_fp8w": ("bf16", "v_mfma_f32_16x16x32_bf16"),
+}
+
+
+def summarize_mfma_counters(pmc_csv, fetch_csv, write_csv, cus=256, simds_per_cu=4, xcds=8):
+    """Markdown record of the MFMA kernels in a rocprofv3 --pmc run (SQ_BUSY_CYCLES,
+    SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_VALU, SQ_INSTS_LDS, SQ_LDS_BANK_CONFLICT,
+    SQ_INSTS_MFMA, SQ_WAVES, GRBM_GUI_ACTIVE) and two --copy-calibration passes
+    (FETCH_SIZE, WRITE_SIZE), averaged per dispatch.  MFMA utilization = MFMA busy cycles
+    (summed over SIMDs) over the SIMD cycles of the dispatch (GRBM_GUI_ACTIVE per XCD x
+    SIMDs); each busy cycle runs at the peak of the instruction's dtype, so the fraction of
+    another dtype's peak scales by the ratio of the peaks."""
+    import csv
+    from collections import defaultdict
+
+    def per_kernel(path):
+        # one row per kernel instantiation (template arguments kept, "void mxg::" dropped)
+        out = defaultdict(lambda: defaultdict(list))
+        for r in csv.DictReader(open(path)):
+            name = r["Kernel_Name"]
+            if "copyBuffer" in name:
+                key = "copy"
+            elif any(k in name for k in MFMA_KERNELS):
+                key = name.split("(")[0].replace("void ", "").replace("mxg::", "")
+            else:
+                continue
+            out[key][r["Counter_Name"]].append(float(r["Counter_Value"]))
+        return out
+
+    pmc, fet, wri = per_kernel(pmc_csv), per_kernel(fetch_csv), per_kernel(write_csv)
+    known_kib = (1 << 30) / 1024.0
+    f_scale = known_kib / max(x for x in fet["copy"]["FETCH_SIZE"] if x >= 0.25 * known_kib)
+    w_scale = known_kib / max(x for x in wri["copy"]["WRITE_SIZE"] if x >= 0.25 * known_kib)
+    lines = ["| kernel | dispatches | MFMA dtype | MFMA instr / dispatch | busy cycles / MFMA | MFMA busy | "
+             "of fp16 / fp8 / fp4 peak | VALU instr / wave | LDS instr / wave | LDS bank-conflict cycles / busy | "
+             "HBM read MB | HBM write MB |",
+             "|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for k in sorted(x for x in pmc if x != "copy"):
+        dt, instr = next(v for n, v in MFMA_KERNELS.items() if n in k)
+        c = {n: float(np.mean(v)) for n, v in pmc[k].items()}
+        simd_cycles = c["GRBM_GUI_ACTIVE"] / xcds * cus * simds_per_cu
+        util = c["SQ_VALU_MFMA_BUSY_CYCLES"] / simd_cycles
+        rate = util * PEAK_TFLOPS[dt]
+        fr = "/".join(f"{rate / PEAK_TFLOPS[p]:.1%}" for p in ("fp16", "fp8", "fp4"))
+        rd = float(np.mean(fet[k]["FETCH_SIZE"])) * f_scale * 1024 / 1e6 if k in fet else float("nan")
+        wr = float(np.mean(wri[k]["WRITE_SIZE"])) * w_scale * 1024 / 1e6 if k in wri else float("nan")
+        per_mfma = c["SQ_VALU_MFMA_BUSY_CYCLES"] / max(c["SQ_INSTS_MFMA"], 1)
+        lines.append(f"| `{k}` | {len(pmc[k]['SQ_WAVES'])} | {dt} ({instr}) | {c['SQ_INSTS_MFMA']:.4g} | "
+                     f"{per_mfma:.1f} | {util:.1%} | {fr} | "
+                     f"{c['SQ_INSTS_VALU'] / c['SQ_WAVES']:.0f} | {c['SQ_INSTS_LDS'] / c['SQ_WAVES']:.0f} | "
+                     f"{c['SQ_LDS_BANK_CONFLICT'] / max(c['SQ_BUSY_CYCLES'], 1):.1%} | {rd:.1f} | {wr:.1f} |")
+    lines += ["", f"source_sha256: {kernel_source_hash(MFMA_KERNEL_SOURCES)}",
+              "sources hashed: " + ", ".join(MFMA_KERNEL_SOURCES),
+              f"counter scales from the 1 GiB copy: FETCH_SIZE x{f_scale:.3f}, WRITE_SIZE x{w_scale:.3f}"]
+    return "\n".join(lines)
+
+
 def _ensure_built():
     if not os.path.exists(mxg.LIB_PATH):
         from fp8_grouped_gemm_nvfp4_amd import _build
@@ -667,9 +735,14 @@ def main():
                     help="cold-cache samples of the main workload (each after a 1 GiB scrub); 0 = none")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration under rocprofv3 --pmc)")
+    ap.add_argument("--summarize-mfma", nargs=3, metavar=("PMC_CSV", "FETCH_CSV", "WRITE_CSV"),
+                    help="print the MFMA-kernel counter record of three rocprofv3 --pmc runs")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="print the traffic record of the dominant kernel from two rocprofv3 --pmc runs")
     args = ap.parse_args()
+    if args.summarize_mfma:
+        print(summarize_mfma_counters(*args.summarize_mfma))
+        return
     if args.summarize_counters:
         print(summarize_counters(*args.summarize_counters, workload=args.workload))
         return

@@ -70,3 +70,29 @@ def test_recorded_traffic_follows_the_source_hash(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "TRAFFIC_RECORDS", {"decode_gemm1": (str(bad), files)})
     assert bench.recorded_traffic("decode_gemm1") is None
     assert bench.recorded_traffic("hetero") is None
+
+
+def _pmc_csv(path, rows):
+    with open(path, "w") as f:
+        f.write("Kernel_Name,Counter_Name,Counter_Value\n")
+        for name, counter, value in rows:
+            f.write(f"\"{name}\",{counter},{value}\n")
+
+
+def test_summarize_mfma_counters(tmp_path):
+    kern = "void mxg::k_gemm_nvfp4_mx<0>(mxg::MxGemmArgs)"
+    copy = "__amd_rocclr_copyBuffer"
+    # one dispatch: 1000 GRBM cycles summed over 8 XCDs = 125 per XCD; 1024 SIMDs;
+    # a quarter of the SIMD cycles MFMA-busy
+    busy = 0.25 * 125 * 1024
+    pmc = [(kern, "GRBM_GUI_ACTIVE", 1000), (kern, "SQ_VALU_MFMA_BUSY_CYCLES", busy), (kern, "SQ_WAVES", 10),
+           (kern, "SQ_INSTS_VALU", 500), (kern, "SQ_INSTS_LDS", 70), (kern, "SQ_LDS_BANK_CONFLICT", 5),
+           (kern, "SQ_BUSY_CYCLES", 100), (kern, "SQ_INSTS_MFMA", 1)]
+    _pmc_csv(tmp_path / "p.csv", pmc)
+    _pmc_csv(tmp_path / "f.csv", [(kern, "FETCH_SIZE", 1000), (copy, "FETCH_SIZE", 524288)])
+    _pmc_csv(tmp_path / "w.csv", [(kern, "WRITE_SIZE", 100), (copy, "WRITE_SIZE", 1048576)])
+    text = bench.summarize_mfma_counters(str(tmp_path / "p.csv"), str(tmp_path / "f.csv"), str(tmp_path / "w.csv"))
+    row = next(l for l in text.splitlines() if "`k_gemm_nvfp4_mx<0>`" in l)
+    # 25% of the fp4 peak is 2525 TFLOP/s: 101% of fp16, 50.5% of fp8, 25% of fp4
+    assert "| 1 | 32000.0 | 25.0% | 101.0%/50.5%/25.0% | 50 | 7 | 5.0% | 2.0 | 0.1 |" in row
+    assert f"source_sha256: {bench.kernel_source_hash(bench.MFMA_KERNEL_SOURCES)}" in text

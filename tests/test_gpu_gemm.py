@@ -366,7 +366,7 @@ def _pow2_groups(shapes, seed, out_dtype, ldc_pad=0, extreme=False):
 
 
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
-@pytest.mark.parametrize("case", ["tails", "extreme_scales", "many_groups"])
+@pytest.mark.parametrize("case", ["tails", "extreme_scales", "many_groups", "fallback_ldc"])
 def test_hetero_gemm_pow2_against_oracle(out_dtype, case):
     """The fp4-MFMA path (scales declared powers of two) against the oracle on every output:
     M tails inside and past the first 128 rows of a tile, an empty group, K from one step up,
@@ -374,11 +374,14 @@ def test_hetero_gemm_pow2_against_oracle(out_dtype, case):
     groups than one item each."""
     mxg = _mxg()
     if case == "tails":
-        shapes, pad, extreme = ((300, 256, 384), (0, 128, 128), (37, 384, 1024), (513, 128, 256), (128, 128, 128)), 68, False
+        shapes, pad, extreme = ((300, 256, 384), (0, 128, 128), (37, 384, 1024), (513, 128, 256), (128, 128, 128),
+                                (129, 640, 5120)), 72, False
     elif case == "extreme_scales":
         shapes, pad, extreme = ((200, 256, 512), (16, 128, 896)), 0, True
-    else:
-        shapes, pad, extreme = tuple((17 * g + 1, 128 * (1 + g % 3), 128 * (1 + g % 5)) for g in range(12)), 4, False
+    elif case == "many_groups":
+        shapes, pad, extreme = tuple((17 * g + 1, 128 * (1 + g % 3), 128 * (1 + g % 5)) for g in range(12)), 8, False
+    else:  # output rows not 16-byte aligned: the general kernels run, with the same results
+        shapes, pad, extreme = ((300, 256, 384), (37, 128, 256)), 2, False
     log(f"power-of-two scales on the fp4 MFMA: {case} {shapes} {out_dtype}")
     groups = _pow2_groups(shapes, 4242 + len(case), out_dtype, pad, extreme)
     mxg.mx_grouped_gemm(groups, out_dtype=out_dtype, sf_dtype=mxg.MXG_E4M3_POW2)
