@@ -281,16 +281,34 @@ def cold_samples(step, n, nbytes=1 << 30):
     return out
 
 
+# The timed steps follow at least this much untimed back-to-back GPU work: the host then
+# queues the timed launches ahead of the GPU, and the GPU is in its loaded power state (a
+# GPU that idled for a few ms runs the next memory-bound launches measurably slower).
+HEAD_MS = 25.0
+
+
+def head_steps(step):
+    """Number of untimed steps that take about HEAD_MS, from a timed warm-up step."""
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    step(None)
+    b.record()
+    torch.cuda.synchronize()
+    return int(min(max(np.ceil(HEAD_MS / max(a.elapsed_time(b), 1e-3)), 2), 2000))
+
+
 def timed_loop(step, steps, warmup):
     for _ in range(warmup):
         step(None)
     torch.cuda.synchronize()
+    n_head = head_steps(step)
     kt = Timer()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    gpu_head_start(20.0 + 0.2 * steps)
+    for _ in range(n_head):
+        step(None)
     t0.record()
     for _ in range(steps):
         step(kt)
@@ -317,9 +335,16 @@ def graph_loop(step, steps):
         step(None)
     g.replay()
     torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    n_head = int(min(max(np.ceil(HEAD_MS / max(a.elapsed_time(b), 1e-3)), 2), 20000))
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    gpu_head_start(5.0 + 0.05 * steps)
+    for _ in range(n_head):
+        g.replay()
     t0.record()
     for _ in range(steps):
         g.replay()
@@ -396,6 +421,115 @@ def bench_decode_gemm1(dev, steps, warmup, seed=1001, cpu=True):
     if cpu:
         res["cpu_baseline"] = cpu_baseline_decode_gemm1(t, s, step_bytes)
     return res
+
+
+def power_clock_samples(dev, seconds=3.0, seed=1001):
+    """Board power (hwmon power1_input), its cap, and the graphics / memory clocks
+    (rocm-smi) while the decode GEMM1 runs back to back, with 1 ms and 5 ms idle gaps
+    between launches, and after a dispatch kernel per launch as in the timed step; with
+    each launch's duration from HIP events (median over the last three quarters)."""
+    import glob
+    import subprocess
+    import threading
+    hw = None
+    for d in sorted(glob.glob("/sys/class/drm/card*/device/hwmon/hwmon*")):
+        if os.path.exists(os.path.join(d, "power1_input")):
+            hw = d
+            break
+
+    def read(name):
+        try:
+            return int(open(os.path.join(hw, name)).read())
+        except (OSError, TypeError, ValueError):
+            return None
+
+    def clocks():
+        try:
+            r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=5)
+            card = next(iter(json.loads(r.stdout).values()))
+            pick = lambda key: next((int(re.sub(r"[^0-9]", "", v)) for k, v in card.items() if k.startswith(key)), None)
+            return pick("sclk clock speed"), pick("mclk clock speed")
+        except Exception:  # no rocm-smi or unexpected output: no clock sample
+            return None, None
+
+    wl = datagen.decode_gemm1_workload(seed, dev)
+    t, sc = wl.tensors, wl.scalars
+    E, T, H, N, top_k, max_m = 256, sc["T"], sc["H"], sc["N"], sc["top_k"], 8
+    alpha = torch.full((E,), np.float32(sc["g_x"]) * np.float32(sc["g_w"]), dtype=torch.float32, device=dev)
+    masked_m = torch.empty((E,), dtype=torch.int32, device=dev)
+    row = torch.empty((T, top_k), dtype=torch.int32, device=dev)
+    a = torch.empty((E, max_m, H // 2), dtype=torch.uint8, device=dev)
+    a_sf = torch.empty((E, max_m, H // 16), dtype=torch.uint8, device=dev)
+    out = torch.empty((E, max_m, N), dtype=torch.bfloat16, device=dev)
+
+    def disp():
+        mxg.moe_dispatch_quantize_gather_nvfp4(t["x"], sc["g_x"], t["ids"], E, max_m, masked_m=masked_m, row=row,
+                                               a=a, a_sf=a_sf)
+
+    def gemm():
+        mxg.mx_grouped_gemm_masked(a, a_sf, t["w13"], t["w13_sf"], alpha, masked_m, out)
+
+    disp()
+    for _ in range(20):
+        gemm()
+    torch.cuda.synchronize()
+    samples, phase, stop = [], ["idle"], [False]
+
+    def sampler():
+        k = 0
+        while not stop[0]:
+            sclk = mclk = None
+            if k % 25 == 0:
+                sclk, mclk = clocks()
+            samples.append((phase[0], read("power1_input"), sclk, mclk))
+            k += 1
+            time.sleep(0.01)
+
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    time.sleep(1.0)
+    kern = {}
+    for name, gap in (("back_to_back", 0.0), ("gap_1ms", 1e-3), ("gap_5ms", 5e-3), ("with_dispatch", -1.0)):
+        phase[0] = name
+        ev, n, t_end = [], 0, time.perf_counter() + seconds
+        while time.perf_counter() < t_end:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            if gap < 0:
+                disp()
+            e0.record()
+            gemm()
+            e1.record()
+            ev.append((e0, e1))
+            n += 1
+            if gap > 0:
+                torch.cuda.synchronize()
+                time.sleep(gap)
+            elif n % 200 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        ms = np.array([x.elapsed_time(y) for x, y in ev[len(ev) // 4:]])
+        kern[name] = {"launches": n, "kernel_us_median": float(np.median(ms)) * 1e3,
+                      "kernel_us_p90": float(np.percentile(ms, 90)) * 1e3}
+        phase[0] = "idle"
+        time.sleep(1.0)
+    stop[0] = True
+    th.join()
+    rows = []
+    for name in ("idle", "back_to_back", "gap_1ms", "gap_5ms", "with_dispatch"):
+        ss = [x for x in samples if x[0] == name]
+        ss = ss[len(ss) // 3:]
+        pw = [x[1] for x in ss if x[1] is not None]
+        sclk = [x[2] for x in ss if x[2] is not None]
+        mclk = [x[3] for x in ss if x[3] is not None]
+        k = kern.get(name, {})
+        rows.append(f"| {name} | {np.mean(pw) / 1e6 if pw else float('nan'):.0f} | "
+                    f"{np.mean(sclk) if sclk else float('nan'):.0f} | {np.mean(mclk) if mclk else float('nan'):.0f} | "
+                    f"{k.get('kernel_us_median', float('nan')):.1f} | {k.get('kernel_us_p90', float('nan')):.1f} | "
+                    f"{k.get('launches', 0)} |")
+    cap = read("power1_cap")
+    return "\n".join([f"power cap: {cap / 1e6 if cap else float('nan'):.0f} W (hwmon {hw})", "",
+                      "| phase | board power (W) | sclk (MHz) | mclk (MHz) | GEMM us median | GEMM us p90 | launches |",
+                      "|---|---|---|---|---|---|---|", *rows])
 
 
 def cpu_baseline_decode_gemm1(t, s, step_bytes, min_seconds=10.0):
@@ -735,6 +869,8 @@ def main():
                     help="cold-cache samples of the main workload (each after a 1 GiB scrub); 0 = none")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration under rocprofv3 --pmc)")
+    ap.add_argument("--power-clock", action="store_true",
+                    help="print board power and clock samples around back-to-back and gapped decode GEMM1 launches")
     ap.add_argument("--summarize-mfma", nargs=3, metavar=("PMC_CSV", "FETCH_CSV", "WRITE_CSV"),
                     help="print the MFMA-kernel counter record of three rocprofv3 --pmc runs")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -753,6 +889,9 @@ def main():
     _ensure_built()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.power_clock:
+        print(power_clock_samples(dev))
+        return
     COLD["samples"] = max(0, args.cold)
     r = WORKLOADS[args.workload](dev, args.steps, args.warmup, not args.no_cpu_baseline)
     COLD["samples"] = 0
