@@ -3,14 +3,15 @@
 Headline workload (one "step" = the whole decode GEMM1 path): 8 tokens routed top-8
 to 256 experts (ids from the seed) -> dispatch (masked_m, rows) -> NVFP4 quantization
 of the bf16 activations into the masked layout -> masked grouped NVFP4 GEMM1 against
-W13 [256, 4096, 7168] with bf16 output.  Inputs are resident in HBM before timing.
+W13 [256, 4096, 7168] with bf16 output.  Inputs are resident in HBM before timing, and the
+timed steps follow about 25 ms of untimed back-to-back steps (the loaded steady state).
 
 Prints ONE JSON line with the metric, a roofline object for the dominant kernel
 (algorithmic bytes / its HIP-event-timed average duration), cold-cache samples, the
 captured-graph replay time of the decode workloads and the oracle's CPU baseline on a
 bounded sample.  The default run adds the other four configurations under "workloads"
-(the masked GEMM of 4 groups, the heterogeneous GEMM, the FP8 layer at T=4096 and the
-NVFP4 layer at T=64 and T=8192), each with its roofline against HBM and the MFMA peaks,
+(the masked GEMM of 4 groups, the heterogeneous GEMM with general and with power-of-two
+scales, the FP8 layer at T=4096 and the NVFP4 layer at T=64 and T=8192), each with its roofline against HBM and the MFMA peaks,
 tokens/s for the layers and an oracle baseline (token subsets for the prefill layers).
 --all adds the rows beyond the configurations (full-precision FP8 intermediate,
 interleaved W13, W4A16 GEMV, contiguous layout); --workload X makes X the main line.

@@ -141,12 +141,13 @@ typedef struct {
  * it inside the kernel-argument space.  Larger group counts with one shared N and K
  * are the masked (mx_grouped_gemm_masked) or contiguous layouts.
  * sf_dtype = MXG_E4M3_POW2 declares that every scale byte of every group is a positive
- * power of two.  Groups whose N and K are multiples of 128 (with 8-byte aligned bf16 or
- * 16-byte aligned fp32 output rows) then run on the scaled fp4 MFMA: each power-of-two
- * scale is exactly an e8m0 MFMA scale, so the result is the same exact-product fp32 sum
- * as with general scales, at up to four times the rate of the fp16 MFMA the general
- * decode uses (two fp4 MFMAs per 128-K block, one per 16-element half of each 32-element
- * MFMA scale block).  Other shapes run the general kernels.  Scale bytes outside the
+ * power of two.  When every group with rows has N and K multiples of 128 and 16-byte
+ * aligned output rows (out and ldc), the call runs on the scaled fp4 MFMA: each
+ * power-of-two scale is exactly an e8m0 MFMA scale, so the result is the same
+ * exact-product fp32 sum as with general scales, at up to twice the rate of the fp16 MFMA
+ * the general decode uses (two fp4 MFMAs per 128-K block, one per 16-element half of each
+ * 32-element MFMA scale block, each at four times the fp16 rate).  Otherwise the general
+ * kernels run.  Scale bytes outside the
  * declared set give wrong results (a zero scale counts as 2^-127, a mantissa is
  * dropped), never an out-of-bounds access.
  * Source for the power-of-two path: the per-16 e4m3 scales of NVFP4 do not map onto the
