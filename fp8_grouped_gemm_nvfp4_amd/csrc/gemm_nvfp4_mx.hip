@@ -105,12 +105,13 @@ __global__ __launch_bounds__(mx::THREADS) void k_gemm_nvfp4_mx(const MxGemmArgs 
     const int g = tid;
     int cnt = 0, base = 0;
     if (g < G) {
-      if (p.npat > 0) {
+      const HeteroSchedule& sc = p.sched;
+      if (sc.npat > 0) {
         int pp = 0;
-        while (pp + 1 < p.npat && p.pat_start[pp + 1] <= bx) pp++;
-        for (int t = 0; t < pp; t++) base += (p.pat_start[t + 1] - p.pat_start[t]) * p.pat_cnt[t][g];
-        cnt = bx < p.pat_start[p.npat] ? p.pat_cnt[pp][g] : 0;
-        base += (bx - p.pat_start[pp]) * cnt;
+        while (pp + 1 < sc.npat && sc.pat_start[pp + 1] <= bx) pp++;
+        for (int t = 0; t < pp; t++) base += (sc.pat_start[t + 1] - sc.pat_start[t]) * sc.pat_cnt[t][g];
+        cnt = bx < sc.pat_start[sc.npat] ? sc.pat_cnt[pp][g] : 0;
+        base += (bx - sc.pat_start[pp]) * cnt;
       } else {
         // round robin over the items in group order: item t goes to workgroup t % grid
         const int t0 = p.grp[g].tile_base, n = p.grp[g].tiles_m * p.grp[g].tiles_n;
@@ -123,7 +124,7 @@ __global__ __launch_bounds__(mx::THREADS) void k_gemm_nvfp4_mx(const MxGemmArgs 
     my_base[g] = base;
   }
   __syncthreads();
-  const int stride = p.npat > 0 ? 1 : grid;  // local index step between a workgroup's items of a group
+  const int stride = p.sched.npat > 0 ? 1 : grid;  // local index step between a workgroup's items of a group
   int n_items = 0, nsteps = 0;
   for (int g = 0; g < G; g++) {
     const int c = __builtin_amdgcn_readfirstlane(my_cnt[g]);
@@ -370,55 +371,6 @@ int mx_bm(const HeteroGroup& q) { return (q.M <= 128 || q.K / mx::BK >= 40) ? 12
 // fragment reads and the DMA issue (measured: about 0.6 of a full step's MFMA time).
 double mx_item_cost(const HeteroGroup& q) { return (q.K / mx::BK) * (mx_bm(q) / 256.0 + 0.6); }
 
-// Longest-first deal of the items (groups in schedule order, every item of a group at the
-// group's cost) to the least-loaded of W workgroups, ties to the lower index; the count
-// vectors are folded into patterns.  npat = 0 when they do not fit the pattern table.
-void mx_schedule(MxGemmArgs& p, int W) {
-  p.npat = 0;
-  if (W > 4096) return;
-  std::vector<double> load(W, 0.0);
-  std::vector<unsigned char> cnt((size_t)W * MXG_MAX_GROUPS, 0);
-  // a min-heap of (load, workgroup) would do the same; the linear scan is cheap at these
-  // sizes and the result is cached per shape
-  for (int g = 0; g < p.G; g++) {
-    const double c = mx_item_cost(p.grp[g]);
-    const long long ng = (long long)p.grp[g].tiles_m * p.grp[g].tiles_n;
-    for (long long t = 0; t < ng; t++) {
-      int best = 0;
-      for (int w = 1; w < W; w++)
-        if (load[w] < load[best]) best = w;
-      load[best] += c;
-      unsigned char& k = cnt[(size_t)best * MXG_MAX_GROUPS + g];
-      if (k == 255) return;
-      k++;
-    }
-  }
-  int npat = 0, members[MX_MAX_PAT] = {};
-  for (int w = 0; w < W; w++) {
-    const unsigned char* cw = &cnt[(size_t)w * MXG_MAX_GROUPS];
-    int pp = 0;
-    for (; pp < npat; pp++)
-      if (memcmp(p.pat_cnt[pp], cw, MXG_MAX_GROUPS) == 0) break;
-    if (pp == npat) {
-      if (npat == MX_MAX_PAT) return;
-      memcpy(p.pat_cnt[pp], cw, MXG_MAX_GROUPS);
-      npat++;
-    }
-    members[pp]++;
-  }
-  p.pat_start[0] = 0;
-  for (int pp = 0; pp < npat; pp++) p.pat_start[pp + 1] = p.pat_start[pp] + members[pp];
-  p.npat = npat;
-}
-
-struct MxSchedCache {
-  int W = -1, G = 0;
-  int shape[MXG_MAX_GROUPS][3];
-  int npat = 0;
-  int pat_start[MX_MAX_PAT + 1];
-  unsigned char pat_cnt[MX_MAX_PAT][MXG_MAX_GROUPS];
-};
-
 }  // namespace
 
 // Groups with rows need N % 128 == 0, K % 128 == 0 and 16-byte aligned output rows;
@@ -466,31 +418,91 @@ hipError_t gemm_nvfp4_mx_hetero(HeteroGemmArgs in, int epi, int cu_limit, hipStr
   const int grid = resident_grid(k, THREADS, cu_limit);
   if (grid <= 0) return hipErrorInvalidValue;
 
-  // the schedule depends only on the shapes and the grid: computed once per shape set
-  static thread_local MxSchedCache cache;
-  bool hit = cache.W == grid && cache.G == n;
-  for (int g = 0; g < n && hit; g++)
-    hit = cache.shape[g][0] == p.grp[g].M && cache.shape[g][1] == p.grp[g].N && cache.shape[g][2] == p.grp[g].K;
-  if (!hit) {
-    if (items <= 65536) mx_schedule(p, grid);
-    cache.W = grid;
-    cache.G = n;
-    for (int g = 0; g < n; g++) {
-      cache.shape[g][0] = p.grp[g].M;
-      cache.shape[g][1] = p.grp[g].N;
-      cache.shape[g][2] = p.grp[g].K;
-    }
-    cache.npat = p.npat;
-    memcpy(cache.pat_start, p.pat_start, sizeof(p.pat_start));
-    memcpy(cache.pat_cnt, p.pat_cnt, sizeof(p.pat_cnt));
-  } else {
-    p.npat = cache.npat;
-    memcpy(p.pat_start, cache.pat_start, sizeof(p.pat_start));
-    memcpy(p.pat_cnt, cache.pat_cnt, sizeof(p.pat_cnt));
-  }
+  double cost[MXG_MAX_GROUPS];
+  for (int g = 0; g < n; g++) cost[g] = mx_item_cost(p.grp[g]);
+  hetero_lpt_schedule(p.grp, cost, n, grid, p.sched);
   if (epi == EPI_BF16) hipLaunchKernelGGL((k_gemm_nvfp4_mx<EPI_BF16>), dim3(grid), dim3(THREADS), 0, s, p);
   else hipLaunchKernelGGL((k_gemm_nvfp4_mx<EPI_F32>), dim3(grid), dim3(THREADS), 0, s, p);
   return hipGetLastError();
+}
+
+void hetero_lpt_schedule(const HeteroGroup* grp, const double* cost, int G, int W, HeteroSchedule& out) {
+  // the schedule depends only on its inputs: computed once per input set and thread
+  struct Cache {
+    int W = -1, G = -1;
+    long long key[MXG_MAX_GROUPS][3];
+    HeteroSchedule sched;
+  };
+  static thread_local Cache cache[2];  // the two callers use different costs
+  static thread_local int next = 0;
+  for (Cache& c : cache) {
+    bool hit = c.W == W && c.G == G;
+    for (int g = 0; g < G && hit; g++) {
+      long long cb;
+      memcpy(&cb, &cost[g], sizeof cb);
+      hit = c.key[g][0] == grp[g].tiles_m && c.key[g][1] == grp[g].tiles_n && c.key[g][2] == cb;
+    }
+    if (hit) {
+      out = c.sched;
+      return;
+    }
+  }
+  HeteroSchedule s{};
+  s.npat = 0;
+  long long items = 0;
+  for (int g = 0; g < G; g++) items += (long long)grp[g].tiles_m * grp[g].tiles_n;
+  bool ok = W > 0 && W <= 4096 && items <= 65536;
+  std::vector<double> load(ok ? W : 0, 0.0);
+  std::vector<unsigned char> cnt(ok ? (size_t)W * MXG_MAX_GROUPS : 0, 0);
+  // a min-heap of (load, workgroup) would do the same; the linear scan is cheap at these
+  // sizes and the result is cached
+  for (int g = 0; g < G && ok; g++) {
+    const long long ng = (long long)grp[g].tiles_m * grp[g].tiles_n;
+    for (long long t = 0; t < ng && ok; t++) {
+      int best = 0;
+      for (int w = 1; w < W; w++)
+        if (load[w] < load[best]) best = w;
+      load[best] += cost[g];
+      unsigned char& k = cnt[(size_t)best * MXG_MAX_GROUPS + g];
+      if (k == 255) ok = false;
+      else k++;
+    }
+  }
+  if (ok) {
+    int npat = 0, members[MX_MAX_PAT] = {};
+    for (int w = 0; w < W && ok; w++) {
+      const unsigned char* cw = &cnt[(size_t)w * MXG_MAX_GROUPS];
+      int pp = 0;
+      for (; pp < npat; pp++)
+        if (memcmp(s.pat_cnt[pp], cw, MXG_MAX_GROUPS) == 0) break;
+      if (pp == npat) {
+        if (npat == MX_MAX_PAT) {
+          ok = false;
+          break;
+        }
+        memcpy(s.pat_cnt[pp], cw, MXG_MAX_GROUPS);
+        npat++;
+      }
+      members[pp]++;
+    }
+    if (ok) {
+      s.pat_start[0] = 0;
+      for (int pp = 0; pp < npat; pp++) s.pat_start[pp + 1] = s.pat_start[pp] + members[pp];
+      s.npat = npat;
+    }
+  }
+  if (!ok) s = HeteroSchedule{};
+  Cache& c = cache[next];
+  next ^= 1;
+  c.W = W;
+  c.G = G;
+  for (int g = 0; g < G; g++) {
+    c.key[g][0] = grp[g].tiles_m;
+    c.key[g][1] = grp[g].tiles_n;
+    memcpy(&c.key[g][2], &cost[g], sizeof(long long));
+  }
+  c.sched = s;
+  out = s;
 }
 
 }  // namespace mxg

@@ -121,9 +121,28 @@ __global__ __launch_bounds__(ns::THREADS) void k_gemm_nvfp4_stream(const typenam
       stream_tile_prefix(p.masked_m, G, cap, tprefix, mm_s, tid);
     }
     total = __builtin_amdgcn_readfirstlane(tprefix[G]) * tiles_n;
-  } else {
-    // heterogeneous groups: tprefix counts items (M tiles x N tiles) per group
-    if (tid == 0) {
+  }
+  const int I = N / 2;
+  const int grid = gridDim.x;
+  const int bx = stream_bx();
+  // heterogeneous groups with a schedule: tprefix[g] / mm_s[g] hold this workgroup's item
+  // count and first local item of group g (consecutive items); without one, tprefix counts
+  // the items (M tiles x N tiles) per group for the round-robin deal
+  bool sched = false;
+  if constexpr (!MASKED) {
+    const HeteroSchedule& sc = p.sched;
+    sched = sc.npat > 0;
+    if (sched) {
+      if (tid < G) {
+        const int g = tid;
+        int pp = 0, base = 0;
+        while (pp + 1 < sc.npat && sc.pat_start[pp + 1] <= bx) pp++;
+        for (int t = 0; t < pp; t++) base += (sc.pat_start[t + 1] - sc.pat_start[t]) * sc.pat_cnt[t][g];
+        const int cnt = bx < sc.pat_start[sc.npat] ? sc.pat_cnt[pp][g] : 0;
+        tprefix[g] = cnt;
+        mm_s[g] = base + (bx - sc.pat_start[pp]) * cnt;
+      }
+    } else if (tid == 0) {
       int run = 0;
       for (int g = 0; g < G; g++) {
         tprefix[g] = run;
@@ -132,13 +151,16 @@ __global__ __launch_bounds__(ns::THREADS) void k_gemm_nvfp4_stream(const typenam
       tprefix[G] = run;
     }
     __syncthreads();
-    total = __builtin_amdgcn_readfirstlane(tprefix[G]);
+    if (!sched) total = __builtin_amdgcn_readfirstlane(tprefix[G]);
   }
-  const int I = N / 2;
-  const int grid = gridDim.x;
-  const int bx = stream_bx();
-  if (bx >= total) return;
-  const int n_items = (total - 1 - bx) / grid + 1;
+  int n_items = 0;
+  if (sched) {
+    for (int g = 0; g < G; g++) n_items += __builtin_amdgcn_readfirstlane(tprefix[g]);
+    if (n_items == 0) return;
+  } else {
+    if (bx >= total) return;
+    n_items = (total - 1 - bx) / grid + 1;
+  }
 
   auto job_at = [&](int k) {
     NsJob j;
@@ -151,15 +173,27 @@ __global__ __launch_bounds__(ns::THREADS) void k_gemm_nvfp4_stream(const typenam
       j.b = p.b + (size_t)it.g * N * (p.K / 2);
       j.b_sf = p.b_sf + (size_t)it.g * N * (p.K / 16);
     } else {
-      const int w = bx + k * grid;
-      int lo = 0, hi = G;  // tprefix[lo] <= w < tprefix[hi]
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (__builtin_amdgcn_readfirstlane(tprefix[mid]) <= w) lo = mid;
-        else hi = mid;
+      int lo = 0, local = 0;
+      if (sched) {  // this workgroup's k-th item: groups in order, consecutive items of each
+        for (; lo < G; lo++) {
+          const int c = __builtin_amdgcn_readfirstlane(tprefix[lo]);
+          if (k < c) break;
+          k -= c;
+        }
+        if (lo == G) lo = G - 1, k = 0;  // past the last item (not reached)
+        local = __builtin_amdgcn_readfirstlane(mm_s[lo]) + k;
+      } else {
+        const int w = bx + k * grid;
+        int hi = G;  // tprefix[lo] <= w < tprefix[hi]
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (__builtin_amdgcn_readfirstlane(tprefix[mid]) <= w) lo = mid;
+          else hi = mid;
+        }
+        local = w - __builtin_amdgcn_readfirstlane(tprefix[lo]);
       }
       const HeteroGroup& q = p.grp[lo];
-      const int tn = q.N / BN, local = w - __builtin_amdgcn_readfirstlane(tprefix[lo]);
+      const int tn = q.N / BN;
       const int mt = local / tn;
       j.g = lo; j.m0 = mt * BM; j.mm = q.M; j.n0 = (local - mt * tn) * BN; j.K = q.K;
       j.a = q.a; j.a_sf = q.a_sf; j.b = q.b; j.b_sf = q.b_sf;
@@ -487,8 +521,11 @@ hipError_t gemm_nvfp4_contiguous(MaskedGemmArgs p, int epi, int cu_limit, hipStr
 }
 
 // Heterogeneous groups: every group with rows needs N % 128 == 0, K % 128 == 0 and an
-// output row stride and base that keep the 4-column stores aligned; the groups are
-// reordered by decreasing K so that the round-robin deal of the items balances.
+// output row stride and base that keep the 4-column stores aligned.  The groups are
+// reordered by decreasing item cost and their items dealt longest-first onto the
+// workgroups (hetero_lpt_schedule); the item cost is the item's K steps times (0.6 + its
+// share of a full 256-row tile), the weight stream and decode being paid per step whatever
+// the rows.
 hipError_t gemm_nvfp4_stream_hetero(HeteroGemmArgs p, int epi, int cu_limit, hipStream_t s) {
   using namespace ns;
   if (epi != EPI_BF16 && epi != EPI_F32) return hipErrorNotSupported;
@@ -503,20 +540,31 @@ hipError_t gemm_nvfp4_stream_hetero(HeteroGemmArgs p, int epi, int cu_limit, hip
   }
   if (items == 0) return hipSuccess;
   if (items > 0x7FFFFFFFLL) return hipErrorNotSupported;
+  auto cost = [&](const HeteroGroup& q) { return (q.K / BK) * (0.6 + (q.M < BM ? q.M : BM) / (double)BM); };
   HeteroGemmArgs r = p;
   bool taken[MXG_MAX_GROUPS] = {};
+  double c[MXG_MAX_GROUPS];
   int n = 0;
-  for (int pass = 0; pass < p.G; pass++) {  // stable selection by decreasing K, empty groups dropped
+  for (int pass = 0; pass < p.G; pass++) {  // stable selection by decreasing cost, empty groups dropped
     int best = -1;
     for (int g = 0; g < p.G; g++) {
       if (p.grp[g].M == 0 || taken[g]) continue;
-      if (best < 0 || p.grp[g].K > p.grp[best].K) best = g;
+      if (best < 0 || cost(p.grp[g]) > cost(p.grp[best])) best = g;
     }
     if (best < 0) break;
-    r.grp[n++] = p.grp[best];
+    HeteroGroup q = p.grp[best];
+    q.tiles_m = (q.M + BM - 1) / BM;
+    q.tiles_n = q.N / BN;
+    c[n] = cost(q);
+    r.grp[n++] = q;
     taken[best] = true;
   }
   r.G = n;
+  const void* k = epi == EPI_BF16 ? (const void*)k_gemm_nvfp4_stream<EPI_BF16, MODE_HETERO, 8>
+                                  : (const void*)k_gemm_nvfp4_stream<EPI_F32, MODE_HETERO, 8>;
+  const int grid = resident_grid(k, ns::THREADS, cu_limit);
+  if (grid <= 0) return hipErrorInvalidValue;
+  hetero_lpt_schedule(r.grp, c, n, grid, r.sched);
   return epi == EPI_BF16 ? launch_stream<EPI_BF16, MODE_HETERO>(r, cu_limit, s)
                          : launch_stream<EPI_F32, MODE_HETERO>(r, cu_limit, s);
 }

@@ -50,23 +50,37 @@ struct HeteroGroup {
   int tiles_m, tiles_n, tile_base;
 };
 
+// An item schedule of heterogeneous groups over the workgroups (numbered XCD by XCD):
+// npat > 0 patterns, where workgroups [pat_start[p], pat_start[p + 1]) take pat_cnt[p][g]
+// items of group g each, as contiguous ranges of the group's items in workgroup order; or
+// npat = 0, round robin over the items in group order (item t to workgroup t % grid).
+constexpr int MX_MAX_PAT = 16;
+struct HeteroSchedule {
+  int npat;
+  int pat_start[MX_MAX_PAT + 1];
+  unsigned char pat_cnt[MX_MAX_PAT][MXG_MAX_GROUPS];
+};
+// Longest-first deal of every group's tiles_m * tiles_n items (all items of group g at
+// cost[g], groups in the given order) to the least-loaded of W workgroups, ties to the
+// lower index, folded into patterns; npat = 0 when they do not fit the table (more than
+// MX_MAX_PAT distinct count vectors, a count above 255, W above 4096, or more than 65,536
+// items).  The result depends only on its inputs and is cached per input set.
+void hetero_lpt_schedule(const HeteroGroup* grp, const double* cost, int G, int W, HeteroSchedule& out);
+
 struct HeteroGemmArgs {
   HeteroGroup grp[MXG_MAX_GROUPS];
   int G;
   int total_tiles;
+  HeteroSchedule sched;  // used by the streaming kernel's heterogeneous mode
 };
 
 // Heterogeneous groups on the scaled fp4 MFMA (power-of-two e4m3 scales): the groups in
-// schedule order (tiles_m, tiles_n and tile_base filled in) and the item schedule, either
-// npat > 0 patterns (workgroups [pat_start[p], pat_start[p + 1]) take pat_cnt[p][g] items
-// of group g each, as contiguous ranges in workgroup order) or npat = 0 (round robin).
-constexpr int MX_MAX_PAT = 16;
+// schedule order (tiles_m, tiles_n and tile_base filled in) and their item schedule.
 struct MxGemmArgs {
   HeteroGroup grp[MXG_MAX_GROUPS];
   int bm[MXG_MAX_GROUPS];  // M tile of each group (128 or 256 rows)
-  int G, npat;
-  int pat_start[MX_MAX_PAT + 1];
-  unsigned char pat_cnt[MX_MAX_PAT][MXG_MAX_GROUPS];
+  int G;
+  HeteroSchedule sched;
 };
 hipError_t gemm_nvfp4_mx_hetero(HeteroGemmArgs p, int epi, int cu_limit, hipStream_t s);
 

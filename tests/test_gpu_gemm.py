@@ -403,6 +403,31 @@ def test_hetero_gemm_pow2_against_oracle(out_dtype, case):
         assert_within(got, y, S, f"pow2 {case} group {gi} ({M},{N},{K})", **kw)
 
 
+def test_hetero_gemm_exact_grid_independent():
+    """The exact heterogeneous path (longest-first item schedule over the resident grid)
+    gives the same bits whatever the grid (cu_limit), and matches the oracle."""
+    mxg = _mxg()
+    shapes = ((300, 256, 384), (1000, 512, 1024), (64, 768, 256), (37, 384, 2048))
+    outs = []
+    for cu in (0, 7, 64):
+        wl = datagen.hetero_gemm_workload(78, DEV, shapes)
+        groups = []
+        for q in wl.tensors["groups"]:
+            q = dict(q)
+            q["out"] = torch.empty((q["M"], q["N"]), dtype=torch.float32, device=DEV)
+            groups.append(q)
+        mxg.mx_grouped_gemm(groups, out_dtype=torch.float32, cu_limit=cu)
+        torch.cuda.synchronize()
+        outs.append([np_(q["out"]).view(np.uint32) for q in groups])
+    for o in outs[1:]:
+        assert all(np.array_equal(x, y) for x, y in zip(outs[0], o))
+    for gi, q in enumerate(groups):
+        M, N, K = q["M"], q["N"], q["K"]
+        y, S = oracle.gemm_nvfp4_rows(np_(q["a"]), np_(q["a_sf"]), np.arange(M), np_(q["b"]), np_(q["b_sf"]), K,
+                                      q["alpha"])
+        assert_within(np_(q["out"]).astype(np.float64), y, S, f"exact group {gi} ({M},{N},{K})", ulp=ulp_f32)
+
+
 def test_hetero_gemm_pow2_grid_independent():
     """The fp4-MFMA path gives the same bits whatever the grid (cu_limit) and schedule."""
     mxg = _mxg()
