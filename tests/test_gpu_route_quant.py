@@ -50,6 +50,28 @@ def test_dispatch_bit_exact(T, k, max_m):
     assert np.array_equal(np_(offs), np.concatenate([[0], np.cumsum(mm_o)]))
 
 
+@pytest.mark.parametrize("T,E,k,max_m,unaligned", [
+    (128, 256, 8, 16, False),    # exactly one 1024-slot chunk
+    (129, 16, 8, 40, True),      # one slot past the chunk, 16 experts, ids not 16-byte aligned
+    (2048, 7, 3, 4096, True),    # few experts, six chunks, unaligned
+    (300, 5000, 4, 3, False),    # more experts than the chunked kernel takes: one workgroup per expert
+])
+def test_dispatch_edges(T, E, k, max_m, unaligned):
+    log(f"dispatch T={T} E={E} top_k={k} max_m={max_m}{' unaligned ids' if unaligned else ''}")
+    gen = datagen.generator(4400 + T + E, DEV)
+    ids = datagen.distinct_topk_ids(gen, T, E, k, DEV)
+    if unaligned:  # the same ids 4 bytes past a 16-byte boundary
+        buf = torch.empty((T * k + 1,), dtype=torch.int32, device=DEV)
+        buf[1:] = ids.flatten()
+        ids = buf[1:].view(T, k)
+        assert ids.data_ptr() % 16 == 4
+    mm, row = _mxg().moe_dispatch(ids, E, max_m)
+    torch.cuda.synchronize()
+    mm_o, row_o = oracle.dispatch(np_(ids), E, max_m)
+    assert np.array_equal(np_(mm), mm_o)
+    assert np.array_equal(np_(row), row_o)
+
+
 def _quant_inputs(gen, rows, K):
     x = torch.randn((rows, K), generator=gen, device=DEV) * 3
     x[0] = 0.0
