@@ -421,12 +421,16 @@ int moe_expert_forward(const mxg_moe_desc* d, void* ws, size_t ws_bytes, void* s
     p1.G = E; p1.max_m = mm; p1.N = 2 * I; p1.K = H;
     p1.h_codes = hc; p1.h_sf = hsf; p1.dbg_h = d->dbg_h; p1.dbg_g1 = d->dbg_g1; p1.g_h = d->g_h;
     p1.w13_il16 = d->w13_layout == MXG_W13_INTERLEAVED16;
+    // a decode batch leaves most experts with a few rows: 8-row tiles stream less padding
+    const int sparse = (long long)T * k <= 4LL * E;
+    p1.sparse_rows = sparse;
     e = mxg::gemm_nvfp4_masked(p1, mxg::EPI_SWIGLU_NVFP4, 0, s);
     if (e != hipSuccess) return hip_status(e, "gemm1 nvfp4 swiglu");
     mxg::MaskedGemmArgs p2{};
     p2.a = hc; p2.a_sf = hsf; p2.b = d->w2; p2.b_sf = (const uint8_t*)d->w2_scale; p2.out = o;
     p2.masked_m = d->masked_m; p2.alpha = d->g_w2; p2.alpha_scale = d->g_h;
     p2.G = E; p2.max_m = mm; p2.N = H; p2.K = I;
+    p2.sparse_rows = sparse;
     e = mxg::gemm_nvfp4_masked(p2, mxg::EPI_F32, 0, s);
     if (e != hipSuccess) return hip_status(e, "gemm2 nvfp4");
   }

@@ -511,7 +511,7 @@ static hipError_t launch_skinny(MaskedGemmArgs p, int cu_limit, hipStream_t s) {
 // Returns hipErrorNotSupported (nothing launched) for shapes the kernel does not take.
 hipError_t gemm_nvfp4_skinny(MaskedGemmArgs p, int epi, int cu_limit, hipStream_t s) {
   if (p.max_m > SKINNY_MAX_M || p.K % sk::KC != 0) return hipErrorNotSupported;
-  const bool small = p.max_m <= 8;
+  const bool small = p.max_m <= 8 || (p.sparse_rows && p.max_m <= 16);
   switch (epi) {
     case EPI_BF16:
       return small ? launch_skinny<8, 1, EPI_BF16, 8, 3, 4>(p, cu_limit, s) : launch_skinny<16, 1, EPI_BF16, 8, 3, 3>(p, cu_limit, s);

@@ -37,6 +37,10 @@ struct MaskedGemmArgs {
   // SwiGLU epilogue: B holds W13 with gate and up rows interleaved in 16-row blocks
   // (gate rows [16 j, 16 j + 16) at [32 j, 32 j + 16), the matching up rows after them)
   int w13_il16;
+  // the caller expects most groups to hold at most 8 valid rows (a decode batch: T * top_k
+  // at most 4 E): the decode kernel then uses 8-row M tiles up to max_m = 16, a group with
+  // more rows taking two (its weights streamed twice)
+  int sparse_rows;
 };
 
 struct HeteroGroup {
