@@ -133,6 +133,7 @@ def summarize_counters(fetch_csv, write_csv, workload="decode_gemm1", kernel_sub
 
 # Sources of the MFMA kernels whose counters the MFMA record summarizes.
 MFMA_KERNEL_SOURCES = ["fp8_grouped_gemm_nvfp4_amd/csrc/gemm_nvfp4_stream.hip",
+                       "fp8_grouped_gemm_nvfp4_amd/csrc/gemm_nvfp4_skinny.hip",
                        "fp8_grouped_gemm_nvfp4_amd/csrc/gemm_nvfp4_mx.hip",
                        "fp8_grouped_gemm_nvfp4_amd/csrc/gemm_fp8.hip",
                        "fp8_grouped_gemm_nvfp4_amd/csrc/stream_common.h",
@@ -140,6 +141,7 @@ MFMA_KERNEL_SOURCES = ["fp8_grouped_gemm_nvfp4_amd/csrc/gemm_nvfp4_stream.hip",
                        "fp8_grouped_gemm_nvfp4_amd/csrc/kernels.h"]
 MFMA_KERNELS = {  # kernel name substring -> (MFMA dtype, the instruction's peak), for the record
     "k_gemm_nvfp4_stream": ("fp16", "v_mfma_f32_16x16x32_f16"),
+    "k_gemm_nvfp4_skinny": ("fp16", "v_mfma_f32_16x16x32_f16"),
     "k_gemm_nvfp4_mx": ("fp4", "v_mfma_scale_f32_16x16x128_f8f6f4, e2m1 operands"),
     "k_gemm_fp8_swiglu": ("fp8", "v_mfma_scale_f32_16x16x128_f8f6f4, e4m3 operands"),
     "k_gemm_bf16_fp8w": ("bf16", "v_mfma_f32_16x16x32_bf16"),
@@ -933,8 +935,14 @@ def main():
     if names:
         rows = []
         for name in names:
+            # each row also gets its cold-cache samples (a scrub before every sample)
+            COLD["samples"], COLD["result"] = max(0, args.cold), None
             q = WORKLOADS[name](dev, max(10, args.steps // 5), 3, not args.no_cpu_baseline and name in CONFIG_ROWS)
-            rows.append(table_row(q))
+            COLD["samples"] = 0
+            row = table_row(q)
+            if COLD["result"] is not None:
+                row["cold"] = COLD["result"]
+            rows.append(row)
             print(f"[bench] {name}: {q['ms']:.4f} ms/step", file=sys.stderr, flush=True)
             del q
             torch.cuda.empty_cache()
