@@ -30,10 +30,17 @@
 // the fp32 sum.  The MFMA computes the transposed tile D = B A^T, so each lane ends
 // with four consecutive output columns of one row: 16-byte fp32 stores, and the
 // 16-column NVFP4 blocks of the SwiGLU epilogue sit in 4 lanes (quantize_block_x4).
-// Waves: MW (M) x 8 / MW (N); wave (wm, wn) owns the 16-row groups 16 wm + 16 MW i, so
-// both waves of a SIMD compute when masked_m <= 128.  With MW = 8 every wave decodes
-// activation rows no other wave decodes (with MW = 4 the two N waves of a row block
-// decode the same rows) and reads twice the fp16 weight fragments from LDS.
+// Waves: the two roles are split.  Waves 4..7 (one per SIMD; waves w and w + 4 share a
+// SIMD) issue every DMA and decode the next weight step; waves 0..3 only read
+// fragments, decode their activation rows and run MFMAs, each on a 64-row x 128-column
+// register tile (wave c owns the 16-row groups 16 c + 64 i, so all four compute when
+// masked_m > 48).  One barrier per step hands a step's buffers from one role to the
+// other.  The MFMA waves cross it pipelined: the operands of their last sub-step are in
+// registers before it, and the next step's fragment reads go out under that sub-step's
+// MFMAs.  Each item runs a loop specialised on the wave's valid row groups, so the MFMA
+// stream has no branches.
+#include <type_traits>
+
 #include "kernels.h"
 #include "stream_common.h"
 
@@ -42,9 +49,14 @@ namespace mxg {
 namespace ns {
 constexpr int BM = STREAM_BM, BN = 128, BK = 128;
 constexpr int WAVES = 8, THREADS = WAVES * 64;
+constexpr int CW = 4;                                       // MFMA waves; waves CW .. 7 move data
+constexpr int RG = BM / 16 / CW;                            // 16-row groups per MFMA wave
+constexpr int NB = BN / 16;                                 // 16-column groups per MFMA wave
 constexpr int A_CODE = BM * 64, A_STAGE = A_CODE + BM * 8;  // codes [256][64], scales [256][8]
 constexpr int B_CODE = BN * 64, B_STAGE = B_CODE + BN * 8;  // codes [128][64], scales [128][8]
-constexpr int DB = 4;                                       // weight steps in flight (>= 3)
+constexpr int DB = 3;                                       // weight steps in flight
+constexpr int SB = DB;                                      // raw weight stages
+constexpr int B_DMAS = 3;                                   // weight DMAs of one data wave per step
 }  // namespace ns
 
 __device__ __forceinline__ int ns_swz_a(int r) { return (r >> 2) & 2; }          // activation code rows
@@ -57,23 +69,17 @@ struct NsJob {
   int g, m0, mm, n0, K;
 };
 
-template <int EPI, int MODE, int MW>
+template <int EPI, int MODE>
 __global__ __launch_bounds__(ns::THREADS) void k_gemm_nvfp4_stream(const typename ArgsOf<MODE>::type p) {
   using namespace ns;
-  static_assert(MW == 4 || MW == 8, "waves along M");
-  constexpr int NW = WAVES / MW;        // waves along N
-  constexpr int RG = BM / 16 / MW;      // 16-row groups per wave
-  constexpr int NB = BN / 16 / NW;      // 16-column groups per wave
-  constexpr int WC = BN / NW;           // weight rows (output columns) per wave
   constexpr bool SWIGLU = (EPI == EPI_SWIGLU_NVFP4);
   // the contiguous layout is the masked one with each group's rows starting at row_start[g]
   constexpr bool CONTIG = (MODE == MODE_CONTIG);
   constexpr bool MASKED = (MODE == MODE_MASKED) || CONTIG;
   constexpr int MAXG = CONTIG ? STREAM_CONTIG_MAX_G : STREAM_MAX_G;
   static_assert(MASKED || !SWIGLU, "the SwiGLU epilogue is the MoE GEMM1's (masked)");
-  constexpr int SA = 2, SB = DB + 1;
   static_assert(DB >= 3, "B(s + 1) must be issued before A(s)");
-  __shared__ __attribute__((aligned(16))) uint8_t ringA[SA * A_STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t ringA[2 * A_STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t ringB[SB * B_STAGE];
   __shared__ __attribute__((aligned(16))) _Float16 bdec[2][BN * BK];
   __shared__ int tprefix[MAXG + 1];
@@ -83,7 +89,6 @@ __global__ __launch_bounds__(ns::THREADS) void k_gemm_nvfp4_stream(const typenam
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: branches on it are scalar
-  const int wm = wave / NW, wn = wave % NW;
   const int G = p.G;
   int N = 0, cap = 0, tiles_n = 0, total = 0;  // masked: common N, row capacity, N tiles
   const int ncols = SWIGLU ? BN / 2 : BN;      // output (h) columns per item
@@ -205,211 +210,248 @@ __global__ __launch_bounds__(ns::THREADS) void k_gemm_nvfp4_stream(const typenam
   else
     for (int k = 0; k < n_items; k++) nsteps += job_at(k).K / BK;
 
-  // B row r of an item (stage row): SwiGLU rows [0, 64) are gate rows n0 + r, [64, 128)
-  // the matching up rows I + n0 + r - 64
-  auto b_row = [&](const NsJob& it, int r) {
-    if constexpr (SWIGLU) return w13_row(r < BN / 2 ? it.n0 + r : I + it.n0 + (r - BN / 2), I, p.w13_il16 != 0);
-    else return it.n0 + r;
-  };
-
-  // ---- DMA cursors (rows past masked_m re-read the last valid row and are never stored;
-  // 16-row code groups and 32-row scale groups entirely past it are not fetched)
-  const uint8_t* asrc[2];
-  const uint8_t* asrc_s;
-  int a_n = 0, a_ns = 0, a_KT = 0;
-  auto a_setup = [&](const NsJob& it) {
-    const int K = it.K;
-    a_KT = K / BK;
-    const int left = it.mm - it.m0 - 32 * wave;
-    a_n = left <= 0 ? 0 : (left > 16 ? 2 : 1);
-    a_ns = left > 0 ? 1 : 0;
+  if (wave >= CW) {
+    // ======== data waves: every DMA, and the weight decode one step ahead ========
+    const int pw = wave - CW;
+    // B row r of an item (stage row): SwiGLU rows [0, 64) are gate rows n0 + r, [64, 128)
+    // the matching up rows I + n0 + r - 64
+    auto b_row = [&](const NsJob& it, int r) {
+      if constexpr (SWIGLU) return w13_row(r < BN / 2 ? it.n0 + r : I + it.n0 + (r - BN / 2), I, p.w13_il16 != 0);
+      else return it.n0 + r;
+    };
+    // data wave pw moves activation rows [64 pw, 64 pw + 64) and weight rows [32 pw,
+    // 32 pw + 32) of each step.  Rows past masked_m re-read the last valid row and are
+    // never stored; 16-row code groups and 32-row scale groups entirely past it are not
+    // fetched.
+    const uint8_t* asrc[4];
+    const uint8_t* asrc_s[2];
+    int a_n = 0, a_ns = 0, a_KT = 0;
+    auto a_setup = [&](const NsJob& it) {
+      const int K = it.K;
+      a_KT = K / BK;
+      const int left = it.mm - it.m0 - 64 * pw;
+      a_n = left <= 0 ? 0 : (left >= 64 ? 4 : (left + 15) >> 4);
+      a_ns = left <= 0 ? 0 : (left > 32 ? 2 : 1);
 #pragma unroll
-    for (int j = 0; j < 2; j++) {
-      const int r = 32 * wave + 16 * j + (lane >> 2);
-      const int row = it.m0 + r < it.mm ? it.m0 + r : it.mm - 1;
-      asrc[j] = it.a + (size_t)row * (K / 2) + (((lane & 3) ^ ns_swz_a(r)) << 4);
-    }
-    const int r = 32 * wave + (lane >> 1);
-    const int row = it.m0 + r < it.mm ? it.m0 + r : it.mm - 1;
-    asrc_s = it.a_sf + (size_t)row * (K / 16) + (lane & 1) * 4;
-  };
-  const uint8_t* bsrc;
-  const uint8_t* bsrc_s;
-  int b_KT = 0;
-  auto b_setup = [&](const NsJob& it) {
-    const int K = it.K;
-    b_KT = K / BK;
-    const int r = 16 * wave + (lane >> 2);
-    bsrc = it.b + (size_t)b_row(it, r) * (K / 2) + ((lane & 3) << 4);
-    const int rs = 32 * (wave & 3) + (lane >> 1);
-    bsrc_s = it.b_sf + (size_t)b_row(it, rs) * (K / 16) + (lane & 1) * 4;
-  };
-  int a_k = 0, a_kt = 0, a_step = 0, a_st = 0;
-  int b_k = 0, b_kt = 0, b_step = 0, b_st = 0;
-  auto issue_a = [&]() {
-    uint8_t* st = ringA + a_st * A_STAGE;
-#pragma unroll
-    for (int j = 0; j < 2; j++)
-      if (j < a_n) dma16(asrc[j] + a_kt * (BK / 2), st + (32 * wave + 16 * j) * 64);
-    if (a_ns) dma4(asrc_s + a_kt * (BK / 16), st + A_CODE + 32 * wave * 8);
-    a_st ^= 1;
-    if (a_step + 1 < nsteps) {
-      a_step++;
-      if (++a_kt == a_KT) {
-        a_kt = 0;
-        a_setup(job_at(++a_k));
+      for (int j = 0; j < 4; j++) {
+        const int r = 64 * pw + 16 * j + (lane >> 2);
+        const int row = it.m0 + r < it.mm ? it.m0 + r : it.mm - 1;
+        asrc[j] = it.a + (size_t)row * (K / 2) + (((lane & 3) ^ ns_swz_a(r)) << 4);
       }
-    }
-  };
-  auto issue_b = [&]() {
-    uint8_t* st = ringB + b_st * B_STAGE;
-    dma16(bsrc + b_kt * (BK / 2), st + 16 * wave * 64);
-    if (wave < 4) dma4(bsrc_s + b_kt * (BK / 16), st + B_CODE + 32 * wave * 8);
-    b_st = b_st + 1 == SB ? 0 : b_st + 1;
-    if (b_step + 1 < nsteps) {
-      b_step++;
-      if (++b_kt == b_KT) {
-        b_kt = 0;
-        b_setup(job_at(++b_k));
+#pragma unroll
+      for (int j = 0; j < 2; j++) {
+        const int r = 64 * pw + 32 * j + (lane >> 1);
+        const int row = it.m0 + r < it.mm ? it.m0 + r : it.mm - 1;
+        asrc_s[j] = it.a_sf + (size_t)row * (K / 16) + (lane & 1) * 4;
       }
+    };
+    const uint8_t* bsrc[2];
+    const uint8_t* bsrc_s;
+    int b_KT = 0;
+    auto b_setup = [&](const NsJob& it) {
+      const int K = it.K;
+      b_KT = K / BK;
+#pragma unroll
+      for (int j = 0; j < 2; j++) {
+        const int r = 32 * pw + 16 * j + (lane >> 2);
+        bsrc[j] = it.b + (size_t)b_row(it, r) * (K / 2) + ((lane & 3) << 4);
+      }
+      bsrc_s = it.b_sf + (size_t)b_row(it, 32 * pw + (lane >> 1)) * (K / 16) + (lane & 1) * 4;
+    };
+    int a_k = 0, a_kt = 0, a_step = 0, a_st = 0;
+    int b_k = 0, b_kt = 0, b_step = 0, b_st = 0;
+    // A(step) into slot step & 1; past the last step the cursor stays and re-reads it
+    auto issue_a = [&]() {
+      uint8_t* st = ringA + a_st * A_STAGE;
+#pragma unroll
+      for (int j = 0; j < 4; j++)
+        if (j < a_n) dma16(asrc[j] + a_kt * (BK / 2), st + (64 * pw + 16 * j) * 64);
+#pragma unroll
+      for (int j = 0; j < 2; j++)
+        if (j < a_ns) dma4(asrc_s[j] + a_kt * (BK / 16), st + A_CODE + (64 * pw + 32 * j) * 8);
+      a_st ^= 1;
+      if (a_step + 1 < nsteps) {
+        a_step++;
+        if (++a_kt == a_KT) {
+          a_kt = 0;
+          a_setup(job_at(++a_k));
+        }
+      }
+    };
+    // B(step) into stage step % SB: always B_DMAS instructions
+    auto issue_b = [&]() {
+      uint8_t* st = ringB + b_st * B_STAGE;
+#pragma unroll
+      for (int j = 0; j < 2; j++) dma16(bsrc[j] + b_kt * (BK / 2), st + (32 * pw + 16 * j) * 64);
+      dma4(bsrc_s + b_kt * (BK / 16), st + B_CODE + 32 * pw * 8);
+      b_st = b_st + 1 == SB ? 0 : b_st + 1;
+      if (b_step + 1 < nsteps) {
+        b_step++;
+        if (++b_kt == b_KT) {
+          b_kt = 0;
+          b_setup(job_at(++b_k));
+        }
+      }
+    };
+    // Weight step decode into fp16: data wave pw takes rows 32 pw .. 32 pw + 31 in two
+    // passes of 16; lane l takes row 16 t + (l & 7) + 8 (l >> 5) of pass t and 16-byte
+    // code chunk cq = (l >> 3) & 3, so that 8 consecutive lanes write 8 rows of one chunk
+    // column; row r's fp16 chunk c (K 8c .. 8c + 7 in the permuted order of the
+    // activation side) sits at slot c ^ sigma(r).
+    int d_st = 0;  // raw stage of the next weight step to decode
+    auto decode_b = [&](int buf) {
+      const uint8_t* st = ringB + d_st * B_STAGE;
+      const int cq = (lane >> 3) & 3;
+#pragma unroll
+      for (int t = 0; t < 2; t++) {
+        const int r = 32 * pw + 16 * t + (lane & 7) + 8 * (lane >> 5);
+        const u32x4_t raw = *(const u32x4_t*)(st + r * 64 + (cq << 4));
+        const uint32_t sb = *(const uint16_t*)(st + B_CODE + r * 8 + 2 * cq);
+        const half2_t s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sb, 1.0f, false);
+        const half2_t s0 = half2_t{s01[0], s01[0]}, s1 = half2_t{s01[1], s01[1]};
+        _Float16* row = bdec[buf] + r * BK;
+#pragma unroll
+        for (int ks = 0; ks < 4; ks++)
+          *(half8_t*)(row + (((4 * cq + ks) ^ ns_sigma(r)) << 3)) = decode8_e2m1_f16(raw[ks], ks < 2 ? s0 : s1);
+      }
+      d_st = d_st + 1 == SB ? 0 : d_st + 1;
+    };
+
+    {
+      const NsJob it0 = job_at(0);
+      a_setup(it0);
+      b_setup(it0);
+    }
+#pragma unroll
+    for (int i = 0; i < DB; i++) issue_b();
+    issue_a();
+    wait_vmcnt<0>();
+    __syncthreads();  // B(0 .. DB - 1) and A(0) are in LDS
+    decode_b(0);
+    for (int s = 0; s < nsteps; s++) {
+      // A(s) and everything issued before it (B(s + 1) among them) have landed; only the
+      // weight DMAs of B(s + DB - 1) may be outstanding
+      wait_vmcnt<B_DMAS>();
+      // every wave is done with step s - 1, whose activation slot and fp16 buffer the
+      // next issues and decode overwrite; the decode of B(s) is visible
+      __syncthreads();
+      issue_a();                // A(s + 1)
+      issue_b();                // B(s + DB), into the stage of B(s), decoded during step s - 1
+      decode_b((s + 1) & 1);    // B(s + 1); past the end a stage that is not read again
+    }
+    __syncthreads();  // the MFMA waves' barrier after their last step
+    wait_vmcnt<0>();  // the trailing re-reads land before the workgroup ends
+    return;
+  }
+
+  // ======== MFMA waves: fragments, activation decode, MFMAs and the epilogue ========
+  // Wave c owns the 16-row groups 16 c + 64 i (i < RG) of the M tile and all 128 columns,
+  // so every MFMA wave computes whenever masked_m > 16 c.  Each item runs a loop
+  // specialised on the wave's valid row groups (branch-free, its accumulators local to
+  // it).  The step loop is pipelined across the barrier: the operands of sub-step 3 are
+  // in registers before it, and after it the loads of the next step's fragments go out
+  // under sub-step 3's MFMAs.
+  const int c = wave;
+  const int q = lane >> 4, rr = lane & 15;
+  __syncthreads();  // the data waves' prologue
+
+  // valid 16-row groups of this wave in an item
+  auto nv_of = [&](const NsJob& it) {
+    const int left = it.mm - it.m0 - 16 * c;
+    return left <= 0 ? 0 : (left > 64 * (RG - 1) ? RG : (left + 63) >> 6);
+  };
+  // dword ks of a lane's chunk q holds K elements 32 q + 8 ks .. +7 of the step, in
+  // 16-block 2 q + ks / 2
+  half8_t bf[NB];
+  u32x4_t araw[RG];
+  uint32_t asc[RG];
+  // fp16 weight fragment n of sub-step ks: row 16 n + rr, chunk (4 q + ks) ^ sigma(rr) =
+  // ((4 q) ^ sigma(rr)) ^ ks, i.e. the lane's byte offset for sub-step 0 with ks XORed
+  // into bits 4..5.  The base is re-derived every step (an opaque copy), so the compiler
+  // does not keep four offsets live across the loop.
+  const int bf_lane = rr * (BK * 2) + (((4 * q) ^ ns_sigma(rr)) << 4);
+  int bf_off = bf_lane;
+  auto load_bf = [&](int s, int n, int ks) {
+    const uint8_t* base = (const uint8_t*)bdec[s & 1] + 16 * n * (BK * 2);
+    bf[n] = *(const half8_t*)(base + (bf_off ^ (ks << 4)));
+  };
+  // all RG row groups, valid or not (rows without valid data are never used); row
+  // 16 c + 64 i + rr has the swizzle of rr, so the groups sit at fixed offsets
+  const int a_off = (16 * c + rr) * 64 + ((q ^ ns_swz_a(rr)) << 4);
+  const int as_off = A_CODE + (16 * c + rr) * 8 + 2 * q;
+  auto load_a = [&](int s) {
+    const uint8_t* As = ringA + (s & 1) * A_STAGE;
+#pragma unroll
+    for (int i = 0; i < RG; i++) {
+      araw[i] = *(const u32x4_t*)(As + a_off + 64 * 64 * i);
+      asc[i] = *(const uint16_t*)(As + as_off + 64 * 8 * i);
     }
   };
-
-  {
-    const NsJob it0 = job_at(0);
-    a_setup(it0);
-    b_setup(it0);
-  }
-  // prologue in the steady-state order: "step" i < 0 issues A(i + 1) (if >= 0), then B(i + DB)
-#pragma unroll
-  for (int i = -DB; i < 0; i++) {
-    if (i + 1 >= 0) issue_a();
-    issue_b();
-  }
-
-  // The weight step is decoded once per workgroup into fp16, one step ahead of its use.
-  // Wave w takes rows 16 w .. 16 w + 15, lane l row 16 w + (l & 7) + 8 (l >> 5) and
-  // 16-byte code chunk cq = (l >> 3) & 3, so that 8 consecutive lanes write 8 rows of one
-  // chunk column; row r's fp16 chunk c (K 8c .. 8c + 7 in the permuted order of the
-  // activation side) sits at slot c ^ sigma(r).
-  int d_st = 0;  // raw stage of the next weight step to decode
-  struct DecB {
-    u32x4_t raw;
-    half2_t s0, s1;
-    _Float16* row;
-    int r, cq;
-  };
-  auto decode_b_begin = [&](int buf) {
-    const uint8_t* st = ringB + d_st * B_STAGE;
-    DecB d;
-    d.r = 16 * wave + (lane & 7) + 8 * (lane >> 5);
-    d.cq = (lane >> 3) & 3;
-    d.raw = *(const u32x4_t*)(st + d.r * 64 + (d.cq << 4));
-    const uint32_t sb = *(const uint16_t*)(st + B_CODE + d.r * 8 + 2 * d.cq);
-    const half2_t s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sb, 1.0f, false);
-    d.s0 = half2_t{s01[0], s01[0]};
-    d.s1 = half2_t{s01[1], s01[1]};
-    d.row = bdec[buf] + d.r * BK;
-    d_st = d_st + 1 == SB ? 0 : d_st + 1;
-    return d;
-  };
-  auto decode_b_part = [&](const DecB& d, int ks) {
-    *(half8_t*)(d.row + (((4 * d.cq + ks) ^ ns_sigma(d.r)) << 3)) = decode8_e2m1_f16(d.raw[ks], ks < 2 ? d.s0 : d.s1);
-  };
-  auto decode_b = [&](int buf) {
-    const DecB d = decode_b_begin(buf);
-#pragma unroll
-    for (int ks = 0; ks < 4; ks++) decode_b_part(d, ks);
-  };
-  // B(0) is followed by DB - 2 weight steps, A(0) and B(DB - 1): allowing only the weight
-  // DMAs behind it outstanding is enough
-  if (wave < 4) wait_vmcnt<2 * (DB - 1)>();
-  else wait_vmcnt<DB - 1>();
-  __syncthreads();
-  decode_b(0);
-
-  float4_t acc[RG][NB];
-#pragma unroll
-  for (int i = 0; i < RG; i++)
-#pragma unroll
-    for (int n = 0; n < NB; n++) acc[i][n] = float4_t{0.f, 0.f, 0.f, 0.f};
 
   NsJob cit = job_at(0);
-  int c_k = 0, c_kt = 0, c_sa = 0;
-  const int q = lane >> 4, rr = lane & 15;
+  int nv = nv_of(cit);
+  int s = 0;  // global step
+  __syncthreads();  // top of step 0
+#pragma unroll
+  for (int n = 0; n < NB; n++) load_bf(0, n, 0);
+  load_a(0);
 
-  for (int s = 0; s < nsteps; s++) {
-    // A(s) is followed only by B(s + DB - 1) (1 or 2 DMAs of this wave), whatever number
-    // of activation DMAs the wave skipped
-    if (wave < 4) wait_vmcnt<2>();
-    else wait_vmcnt<1>();
-    // every wave's DMAs of step s have landed and every wave is done with step s - 1,
-    // whose stages the next issues overwrite
-    __syncthreads();
-    issue_a();
-    issue_b();
-    // weight step s + 1 (issued before A(s), so it has landed) into the other fp16 buffer,
-    // whose readers finished step s - 1 before the barrier; past the end it re-decodes
-    // a stage that is not read again.  Its four 16-byte chunks are decoded one per
-    // sub-step, after that sub-step's MFMAs (all at once in a wave without valid rows).
-    const DecB db = decode_b_begin((s + 1) & 1);
-
-    const bool active = cit.m0 + 16 * wm < cit.mm;
-    if (!active) {
+  for (int k = 0; k < n_items; k++) {
+    const int ksteps = cit.K / BK;
+    const NsJob nit = k + 1 < n_items ? job_at(k + 1) : cit;
+    const int nv_next = nv_of(nit);
+    auto item = [&](auto nvc) {
+      constexpr int NV = decltype(nvc)::value;
+      constexpr int NA = NV > 0 ? NV : 1;
+      float4_t acc[NA][NB];
 #pragma unroll
-      for (int ks = 0; ks < 4; ks++) decode_b_part(db, ks);
-    } else {
-      const uint8_t* As = ringA + c_sa * A_STAGE;
-      const _Float16* Bd = bdec[s & 1];
-      u32x4_t araw[RG];
-      uint32_t asc[RG];
+      for (int i = 0; i < NA; i++)
 #pragma unroll
-      for (int i = 0; i < RG; i++) {
-        if (cit.m0 + 16 * wm + 16 * MW * i >= cit.mm) break;
-        const int r = 16 * wm + 16 * MW * i + rr;
-        araw[i] = *(const u32x4_t*)(As + r * 64 + ((q ^ ns_swz_a(r)) << 4));
-        asc[i] = *(const uint16_t*)(As + A_CODE + r * 8 + 2 * q);
-      }
-      half2_t as2[RG][2];
+        for (int n = 0; n < NB; n++) acc[i][n] = float4_t{0.f, 0.f, 0.f, 0.f};
+      for (int t = 0; t < ksteps; t++, s++) {
+        bf_off = bf_lane;
+        asm volatile("" : "+v"(bf_off));
+        half2_t as2[NA][2];
+        half8_t af[NA];
 #pragma unroll
-      for (int i = 0; i < RG; i++) {
-        const half2_t s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(asc[i], 1.0f, false);
-        as2[i][0] = half2_t{s01[0], s01[0]};
-        as2[i][1] = half2_t{s01[1], s01[1]};
-      }
-      // dword ks of a lane's chunk q holds K elements 32 q + 8 ks .. +7 of the step, in
-      // 16-block 2 q + ks / 2.  The weight fragments of sub-step ks + 1 are read while the
-      // MFMAs of sub-step ks run (two register sets), so no MFMA waits on a fresh LDS read.
-      half8_t bf[2][NB];
-      auto load_bf = [&](half8_t* dst, int ks) {
+        for (int i = 0; i < NV; i++) {
+          const half2_t s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(asc[i], 1.0f, false);
+          as2[i][0] = half2_t{s01[0], s01[0]};
+          as2[i][1] = half2_t{s01[1], s01[1]};
+          af[i] = decode8_e2m1_f16(araw[i][0], as2[i][0]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ks = 0; ks < 3; ks++) {
+#pragma unroll
+          for (int n = 0; n < NB; n++) {
+#pragma unroll
+            for (int i = 0; i < NV; i++)
+              acc[i][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bf[n], af[i], acc[i][n], 0, 0, 0);
+            load_bf(s, n, ks + 1);
+          }
+#pragma unroll
+          for (int i = 0; i < NV; i++) af[i] = decode8_e2m1_f16(araw[i][ks + 1], as2[i][(ks + 1) >> 1]);
+          __builtin_amdgcn_sched_barrier(0);  // keeps each sub-step's operands to one register set
+        }
+        // every LDS read of step s is in registers: the data waves may overwrite its
+        // buffers once all MFMA waves pass this barrier (the top of step s + 1; after the
+        // last step, the data waves' closing barrier, and the reads of a step that does
+        // not exist are never used)
+        __syncthreads();
+        load_a(s + 1);
 #pragma unroll
         for (int n = 0; n < NB; n++) {
-          const int r = (SWIGLU ? (n < NB / 2 ? WC / 2 * wn + 16 * n : BN / 2 + WC / 2 * wn + 16 * (n - NB / 2))
-                                : WC * wn + 16 * n) + rr;
-          dst[n] = *(const half8_t*)(Bd + r * BK + (((4 * q + ks) ^ ns_sigma(rr)) << 3));
+#pragma unroll
+          for (int i = 0; i < NV; i++)
+            acc[i][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bf[n], af[i], acc[i][n], 0, 0, 0);
+          load_bf(s + 1, n, 0);
         }
-      };
-      load_bf(bf[0], 0);
-#pragma unroll
-      for (int ks = 0; ks < 4; ks++) {
-        if (ks + 1 < 4) load_bf(bf[(ks + 1) & 1], ks + 1);
-#pragma unroll
-        for (int i = 0; i < RG; i++) {
-          if (cit.m0 + 16 * wm + 16 * MW * i >= cit.mm) break;
-          const half8_t af = decode8_e2m1_f16(araw[i][ks], as2[i][ks >> 1]);
-#pragma unroll
-          for (int n = 0; n < NB; n++)
-            acc[i][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bf[ks & 1][n], af, acc[i][n], 0, 0, 0);
-        }
-        decode_b_part(db, ks);
+        __builtin_amdgcn_sched_barrier(0);
       }
-    }
-    c_sa ^= 1;
-
-    if (++c_kt == cit.K / BK) {
-      // lane (rr, q) holds, for row group i, output row 16 wm + 16 MW i + rr and the four
-      // columns 4 q .. 4 q + 3 of each 16-column group n
-      if (active) {
+      if constexpr (NV > 0) {
+        // lane (rr, q) holds, for row group i, output row 16 c + 64 i + rr and the four
+        // columns 4 q .. 4 q + 3 of each 16-column group n
         float alpha;
         void* obase;
         size_t ldo;
@@ -423,8 +465,8 @@ __global__ __launch_bounds__(ns::THREADS) void k_gemm_nvfp4_stream(const typenam
           ldo = p.grp[cit.g].ldc;
         }
 #pragma unroll
-        for (int i = 0; i < RG; i++) {
-          const int m = cit.m0 + 16 * wm + 16 * MW * i + rr;
+        for (int i = 0; i < NV; i++) {
+          const int m = cit.m0 + 16 * c + 64 * i + rr;
           const bool ok = m < cit.mm;
           const size_t orow = CONTIG ? (size_t)__builtin_amdgcn_readfirstlane(rs_s[cit.g]) + m
                               : MASKED ? (size_t)cit.g * cap + m : (size_t)m;
@@ -439,7 +481,7 @@ __global__ __launch_bounds__(ns::THREADS) void k_gemm_nvfp4_stream(const typenam
                 uv[r] = up;
                 h[r] = gt / (1.0f + expf(-gt)) * up;
               }
-              const int hc0 = cit.n0 + WC / 2 * wn + 16 * n;  // first column of this lane's 16-block
+              const int hc0 = cit.n0 + 16 * n;  // first column of this lane's 16-block
               if (p.dbg_h && ok) *(float4_t*)(p.dbg_h + orow * I + hc0 + 4 * q) = float4_t{h[0], h[1], h[2], h[3]};
               if (p.dbg_g1 && ok) {
                 *(float4_t*)(p.dbg_g1 + orow * 2 * I + hc0 + 4 * q) = float4_t{gv[0], gv[1], gv[2], gv[3]};
@@ -456,38 +498,39 @@ __global__ __launch_bounds__(ns::THREADS) void k_gemm_nvfp4_stream(const typenam
           } else {
 #pragma unroll
             for (int n = 0; n < NB; n++) {
-              const int c = cit.n0 + WC * wn + 16 * n + 4 * q;
+              const int col = cit.n0 + 16 * n + 4 * q;
               const float4_t v = acc[i][n] * alpha;
               if (!ok) continue;
               if constexpr (EPI == EPI_BF16) {
                 const uint32_t lo = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
                 const uint32_t hi = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
-                *(u32x2_t*)((uint16_t*)obase + orow * ldo + c) = u32x2_t{lo, hi};
+                *(u32x2_t*)((uint16_t*)obase + orow * ldo + col) = u32x2_t{lo, hi};
               } else {
-                *(float4_t*)((float*)obase + orow * ldo + c) = v;
+                *(float4_t*)((float*)obase + orow * ldo + col) = v;
               }
             }
           }
         }
       }
-#pragma unroll
-      for (int i = 0; i < RG; i++)
-#pragma unroll
-        for (int n = 0; n < NB; n++) acc[i][n] = float4_t{0.f, 0.f, 0.f, 0.f};
-      c_kt = 0;
-      if (++c_k < n_items) cit = job_at(c_k);
+    };
+    switch (nv) {
+      case 4: item(std::integral_constant<int, 4>{}); break;
+      case 3: item(std::integral_constant<int, 3>{}); break;
+      case 2: item(std::integral_constant<int, 2>{}); break;
+      case 1: item(std::integral_constant<int, 1>{}); break;
+      default: item(std::integral_constant<int, 0>{}); break;
     }
+    cit = nit;
+    nv = nv_next;
   }
-  wait_vmcnt<0>();  // the trailing re-reads land before the workgroup ends
 }
 
 template <int EPI, int MODE>
 static hipError_t launch_stream(const typename ArgsOf<MODE>::type& p, int cu_limit, hipStream_t s) {
-  constexpr int MW = 8;  // 8 x 1 waves: measured about 1% ahead of 4 x 2 (T=8192 layer, hetero)
-  const void* k = (const void*)k_gemm_nvfp4_stream<EPI, MODE, MW>;
+  const void* k = (const void*)k_gemm_nvfp4_stream<EPI, MODE>;
   const int grid = resident_grid(k, ns::THREADS, cu_limit);
   if (grid <= 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((k_gemm_nvfp4_stream<EPI, MODE, MW>), dim3(grid), dim3(ns::THREADS), 0, s, p);
+  hipLaunchKernelGGL((k_gemm_nvfp4_stream<EPI, MODE>), dim3(grid), dim3(ns::THREADS), 0, s, p);
   return hipGetLastError();
 }
 
@@ -560,8 +603,8 @@ hipError_t gemm_nvfp4_stream_hetero(HeteroGemmArgs p, int epi, int cu_limit, hip
     taken[best] = true;
   }
   r.G = n;
-  const void* k = epi == EPI_BF16 ? (const void*)k_gemm_nvfp4_stream<EPI_BF16, MODE_HETERO, 8>
-                                  : (const void*)k_gemm_nvfp4_stream<EPI_F32, MODE_HETERO, 8>;
+  const void* k = epi == EPI_BF16 ? (const void*)k_gemm_nvfp4_stream<EPI_BF16, MODE_HETERO>
+                                  : (const void*)k_gemm_nvfp4_stream<EPI_F32, MODE_HETERO>;
   const int grid = resident_grid(k, ns::THREADS, cu_limit);
   if (grid <= 0) return hipErrorInvalidValue;
   hetero_lpt_schedule(r.grp, c, n, grid, r.sched);
