@@ -37,48 +37,43 @@ namespace mxg {
 // its eight 16-byte chunks XOR-permuted by (r ^ r >> 3) & 7, which keeps the MFMA
 // operand reads free of bank conflicts.
 //
-// Waves: 4 (M) x 2 (N).  Wave (wm, wn) owns the 16-row groups 16 wm + 64 i (i = 0..3)
-// and h columns 32 wn.. of the item, i.e. gate columns 32 wn.. and the matching up
-// columns, so the SwiGLU epilogue runs in registers.  Interleaving the row groups keeps
-// both waves of every SIMD busy when masked_m <= 128; row groups that are entirely
-// masked skip their MFMAs, and every wave keeps issuing its share of the DMAs.
+// Waves: 12, in two roles.  Waves 8..11 (one per SIMD) issue every DMA; waves 0..7 (two
+// per SIMD) only read fragments, run MFMAs and store h.  One barrier per step hands a
+// step's stages from one role to the other.  MFMA wave w owns the 16-row groups 16 w
+// and 16 w + 128 and every column of the item (its 64 gate and 64 up weight rows), so the
+// SwiGLU epilogue runs in registers; interleaving the row groups keeps every MFMA wave
+// busy when masked_m <= 128, and row groups that are entirely masked skip their MFMAs.
 #ifndef MXG_F1_DB
 #define MXG_F1_DB 4
 #endif
 namespace f1 {
 constexpr int BM = 256, BN = 128, HN = BN / 2, BK = 128;
-constexpr int WAVES = 8, THREADS = WAVES * 64;
+constexpr int MW = 8, DW = 4;  // MFMA waves, data waves
+constexpr int WAVES = MW + DW, THREADS = WAVES * 64;
 constexpr int A_STAGE = BM * BK + BM * 4;  // codes, then the fp32 row scales
 constexpr int B_STAGE = BN * BK + 16;      // codes, then the {gate, up} block scales
 constexpr int MAX_G = STREAM_MAX_G;
 static_assert(BM == STREAM_BM, "M tile of the shared work distribution");
-// DMA instructions per wave per step: 4 of activations (32 rows), 2 of weights (16 rows);
-// wave 0 adds the activation row scales, wave 1 the two weight block scales
-constexpr int A_OPS = 4, B_OPS = 2;
-// vmcnt allowance at the top of step j: A(j) is followed by B(j + DB - DA) and DA - 1
-// full steps, B(j) by DB - 1 full steps
-constexpr int wait_count(int da, int db, int ao, int bo) {
-  return (bo + (da - 1) * (ao + bo)) < (db - 1) * (ao + bo) ? bo + (da - 1) * (ao + bo) : (db - 1) * (ao + bo);
-}
+// DMA instructions per data wave per step: up to 8 of activations (64 rows), 4 of weights
+// (32 rows); data wave 0 adds the activation row scales, data wave 1 the two weight
+// block scales
+constexpr int A_OPS = 8, B_OPS = 4;
 }  // namespace f1
 
 __device__ __forceinline__ int f1_swz(int r) { return (r ^ (r >> 3)) & 7; }
 
-template <int DA, int DB, bool SPLIT, bool DBG>
+template <int DB, bool SPLIT, bool DBG>
 __global__ __launch_bounds__(f1::THREADS) void k_gemm_fp8_swiglu(const Fp8GemmArgs p) {
   using namespace f1;
-  constexpr int SA = DA + 1, SB = DB + 1;
-  // DA = 1: the wait for A(j) counts only B(j + DB - 1) behind it, so the number of
-  // activation DMAs a wave issues per step may vary (masked 8-row groups are skipped)
-  static_assert(DA == 1 && DB >= 2, "ring depths");
-  __shared__ __attribute__((aligned(16))) uint8_t ringA[SA * A_STAGE];
+  constexpr int SB = DB + 1;
+  static_assert(DB >= 2, "B(s + 1) must be issued before A(s)");
+  __shared__ __attribute__((aligned(16))) uint8_t ringA[2 * A_STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t ringB[SB * B_STAGE];
   __shared__ int tprefix[MAX_G + 1];
   __shared__ int mm_s[MAX_G];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: branches on it are scalar
-  const int wm = wave >> 1, wn = wave & 1;
   const int G = p.G, K = p.K, KB = K / BK, N = p.N, I = N / 2, cap = p.max_m, capS = p.a_s_stride;
   const int tiles_n = I / HN;
 
@@ -92,200 +87,192 @@ __global__ __launch_bounds__(f1::THREADS) void k_gemm_fp8_swiglu(const Fp8GemmAr
 
   auto item_at = [&](int k) { return stream_item(bx + k * grid, tiles_n, G, tprefix, mm_s, HN); };
 
-  // ---- DMA cursors: per-lane sources of the current item (rows past masked_m re-read
-  // the last valid row, never stored); past the last step they stay on it
-  const uint8_t* asrc[A_OPS];
-  const float* asrc_s;
-  int a_n = 0;  // this wave's activation DMAs per step: 8-row groups entirely past masked_m are skipped
-  auto a_setup = [&](const StreamItem& it) {
-    const uint8_t* A = p.a + (size_t)it.g * cap * K;
-    const int left = it.mm - it.m0 - 32 * wave;
-    a_n = left <= 0 ? 0 : (left >= 8 * A_OPS ? A_OPS : (left + 7) / 8);
+  if (wave >= MW) {
+    // ======== data waves: activations one step ahead, weights DB steps ahead ========
+    const int pw = wave - MW;
+    // DMA cursors: per-lane sources of the current item (rows past masked_m re-read the
+    // last valid row, never stored); past the last step they stay on it
+    const uint8_t* asrc[A_OPS];
+    const float* asrc_s;
+    int a_n = 0;  // activation DMAs per step: 8-row groups entirely past masked_m are skipped
+    auto a_setup = [&](const StreamItem& it) {
+      const uint8_t* A = p.a + (size_t)it.g * cap * K;
+      const int left = it.mm - it.m0 - 64 * pw;
+      a_n = left <= 0 ? 0 : (left >= 8 * A_OPS ? A_OPS : (left + 7) / 8);
 #pragma unroll
-    for (int j = 0; j < A_OPS; j++) {
-      const int r = 32 * wave + 8 * j + (lane >> 3);
-      const int row = it.m0 + r < it.mm ? it.m0 + r : it.mm - 1;
-      asrc[j] = A + (size_t)row * K + (((lane & 7) ^ f1_swz(r)) << 4);
-    }
-    const int rs = it.m0 + 4 * lane < capS - 4 ? it.m0 + 4 * lane : capS - 4;
-    asrc_s = p.a_s + (size_t)it.g * KB * capS + rs;
-  };
-  const uint8_t* bsrc[B_OPS];
-  const float* bsrc_s;
-  auto b_setup = [&](const StreamItem& it) {
-    const uint8_t* B = p.b + (size_t)it.g * N * K;
-#pragma unroll
-    for (int j = 0; j < B_OPS; j++) {
-      const int r = 16 * wave + 8 * j + (lane >> 3);
-      const int brow = r < HN ? it.n0 + r : I + it.n0 + (r - HN);
-      bsrc[j] = B + (size_t)brow * K + (((lane & 7) ^ f1_swz(r)) << 4);
-    }
-    const int blk = (lane == 0 ? it.n0 : I + it.n0) / 128;
-    bsrc_s = p.b_s + ((size_t)it.g * (N / 128) + blk) * KB;
-  };
-  int a_k = 0, a_kb = 0, a_step = 0, a_st = 0;
-  int b_k = 0, b_kb = 0, b_step = 0, b_st = 0;
-  auto issue_a = [&]() {
-    uint8_t* st = ringA + a_st * A_STAGE;
-#pragma unroll
-    for (int j = 0; j < A_OPS; j++)
-      if (j < a_n) dma16(asrc[j] + a_kb * BK, st + (32 * wave + 8 * j) * BK);
-    if (wave == 0) dma16(asrc_s + (size_t)a_kb * capS, st + BM * BK);
-    a_st = a_st + 1 == SA ? 0 : a_st + 1;
-    if (a_step + 1 < nsteps) {
-      a_step++;
-      if (++a_kb == KB) {
-        a_kb = 0;
-        a_setup(item_at(++a_k));
+      for (int j = 0; j < A_OPS; j++) {
+        const int r = 64 * pw + 8 * j + (lane >> 3);
+        const int row = it.m0 + r < it.mm ? it.m0 + r : it.mm - 1;
+        asrc[j] = A + (size_t)row * K + (((lane & 7) ^ f1_swz(r)) << 4);
       }
-    }
-  };
-  auto issue_b = [&]() {
-    uint8_t* st = ringB + b_st * B_STAGE;
+      const int rs = it.m0 + 4 * lane < capS - 4 ? it.m0 + 4 * lane : capS - 4;
+      asrc_s = p.a_s + (size_t)it.g * KB * capS + rs;
+    };
+    const uint8_t* bsrc[B_OPS];
+    const float* bsrc_s;
+    auto b_setup = [&](const StreamItem& it) {
+      const uint8_t* B = p.b + (size_t)it.g * N * K;
 #pragma unroll
-    for (int j = 0; j < B_OPS; j++) dma16(bsrc[j] + b_kb * BK, st + (16 * wave + 8 * j) * BK);
-    if (wave == 1 && lane < 2) dma4(bsrc_s + b_kb, st + BN * BK);
-    b_st = b_st + 1 == SB ? 0 : b_st + 1;
-    if (b_step + 1 < nsteps) {
-      b_step++;
-      if (++b_kb == KB) {
-        b_kb = 0;
-        b_setup(item_at(++b_k));
+      for (int j = 0; j < B_OPS; j++) {
+        const int r = 32 * pw + 8 * j + (lane >> 3);
+        const int brow = r < HN ? it.n0 + r : I + it.n0 + (r - HN);
+        bsrc[j] = B + (size_t)brow * K + (((lane & 7) ^ f1_swz(r)) << 4);
       }
-    }
-  };
-
-  {
-    const StreamItem it0 = item_at(0);
-    a_setup(it0);
-    b_setup(it0);
-  }
-  // prologue in the steady-state order: "step" i < 0 issues A(i + DA) (if >= 0), then B(i + DB)
+      const int blk = (lane == 0 ? it.n0 : I + it.n0) / 128;
+      bsrc_s = p.b_s + ((size_t)it.g * (N / 128) + blk) * KB;
+    };
+    int a_k = 0, a_kb = 0, a_step = 0, a_st = 0;
+    int b_k = 0, b_kb = 0, b_step = 0, b_st = 0;
+    auto issue_a = [&]() {  // A(step) into slot step & 1
+      uint8_t* st = ringA + a_st * A_STAGE;
 #pragma unroll
-  for (int i = -DB; i < 0; i++) {
-    if (i + DA >= 0) issue_a();
-    issue_b();
-  }
-
-  float4_t acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; i++)
-#pragma unroll
-    for (int n = 0; n < 4; n++) acc[i][n] = float4_t{0.f, 0.f, 0.f, 0.f};
-
-  StreamItem cit = item_at(0);
-  int c_k = 0, c_kb = 0, c_sa = 0, c_sb = 0;
-  const int q = lane >> 4, rr = lane & 15, odd = lane & 1;
-
-  // A finished item's h values (bf16 pairs) wait in registers for the next step: stored
-  // right after its barrier, they sit in the counter just ahead of that step's
-  // activation DMA and hold up no wait for a weight DMA issued before them.  Masked rows
-  // store into the scratch row after the last expert.
-  // With SPLIT, rows are 2I wide: hi = bf16(h) in columns [0, I), lo = bf16(h - hi) in
-  // [I, 2I) (h - hi is exact in fp32, so hi + lo holds h to about 16 significant bits).
-  constexpr int PL = SPLIT ? 2 : 1;
-  const int RS = PL * I;  // h row stride (elements)
-  uint32_t hw[PL][4][2][2];
-  bool pend = false;
-  StreamItem pit = cit;
-  auto store_h = [&]() {
-    uint16_t* H = (uint16_t*)p.out;
-    uint16_t* scratch_row = H + (size_t)G * cap * RS;
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int row0 = pit.m0 + 16 * wm + 64 * i + 4 * q;
-#pragma unroll
-      for (int n = 0; n < 2; n++) {
-        const int c = (pit.n0 + 32 * wn + 16 * n + rr) & ~1;
-        const int ra = row0 + odd, rb = row0 + 2 + odd;
-        uint16_t* pa = ra < pit.mm ? H + ((size_t)pit.g * cap + ra) * RS + c : scratch_row + c;
-        uint16_t* pb = rb < pit.mm ? H + ((size_t)pit.g * cap + rb) * RS + c : scratch_row + c;
-#pragma unroll
-        for (int pl = 0; pl < PL; pl++) {
-          *(uint32_t*)(pa + pl * I) = hw[pl][i][n][0];
-          *(uint32_t*)(pb + pl * I) = hw[pl][i][n][1];
+      for (int j = 0; j < A_OPS; j++)
+        if (j < a_n) dma16(asrc[j] + a_kb * BK, st + (64 * pw + 8 * j) * BK);
+      if (pw == 0) dma16(asrc_s + (size_t)a_kb * capS, st + BM * BK);
+      a_st ^= 1;
+      if (a_step + 1 < nsteps) {
+        a_step++;
+        if (++a_kb == KB) {
+          a_kb = 0;
+          a_setup(item_at(++a_k));
         }
       }
+    };
+    auto issue_b = [&]() {  // B(step) into stage step % SB: B_OPS (+ 1) instructions
+      uint8_t* st = ringB + b_st * B_STAGE;
+#pragma unroll
+      for (int j = 0; j < B_OPS; j++) dma16(bsrc[j] + b_kb * BK, st + (32 * pw + 8 * j) * BK);
+      if (pw == 1 && lane < 2) dma4(bsrc_s + b_kb, st + BN * BK);
+      b_st = b_st + 1 == SB ? 0 : b_st + 1;
+      if (b_step + 1 < nsteps) {
+        b_step++;
+        if (++b_kb == KB) {
+          b_kb = 0;
+          b_setup(item_at(++b_k));
+        }
+      }
+    };
+    {
+      const StreamItem it0 = item_at(0);
+      a_setup(it0);
+      b_setup(it0);
     }
+#pragma unroll
+    for (int i = 0; i < DB; i++) issue_b();
+    issue_a();
+    wait_vmcnt<0>();  // B(0 .. DB - 1) and A(0)
+    for (int s = 0; s < nsteps; s++) {
+      // A(s) and B(s) are in LDS, and the MFMA waves are done with step s - 1, whose
+      // activation slot and weight stage the next issues overwrite
+      __syncthreads();
+      issue_a();  // A(s + 1)
+      issue_b();  // B(s + DB)
+      // A(s + 1) and everything issued before it (B(s + 1) among them) land before the
+      // next barrier; only this step's weight DMAs may stay outstanding
+      if (pw == 1) wait_vmcnt<B_OPS + 1>();
+      else wait_vmcnt<B_OPS>();
+    }
+    wait_vmcnt<0>();  // the trailing re-reads land before the workgroup ends
+    return;
+  }
+
+  // ======== MFMA waves ========
+  // Wave w owns the 16-row groups 16 w and 16 w + 128 of the M tile and all 128 weight
+  // rows of the item (gate rows 0..63, up rows 64..127), so SwiGLU pairs fragment group
+  // n with n + 4 in registers.  The weight fragments are read two groups ahead.
+  float4_t acc[2][8];
+#pragma unroll
+  for (int i = 0; i < 2; i++)
+#pragma unroll
+    for (int n = 0; n < 8; n++) acc[i][n] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+  StreamItem cit = item_at(0);
+  int c_k = 0, c_kb = 0, c_sb = 0;
+  const int q = lane >> 4, rr = lane & 15, odd = lane & 1;
+
+  // h rows: with SPLIT they are 2I wide, hi = bf16(h) in columns [0, I), lo = bf16(h - hi)
+  // in [I, 2I) (h - hi is exact in fp32, so hi + lo holds h to about 16 significant bits).
+  // Masked rows store into the scratch row after the last expert.
+  constexpr int PL = SPLIT ? 2 : 1;
+  const int RS = PL * I;  // h row stride (elements)
+  // Fragment of 16-byte chunks 2q, 2q + 1 (K 32 q .. 32 q + 31) of row 16 j + rr of a
+  // stage: f1_swz(16 j + rr) = f1_swz(rr) ^ (2 j mod 8), so the lane's byte offset in the
+  // row is its offset for j = 0 with (j mod 4) XORed into bits 5..6, and the second chunk
+  // sits at the first one XOR 16.
+  // The base is re-derived every step (an opaque copy), so the compiler does not keep
+  // eight offsets live across the loop.
+  const int frag_lane = rr * BK + (((2 * q) ^ f1_swz(rr)) << 4);
+  int frag_off = frag_lane;
+  auto frag = [&](const uint8_t* stage, int j) {
+    const uint8_t* row = stage + 16 * j * BK;
+    const int off = frag_off ^ ((j & 3) << 5);
+    const u32x4_t x0 = *(const u32x4_t*)(row + off);
+    const u32x4_t x1 = *(const u32x4_t*)(row + (off ^ 16));
+    return int8v_t{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3], (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
   };
 
   for (int s = 0; s < nsteps; s++) {
-    if (wave == 0) wait_vmcnt<wait_count(DA, DB, A_OPS + 1, B_OPS)>();
-    else if (wave == 1) wait_vmcnt<wait_count(DA, DB, A_OPS, B_OPS + 1)>();
-    else wait_vmcnt<wait_count(DA, DB, A_OPS, B_OPS)>();
-    // every wave's DMAs of step s have landed, and every wave is done with step s - 1,
-    // whose stages the next issues overwrite
-    __syncthreads();
-    if (pend) {
-      store_h();
-      pend = false;
-    }
-    issue_a();
-    issue_b();
-
-    const bool active = cit.m0 + 16 * wm < cit.mm;
-    if (active) {
-      const uint8_t* As = ringA + c_sa * A_STAGE;
+    __syncthreads();  // A(s) and B(s) are in LDS
+    frag_off = frag_lane;
+    asm volatile("" : "+v"(frag_off));
+    const int left = cit.mm - cit.m0 - 16 * wave;  // valid rows from this wave's first row
+    const int nv = left <= 0 ? 0 : (left > 128 ? 2 : 1);
+    if (nv > 0) {
+      const uint8_t* As = ringA + (s & 1) * A_STAGE;
       const uint8_t* Bs = ringB + c_sb * B_STAGE;
-      int8v_t af[4], bfr[4];
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        if (cit.m0 + 16 * wm + 64 * i >= cit.mm) break;
-        const int r = 16 * wm + 64 * i + rr;
-        const uint8_t* row = As + r * BK;
-        const int f = f1_swz(r);
-        const u32x4_t x0 = *(const u32x4_t*)(row + (((2 * q) ^ f) << 4));
-        const u32x4_t x1 = *(const u32x4_t*)(row + (((2 * q + 1) ^ f) << 4));
-        af[i] = int8v_t{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3], (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
-      }
-#pragma unroll
-      for (int n = 0; n < 4; n++) {
-        const int r = (n < 2 ? 32 * wn + 16 * n : HN + 32 * wn + 16 * (n - 2)) + rr;
-        const uint8_t* row = Bs + r * BK;
-        const int f = f1_swz(r);
-        const u32x4_t y0 = *(const u32x4_t*)(row + (((2 * q) ^ f) << 4));
-        const u32x4_t y1 = *(const u32x4_t*)(row + (((2 * q + 1) ^ f) << 4));
-        bfr[n] = int8v_t{(int)y0[0], (int)y0[1], (int)y0[2], (int)y0[3], (int)y1[0], (int)y1[1], (int)y1[2], (int)y1[3]};
-      }
+      int8v_t af[2];
+      float4_t sw[2][2];  // row scale x {gate, up} block scale
       const float* AS = (const float*)(As + BM * BK);
       const float* WS = (const float*)(Bs + BN * BK);
       const float wg = WS[0], wu = WS[1];
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
-        if (cit.m0 + 16 * wm + 64 * i >= cit.mm) break;
-        const float4_t sa = *(const float4_t*)(AS + 16 * wm + 64 * i + 4 * q);
+      for (int i = 0; i < 2; i++) {
+        if (i >= nv) break;
+        af[i] = frag(As, wave + 8 * i);
+        const float4_t sa = *(const float4_t*)(AS + 16 * wave + 128 * i + 4 * q);
+        sw[i][0] = sa * wg;
+        sw[i][1] = sa * wu;
+      }
+      int8v_t bf[8];
+      bf[0] = frag(Bs, 0);
+      bf[1] = frag(Bs, 1);
 #pragma unroll
-        for (int n = 0; n < 4; n++) {
+      for (int n = 0; n < 8; n++) {
+        if (n + 2 < 8) bf[n + 2] = frag(Bs, n + 2);
+#pragma unroll
+        for (int i = 0; i < 2; i++) {
+          if (i >= nv) break;
           // 128 exact e4m3 products summed in fp32 (unit e8m0 scales), then promoted with
           // the row's activation scale times the block's weight scale
           const float4_t t = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              af[i], bfr[n], float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
-          const float w = n < 2 ? wg : wu;
+              af[i], bf[n], float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
 #pragma unroll
-          for (int r = 0; r < 4; r++) acc[i][n][r] = __builtin_fmaf(t[r], sa[r] * w, acc[i][n][r]);
+          for (int r = 0; r < 4; r++) acc[i][n][r] = __builtin_fmaf(t[r], sw[i][n >> 2][r], acc[i][n][r]);
         }
       }
     }
-    c_sa = c_sa + 1 == SA ? 0 : c_sa + 1;
     c_sb = c_sb + 1 == SB ? 0 : c_sb + 1;
 
     if (++c_kb == KB) {
       // SwiGLU in registers: lanes 2c and 2c+1 hold neighbouring columns of the same four
       // rows; one swap gives each lane both columns of two rows (rows +odd and +2+odd)
-      if (active) {
+      if (nv > 0) {
+        uint16_t* H = (uint16_t*)p.out;
+        uint16_t* scratch_row = H + (size_t)G * cap * RS;
 #pragma unroll
-        for (int i = 0; i < 4; i++)
+        for (int i = 0; i < 2; i++) {
+          if (i >= nv) break;
 #pragma unroll
-          for (int n = 0; n < 2; n++) {
+          for (int n = 0; n < 4; n++) {
             uint32_t b[PL][4];
 #pragma unroll
             for (int r = 0; r < 4; r++) {
-              const float gt = acc[i][n][r], up = acc[i][n + 2][r];
+              const float gt = acc[i][n][r], up = acc[i][n + 4][r];
               if constexpr (DBG) {  // the promoted GEMM1 sums, for stage checks only
-                const int row = cit.m0 + 16 * wm + 64 * i + 4 * q + r;
+                const int row = cit.m0 + 16 * wave + 128 * i + 4 * q + r;
                 if (row < cit.mm) {
                   float* d = p.dbg_g1 + ((size_t)cit.g * cap + row) * N;
-                  const int c = cit.n0 + 32 * wn + 16 * n + rr;
+                  const int c = cit.n0 + 16 * n + rr;
                   d[c] = gt;
                   d[I + c] = up;
                 }
@@ -294,50 +281,52 @@ __global__ __launch_bounds__(f1::THREADS) void k_gemm_fp8_swiglu(const Fp8GemmAr
               b[0][r] = f32_to_bf16_rne(h);
               if constexpr (SPLIT) b[PL - 1][r] = f32_to_bf16_rne(h - __uint_as_float(b[0][r] << 16));
             }
+            const int row0 = cit.m0 + 16 * wave + 128 * i + 4 * q;
+            const int c = (cit.n0 + 16 * n + rr) & ~1;
+            const int ra = row0 + odd, rb = row0 + 2 + odd;
+            uint16_t* pa = ra < cit.mm ? H + ((size_t)cit.g * cap + ra) * RS + c : scratch_row + c;
+            uint16_t* pb = rb < cit.mm ? H + ((size_t)cit.g * cap + rb) * RS + c : scratch_row + c;
 #pragma unroll
             for (int pl = 0; pl < PL; pl++) {
               const uint32_t y0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)(odd ? b[pl][0] : b[pl][1]), 0xB1, 0xF, 0xF, false);
               const uint32_t y1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)(odd ? b[pl][2] : b[pl][3]), 0xB1, 0xF, 0xF, false);
-              hw[pl][i][n][0] = odd ? (y0 | (b[pl][1] << 16)) : (b[pl][0] | (y0 << 16));
-              hw[pl][i][n][1] = odd ? (y1 | (b[pl][3] << 16)) : (b[pl][2] | (y1 << 16));
+              *(uint32_t*)(pa + pl * I) = odd ? (y0 | (b[pl][1] << 16)) : (b[pl][0] | (y0 << 16));
+              *(uint32_t*)(pb + pl * I) = odd ? (y1 | (b[pl][3] << 16)) : (b[pl][2] | (y1 << 16));
             }
           }
-        pend = true;
-        pit = cit;
+        }
       }
 #pragma unroll
-      for (int i = 0; i < 4; i++)
+      for (int i = 0; i < 2; i++)
 #pragma unroll
-        for (int n = 0; n < 4; n++) acc[i][n] = float4_t{0.f, 0.f, 0.f, 0.f};
+        for (int n = 0; n < 8; n++) acc[i][n] = float4_t{0.f, 0.f, 0.f, 0.f};
       c_kb = 0;
       if (++c_k < n_items) cit = item_at(c_k);
     }
   }
-  if (pend) store_h();
-  wait_vmcnt<0>();  // the trailing re-reads land before the workgroup ends
 }
 
-template <int DA, int DB, bool SPLIT, bool DBG>
+template <int DB, bool SPLIT, bool DBG>
 static hipError_t launch_fp8_swiglu(Fp8GemmArgs p, int cu_limit, hipStream_t s) {
   using namespace f1;
   if (p.G > MAX_G || (p.N / 2) % HN != 0 || p.K % BK != 0 || p.a_s_stride % 4 != 0 ||
       p.a_s_stride < p.max_m || p.a_s_stride < 4)
     return hipErrorNotSupported;
   if ((long long)p.G * ((p.max_m + BM - 1) / BM) * ((p.N / 2) / HN) > 0x7FFFFFFFLL) return hipErrorNotSupported;
-  const void* k = (const void*)k_gemm_fp8_swiglu<DA, DB, SPLIT, DBG>;
+  const void* k = (const void*)k_gemm_fp8_swiglu<DB, SPLIT, DBG>;
   const int grid = resident_grid(k, THREADS, cu_limit);
   if (grid <= 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((k_gemm_fp8_swiglu<DA, DB, SPLIT, DBG>), dim3(grid), dim3(THREADS), 0, s, p);
+  hipLaunchKernelGGL((k_gemm_fp8_swiglu<DB, SPLIT, DBG>), dim3(grid), dim3(THREADS), 0, s, p);
   return hipGetLastError();
 }
 
 hipError_t gemm_fp8_swiglu(Fp8GemmArgs p, int cu_limit, hipStream_t s) {
   if (p.G <= 0 || p.max_m <= 0 || p.N <= 0 || p.K <= 0) return hipSuccess;
   if (p.dbg_g1)
-    return p.h_split ? launch_fp8_swiglu<1, MXG_F1_DB, true, true>(p, cu_limit, s)
-                     : launch_fp8_swiglu<1, MXG_F1_DB, false, true>(p, cu_limit, s);
-  return p.h_split ? launch_fp8_swiglu<1, MXG_F1_DB, true, false>(p, cu_limit, s)
-                   : launch_fp8_swiglu<1, MXG_F1_DB, false, false>(p, cu_limit, s);
+    return p.h_split ? launch_fp8_swiglu<MXG_F1_DB, true, true>(p, cu_limit, s)
+                     : launch_fp8_swiglu<MXG_F1_DB, false, true>(p, cu_limit, s);
+  return p.h_split ? launch_fp8_swiglu<MXG_F1_DB, true, false>(p, cu_limit, s)
+                   : launch_fp8_swiglu<MXG_F1_DB, false, false>(p, cu_limit, s);
 }
 
 // ----------------------------------------------------------------------------- GEMM2
