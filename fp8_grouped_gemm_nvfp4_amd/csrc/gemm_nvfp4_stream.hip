@@ -36,9 +36,12 @@
 // register tile (wave c owns the 16-row groups 16 c + 64 i, so all four compute when
 // masked_m > 48).  One barrier per step hands a step's buffers from one role to the
 // other.  The MFMA waves cross it pipelined: the operands of their last sub-step are in
-// registers before it, and the next step's fragment reads go out under that sub-step's
-// MFMAs.  Each item runs a loop specialised on the wave's valid row groups, so the MFMA
-// stream has no branches.
+// registers before it, and the next step's fragment reads and first activation decode go
+// out under that sub-step's MFMAs; each sub-step likewise decodes the next one's
+// activation rows between its MFMAs.  Each item runs a loop specialised on the wave's
+// valid row groups, so the MFMA stream has no branches; the loop keeps its pipeline
+// state to itself (nothing crosses from one specialisation to another), which keeps the
+// kernel free of register spills.
 #include <type_traits>
 
 #include "kernels.h"
@@ -362,16 +365,13 @@ __global__ __launch_bounds__(ns::THREADS) void k_gemm_nvfp4_stream(const typenam
   };
   // dword ks of a lane's chunk q holds K elements 32 q + 8 ks .. +7 of the step, in
   // 16-block 2 q + ks / 2
-  half8_t bf[NB];
-  u32x4_t araw[RG];
-  uint32_t asc[RG];
   // fp16 weight fragment n of sub-step ks: row 16 n + rr, chunk (4 q + ks) ^ sigma(rr) =
   // ((4 q) ^ sigma(rr)) ^ ks, i.e. the lane's byte offset for sub-step 0 with ks XORed
   // into bits 4..5.  The base is re-derived every step (an opaque copy), so the compiler
   // does not keep four offsets live across the loop.
   const int bf_lane = rr * (BK * 2) + (((4 * q) ^ ns_sigma(rr)) << 4);
   int bf_off = bf_lane;
-  auto load_bf = [&](int s, int n, int ks) {
+  auto load_bf = [&](half8_t* bf, int s, int n, int ks) {
     const uint8_t* base = (const uint8_t*)bdec[s & 1] + 16 * n * (BK * 2);
     bf[n] = *(const half8_t*)(base + (bf_off ^ (ks << 4)));
   };
@@ -379,7 +379,7 @@ __global__ __launch_bounds__(ns::THREADS) void k_gemm_nvfp4_stream(const typenam
   // 16 c + 64 i + rr has the swizzle of rr, so the groups sit at fixed offsets
   const int a_off = (16 * c + rr) * 64 + ((q ^ ns_swz_a(rr)) << 4);
   const int as_off = A_CODE + (16 * c + rr) * 8 + 2 * q;
-  auto load_a = [&](int s) {
+  auto load_a = [&](u32x4_t* araw, uint32_t* asc, int s) {
     const uint8_t* As = ringA + (s & 1) * A_STAGE;
 #pragma unroll
     for (int i = 0; i < RG; i++) {
@@ -392,46 +392,61 @@ __global__ __launch_bounds__(ns::THREADS) void k_gemm_nvfp4_stream(const typenam
   int nv = nv_of(cit);
   int s = 0;  // global step
   __syncthreads();  // top of step 0
-#pragma unroll
-  for (int n = 0; n < NB; n++) load_bf(0, n, 0);
-  load_a(0);
 
   for (int k = 0; k < n_items; k++) {
     const int ksteps = cit.K / BK;
     const NsJob nit = k + 1 < n_items ? job_at(k + 1) : cit;
-    const int nv_next = nv_of(nit);
     auto item = [&](auto nvc) {
       constexpr int NV = decltype(nvc)::value;
       constexpr int NA = NV > 0 ? NV : 1;
+      // The pipeline state is the item's own: the barrier of its first step has been
+      // passed (before step 0, or inside the previous item's last step), and that step's
+      // buffers stay until this wave reaches the next barrier, so its fragments are read
+      // again here rather than carried over from the previous item's last sub-step.
+      half8_t bf[NB];
+      u32x4_t araw[RG];
+      uint32_t asc[RG];
+      bf_off = bf_lane;
+      asm volatile("" : "+v"(bf_off));
+#pragma unroll
+      for (int n = 0; n < NB; n++) load_bf(bf, s, n, 0);
+      load_a(araw, asc, s);
       float4_t acc[NA][NB];
 #pragma unroll
       for (int i = 0; i < NA; i++)
 #pragma unroll
         for (int n = 0; n < NB; n++) acc[i][n] = float4_t{0.f, 0.f, 0.f, 0.f};
-      for (int t = 0; t < ksteps; t++, s++) {
-        bf_off = bf_lane;
-        asm volatile("" : "+v"(bf_off));
-        half2_t as2[NA][2];
-        half8_t af[NA];
+      half2_t as2[NA][2];
+      half8_t af[NA];
+      auto cvt_scales = [&]() {
 #pragma unroll
         for (int i = 0; i < NV; i++) {
           const half2_t s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(asc[i], 1.0f, false);
           as2[i][0] = half2_t{s01[0], s01[0]};
           as2[i][1] = half2_t{s01[1], s01[1]};
-          af[i] = decode8_e2m1_f16(araw[i][0], as2[i][0]);
         }
+      };
+      cvt_scales();
+#pragma unroll
+      for (int i = 0; i < NV; i++) af[i] = decode8_e2m1_f16(araw[i][0], as2[i][0]);
+      for (int t = 0; t < ksteps; t++, s++) {
+        bf_off = bf_lane;
+        asm volatile("" : "+v"(bf_off));
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ks = 0; ks < 3; ks++) {
+          half8_t afn[NA];
 #pragma unroll
           for (int n = 0; n < NB; n++) {
 #pragma unroll
             for (int i = 0; i < NV; i++)
               acc[i][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bf[n], af[i], acc[i][n], 0, 0, 0);
-            load_bf(s, n, ks + 1);
+            load_bf(bf, s, n, ks + 1);
+            // row group n / 2 of the next sub-step, decoded between the MFMAs
+            if ((n & 1) && (n >> 1) < NV) afn[n >> 1] = decode8_e2m1_f16(araw[n >> 1][ks + 1], as2[n >> 1][(ks + 1) >> 1]);
           }
 #pragma unroll
-          for (int i = 0; i < NV; i++) af[i] = decode8_e2m1_f16(araw[i][ks + 1], as2[i][(ks + 1) >> 1]);
+          for (int i = 0; i < NV; i++) af[i] = afn[i];
           __builtin_amdgcn_sched_barrier(0);  // keeps each sub-step's operands to one register set
         }
         // every LDS read of step s is in registers: the data waves may overwrite its
@@ -439,19 +454,31 @@ __global__ __launch_bounds__(ns::THREADS) void k_gemm_nvfp4_stream(const typenam
         // last step, the data waves' closing barrier, and the reads of a step that does
         // not exist are never used)
         __syncthreads();
-        load_a(s + 1);
+        load_a(araw, asc, s + 1);
+        half8_t afn[NA];
 #pragma unroll
         for (int n = 0; n < NB; n++) {
 #pragma unroll
           for (int i = 0; i < NV; i++)
             acc[i][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bf[n], af[i], acc[i][n], 0, 0, 0);
-          load_bf(s + 1, n, 0);
+          load_bf(bf, s + 1, n, 0);
+          // the next step's first sub-step: its scales, then row group n - 4
+          if (n == NB / 2 - 1) cvt_scales();
+          if (n >= NB / 2 && n - NB / 2 < NV) afn[n - NB / 2] = decode8_e2m1_f16(araw[n - NB / 2][0], as2[n - NB / 2][0]);
         }
+#pragma unroll
+        for (int i = 0; i < NV; i++) af[i] = afn[i];
         __builtin_amdgcn_sched_barrier(0);
       }
       if constexpr (NV > 0) {
         // lane (rr, q) holds, for row group i, output row 16 c + 64 i + rr and the four
-        // columns 4 q .. 4 q + 3 of each 16-column group n
+        // columns 4 q .. 4 q + 3 of each 16-column group n.  The lane terms come from an
+        // opaque copy of the lane id, so that the compiler does not hoist the epilogue's
+        // address arithmetic out of the step loop (it would spill it there, and the reload
+        // would then wait for this item's output stores).
+        int elane = lane;
+        asm volatile("" : "+v"(elane));
+        const int q = elane >> 4, rr = elane & 15;
         float alpha;
         void* obase;
         size_t ldo;
@@ -521,7 +548,7 @@ __global__ __launch_bounds__(ns::THREADS) void k_gemm_nvfp4_stream(const typenam
       default: item(std::integral_constant<int, 0>{}); break;
     }
     cit = nit;
-    nv = nv_next;
+    nv = nv_of(nit);
   }
 }
 
