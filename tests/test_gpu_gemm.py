@@ -142,6 +142,24 @@ def test_masked_gemm_cu_limit_and_determinism():
 
 
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_masked_gemm_item_transitions(out_dtype):
+    """Groups whose row counts give each MFMA wave of the streaming kernel every count of
+    valid 16-row groups (0 to 4) and a second M tile, run with 1 and 2 CUs so that one
+    workgroup chains many items of different shapes (each item re-reads its first step's
+    fragments and runs its own specialised loop).  Every output against the oracle, and
+    bit-identical across CU limits."""
+    mm = [1, 16, 17, 48, 49, 64, 65, 113, 129, 193, 256, 257, 300, 0]
+    G, max_m, N, K = len(mm), 300, 256, 384
+    log(f"masked NVFP4 GEMM item transitions G={G} max_m={max_m} N={N} K={K} {out_dtype}")
+    wl = datagen.masked_gemm_workload(31, DEV, G=G, max_m=max_m, N=N, K=K, masked_m=mm)
+    outs = [_run_masked(wl.tensors, max_m, N, out_dtype=out_dtype, cu_limit=cl) for cl in (1, 2, 0)]
+    view = torch.int16 if out_dtype == torch.bfloat16 else torch.int32
+    for o in outs[1:]:
+        assert torch.equal(outs[0].view(view), o.view(view)), "result depends on the CU limit"
+    _check_masked(wl.tensors, outs[0], max_m, N, K, "item transitions")
+
+
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
 def test_masked_gemm_decode_many_groups(out_dtype):
     """Row capacity 8 with 256 groups (valid rows 0..8), an N tail inside a 16-column
     group, and the same bits whatever the grid."""
