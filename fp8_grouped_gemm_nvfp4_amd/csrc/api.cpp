@@ -320,6 +320,12 @@ static int check_moe(const mxg_moe_desc* d) {
   if (d->top_k > 8) return fail(MXG_ERR_UNSUPPORTED, "moe_expert_forward: top_k > 8");
   if (fp8 && d->E > 1024)
     return fail(MXG_ERR_UNSUPPORTED, "moe_expert_forward: FP8 takes at most 1024 experts");
+  // the FP8 GEMMs address an expert's rows and weights with 32-bit byte offsets
+  if (fp8 && ((unsigned long long)d->max_m * d->H >= (1ull << 32) ||
+              (unsigned long long)d->max_m * d->I * 4 >= (1ull << 32) ||
+              2ull * d->I * d->H >= (1ull << 32) ||
+              4ull * d->E * (d->H / 128) * (d->I / 128) >= (1ull << 32)))
+    return fail(MXG_ERR_UNSUPPORTED, "moe_expert_forward: FP8 needs max_m*H, 4*max_m*I, 2*I*H below 2^32");
   if (!d->x || !d->w13 || !d->w13_scale || !d->w2 || !d->w2_scale || !d->topk_ids || !d->topk_w ||
       !d->masked_m || !d->row || !d->y)
     return fail(MXG_ERR_INVALID_ARG, "moe_expert_forward: null pointer");

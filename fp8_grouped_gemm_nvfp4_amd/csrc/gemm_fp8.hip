@@ -54,9 +54,10 @@ constexpr int A_STAGE = BM * BK + BM * 4;  // codes, then the fp32 row scales
 constexpr int B_STAGE = BN * BK + 16;      // codes, then the {gate, up} block scales
 constexpr int MAX_G = STREAM_MAX_G;
 static_assert(BM == STREAM_BM, "M tile of the shared work distribution");
-// DMA instructions per data wave per step: up to 8 of activations (64 rows), 4 of weights
-// (32 rows); data wave 0 adds the activation row scales, data wave 1 the two weight
-// block scales
+// DMA instructions per data wave per step: up to 8 of activations (the 8-row groups
+// 8 pw + 32 j, so that the data waves share them evenly when masked_m is small), 4 of
+// weights (32 rows); data wave 0 adds the activation row scales, data wave 1 the two
+// weight block scales
 constexpr int A_OPS = 8, B_OPS = 4;
 }  // namespace f1
 
@@ -92,31 +93,34 @@ __global__ __launch_bounds__(f1::THREADS) void k_gemm_fp8_swiglu(const Fp8GemmAr
     const int pw = wave - MW;
     // DMA cursors: per-lane sources of the current item (rows past masked_m re-read the
     // last valid row, never stored); past the last step they stay on it
-    const uint8_t* asrc[A_OPS];
+    // byte offsets from the item's expert base (below 2^32, checked by the host)
+    uint32_t asrc[A_OPS];
+    const uint8_t* abase = p.a;
     const float* asrc_s;
     int a_n = 0;  // activation DMAs per step: 8-row groups entirely past masked_m are skipped
     auto a_setup = [&](const StreamItem& it) {
-      const uint8_t* A = p.a + (size_t)it.g * cap * K;
-      const int left = it.mm - it.m0 - 64 * pw;
-      a_n = left <= 0 ? 0 : (left >= 8 * A_OPS ? A_OPS : (left + 7) / 8);
+      abase = p.a + (size_t)it.g * cap * K;
+      const int left = it.mm - it.m0 - 8 * pw;
+      a_n = left <= 0 ? 0 : (left >= 32 * A_OPS ? A_OPS : (left + 31) / 32);
 #pragma unroll
       for (int j = 0; j < A_OPS; j++) {
-        const int r = 64 * pw + 8 * j + (lane >> 3);
+        const int r = 8 * pw + 32 * j + (lane >> 3);
         const int row = it.m0 + r < it.mm ? it.m0 + r : it.mm - 1;
-        asrc[j] = A + (size_t)row * K + (((lane & 7) ^ f1_swz(r)) << 4);
+        asrc[j] = (uint32_t)row * K + (((lane & 7) ^ f1_swz(r)) << 4);
       }
       const int rs = it.m0 + 4 * lane < capS - 4 ? it.m0 + 4 * lane : capS - 4;
       asrc_s = p.a_s + (size_t)it.g * KB * capS + rs;
     };
-    const uint8_t* bsrc[B_OPS];
+    uint32_t bsrc[B_OPS];
+    const uint8_t* bbase = p.b;
     const float* bsrc_s;
     auto b_setup = [&](const StreamItem& it) {
-      const uint8_t* B = p.b + (size_t)it.g * N * K;
+      bbase = p.b + (size_t)it.g * N * K;
 #pragma unroll
       for (int j = 0; j < B_OPS; j++) {
         const int r = 32 * pw + 8 * j + (lane >> 3);
         const int brow = r < HN ? it.n0 + r : I + it.n0 + (r - HN);
-        bsrc[j] = B + (size_t)brow * K + (((lane & 7) ^ f1_swz(r)) << 4);
+        bsrc[j] = (uint32_t)brow * K + (((lane & 7) ^ f1_swz(r)) << 4);
       }
       const int blk = (lane == 0 ? it.n0 : I + it.n0) / 128;
       bsrc_s = p.b_s + ((size_t)it.g * (N / 128) + blk) * KB;
@@ -127,7 +131,7 @@ __global__ __launch_bounds__(f1::THREADS) void k_gemm_fp8_swiglu(const Fp8GemmAr
       uint8_t* st = ringA + a_st * A_STAGE;
 #pragma unroll
       for (int j = 0; j < A_OPS; j++)
-        if (j < a_n) dma16(asrc[j] + a_kb * BK, st + (64 * pw + 8 * j) * BK);
+        if (j < a_n) dma16_s(abase, asrc[j] + a_kb * BK, st + (8 * pw + 32 * j) * BK);
       if (pw == 0) dma16(asrc_s + (size_t)a_kb * capS, st + BM * BK);
       a_st ^= 1;
       if (a_step + 1 < nsteps) {
@@ -141,7 +145,7 @@ __global__ __launch_bounds__(f1::THREADS) void k_gemm_fp8_swiglu(const Fp8GemmAr
     auto issue_b = [&]() {  // B(step) into stage step % SB: B_OPS (+ 1) instructions
       uint8_t* st = ringB + b_st * B_STAGE;
 #pragma unroll
-      for (int j = 0; j < B_OPS; j++) dma16(bsrc[j] + b_kb * BK, st + (32 * pw + 8 * j) * BK);
+      for (int j = 0; j < B_OPS; j++) dma16_s(bbase, bsrc[j] + b_kb * BK, st + (32 * pw + 8 * j) * BK);
       if (pw == 1 && lane < 2) dma4(bsrc_s + b_kb, st + BN * BK);
       b_st = b_st + 1 == SB ? 0 : b_st + 1;
       if (b_step + 1 < nsteps) {
@@ -257,6 +261,11 @@ __global__ __launch_bounds__(f1::THREADS) void k_gemm_fp8_swiglu(const Fp8GemmAr
       // SwiGLU in registers: lanes 2c and 2c+1 hold neighbouring columns of the same four
       // rows; one swap gives each lane both columns of two rows (rows +odd and +2+odd)
       if (nv > 0) {
+        // the lane terms come from an opaque copy, so the compiler does not keep them
+        // live (or spilled) across the step loop
+        int el = lane;
+        asm volatile("" : "+v"(el));
+        const int q = el >> 4, rr = el & 15, odd = el & 1;
         uint16_t* H = (uint16_t*)p.out;
         uint16_t* scratch_row = H + (size_t)G * cap * RS;
 #pragma unroll
@@ -313,6 +322,9 @@ static hipError_t launch_fp8_swiglu(Fp8GemmArgs p, int cu_limit, hipStream_t s) 
       p.a_s_stride < p.max_m || p.a_s_stride < 4)
     return hipErrorNotSupported;
   if ((long long)p.G * ((p.max_m + BM - 1) / BM) * ((p.N / 2) / HN) > 0x7FFFFFFFLL) return hipErrorNotSupported;
+  // the DMA offsets from an expert's base are 32-bit
+  if ((unsigned long long)p.max_m * p.K >= (1ull << 32) || (unsigned long long)p.N * p.K >= (1ull << 32))
+    return hipErrorNotSupported;
   const void* k = (const void*)k_gemm_fp8_swiglu<DB, SPLIT, DBG>;
   const int grid = resident_grid(k, THREADS, cu_limit);
   if (grid <= 0) return hipErrorInvalidValue;
@@ -351,12 +363,13 @@ namespace f2 {
 constexpr int BM = 256, BK = 64;
 constexpr int WAVES = 8, THREADS = WAVES * 64;
 constexpr int A_STAGE = BM * BK * 2;  // bf16 h rows, 128 bytes each
-constexpr int A_OPS = 4;              // h DMAs per wave per step (32 rows)
+constexpr int DW = 4;                 // waves 0..3 issue every DMA
+constexpr int A_OPS = 8;              // h DMAs per issuing wave per step (64 rows)
 template <int NBW>
 struct Cfg {
   static constexpr int BN = 32 * NBW;              // two waves across, 16 * NBW columns each
   static constexpr int B_STAGE = BN * BK + 16;     // e4m3 W2 rows, 64 bytes each, then two block scales
-  static constexpr int B_OPS = BN * BK / (WAVES * 1024);  // weight DMAs per wave per step
+  static constexpr int B_OPS = BN * BK / (DW * 1024);  // weight DMAs per issuing wave per step
 };
 }  // namespace f2
 
@@ -412,30 +425,34 @@ __global__ __launch_bounds__(f2::THREADS) void k_gemm_bf16_fp8w(const Fp8GemmArg
 
   auto item_at = [&](int k) { return stream_item(bx + k * grid, tiles_n, G, tprefix, mm_s, BN); };
 
-  const uint8_t* asrc[A_OPS];
+  // DMA sources: byte offsets from the item's expert base (below 2^32, checked by the host)
+  uint32_t asrc[A_OPS];
+  const uint8_t* abase = p.a;
   int a_n = 0;
   auto a_setup = [&](const StreamItem& it) {
-    const uint8_t* A = p.a + (size_t)it.g * cap * K * 2;
-    const int left = it.mm - it.m0 - 32 * wave;
+    abase = p.a + (size_t)it.g * cap * K * 2;
+    const int left = it.mm - it.m0 - 64 * wave;
     a_n = left <= 0 ? 0 : (left >= 8 * A_OPS ? A_OPS : (left + 7) / 8);
 #pragma unroll
     for (int j = 0; j < A_OPS; j++) {
-      const int r = 32 * wave + 8 * j + (lane >> 3);
+      const int r = 64 * wave + 8 * j + (lane >> 3);
       const int row = it.m0 + r < it.mm ? it.m0 + r : it.mm - 1;
-      asrc[j] = A + (size_t)row * K * 2 + (((lane & 7) ^ f1_swz(r)) << 4);
+      asrc[j] = (uint32_t)row * K * 2 + (((lane & 7) ^ f1_swz(r)) << 4);
     }
   };
-  // wave w DMAs weight rows 16 * (B_OPS * w + j) + lane / 4; lanes 0 and 1 of wave 1 the
-  // scale blocks of the two column halves
-  const uint8_t* bsrc[B_OPS];
-  const float* bsrc_s;
+  // issuing wave w DMAs weight rows 16 * (B_OPS * w + j) + lane / 4; lanes 0 and 1 of
+  // wave 1 the scale blocks of the two column halves
+  uint32_t bsrc[B_OPS];
+  const uint8_t* bbase = p.b;
+  uint32_t bsrc_s;  // byte offset of the item's first scale from b_s
   auto b_setup = [&](const StreamItem& it) {
+    bbase = p.b + (size_t)it.g * N * WK;
 #pragma unroll
     for (int j = 0; j < B_OPS; j++) {
       const int r = 16 * (B_OPS * wave + j) + (lane >> 2);
-      bsrc[j] = p.b + ((size_t)it.g * N + it.n0 + r) * WK + (((lane & 3) ^ f2_swz_b(r)) << 4);
+      bsrc[j] = (uint32_t)(it.n0 + r) * WK + (((lane & 3) ^ f2_swz_b(r)) << 4);
     }
-    bsrc_s = p.b_s + ((size_t)it.g * (N / 128) + (it.n0 + (lane & 1) * WCOLS) / 128) * KB;
+    bsrc_s = 4u * (((uint32_t)it.g * (N / 128) + (it.n0 + (lane & 1) * WCOLS) / 128) * KB);
   };
   int a_k = 0, a_kt = 0, a_step = 0, a_st = 0;
   int b_k = 0, b_kt = 0, b_step = 0, b_st = 0;
@@ -443,7 +460,7 @@ __global__ __launch_bounds__(f2::THREADS) void k_gemm_bf16_fp8w(const Fp8GemmArg
     uint8_t* st = ringA + a_st * A_STAGE;
 #pragma unroll
     for (int j = 0; j < A_OPS; j++)
-      if (j < a_n) dma16(asrc[j] + a_kt * (BK * 2), st + (32 * wave + 8 * j) * (BK * 2));
+      if (j < a_n) dma16_s(abase, asrc[j] + a_kt * (BK * 2), st + (64 * wave + 8 * j) * (BK * 2));
     a_st ^= 1;
     if (a_step + 1 < nsteps) {
       a_step++;
@@ -457,8 +474,8 @@ __global__ __launch_bounds__(f2::THREADS) void k_gemm_bf16_fp8w(const Fp8GemmArg
     uint8_t* st = ringB + b_st * B_STAGE;
     const int wkt = b_kt < WKT ? b_kt : b_kt - WKT;  // W2 step of A step b_kt
 #pragma unroll
-    for (int j = 0; j < B_OPS; j++) dma16(bsrc[j] + wkt * BK, st + 16 * (B_OPS * wave + j) * BK);
-    if (wave == 1 && lane < 2) dma4(bsrc_s + (wkt >> 1), st + BN * BK);
+    for (int j = 0; j < B_OPS; j++) dma16_s(bbase, bsrc[j] + wkt * BK, st + 16 * (B_OPS * wave + j) * BK);
+    if (wave == 1 && lane < 2) dma4_s(p.b_s, bsrc_s + 4 * (wkt >> 1), st + BN * BK);
     b_st = b_st + 1 == SB ? 0 : b_st + 1;
     if (b_step + 1 < nsteps) {
       b_step++;
@@ -469,15 +486,19 @@ __global__ __launch_bounds__(f2::THREADS) void k_gemm_bf16_fp8w(const Fp8GemmArg
     }
   };
 
-  {
+  // Waves 0..3 issue every DMA while their SIMD partners 4..7 go straight to the MFMAs
+  // after each barrier, which staggers the two waves of a SIMD (spreading the DMAs over
+  // all eight waves measured 4% slower).
+  const bool dw = wave < DW;
+  if (dw) {
     const StreamItem it0 = item_at(0);
     a_setup(it0);
     b_setup(it0);
-  }
 #pragma unroll
-  for (int i = -DB; i < 0; i++) {
-    if (i + 1 >= 0) issue_a();
-    issue_b();
+    for (int i = -DB; i < 0; i++) {
+      if (i + 1 >= 0) issue_a();
+      issue_b();
+    }
   }
 
   // acc: the item's sums in units of the current block scale c_cur (0 before the first
@@ -512,14 +533,16 @@ __global__ __launch_bounds__(f2::THREADS) void k_gemm_bf16_fp8w(const Fp8GemmArg
 
   for (int s = 0; s < nsteps; s++) {
     if (wave == 1) wait_vmcnt<B_OPS + 1>();
-    else wait_vmcnt<B_OPS>();
+    else if (dw) wait_vmcnt<B_OPS>();
     __syncthreads();
     if (pend) {
       store_out();
       pend = false;
     }
-    issue_a();
-    issue_b();
+    if (dw) {
+      issue_a();
+      issue_b();
+    }
 
     const bool active = cit.m0 + 16 * wm < cit.mm;
     const uint8_t* Bs = ringB + c_sb * B_STAGE;
@@ -616,6 +639,11 @@ hipError_t gemm_bf16_fp8w(Fp8GemmArgs p, int cu_limit, hipStream_t s) {
   if (p.G <= 0 || p.max_m <= 0 || p.N <= 0 || p.K <= 0) return hipSuccess;
   if (p.G > f1::MAX_G || p.N % 128 != 0 || p.K % 128 != 0) return hipErrorNotSupported;
   if (p.b_k && (p.b_k % 128 != 0 || (p.K != p.b_k && p.K != 2 * p.b_k))) return hipErrorNotSupported;
+  // the DMA offsets (from an expert's base, and of the scales from b_s) are 32-bit
+  const unsigned long long wk = p.b_k ? p.b_k : p.K;
+  if ((unsigned long long)p.max_m * p.K * 2 >= (1ull << 32) || (unsigned long long)p.N * wk >= (1ull << 32) ||
+      4ull * p.G * (p.N / 128) * (wk / 128) >= (1ull << 32))
+    return hipErrorNotSupported;
   // 256 columns per item where N allows it (half the h re-reads), else 128
   if (p.N % 256 == 0) return launch_bf16_fp8w<8, 4>(p, cu_limit, s);
   return launch_bf16_fp8w<4, 6>(p, cu_limit, s);

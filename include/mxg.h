@@ -337,7 +337,9 @@ int moe_interleave_w13(const uint8_t* src, uint8_t* dst, int E, int I, int row_b
  *            result does not depend on the layout: y is bit-identical for the same
  *            logical weights.
  * Requirements: H % 128 == 0, I % 128 == 0, 1 <= top_k <= 8, max_m >= 1; both FP8
- * precisions also E <= 1024 (else MXG_ERR_UNSUPPORTED).
+ * precisions also E <= 1024 and max_m*H, 4*max_m*I and 2*I*H below 2^32 (the GEMMs
+ * address an expert's rows and weights with 32-bit byte offsets), else
+ * MXG_ERR_UNSUPPORTED.
  * Workspace: ws of at least moe_expert_forward_workspace_size(desc) bytes,
  * 256-byte aligned, device; its regions hold the gathered activations, h and
  * the GEMM2 output (offsets from moe_expert_forward_workspace_layout).

@@ -169,6 +169,11 @@ def test_moe_fp8_workspace_layout_and_expert_limit():
     for E, want in ((1024, mxg.MXG_OK), (1025, mxg.MXG_ERR_UNSUPPORTED)):
         d = _desc(precision=mxg.MXG_MOE_FP8_BLOCK128, E=E)
         assert L.moe_expert_forward_workspace_layout(ctypes.byref(d), off) == want, E
+    # an expert's h rows (4 * max_m * I bytes with both planes) stay below 2^32
+    for mm, want in ((524287, mxg.MXG_OK), (524288, mxg.MXG_ERR_UNSUPPORTED)):
+        for prec in (mxg.MXG_MOE_FP8_BLOCK128, mxg.MXG_MOE_FP8_BLOCK128_F32H):
+            d = _desc(precision=prec, max_m=mm)
+            assert L.moe_expert_forward_workspace_layout(ctypes.byref(d), off) == want, (mm, prec)
 
 
 def test_moe_workspace_layout_and_rejects():
