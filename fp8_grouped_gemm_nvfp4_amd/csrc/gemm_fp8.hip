@@ -30,9 +30,9 @@ namespace mxg {
 // masked_m <= 256.
 //
 // Operands travel from HBM into LDS by DMA through two rings that run on across item
-// boundaries: activations (and their row scales) one step ahead, weights (and the two
-// block scales) DB steps ahead, since they come from HBM while the activations are
-// mostly L2 hits.  One step is one 128-wide K block.  Activation rows past masked_m
+// boundaries: activations (and their row scales) two steps ahead, so that a step never
+// waits out the round trip of a DMA issued in it, and weights (and the two block scales)
+// DB = 2 steps ahead (the LDS holds three activation and three weight stages).  One step is one 128-wide K block.  Activation rows past masked_m
 // are not fetched at all in 8-row groups (the rest re-read the last valid row).  In LDS, 128-byte row r holds
 // its eight 16-byte chunks XOR-permuted by (r ^ r >> 3) & 7, which keeps the MFMA
 // operand reads free of bank conflicts.
@@ -44,13 +44,34 @@ namespace mxg {
 // SwiGLU epilogue runs in registers; interleaving the row groups keeps every MFMA wave
 // busy when masked_m <= 128, and row groups that are entirely masked skip their MFMAs.
 #ifndef MXG_F1_DB
-#define MXG_F1_DB 4
+#define MXG_F1_DB 2
 #endif
+// Wait until at most n (0..14) of this wave's vector memory operations are outstanding.
+__device__ __forceinline__ void wait_vmcnt_le(int n) {
+  switch (n) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<1>(); break;
+    case 2: wait_vmcnt<2>(); break;
+    case 3: wait_vmcnt<3>(); break;
+    case 4: wait_vmcnt<4>(); break;
+    case 5: wait_vmcnt<5>(); break;
+    case 6: wait_vmcnt<6>(); break;
+    case 7: wait_vmcnt<7>(); break;
+    case 8: wait_vmcnt<8>(); break;
+    case 9: wait_vmcnt<9>(); break;
+    case 10: wait_vmcnt<10>(); break;
+    case 11: wait_vmcnt<11>(); break;
+    case 12: wait_vmcnt<12>(); break;
+    case 13: wait_vmcnt<13>(); break;
+    default: wait_vmcnt<14>(); break;
+  }
+}
 namespace f1 {
 constexpr int BM = 256, BN = 128, HN = BN / 2, BK = 128;
 constexpr int MW = 8, DW = 4;  // MFMA waves, data waves
 constexpr int WAVES = MW + DW, THREADS = WAVES * 64;
 constexpr int A_STAGE = BM * BK + BM * 4;  // codes, then the fp32 row scales
+constexpr int SA = 3;                      // activation slots: two steps in flight
 constexpr int B_STAGE = BN * BK + 16;      // codes, then the {gate, up} block scales
 constexpr int MAX_G = STREAM_MAX_G;
 static_assert(BM == STREAM_BM, "M tile of the shared work distribution");
@@ -59,6 +80,7 @@ static_assert(BM == STREAM_BM, "M tile of the shared work distribution");
 // weights (32 rows); data wave 0 adds the activation row scales, data wave 1 the two
 // weight block scales
 constexpr int A_OPS = 8, B_OPS = 4;
+static_assert(A_OPS + B_OPS + 2 <= 14, "one step's DMAs fit the waits of wait_vmcnt_le");
 }  // namespace f1
 
 __device__ __forceinline__ int f1_swz(int r) { return (r ^ (r >> 3)) & 7; }
@@ -67,8 +89,8 @@ template <int DB, bool SPLIT, bool DBG>
 __global__ __launch_bounds__(f1::THREADS) void k_gemm_fp8_swiglu(const Fp8GemmArgs p) {
   using namespace f1;
   constexpr int SB = DB + 1;
-  static_assert(DB >= 2, "B(s + 1) must be issued before A(s)");
-  __shared__ __attribute__((aligned(16))) uint8_t ringA[2 * A_STAGE];
+  static_assert(DB >= 2, "B(s + 1) must be issued before A(s + 1)");
+  __shared__ __attribute__((aligned(16))) uint8_t ringA[SA * A_STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t ringB[SB * B_STAGE];
   __shared__ int tprefix[MAX_G + 1];
   __shared__ int mm_s[MAX_G];
@@ -89,7 +111,7 @@ __global__ __launch_bounds__(f1::THREADS) void k_gemm_fp8_swiglu(const Fp8GemmAr
   auto item_at = [&](int k) { return stream_item(bx + k * grid, tiles_n, G, tprefix, mm_s, HN); };
 
   if (wave >= MW) {
-    // ======== data waves: activations one step ahead, weights DB steps ahead ========
+    // ======== data waves: activations two steps ahead, weights DB steps ahead ========
     const int pw = wave - MW;
     // DMA cursors: per-lane sources of the current item (rows past masked_m re-read the
     // last valid row, never stored); past the last step they stay on it
@@ -127,13 +149,15 @@ __global__ __launch_bounds__(f1::THREADS) void k_gemm_fp8_swiglu(const Fp8GemmAr
     };
     int a_k = 0, a_kb = 0, a_step = 0, a_st = 0;
     int b_k = 0, b_kb = 0, b_step = 0, b_st = 0;
-    auto issue_a = [&]() {  // A(step) into slot step & 1
+    int a_cnt = 0;  // DMA instructions of the last issue_a
+    auto issue_a = [&]() {  // A(step) into slot step % SA
       uint8_t* st = ringA + a_st * A_STAGE;
 #pragma unroll
       for (int j = 0; j < A_OPS; j++)
         if (j < a_n) dma16_s(abase, asrc[j] + a_kb * BK, st + (8 * pw + 32 * j) * BK);
       if (pw == 0) dma16(asrc_s + (size_t)a_kb * capS, st + BM * BK);
-      a_st ^= 1;
+      a_cnt = a_n + (pw == 0);
+      a_st = a_st == SA - 1 ? 0 : a_st + 1;
       if (a_step + 1 < nsteps) {
         a_step++;
         if (++a_kb == KB) {
@@ -164,17 +188,17 @@ __global__ __launch_bounds__(f1::THREADS) void k_gemm_fp8_swiglu(const Fp8GemmAr
 #pragma unroll
     for (int i = 0; i < DB; i++) issue_b();
     issue_a();
-    wait_vmcnt<0>();  // B(0 .. DB - 1) and A(0)
+    issue_a();
+    wait_vmcnt_le(a_cnt);  // B(0 .. DB - 1) and A(0); A(1) may stay outstanding
     for (int s = 0; s < nsteps; s++) {
       // A(s) and B(s) are in LDS, and the MFMA waves are done with step s - 1, whose
       // activation slot and weight stage the next issues overwrite
       __syncthreads();
-      issue_a();  // A(s + 1)
+      issue_a();  // A(s + 2)
       issue_b();  // B(s + DB)
-      // A(s + 1) and everything issued before it (B(s + 1) among them) land before the
-      // next barrier; only this step's weight DMAs may stay outstanding
-      if (pw == 1) wait_vmcnt<B_OPS + 1>();
-      else wait_vmcnt<B_OPS>();
+      // everything issued before this step (A(s + 1) and B(s + 1) among it) lands before
+      // the next barrier; only this step's DMAs may stay outstanding
+      wait_vmcnt_le(a_cnt + B_OPS + (pw == 1));
     }
     wait_vmcnt<0>();  // the trailing re-reads land before the workgroup ends
     return;
@@ -191,7 +215,7 @@ __global__ __launch_bounds__(f1::THREADS) void k_gemm_fp8_swiglu(const Fp8GemmAr
     for (int n = 0; n < 8; n++) acc[i][n] = float4_t{0.f, 0.f, 0.f, 0.f};
 
   StreamItem cit = item_at(0);
-  int c_k = 0, c_kb = 0, c_sb = 0;
+  int c_k = 0, c_kb = 0, c_sb = 0, c_sa = 0;
   const int q = lane >> 4, rr = lane & 15, odd = lane & 1;
 
   // h rows: with SPLIT they are 2I wide, hi = bf16(h) in columns [0, I), lo = bf16(h - hi)
@@ -222,7 +246,7 @@ __global__ __launch_bounds__(f1::THREADS) void k_gemm_fp8_swiglu(const Fp8GemmAr
     const int left = cit.mm - cit.m0 - 16 * wave;  // valid rows from this wave's first row
     const int nv = left <= 0 ? 0 : (left > 128 ? 2 : 1);
     if (nv > 0) {
-      const uint8_t* As = ringA + (s & 1) * A_STAGE;
+      const uint8_t* As = ringA + c_sa * A_STAGE;
       const uint8_t* Bs = ringB + c_sb * B_STAGE;
       int8v_t af[2];
       float4_t sw[2][2];  // row scale x {gate, up} block scale
@@ -256,6 +280,7 @@ __global__ __launch_bounds__(f1::THREADS) void k_gemm_fp8_swiglu(const Fp8GemmAr
       }
     }
     c_sb = c_sb + 1 == SB ? 0 : c_sb + 1;
+    c_sa = c_sa == SA - 1 ? 0 : c_sa + 1;
 
     if (++c_kb == KB) {
       // SwiGLU in registers: lanes 2c and 2c+1 hold neighbouring columns of the same four
