@@ -22,10 +22,34 @@ import oracle
 from _helpers import assert_within, bf16_from_bits_np, log, ulp_bf16, ulp_f32, within
 
 
-def swiglu_tol(g, u, Sg, Su, h):
-    tg = 1e-5 * Sg + ulp_f32(g)
-    tu = 1e-5 * Su + ulp_f32(u)
+def swiglu_tol(g, u, Sg, Su, h, xg=0.0, xu=0.0):
+    """h tolerance from the GEMM1 tolerances of gate and up (xg, xu: their extra terms)."""
+    tg = 1e-5 * Sg + ulp_f32(g) + xg
+    tu = 1e-5 * Su + ulp_f32(u) + xu
     return 1.1 * (np.abs(u) + tu) * tg + np.abs(g * expit(g)) * tu + 8 * ulp_f32(h)
+
+
+def fp8_mfma_extra(qa, sa, qb, sb):
+    """Extra GEMM1 allowance for the scaled fp8 MFMA, [len(qa), len(qb)].  The instruction
+    sums each group of 8 consecutive K products aligned to the group's largest product and
+    drops the bits below 2^-14 of it (measured on gfx950: 1 + 2^-14 survives, 1 + 2^-15
+    and seven 2^-18 products beside a 1 are lost, always toward -inf), so a group loses
+    less than 8 * 2^-14 of its largest |product|.  That product is at most max|a| * max|b|
+    over the group, and the block's two scales multiply the group sums: the bound is
+    2^-11 * sum_blocks |sa * sb| * sum_groups max|a| * max|b|.  qa [M, K] and qb [N, K]
+    e4m3 codes, sa [M, K/128], sb [N/128, K/128]."""
+    mag = np.abs(oracle.e4m3_table())
+    M, K = qa.shape
+    N = qb.shape[0]
+    # |e4m3| grows with the code's low 7 bits, so the group maxima come from the bytes
+    amax = mag[(np.asarray(qa) & 0x7F).reshape(M, K // 8, 8).max(-1)]
+    bmax = mag[(np.asarray(qb) & 0x7F).reshape(N, K // 8, 8).max(-1)]
+    out = np.zeros((M, N))
+    for b in range(K // 128):
+        g = slice(16 * b, 16 * b + 16)
+        out += (amax[:, g] @ bmax[:, g].T) * np.abs(np.asarray(sa, np.float64)[:, b])[:, None] \
+            * np.repeat(np.abs(np.asarray(sb, np.float64)[:, b]), 128)[None, :N]
+    return 2.0 ** -11 * out
 
 
 def tokens_subset(T, n, seed, row=None, max_m=None, n_deep=0):
@@ -51,10 +75,19 @@ def _slots_by_expert(ids, row, max_m, toks):
     return by_e
 
 
-def _check_g1(g1_gpu, gu, S1, what):
-    """GEMM1 debug stage: the GPU's fp32 gate/up sums against the oracle's, 1e-5 S + 1 fp32 ulp."""
-    if g1_gpu is not None:
-        assert_within(g1_gpu.astype(np.float64), gu, S1, what, ulp=ulp_f32)
+def _check_g1(g1_gpu, gu, S1, what, extra=None):
+    """GEMM1 debug stage: the GPU's fp32 gate/up sums against the oracle's, 1e-5 S + 1 fp32
+    ulp.  With `extra` (the fp8 MFMA's allowance) every sum must lie within that bound plus
+    `extra`, and at least 99% within the bound alone."""
+    if g1_gpu is None:
+        return
+    g = g1_gpu.astype(np.float64)
+    if extra is None:
+        assert_within(g, gu, S1, what, ulp=ulp_f32)
+        return
+    assert_within(g, gu, S1, what, ulp=ulp_f32, extra=extra)
+    frac = within(g, gu, S1, ulp=ulp_f32).mean()
+    assert frac >= 0.99, f"{what}: only {frac * 100:.2f}% of the sums within 1e-5 S + 1 ulp"
 
 
 def check_nvfp4_layer(*, x, g_x, ids, w, row, max_m, I, weights, g_w13, g_w2, g_h, gathered, h_pre,
@@ -124,16 +157,17 @@ def check_fp8_layer(*, xq, xs, ids, w, row, max_m, I, weights, gathered, h_plane
         assert np.array_equal(a[rows], xq[toks[pos]]) and np.array_equal(a_s[rows], xs[toks[pos]]), \
             f"{what}: gathered x of expert {e}"
         gu, S1 = oracle.gemm_fp8_block(xq, xs, w13, w13_s, rows=toks[pos])
-        _check_g1(None if g1 is None else g1(e)[rows], gu, S1, f"{what}: GEMM1 of expert {e}")
+        x1 = fp8_mfma_extra(xq[toks[pos]], xs[toks[pos]], w13, w13_s)
+        _check_g1(None if g1 is None else g1(e)[rows], gu, S1, f"{what}: GEMM1 of expert {e}", extra=x1)
         g, u = gu[:, :I], gu[:, I:]
         hstar = oracle.swiglu(gu, I)
         hb = h_planes(e)[rows]
         if f32h:
-            tol_h = swiglu_tol(g, u, S1[:, :I], S1[:, I:], hstar)
+            tol_h = swiglu_tol(g, u, S1[:, :I], S1[:, I:], hstar, x1[:, :I], x1[:, I:])
             tol = tol_h + 2.0 ** -17 * np.abs(hstar)
             hv = bf16_from_bits_np(hb[:, :I]) + bf16_from_bits_np(hb[:, I:])
         else:
-            tol = swiglu_tol(g, u, S1[:, :I], S1[:, I:], hstar) + ulp_bf16(hstar)
+            tol = swiglu_tol(g, u, S1[:, :I], S1[:, I:], hstar, x1[:, :I], x1[:, I:]) + ulp_bf16(hstar)
             hv = bf16_from_bits_np(hb)
         err = np.abs(hv - hstar)
         assert np.all(err <= tol), f"{what}: h of expert {e}: max excess {np.max(err - tol)}"

@@ -222,6 +222,14 @@ def test_moe_fp8_varied_w2_scales(H):
     _run_fp8(256, H, 384, 3002 + H, None, vary_w2_scales=True)
 
 
+@pytest.mark.parametrize("H,I,f32h", [(128, 128, False), (256, 128, False), (128, 256, True)])
+def test_moe_fp8_short_items(H, I, f32h):
+    # GEMM1 items of one or two 128-K steps: its activation ring runs two steps ahead, so
+    # its DMAs cross one or two item boundaries; GEMM2 items of two to four 64-K steps
+    log(f"FP8 MoE with short items: T=256 H={H} I={I} E=256{' hi/lo h' if f32h else ''}, every token")
+    _run_fp8(256, H, I, 3020 + H + I, None, f32h=f32h)
+
+
 def test_moe_fp8_full_precision_intermediate():
     log("FP8 MoE with hi/lo bf16 intermediate: T=256 H=512 I=384 E=256, every token")
     _run_fp8(256, 512, 384, 3010, None, f32h=True, e2e=64)
