@@ -320,12 +320,12 @@ static int check_moe(const mxg_moe_desc* d) {
   if (d->top_k > 8) return fail(MXG_ERR_UNSUPPORTED, "moe_expert_forward: top_k > 8");
   if (fp8 && d->E > 1024)
     return fail(MXG_ERR_UNSUPPORTED, "moe_expert_forward: FP8 takes at most 1024 experts");
-  // the FP8 GEMMs address an expert's rows and weights with 32-bit byte offsets
-  if (fp8 && ((unsigned long long)d->max_m * d->H >= (1ull << 32) ||
+  // the FP8 GEMMs address token rows, an expert's rows and its weights with 32-bit byte offsets
+  if (fp8 && ((unsigned long long)d->T * d->H >= (1ull << 32) ||
               (unsigned long long)d->max_m * d->I * 4 >= (1ull << 32) ||
               2ull * d->I * d->H >= (1ull << 32) ||
               4ull * d->E * (d->H / 128) * (d->I / 128) >= (1ull << 32)))
-    return fail(MXG_ERR_UNSUPPORTED, "moe_expert_forward: FP8 needs max_m*H, 4*max_m*I, 2*I*H below 2^32");
+    return fail(MXG_ERR_UNSUPPORTED, "moe_expert_forward: FP8 needs T*H, 4*max_m*I, 2*I*H below 2^32");
   if (!d->x || !d->w13 || !d->w13_scale || !d->w2 || !d->w2_scale || !d->topk_ids || !d->topk_w ||
       !d->masked_m || !d->row || !d->y)
     return fail(MXG_ERR_INVALID_ARG, "moe_expert_forward: null pointer");
@@ -353,7 +353,7 @@ int moe_expert_forward_workspace_layout(const mxg_moe_desc* d, size_t* off) {
   size_t sz[5];
   if (d->precision != MXG_MOE_NVFP4) {
     const size_t planes = d->precision == MXG_MOE_FP8_BLOCK128_F32H ? 2 : 1;
-    sz[0] = rows * d->H;                     // e4m3 activations
+    sz[0] = rows * 4;                        // the token of each expert row (int32)
     sz[1] = (size_t)d->E * (d->H / 128) * mxg::fp8_scale_stride(d->max_m) * 4;  // fp32 1x128 scales
     sz[2] = (rows + 1) * d->I * 2 * planes;  // bf16 h (hi, lo), plus one row that masked rows' stores land in
     sz[3] = 0;
@@ -394,13 +394,14 @@ int moe_expert_forward(const mxg_moe_desc* d, void* ws, size_t ws_bytes, void* s
   hipError_t e;
   if (d->precision != MXG_MOE_NVFP4) {
     const int split = d->precision == MXG_MOE_FP8_BLOCK128_F32H;
-    uint8_t* a = w + off[0];
+    int32_t* a_tok = (int32_t*)(w + off[0]);
     float* a_s = (float*)(w + off[1]);
     uint16_t* h = (uint16_t*)(w + off[2]);
-    e = mxg::gather_fp8((const uint8_t*)d->x, d->x_scale, T, H, d->topk_ids, d->row, k, mm, a, a_s, s);
-    if (e != hipSuccess) return hip_status(e, "gather_fp8");
+    e = mxg::fp8_expert_rows(d->x_scale, T, H, d->topk_ids, d->row, k, E, mm, d->masked_m, a_tok, a_s, s);
+    if (e != hipSuccess) return hip_status(e, "fp8_expert_rows");
     mxg::Fp8GemmArgs p1{};
-    p1.a = a; p1.a_s = a_s; p1.b = d->w13; p1.b_s = (const float*)d->w13_scale; p1.out = h;
+    p1.a = (const uint8_t*)d->x; p1.a_tok = a_tok; p1.tokens = T;
+    p1.a_s = a_s; p1.b = d->w13; p1.b_s = (const float*)d->w13_scale; p1.out = h;
     p1.masked_m = d->masked_m; p1.G = E; p1.max_m = mm; p1.N = 2 * I; p1.K = H;
     p1.a_s_stride = mxg::fp8_scale_stride(mm);
     p1.h_split = split;

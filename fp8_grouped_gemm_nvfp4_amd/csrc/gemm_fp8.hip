@@ -32,10 +32,12 @@ namespace mxg {
 // Operands travel from HBM into LDS by DMA through two rings that run on across item
 // boundaries: activations (and their row scales) two steps ahead, so that a step never
 // waits out the round trip of a DMA issued in it, and weights (and the two block scales)
-// DB = 2 steps ahead (the LDS holds three activation and three weight stages).  One step is one 128-wide K block.  Activation rows past masked_m
-// are not fetched at all in 8-row groups (the rest re-read the last valid row).  In LDS, 128-byte row r holds
-// its eight 16-byte chunks XOR-permuted by (r ^ r >> 3) & 7, which keeps the MFMA
-// operand reads free of bank conflicts.
+// DB = 2 steps ahead (the LDS holds three activation and three weight stages).  One step
+// is one 128-wide K block.  Activation rows are read straight from the token rows of x
+// (a table gives each expert row's token), so they are never copied per expert.  Rows
+// past masked_m are not fetched at all in 8-row groups (the rest re-read the last valid
+// row).  In LDS, 128-byte row r holds its eight 16-byte chunks XOR-permuted by
+// (r ^ r >> 3) & 7, which keeps the MFMA operand reads free of bank conflicts.
 //
 // Waves: 12, in two roles.  Waves 8..11 (one per SIMD) issue every DMA; waves 0..7 (two
 // per SIMD) only read fragments, run MFMAs and store h.  One barrier per step hands a
@@ -80,7 +82,14 @@ static_assert(BM == STREAM_BM, "M tile of the shared work distribution");
 // weights (32 rows); data wave 0 adds the activation row scales, data wave 1 the two
 // weight block scales
 constexpr int A_OPS = 8, B_OPS = 4;
-static_assert(A_OPS + B_OPS + 2 <= 14, "one step's DMAs fit the waits of wait_vmcnt_le");
+// a data wave's DMAs in one step: activations, one scale block (activation or weight
+// scales, never both), the tokens of an item, weights
+static_assert(A_OPS + 1 + 1 + B_OPS <= 14, "one step's DMAs fit the waits of wait_vmcnt_le");
+// Activation rows are read straight from the token rows of x: each data wave DMAs the
+// tokens of its 64 rows of item k + 2 (one dword per lane) into a ring of three LDS slots
+// when it sets up item k (k >= 1; the prologue loads items 0..2), and every set-up comes
+// at least two steps after the DMA it reads, so a step's wait has covered it.
+constexpr int TOK_SLOTS = 3;
 }  // namespace f1
 
 __device__ __forceinline__ int f1_swz(int r) { return (r ^ (r >> 3)) & 7; }
@@ -94,6 +103,7 @@ __global__ __launch_bounds__(f1::THREADS) void k_gemm_fp8_swiglu(const Fp8GemmAr
   __shared__ __attribute__((aligned(16))) uint8_t ringB[SB * B_STAGE];
   __shared__ int tprefix[MAX_G + 1];
   __shared__ int mm_s[MAX_G];
+  __shared__ int tok_s[TOK_SLOTS][DW][A_OPS * 8];  // per data wave: the tokens of its rows, per item
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: branches on it are scalar
@@ -115,23 +125,36 @@ __global__ __launch_bounds__(f1::THREADS) void k_gemm_fp8_swiglu(const Fp8GemmAr
     const int pw = wave - MW;
     // DMA cursors: per-lane sources of the current item (rows past masked_m re-read the
     // last valid row, never stored); past the last step they stay on it
-    // byte offsets from the item's expert base (below 2^32, checked by the host)
+    // byte offsets of the token rows from x (below 2^32, checked by the host)
     uint32_t asrc[A_OPS];
-    const uint8_t* abase = p.a;
     const float* asrc_s;
     int a_n = 0;  // activation DMAs per step: 8-row groups entirely past masked_m are skipped
-    auto a_setup = [&](const StreamItem& it) {
-      abase = p.a + (size_t)it.g * cap * K;
+    int tok_issued = 0;  // token DMAs issued by the last a_setup (0 or 1)
+    // the tokens of this wave's rows 8 pw + 32 j + (l & 7), j = l >> 3, of item k into
+    // slot k % TOK_SLOTS (rows past masked_m take the last valid row's token)
+    auto issue_tok = [&](int k) {
+      const StreamItem it = item_at(k);
+      const int r = 8 * pw + 32 * (lane >> 3) + (lane & 7);
+      const int row = it.m0 + r < it.mm ? it.m0 + r : it.mm - 1;
+      dma4(p.a_tok + (size_t)it.g * cap + row, &tok_s[k % TOK_SLOTS][pw][0]);
+    };
+    // item k's DMA sources; its tokens are in slot k % TOK_SLOTS
+    auto a_setup = [&](int k) {
+      const StreamItem it = item_at(k);
       const int left = it.mm - it.m0 - 8 * pw;
       a_n = left <= 0 ? 0 : (left >= 32 * A_OPS ? A_OPS : (left + 31) / 32);
 #pragma unroll
       for (int j = 0; j < A_OPS; j++) {
         const int r = 8 * pw + 32 * j + (lane >> 3);
-        const int row = it.m0 + r < it.mm ? it.m0 + r : it.mm - 1;
-        asrc[j] = (uint32_t)row * K + (((lane & 7) ^ f1_swz(r)) << 4);
+        // clamped, so that any table entry addresses a row of x
+        const int t = tok_s[k % TOK_SLOTS][pw][8 * j + (lane >> 3)];
+        const int tok = t < 0 ? 0 : (t >= p.tokens ? p.tokens - 1 : t);
+        asrc[j] = (uint32_t)tok * K + (((lane & 7) ^ f1_swz(r)) << 4);
       }
       const int rs = it.m0 + 4 * lane < capS - 4 ? it.m0 + 4 * lane : capS - 4;
       asrc_s = p.a_s + (size_t)it.g * KB * capS + rs;
+      tok_issued = k >= 1 && k + 2 < n_items;  // the prologue loads the tokens of items 0..2
+      if (tok_issued) issue_tok(k + 2);
     };
     uint32_t bsrc[B_OPS];
     const uint8_t* bbase = p.b;
@@ -154,7 +177,7 @@ __global__ __launch_bounds__(f1::THREADS) void k_gemm_fp8_swiglu(const Fp8GemmAr
       uint8_t* st = ringA + a_st * A_STAGE;
 #pragma unroll
       for (int j = 0; j < A_OPS; j++)
-        if (j < a_n) dma16_s(abase, asrc[j] + a_kb * BK, st + (8 * pw + 32 * j) * BK);
+        if (j < a_n) dma16_s(p.a, asrc[j] + a_kb * BK, st + (8 * pw + 32 * j) * BK);
       if (pw == 0) dma16(asrc_s + (size_t)a_kb * capS, st + BM * BK);
       a_cnt = a_n + (pw == 0);
       a_st = a_st == SA - 1 ? 0 : a_st + 1;
@@ -162,7 +185,8 @@ __global__ __launch_bounds__(f1::THREADS) void k_gemm_fp8_swiglu(const Fp8GemmAr
         a_step++;
         if (++a_kb == KB) {
           a_kb = 0;
-          a_setup(item_at(++a_k));
+          a_setup(++a_k);
+          a_cnt += tok_issued;
         }
       }
     };
@@ -180,16 +204,17 @@ __global__ __launch_bounds__(f1::THREADS) void k_gemm_fp8_swiglu(const Fp8GemmAr
         }
       }
     };
-    {
-      const StreamItem it0 = item_at(0);
-      a_setup(it0);
-      b_setup(it0);
-    }
+    for (int k = 0; k < TOK_SLOTS && k < n_items; k++) issue_tok(k);
+    wait_vmcnt<0>();  // the tokens of items 0..2
+    a_setup(0);
+    b_setup(item_at(0));
 #pragma unroll
     for (int i = 0; i < DB; i++) issue_b();
     issue_a();
     issue_a();
-    wait_vmcnt_le(a_cnt);  // B(0 .. DB - 1) and A(0); A(1) may stay outstanding
+    // B(0 .. DB - 1), A(0) and any tokens issued with it have landed; A(1) (and tokens
+    // issued with it) may stay outstanding
+    wait_vmcnt_le(a_cnt);
     for (int s = 0; s < nsteps; s++) {
       // A(s) and B(s) are in LDS, and the MFMA waves are done with step s - 1, whose
       // activation slot and weight stage the next issues overwrite
@@ -347,8 +372,9 @@ static hipError_t launch_fp8_swiglu(Fp8GemmArgs p, int cu_limit, hipStream_t s) 
       p.a_s_stride < p.max_m || p.a_s_stride < 4)
     return hipErrorNotSupported;
   if ((long long)p.G * ((p.max_m + BM - 1) / BM) * ((p.N / 2) / HN) > 0x7FFFFFFFLL) return hipErrorNotSupported;
-  // the DMA offsets from an expert's base are 32-bit
-  if ((unsigned long long)p.max_m * p.K >= (1ull << 32) || (unsigned long long)p.N * p.K >= (1ull << 32))
+  // the DMA offsets (of token rows, and from an expert's weight base) are 32-bit
+  if ((unsigned long long)p.tokens * p.K >= (1ull << 32) || (unsigned long long)p.N * p.K >= (1ull << 32) ||
+      !p.a_tok)
     return hipErrorNotSupported;
   const void* k = (const void*)k_gemm_fp8_swiglu<DB, SPLIT, DBG>;
   const int grid = resident_grid(k, THREADS, cu_limit);

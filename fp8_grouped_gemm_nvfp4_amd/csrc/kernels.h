@@ -116,7 +116,9 @@ int resident_grid(const void* kernel, int threads, int cu_limit);
 
 // FP8 block-scaled GEMMs of the DeepSeek-V3-style expert path (masked layout).
 struct Fp8GemmArgs {
-  const uint8_t* a;     // GEMM1: e4m3 [G, max_m, K]; GEMM2: bf16 h [G, max_m, K]
+  const uint8_t* a;     // GEMM1: e4m3 token rows [T, K]; GEMM2: bf16 h [G, max_m, K]
+  const int32_t* a_tok; // GEMM1: the token of each expert row [G, max_m] (rows below masked_m)
+  int tokens;           // GEMM1: rows of a (T)
   const float* a_s;     // GEMM1: fp32 [G, K/128, a_s_stride] (row scales, transposed); GEMM2: unused
   const uint8_t* b;     // e4m3 [G, N, K]
   const float* b_s;     // fp32 [G, N/128, K/128]
@@ -169,10 +171,12 @@ hipError_t dispatch_quantize_gather_nvfp4(const uint16_t* x, int T, int H, float
 hipError_t quantize_gather_nvfp4(const uint16_t* x, int T, int H, float g_x, const int32_t* ids,
                                  const int32_t* row, int top_k, int max_m, uint8_t* a,
                                  uint8_t* a_sf, hipStream_t s);
-// a_s receives the row scales transposed: [E, H/128, fp8_scale_stride(max_m)].
-hipError_t gather_fp8(const uint8_t* xq, const float* xs, int T, int H, const int32_t* ids,
-                      const int32_t* row, int top_k, int max_m, uint8_t* a, float* a_s,
-                      hipStream_t s);
+// FP8 expert rows: a_tok [E, max_m] receives the token of every dispatched expert row,
+// a_s the row scales transposed: [E, H/128, fp8_scale_stride(max_m)] (rows below
+// masked_m; the rest are left as they were).
+hipError_t fp8_expert_rows(const float* xs, int T, int H, const int32_t* ids, const int32_t* row, int top_k,
+                           int E, int max_m, const int32_t* masked_m, int32_t* a_tok, float* a_s,
+                           hipStream_t s);
 hipError_t interleave_w13(const uint8_t* src, uint8_t* dst, int E, int I, int row_bytes, hipStream_t s);
 hipError_t combine(const float* o, const int32_t* ids, const int32_t* row, const float* w, int T,
                    int H, int top_k, int max_m, uint16_t* y, hipStream_t s);

@@ -197,36 +197,41 @@ hipError_t dispatch_quantize_gather_nvfp4(const uint16_t* x, int T, int H, float
   return hipGetLastError();
 }
 
-// FP8 rows: copy the e4m3 codes (16 bytes per thread) and the 1x128 scales of
-// token t to every dispatched expert row.  The scales are stored transposed, one
-// contiguous column of rows per (expert, 128-block), as the GEMM streams them.
-__global__ __launch_bounds__(256) void k_gather_fp8(const uint8_t* xq, const float* xs, int T, int H,
-                                                    const int32_t* ids, const int32_t* row, int top_k,
-                                                    int max_m, uint8_t* a, float* a_s) {
-  const int nc = H / 16;
-  long c = (long)blockIdx.x * 256 + threadIdx.x;
-  if (c >= (long)T * nc) return;
-  int t = (int)(c / nc), k = (int)(c % nc);
-  u32x4_t v = *(const u32x4_t*)(xq + (size_t)t * H + (size_t)k * 16);
-  bool has_scale = (k % 8) == 0;
-  float sc = has_scale ? xs[(size_t)t * (H / 128) + k / 8] : 0.0f;
-  for (int j = 0; j < top_k; j++) {
-    int e = ids[(size_t)t * top_k + j];
-    int r = row[(size_t)t * top_k + j];
-    if (r >= max_m) continue;
-    size_t dst = (size_t)e * max_m + r;
-    *(u32x4_t*)(a + dst * H + (size_t)k * 16) = v;
-    if (has_scale) a_s[((size_t)e * (H / 128) + k / 8) * fp8_scale_stride(max_m) + r] = sc;
-  }
+// FP8 expert rows.  GEMM1 reads each expert row's activations straight from its
+// token's row of x, so the rows are not copied: a_tok[e * max_m + r] is the token of
+// expert e's row r (one thread per dispatched slot), and the 1x128 scales are stored
+// transposed, one contiguous column of rows per (expert, 128-block), as the GEMM streams
+// them (one thread per (expert, block, row), reading the token through a_tok).
+__global__ __launch_bounds__(256) void k_fp8_row_tokens(const int32_t* ids, const int32_t* row, int n_slots,
+                                                        int top_k, int E, int max_m, int32_t* a_tok) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= n_slots) return;
+  const int e = ids[i], r = row[i];
+  if ((unsigned)r < (unsigned)max_m && (unsigned)e < (unsigned)E) a_tok[(size_t)e * max_m + r] = i / top_k;
 }
 
-hipError_t gather_fp8(const uint8_t* xq, const float* xs, int T, int H, const int32_t* ids,
-                      const int32_t* row, int top_k, int max_m, uint8_t* a, float* a_s,
-                      hipStream_t s) {
-  long n = (long)T * (H / 16);
-  if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_gather_fp8, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, xq, xs, T, H,
-                     ids, row, top_k, max_m, a, a_s);
+__global__ __launch_bounds__(256) void k_fp8_row_scales(const float* xs, int T, int KB, const int32_t* masked_m,
+                                                        int max_m, const int32_t* a_tok, float* a_s) {
+  const int e = blockIdx.z, kb = blockIdx.y, r = blockIdx.x * 256 + threadIdx.x;
+  int mm = masked_m[e];
+  mm = mm < 0 ? 0 : (mm > max_m ? max_m : mm);
+  if (r >= mm) return;
+  int t = a_tok[(size_t)e * max_m + r];
+  t = t < 0 ? 0 : (t >= T ? T - 1 : t);  // any table entry reads a row of xs
+  a_s[((size_t)e * KB + kb) * fp8_scale_stride(max_m) + r] = xs[(size_t)t * KB + kb];
+}
+
+hipError_t fp8_expert_rows(const float* xs, int T, int H, const int32_t* ids, const int32_t* row, int top_k,
+                           int E, int max_m, const int32_t* masked_m, int32_t* a_tok, float* a_s,
+                           hipStream_t s) {
+  const int n = T * top_k, KB = H / 128;
+  if (n == 0 || E == 0 || KB == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_fp8_row_tokens, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, ids, row, n, top_k,
+                     E, max_m, a_tok);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_fp8_row_scales, dim3((unsigned)((max_m + 255) / 256), (unsigned)KB, (unsigned)E),
+                     dim3(256), 0, s, xs, T, KB, masked_m, max_m, a_tok, a_s);
   return hipGetLastError();
 }
 

@@ -337,12 +337,13 @@ int moe_interleave_w13(const uint8_t* src, uint8_t* dst, int E, int I, int row_b
  *            result does not depend on the layout: y is bit-identical for the same
  *            logical weights.
  * Requirements: H % 128 == 0, I % 128 == 0, 1 <= top_k <= 8, max_m >= 1; both FP8
- * precisions also E <= 1024 and max_m*H, 4*max_m*I and 2*I*H below 2^32 (the GEMMs
- * address an expert's rows and weights with 32-bit byte offsets), else
+ * precisions also E <= 1024 and T*H, 4*max_m*I and 2*I*H below 2^32 (the GEMMs
+ * address token rows, an expert's rows and its weights with 32-bit byte offsets), else
  * MXG_ERR_UNSUPPORTED.
  * Workspace: ws of at least moe_expert_forward_workspace_size(desc) bytes,
- * 256-byte aligned, device; its regions hold the gathered activations, h and
- * the GEMM2 output (offsets from moe_expert_forward_workspace_layout).
+ * 256-byte aligned, device; its regions hold the expert rows' activations (FP8:
+ * their tokens, the rows being read from x), h and the GEMM2 output (offsets from
+ * moe_expert_forward_workspace_layout).
  */
 typedef struct {
   int precision;
@@ -372,7 +373,8 @@ typedef struct {
 size_t moe_expert_forward_workspace_size(const mxg_moe_desc* desc);
 
 /* Byte offsets (host array of 6) of the workspace regions:
- *   [0] gathered activations (FP8: e4m3 [E, max_m, H]; NVFP4: codes [E, max_m, H/2])
+ *   [0] expert rows (FP8: int32 [E, max_m], the token of each row below masked_m, whose
+ *       row of x GEMM1 reads; NVFP4: the gathered codes [E, max_m, H/2])
  *   [1] their scales (FP8: fp32 [E, H/128, max_m rounded up to a multiple of 4], i.e.
  *       transposed; NVFP4: e4m3 [E, max_m, H/16])
  *   [2] h (FP8: bf16 [E, max_m, I] followed by one scratch row; FP8 F32H: bf16 [E, max_m, 2I],

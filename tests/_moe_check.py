@@ -136,7 +136,8 @@ def check_nvfp4_layer(*, x, g_x, ids, w, row, max_m, I, weights, g_w13, g_w2, g_
 
 def check_fp8_layer(*, xq, xs, ids, w, row, max_m, I, weights, gathered, h_planes, y_bits, toks, what,
                     f32h=False, o_gpu=None, e2e_tokens=0, g1=None):
-    """gathered(e) -> (a e4m3 [max_m, H], a scales [max_m, H/128]); h_planes(e) -> GPU bf16
+    """gathered(e) -> (the token of each expert row [max_m], its scales [max_m, H/128]);
+    h_planes(e) -> GPU bf16
     bits [max_m, planes * I]; weights(e) -> (w13, w13 scales, w2, w2 scales).  With f32h
     the intermediate is bf16 hi + lo: h is checked against the unrounded SwiGLU, GEMM2 and
     the combine against the oracle on hi + lo, y also against the oracle's whole layer on
@@ -150,12 +151,12 @@ def check_fp8_layer(*, xq, xs, ids, w, row, max_m, I, weights, gathered, h_plane
         err2 = {"split": 0.0, "bf16": 0.0}
     by_e = _slots_by_expert(ids, row, max_m, toks)
     for i, (e, sl) in enumerate(sorted(by_e.items())):
-        a, a_s = gathered(e)
+        a_tok, a_s = gathered(e)
         w13, w13_s, w2, w2_s = weights(e)
         pos = np.array([p for p, _, _ in sl]); js = np.array([j for _, j, _ in sl])
         rows = np.array([r for _, _, r in sl])
-        assert np.array_equal(a[rows], xq[toks[pos]]) and np.array_equal(a_s[rows], xs[toks[pos]]), \
-            f"{what}: gathered x of expert {e}"
+        assert np.array_equal(a_tok[rows], toks[pos]) and np.array_equal(a_s[rows], xs[toks[pos]]), \
+            f"{what}: expert rows of expert {e}"
         gu, S1 = oracle.gemm_fp8_block(xq, xs, w13, w13_s, rows=toks[pos])
         x1 = fp8_mfma_extra(xq[toks[pos]], xs[toks[pos]], w13, w13_s)
         _check_g1(None if g1 is None else g1(e)[rows], gu, S1, f"{what}: GEMM1 of expert {e}", extra=x1)

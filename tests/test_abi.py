@@ -157,7 +157,7 @@ def test_moe_fp8_workspace_layout_and_expert_limit():
     d = _desc(precision=mxg.MXG_MOE_FP8_BLOCK128, max_m=241)
     assert L.moe_expert_forward_workspace_layout(ctypes.byref(d), off) == mxg.MXG_OK
     rows = 256 * 241
-    assert off[1] - off[0] >= rows * 7168                       # e4m3 activations
+    assert off[1] - off[0] >= rows * 4                          # the token of each expert row
     assert off[2] - off[1] >= 256 * (7168 // 128) * 244 * 4      # transposed scales, stride 244
     assert off[3] - off[2] >= (rows + 1) * 2048 * 2              # h plus the scratch row
     assert off[5] - off[4] >= rows * 7168 * 4
@@ -169,11 +169,15 @@ def test_moe_fp8_workspace_layout_and_expert_limit():
     for E, want in ((1024, mxg.MXG_OK), (1025, mxg.MXG_ERR_UNSUPPORTED)):
         d = _desc(precision=mxg.MXG_MOE_FP8_BLOCK128, E=E)
         assert L.moe_expert_forward_workspace_layout(ctypes.byref(d), off) == want, E
-    # an expert's h rows (4 * max_m * I bytes with both planes) stay below 2^32
+    # an expert's h rows (4 * max_m * I bytes with both planes) and the token rows of x
+    # (T * H bytes) stay below 2^32
     for mm, want in ((524287, mxg.MXG_OK), (524288, mxg.MXG_ERR_UNSUPPORTED)):
         for prec in (mxg.MXG_MOE_FP8_BLOCK128, mxg.MXG_MOE_FP8_BLOCK128_F32H):
             d = _desc(precision=prec, max_m=mm)
             assert L.moe_expert_forward_workspace_layout(ctypes.byref(d), off) == want, (mm, prec)
+    for T, want in ((599186, mxg.MXG_OK), (599187, mxg.MXG_ERR_UNSUPPORTED)):  # 2^32 / 7168 = 599186.3
+        d = _desc(precision=mxg.MXG_MOE_FP8_BLOCK128, T=T)
+        assert L.moe_expert_forward_workspace_layout(ctypes.byref(d), off) == want, T
 
 
 def test_moe_workspace_layout_and_rejects():

@@ -182,7 +182,7 @@ def _run_fp8(T, H, I, seed, n_check, n_deep=0, vary_w2_scales=False, f32h=False,
     assert torch.equal(y.view(torch.int16), y1.view(torch.int16)), "two runs differ"
     assert torch.equal(y.view(torch.int16), y_dbg.view(torch.int16)), "timed run differs from debug run"
     cap_s = (max_m + 3) // 4 * 4  # the row scales are stored transposed: [E, H/128, cap_s]
-    ga = _region(ws, off, 0, (max_m, H))
+    gtok = _region(ws, off, 0, (max_m,), torch.int32)
     gs_t = _region(ws, off, 1, (H // 128, cap_s), torch.float32)
     hp = _region(ws, off, 2, (max_m, planes * I), torch.int16)
     og = _region(ws, off, 4, (max_m, H), torch.float32)
@@ -192,7 +192,7 @@ def _run_fp8(T, H, I, seed, n_check, n_deep=0, vary_w2_scales=False, f32h=False,
     check_fp8_layer(
         xq=np_(t["xq"]), xs=np_(t["xs"]), ids=np_(ids), w=np_(w), row=row_h, max_m=max_m, I=I,
         weights=_cached(lambda e: (np_(t["w13"][e]), np_(t["w13_s"][e]), np_(t["w2"][e]), np_(t["w2_s"][e]))),
-        gathered=lambda e: (ga(e), np.ascontiguousarray(gs_t(e)[:, :max_m].T)),
+        gathered=lambda e: (gtok(e), np.ascontiguousarray(gs_t(e)[:, :max_m].T)),
         h_planes=lambda e: hp(e).view(np.uint16), y_bits=bf16_tensor_bits(y), toks=toks,
         what=f"FP8{' hi/lo h' if f32h else ''} T={T} H={H}", f32h=f32h, o_gpu=og, e2e_tokens=e2e,
         g1=lambda e: np_(dbg_g1[e]))
