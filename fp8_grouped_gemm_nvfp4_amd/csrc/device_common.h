@@ -33,12 +33,15 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
   return mag == 0x7Fu ? __uint_as_float(0x7FC00000u) : v;
 }
 
-// fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
+// fp32 -> bf16 bits, round to nearest even; a NaN becomes the quiet NaN with the upper
+// half of its bits (u >> 16 | 0x40).  gfx950's v_cvt_pk_bf16_f32 does exactly this: it
+// matched that bit-level definition on every one of the 2^32 fp32 inputs.
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return ((u >> 16) | 0x40u) & 0xFFFFu;
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
+}
+// Two values in one instruction: lo in bits 0..15, hi in bits 16..31.
+__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)lo, (__bf16)hi});
 }
 
 // Round a fp32 value to the nearest finite e4m3fn code (ties to even mantissa),

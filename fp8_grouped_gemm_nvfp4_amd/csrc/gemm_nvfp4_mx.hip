@@ -327,10 +327,10 @@ __global__ __launch_bounds__(mx::THREADS) void k_gemm_nvfp4_mx(const MxGemmArgs 
 #pragma unroll
           for (int n = 0; n < NB; n += 2) {
             const float4_t v0 = acc[i][n] * it.alpha, v1 = acc[i][n + 1] * it.alpha;
-            const uint32_t a0 = f32_to_bf16_rne(v0[0]) | (f32_to_bf16_rne(v0[1]) << 16);
-            const uint32_t a1 = f32_to_bf16_rne(v0[2]) | (f32_to_bf16_rne(v0[3]) << 16);
-            const uint32_t b0 = f32_to_bf16_rne(v1[0]) | (f32_to_bf16_rne(v1[1]) << 16);
-            const uint32_t b1 = f32_to_bf16_rne(v1[2]) | (f32_to_bf16_rne(v1[3]) << 16);
+            const uint32_t a0 = bf16x2_rne(v0[0], v0[1]);
+            const uint32_t a1 = bf16x2_rne(v0[2], v0[3]);
+            const uint32_t b0 = bf16x2_rne(v1[0], v1[1]);
+            const uint32_t b1 = bf16x2_rne(v1[2], v1[3]);
             const uint32_t s0 = __shfl_xor(odd ? a0 : b0, 16), s1 = __shfl_xor(odd ? a1 : b1, 16);
             const u32x4_t w = odd ? u32x4_t{s0, s1, b0, b1} : u32x4_t{a0, a1, s0, s1};
             const int c = it.n0 + 64 * wn + 16 * (n + (odd ? 1 : 0)) + 8 * (q >> 1);

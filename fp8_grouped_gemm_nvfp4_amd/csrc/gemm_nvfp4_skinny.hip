@@ -404,8 +404,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_nvfp4_skinny(const MaskedGe
             for (int r = 0; r < 4; r++) v[r] = alpha * acc[i][r];
             if (n + 4 <= p.N && (p.N & 3) == 0) {
               if constexpr (EPI == EPI_BF16) {
-                uint32_t lo = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
-                uint32_t hi = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
+                uint32_t lo = bf16x2_rne(v[0], v[1]);
+                uint32_t hi = bf16x2_rne(v[2], v[3]);
                 *(u32x2_t*)((uint16_t*)p.out + orow * p.N + n) = u32x2_t{lo, hi};
               } else {
                 *(float4_t*)((float*)p.out + orow * p.N + n) = float4_t{v[0], v[1], v[2], v[3]};

@@ -529,8 +529,8 @@ __global__ __launch_bounds__(ns::THREADS) void k_gemm_nvfp4_stream(const typenam
               const float4_t v = acc[i][n] * alpha;
               if (!ok) continue;
               if constexpr (EPI == EPI_BF16) {
-                const uint32_t lo = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
-                const uint32_t hi = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
+                const uint32_t lo = bf16x2_rne(v[0], v[1]);
+                const uint32_t hi = bf16x2_rne(v[2], v[3]);
                 *(u32x2_t*)((uint16_t*)obase + orow * ldo + col) = u32x2_t{lo, hi};
               } else {
                 *(float4_t*)((float*)obase + orow * ldo + col) = v;

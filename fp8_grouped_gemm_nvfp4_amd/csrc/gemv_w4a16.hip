@@ -177,8 +177,8 @@ __global__ __launch_bounds__(gv::THREADS) void k_gemv_w4a16(const GemvArgs p) {
           const size_t base = (size_t)m * N + c0;
           if (c0 + 4 <= N && (N & 3) == 0) {
             if constexpr (EPI == EPI_BF16) {
-              const uint32_t lo = f32_to_bf16_rne(o[0]) | (f32_to_bf16_rne(o[1]) << 16);
-              const uint32_t hi = f32_to_bf16_rne(o[2]) | (f32_to_bf16_rne(o[3]) << 16);
+              const uint32_t lo = bf16x2_rne(o[0], o[1]);
+              const uint32_t hi = bf16x2_rne(o[2], o[3]);
               *(u32x2_t*)((uint16_t*)p.out + base) = u32x2_t{lo, hi};
             } else {
               *(float4_t*)((float*)p.out + base) = float4_t{o[0], o[1], o[2], o[3]};

@@ -274,8 +274,8 @@ __global__ __launch_bounds__(256) void k_combine(const float* o, const int32_t* 
 #pragma unroll
     for (int i = 0; i < 4; i++) acc[i] = __builtin_fmaf(wj[j], v[j][i], acc[i]);
   }
-  uint32_t lo = f32_to_bf16_rne(acc[0]) | (f32_to_bf16_rne(acc[1]) << 16);
-  uint32_t hi = f32_to_bf16_rne(acc[2]) | (f32_to_bf16_rne(acc[3]) << 16);
+  uint32_t lo = bf16x2_rne(acc[0], acc[1]);
+  uint32_t hi = bf16x2_rne(acc[2], acc[3]);
   *(u32x2_t*)(y + (size_t)t * H + (size_t)q * 4) = u32x2_t{lo, hi};
 }
 
@@ -316,8 +316,8 @@ __global__ __launch_bounds__(256) void k_combine_wave(const float* __restrict__ 
 #pragma unroll
     for (int i = 0; i < 4; i++) acc[i] = __builtin_fmaf(wj[j], v[j][i], acc[i]);
   }
-  uint32_t lo = f32_to_bf16_rne(acc[0]) | (f32_to_bf16_rne(acc[1]) << 16);
-  uint32_t hi = f32_to_bf16_rne(acc[2]) | (f32_to_bf16_rne(acc[3]) << 16);
+  uint32_t lo = bf16x2_rne(acc[0], acc[1]);
+  uint32_t hi = bf16x2_rne(acc[2], acc[3]);
   *(u32x2_t*)(y + (size_t)t * H + (size_t)q * 4) = u32x2_t{lo, hi};
 }
 
