@@ -110,7 +110,7 @@ __global__ __launch_bounds__(f1::THREADS) void k_gemm_fp8_swiglu(const Fp8GemmAr
   const int G = p.G, K = p.K, KB = K / BK, N = p.N, I = N / 2, cap = p.max_m, capS = p.a_s_stride;
   const int tiles_n = I / HN;
 
-  stream_tile_prefix(p.masked_m, p.G, p.max_m, tprefix, mm_s, tid);
+  stream_tile_prefix(p.masked_m, p.G, p.max_m, tprefix, mm_s, tid, true);
   const int total = __builtin_amdgcn_readfirstlane(tprefix[G]) * tiles_n;
   const int grid = gridDim.x;
   const int bx = stream_bx();
@@ -118,7 +118,7 @@ __global__ __launch_bounds__(f1::THREADS) void k_gemm_fp8_swiglu(const Fp8GemmAr
   const int n_items = (total - 1 - bx) / grid + 1;
   const int nsteps = n_items * KB;
 
-  auto item_at = [&](int k) { return stream_item(bx + k * grid, tiles_n, G, tprefix, mm_s, HN); };
+  auto item_at = [&](int k) { return stream_item(bx + k * grid, tiles_n, G, tprefix, mm_s, HN, true); };
 
   if (wave >= MW) {
     // ======== data waves: activations two steps ahead, weights DB steps ahead ========
@@ -466,7 +466,7 @@ __global__ __launch_bounds__(f2::THREADS) void k_gemm_bf16_fp8w(const Fp8GemmArg
   const int G = p.G, K = p.K, WK = p.b_k ? p.b_k : p.K, KB = WK / 128, N = p.N, cap = p.max_m;
   const int tiles_n = N / BN, KT = K / BK, WKT = WK / BK;
 
-  stream_tile_prefix(p.masked_m, p.G, p.max_m, tprefix, mm_s, tid);
+  stream_tile_prefix(p.masked_m, p.G, p.max_m, tprefix, mm_s, tid, false);
   const int total = __builtin_amdgcn_readfirstlane(tprefix[G]) * tiles_n;
   const int grid = gridDim.x;
   const int bx = stream_bx();
@@ -474,7 +474,7 @@ __global__ __launch_bounds__(f2::THREADS) void k_gemm_bf16_fp8w(const Fp8GemmArg
   const int n_items = (total - 1 - bx) / grid + 1;
   const int nsteps = n_items * KT;
 
-  auto item_at = [&](int k) { return stream_item(bx + k * grid, tiles_n, G, tprefix, mm_s, BN); };
+  auto item_at = [&](int k) { return stream_item(bx + k * grid, tiles_n, G, tprefix, mm_s, BN, false); };
 
   // DMA sources: byte offsets from the item's expert base (below 2^32, checked by the host)
   uint32_t asrc[A_OPS];
