@@ -124,9 +124,9 @@ __global__ __launch_bounds__(ns::THREADS) void k_gemm_nvfp4_stream(const typenam
         }
       }
       __syncthreads();
-      stream_tile_prefix(p.masked_m, G, cap, tprefix, mm_s, tid, SWIGLU, rs_s);
+      stream_tile_prefix(p.masked_m, G, cap, tprefix, mm_s, tid, SWIGLU || p.K >= 4096, rs_s);
     } else {
-      stream_tile_prefix(p.masked_m, G, cap, tprefix, mm_s, tid, SWIGLU);
+      stream_tile_prefix(p.masked_m, G, cap, tprefix, mm_s, tid, SWIGLU || p.K >= 4096);
     }
     total = __builtin_amdgcn_readfirstlane(tprefix[G]) * tiles_n;
   }
@@ -173,7 +173,7 @@ __global__ __launch_bounds__(ns::THREADS) void k_gemm_nvfp4_stream(const typenam
   auto job_at = [&](int k) {
     NsJob j;
     if constexpr (MASKED) {
-      const StreamItem it = stream_item(bx + k * grid, tiles_n, G, tprefix, mm_s, ncols, SWIGLU);
+      const StreamItem it = stream_item(bx + k * grid, tiles_n, G, tprefix, mm_s, ncols, SWIGLU || p.K >= 4096);
       j.g = it.g; j.m0 = it.m0; j.mm = it.mm; j.n0 = it.n0; j.K = p.K;
       const size_t r0 = CONTIG ? (size_t)__builtin_amdgcn_readfirstlane(rs_s[it.g]) : (size_t)it.g * cap;
       j.a = p.a + r0 * (p.K / 2);

@@ -2,7 +2,7 @@
 // (gemm_fp8.hip, gemm_nvfp4_stream.hip).
 //
 // A work item is (group g, M tile of at most 256 rows, one N tile).  A group's tiles have
-// one height (stream_tile_rows; 256 rows, or balanced for the SwiGLU GEMMs).  Only M tiles
+// one height (stream_tile_rows; 256 rows, or balanced for the SwiGLU GEMMs and long K).  Only M tiles
 // that hold valid rows exist: their count per group comes from masked_m, and a prefix over
 // the groups
 // (in LDS) turns a linear unit index back into (g, M tile) by binary search.  Items are
@@ -25,8 +25,9 @@ struct StreamItem {
 // Height of a group's M tiles: STREAM_BM, or (balanced) the fewest tiles of at most
 // STREAM_BM rows, all of one height (a multiple of 16), so that a group just above a
 // multiple of STREAM_BM rows does not end in a small tile whose weight steps cost as much
-// as a full tile's.  Balanced tiles took GEMM1 of the T=8192 NVFP4 layer from 4.16 to
-// 4.06 ms, but GEMM2 (K = 2048) from 1.93 to 1.96 ms, so only the SwiGLU GEMMs use them.
+// as a full tile's.  Balanced tiles took GEMM1 of the T=8192 NVFP4 layer (K = 7168) from
+// 4.20 to 4.04 ms and the contiguous-layout GEMM1 from 3.69 to 3.51 ms, but GEMM2 (K = 2048)
+// from 1.93 to 1.96 ms, so the SwiGLU GEMMs and those with K >= 4096 use them.
 __device__ __forceinline__ int stream_tile_rows(int mm, bool balanced) {
   const int nt = (mm + STREAM_BM - 1) / STREAM_BM;
   return !balanced || nt <= 1 ? STREAM_BM : ((mm + nt - 1) / nt + 15) & ~15;
