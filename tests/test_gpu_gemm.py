@@ -160,6 +160,22 @@ def test_masked_gemm_item_transitions(out_dtype):
 
 
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_masked_gemm_balanced_tiles(out_dtype):
+    """K >= 4096: groups above 256 rows split into M tiles of one height (257 rows: 144 +
+    113; 600: 208 + 208 + 184; 3841: tiles of 256 and a last one of 1).  Every output
+    against the oracle, bit-identical across CU limits, and the rows past masked_m left
+    untouched."""
+    mm = [257, 300, 432, 511, 513, 600, 256, 3841, 0]
+    G, max_m, N, K = len(mm), 3856, 128, 4096
+    log(f"masked NVFP4 GEMM balanced M tiles G={G} max_m={max_m} N={N} K={K} {out_dtype}")
+    wl = datagen.masked_gemm_workload(37, DEV, G=G, max_m=max_m, N=N, K=K, masked_m=mm)
+    outs = [_run_masked(wl.tensors, max_m, N, out_dtype=out_dtype, cu_limit=cl) for cl in (3, 0)]
+    view = torch.int16 if out_dtype == torch.bfloat16 else torch.int32
+    assert torch.equal(outs[0].view(view), outs[1].view(view)), "result depends on the CU limit"
+    _check_masked(wl.tensors, outs[0], max_m, N, K, "balanced tiles")
+
+
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
 def test_masked_gemm_decode_many_groups(out_dtype):
     """Row capacity 8 with 256 groups (valid rows 0..8), an N tail inside a 16-column
     group, and the same bits whatever the grid."""
