@@ -404,7 +404,10 @@ hipError_t gemm_fp8_swiglu(Fp8GemmArgs p, int cu_limit, hipStream_t s) {
 // k it multiplies the sum by c_{k-1} / c_k, and the epilogue multiplies by the last c_k.
 // The sum equals sum_k c_k * P_k exactly up to those fp32 roundings (about three per
 // block), and the freed registers pay for twice the columns per item, which halves the
-// re-reads of h.  A block whose scale is zero contributes nothing and is skipped.
+// re-reads of h.  A block whose scale is zero contributes nothing and is skipped.  Row
+// groups past masked_m hold zeros and are neither rescaled nor computed.  The MFMA takes
+// the weights as its first operand, so it computes the transposed tile and each lane ends
+// with four consecutive output columns of one row (16-byte stores, no transposition).
 // Inside a step the K order is permuted identically on both operands (only the fp32
 // summation order changes): lane quarter q takes K 16q .. 16q + 15 of the step, the first
 // 8 in the first MFMA and the rest in the second, so that a lane's W2 bytes for the step
@@ -429,22 +432,6 @@ struct Cfg {
 // with this permutation (and f1_swz on the 128-byte h rows) the lanes of a pass hit 16
 // different slots of the 256-byte bank row.
 __device__ __forceinline__ int f2_swz_b(int r) { return (r >> 2) & 2; }
-
-// 4 x 4 transpose inside each quad of lanes: lane q's v[r] (row r, column q) becomes lane
-// r's element q, so that each lane ends up with four consecutive columns of one row.
-__device__ __forceinline__ float4_t quad_transpose(float4_t v, int lane) {
-  const int q = lane & 3;
-  const bool o1 = (q & 1) != 0, o2 = (q & 2) != 0;
-  const float s0 = o1 ? v[0] : v[1], s1 = o1 ? v[2] : v[3];
-  const float r0 = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(s0), 0xB1, 0xF, 0xF, false));
-  const float r1 = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(s1), 0xB1, 0xF, 0xF, false));
-  if (o1) { v[0] = r0; v[2] = r1; } else { v[1] = r0; v[3] = r1; }
-  const float t0 = o2 ? v[0] : v[2], t1 = o2 ? v[1] : v[3];
-  const float u0 = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(t0), 0x4E, 0xF, 0xF, false));
-  const float u1 = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(t1), 0x4E, 0xF, 0xF, false));
-  if (o2) { v[0] = u0; v[1] = u1; } else { v[2] = u0; v[3] = u1; }
-  return v;
-}
 
 template <int NBW, int DB>
 __global__ __launch_bounds__(f2::THREADS) void k_gemm_bf16_fp8w(const Fp8GemmArgs p) {
@@ -554,7 +541,7 @@ __global__ __launch_bounds__(f2::THREADS) void k_gemm_bf16_fp8w(const Fp8GemmArg
 
   // acc: the item's sums in units of the current block scale c_cur (0 before the first
   // block with a nonzero scale); between the end of an item and the next barrier, the
-  // item's results (scaled, transposed: one row of 4 columns per lane)
+  // item's results (scaled)
   float4_t acc[4][NBW];
 #pragma unroll
   for (int i = 0; i < 4; i++)
@@ -572,10 +559,10 @@ __global__ __launch_bounds__(f2::THREADS) void k_gemm_bf16_fp8w(const Fp8GemmArg
     float* O = (float*)p.out;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      const int row = pit.m0 + 16 * wm + 64 * i + 4 * q + (lane & 3);
+      const int row = pit.m0 + 16 * wm + 64 * i + rr;
 #pragma unroll
       for (int n = 0; n < NBW; n++) {
-        const int col = pit.n0 + WCOLS * wn + 16 * n + 4 * (rr >> 2);
+        const int col = pit.n0 + WCOLS * wn + 16 * n + 4 * q;
         if (row < pit.mm) *(float4_t*)(O + ((size_t)pit.g * cap + row) * N + col) = acc[i][n];
         acc[i][n] = float4_t{0.f, 0.f, 0.f, 0.f};
       }
@@ -604,11 +591,13 @@ __global__ __launch_bounds__(f2::THREADS) void k_gemm_bf16_fp8w(const Fp8GemmArg
         if (active && c_cur != 0.f && c_cur != ck) {
           const float r = c_cur / ck;
 #pragma unroll
-          for (int i = 0; i < 4; i++)
+          for (int i = 0; i < 4; i++) {
+            if (cit.m0 + 16 * wm + 64 * i >= cit.mm) break;  // masked row groups hold zeros
 #pragma unroll
             for (int n = 0; n < NBW; n++)
 #pragma unroll
               for (int e = 0; e < 4; e++) acc[i][n][e] *= r;
+          }
         }
         c_cur = ck;
       }
@@ -644,7 +633,7 @@ __global__ __launch_bounds__(f2::THREADS) void k_gemm_bf16_fp8w(const Fp8GemmArg
           if (cit.m0 + 16 * wm + 64 * i >= cit.mm) break;
 #pragma unroll
           for (int n = 0; n < NBW; n++)
-            acc[i][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[n], acc[i][n], 0, 0, 0);
+            acc[i][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[n], af[i], acc[i][n], 0, 0, 0);
         }
       }
     }
@@ -654,14 +643,13 @@ __global__ __launch_bounds__(f2::THREADS) void k_gemm_bf16_fp8w(const Fp8GemmArg
     if (++c_kt == KT) {
       if (active) {
 #pragma unroll
-        for (int i = 0; i < 4; i++)
+        for (int i = 0; i < 4; i++) {
+          if (cit.m0 + 16 * wm + 64 * i >= cit.mm) break;
 #pragma unroll
-          for (int n = 0; n < NBW; n++) {
-            float4_t v = acc[i][n];
+          for (int n = 0; n < NBW; n++)
 #pragma unroll
-            for (int e = 0; e < 4; e++) v[e] *= c_cur;
-            acc[i][n] = quad_transpose(v, lane);
-          }
+            for (int e = 0; e < 4; e++) acc[i][n][e] *= c_cur;
+        }
         pend = true;
         pit = cit;
       }
