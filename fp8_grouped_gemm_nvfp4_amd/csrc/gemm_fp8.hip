@@ -241,7 +241,7 @@ __global__ __launch_bounds__(f1::THREADS) void k_gemm_fp8_swiglu(const Fp8GemmAr
 
   StreamItem cit = item_at(0);
   int c_k = 0, c_kb = 0, c_sb = 0, c_sa = 0;
-  const int q = lane >> 4, rr = lane & 15, odd = lane & 1;
+  const int q = lane >> 4, rr = lane & 15;
 
   // h rows: with SPLIT they are 2I wide, hi = bf16(h) in columns [0, I), lo = bf16(h - hi)
   // in [I, 2I) (h - hi is exact in fp32, so hi + lo holds h to about 16 significant bits).
