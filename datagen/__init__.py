@@ -6,7 +6,7 @@ torch generators on the requested device, so the large weight sets of the MoE
 workloads are drawn directly in HBM; the oracle always receives the very same bytes
 (copied to the host), never a regenerated copy.
 
-Distributions (the workloads' recipes; see DESIGN.md "Inputs"):
+Distributions (the workloads' recipes):
   * NVFP4 operands: e2m1 codes i.i.d. uniform over all 16 codes (so each packed byte
     is uniform over 0..255), e4m3 block scales 2^u with u i.i.d. uniform in [-4, 4]
     (e4m3 byte (u + 7) << 3), fixed fp32 global scales.
